@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Forward implicit-GEMM conv benchmark on one MI355X.
+
+Step = one forward convolution of the headline workload, conv3d bf16 NDHWC
+N=1 C=2048 D=60 H=80 W=45, K=2048, 3x3x3, stride 1, pad 1 (GEMM
+216000 x 2048 x 55296, 4.892e13 flop), with x already resident in HBM in
+NDHWC and the filter packed once beforehand (it is a layer's constant).
+Throughput = 2*M*N*R / time (TFLOPS).
+
+Printed as ONE JSON line on stdout (everything else goes to stderr):
+  value          TFLOPS of the timed steps (W untimed warm-up steps first)
+  roofline       the conv kernel against dense bf16 MFMA peak, its duration
+                 taken with HIP events on the stream it is launched on
+  cpu_baseline   the fp64 CPU oracle timed on a bounded sample of the same
+                 workload's outputs, in the same unit
+  extra          the other workloads (fp8 kernel-only and end-to-end with
+                 amax + scales + pack, the 3x1x1 temporal variant, the
+                 point-output patch embed, the >2^31-element 3x1x1 conv)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # dense MFMA, MI355X published figures
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["implicit_gemm_convolution_conv_amd/csrc/conv_igemm.h",
+                  "implicit_gemm_convolution_conv_amd/csrc/conv_bf16.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv_igemm_c3_bf16_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def conv_flops(xshape, wshape, stride, pad, dil):
+    """2 * M * K * R, R = C*T*R*S, M = N*Do*Ho*Wo (padding taps included)."""
+    n, c, d, h, w = xshape
+    k, _, t, r, s = wshape
+    do = (d + 2 * pad[0] - dil[0] * (t - 1) - 1) // stride[0] + 1
+    ho = (h + 2 * pad[1] - dil[1] * (r - 1) - 1) // stride[1] + 1
+    wo = (w + 2 * pad[2] - dil[2] * (s - 1) - 1) // stride[2] + 1
+    return 2 * n * do * ho * wo * k * c * t * r * s
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def time_launches(fn, steps, warmup, torch):
+    """Run fn warmup times, then `steps` times with an event pair around each call
+    on the current stream (the one the library launches on). Returns (wall ms per
+    step, mean event ms per call)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ev = sum(a.elapsed_time(b) for a, b in evs) / steps
+    return wall, ev
+
+
+def bench_workload(name, steps, warmup, torch, B, I, PL):
+    """Returns a dict of timings for one workload (GPU tensors freed after)."""
+    wl = I.WORKLOADS[name]
+    x, w = I.make(wl, "cuda")
+    xshape, wshape = wl.x_shape, wl.w_shape
+    flops = conv_flops(xshape, wshape, wl.stride, wl.pad, wl.dil)
+    y = PL.output(xshape, wshape, wl.stride, wl.pad, wl.dil, "cuda")
+    res = {"workload": wl.note, "flop": flops}
+    if wl.dtype == "bf16":
+        if name == "c2":  # point output: x read as is (NCHW), filter in (c, r, s) order
+            wp = PL.packed_weight(w, "bf16", "NCDHW")
+            lay, xk = B.IGC_NCDHW, x
+        else:
+            wp = PL.packed_weight(w, "bf16", "NDHWC")
+            lay = B.IGC_NDHWC
+            xk = x if wl.x_layout == "NDHWC" else PL.packed_input(x, "bf16")
+        res["plan"] = B.conv_plan(xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay)
+
+        def step():
+            B.conv_fwd(xk, wp, y, xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay)
+
+        wall, ev = time_launches(step, steps, warmup, torch)
+        res.update(ms=wall, kernel_ms=ev, tflops=flops / (wall * 1e-3) / 1e12,
+                   kernel_tflops=flops / (ev * 1e-3) / 1e12)
+        if name != "c2" and wl.x_layout != "NDHWC":  # also the bf16 transpose that feeds it
+            xt = torch.empty((xshape[0],) + tuple(xshape[2:]) + (xshape[1],), dtype=torch.bfloat16, device="cuda")
+            _, ev_t = time_launches(lambda: B.conv_pack_x(x, xt, xshape, B.IGC_BF16), steps, warmup, torch)
+            nbytes = 4 * x.numel()
+            res.update(transpose_ms=ev_t, transpose_gbs=nbytes / (ev_t * 1e-3) / 1e9)
+            del xt
+    else:
+        scales = PL.fp8_scales(x, w)
+        wq = PL.packed_weight(w, "fp8", "NDHWC", scales[2:4])
+        n, c, d, h, wd = xshape
+        xq = torch.empty((n, d, h, wd, c), dtype=torch.uint8, device="cuda")
+        amax = torch.empty(1, dtype=torch.float32, device="cuda")
+        res["plan"] = B.conv_plan(xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_FP8_E4M3FN, B.IGC_NDHWC)
+
+        def prep():
+            B.conv_amax(x, x.numel(), amax)
+            B.conv_fp8_scales(amax, scales[0:2])
+            B.conv_pack_x(x, xq, xshape, B.IGC_FP8_E4M3FN, scales[0:2])
+
+        def conv():
+            B.conv_fwd(xq, wq, y, xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_FP8_E4M3FN, B.IGC_NDHWC, scales)
+
+        def e2e():
+            prep()
+            conv()
+
+        _, ev_k = time_launches(conv, steps, warmup, torch)
+        wall_e, ev_e = time_launches(e2e, steps, warmup, torch)
+        _, ev_p = time_launches(lambda: B.conv_pack_x(x, xq, xshape, B.IGC_FP8_E4M3FN, scales[0:2]), steps,
+                                warmup, torch)
+        _, ev_a = time_launches(lambda: B.conv_amax(x, x.numel(), amax), steps, warmup, torch)
+        res.update(kernel_ms=ev_k, kernel_tflops=flops / (ev_k * 1e-3) / 1e12, e2e_ms=ev_e,
+                   e2e_tflops=flops / (ev_e * 1e-3) / 1e12, pack_ms=ev_p,
+                   pack_gbs=3 * x.numel() / (ev_p * 1e-3) / 1e9, amax_ms=ev_a,
+                   amax_gbs=2 * x.numel() / (ev_a * 1e-3) / 1e9)
+        del xq, wq, scales
+    del x, w, y
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(seconds: float, I):
+    """The fp64 oracle on a bounded random sample of the headline workload's outputs."""
+    import numpy as np
+    import torch
+    from oracle import oracle as O
+
+    wl = I.WORKLOADS["c3"]
+    x, w = I.make(wl, "cuda")  # same seeded draw as the GPU run
+    xb, wb = I.bf16_bits(x), I.bf16_bits(w)
+    del x, w
+    torch.cuda.empty_cache()
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    O.set_threads(cores)
+    n, c, d, h, wd = wl.x_shape
+    k = wl.w_shape[0]
+    do, ho, wo = O.out_dims(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dil)
+    rng = np.random.default_rng(0)
+    R = wl.reduction
+
+    def run(npts):
+        pts = np.stack([rng.integers(0, m, npts) for m in (n, k, do, ho, wo)], 1)
+        t0 = time.perf_counter()
+        O.conv3d_points(xb, wb, pts, wl.stride, wl.pad, wl.dil, x_layout="NDHWC")
+        return time.perf_counter() - t0
+
+    npts = 8 * cores
+    t = run(npts)
+    while t < 0.5:
+        npts *= 4
+        t = run(npts)
+    npts = max(npts, int(npts * seconds / t))
+    t = run(npts)
+    return {"value": round(2.0 * R * npts / t / 1e12, 6), "unit": "TFLOPS", "cores": O.get_threads(),
+            "kind": "oracle",
+            "sample": f"{npts} random output elements of {wl.note} (each a {R}-term fp64 dot product), "
+                      f"{t:.1f} s"}
+
+
+def traffic_bytes():
+    """HBM bytes per launch of the conv kernel from committed counter runs, if taken on this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--only", default=None, help="comma list of extra workloads (c1,c2,c4,c4t,c5)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path (one process, one device).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from implicit_gemm_convolution_conv_amd import binding as B
+    from implicit_gemm_convolution_conv_amd import inputs as I
+    from implicit_gemm_convolution_conv_amd import pipeline as PL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    B.load()
+    torch.cuda.set_device(0)
+
+    log(f"[bench] headline c3 bf16, {args.steps} steps after {args.warmup} warm-up")
+    head = bench_workload("c3", args.steps, args.warmup, torch, B, I, PL)
+    log(f"[bench] c3: {head['ms']:.3f} ms/step, {head['tflops']:.1f} TFLOPS ({head['plan']})")
+
+    extra = {}
+    if not args.no_extra:
+        names = args.only.split(",") if args.only else ["c1", "c2", "c4", "c4t", "c5"]
+        for name in names:
+            log(f"[bench] extra workload {name}")
+            extra[name] = bench_workload(name, max(5, args.steps // 2), args.warmup, torch, B, I, PL)
+            log(f"[bench] {name}: {json.dumps(extra[name])}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (oracle), ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(args.cpu_seconds, I)
+        log(f"[bench] cpu: {cpu}")
+
+    achieved = head["kernel_tflops"]
+    out = {
+        "metric": "conv fwd TFLOPS + % of MFMA peak (bf16/fp8), c2048 3x3x3 D60xH80xW45",
+        "value": round(head["tflops"], 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; x ~ N(0,1), w ~ N(0, 1/sqrt(C*27)), bf16)",
+        "config": {"workload": "conv3d fwd bf16 NDHWC N=1 C=2048 D=60 H=80 W=45 K=2048 3x3x3 stride 1 pad 1",
+                   "gemm_m": 216000, "gemm_n": 2048, "reduction": 55296, "flop_per_step": head["flop"],
+                   "plan": head["plan"]},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+                     "traffic": traffic_bytes()},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

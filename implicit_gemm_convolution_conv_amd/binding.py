@@ -1,0 +1,154 @@
+"""ctypes binding over libigconv.so -- argument marshalling only.
+
+Every function has the name and the arguments of the C entry point it wraps
+(include/igconv.h). Tensors are torch tensors on the GPU (their data pointer
+is passed); shapes, strides, pads and dilations are Python sequences; stream
+defaults to torch's current stream on the tensor's device. A non-zero status
+raises IgcError with the library's message. Nothing here computes: all work
+runs in the library's HIP kernels.
+
+The library must have been built (``python -m implicit_gemm_convolution_conv_amd.build``);
+there is no other implementation to fall back to.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libigconv.so")
+
+IGC_OK = 0
+IGC_ERR_INVALID, IGC_ERR_UNSUPPORTED, IGC_ERR_ALIGN, IGC_ERR_HIP = -1, -2, -3, -4
+IGC_BF16, IGC_FP8_E4M3FN = 0, 1
+IGC_NCDHW, IGC_NDHWC = 0, 1
+IGC_PATH_AUTO, IGC_PATH_GENERIC, IGC_PATH_TEMPORAL, IGC_PATH_POINT = 0, 1, 2, 3
+
+EXPORTS = ("conv_out_dims", "conv_packed_w_cols", "conv_amax", "conv_fp8_scales", "conv_pack_x", "conv_pack_w",
+           "conv_fwd", "conv_plan", "conv_debug_force", "conv_last_error")
+
+
+class IgcError(RuntimeError):
+    def __init__(self, func: str, status: int, msg: str):
+        super().__init__(f"{func} failed with status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library once (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m implicit_gemm_convolution_conv_amd.build`")
+        lib = ctypes.CDLL(path)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.conv_out_dims.argtypes = [P, P, P, P, P, P]
+        lib.conv_packed_w_cols.argtypes = [P, I32]
+        lib.conv_packed_w_cols.restype = I64
+        lib.conv_amax.argtypes = [P, I64, P, P]
+        lib.conv_fp8_scales.argtypes = [P, P, P]
+        lib.conv_pack_x.argtypes = [P, P, P, I32, P, P]
+        lib.conv_pack_w.argtypes = [P, P, P, I32, I32, P, P]
+        lib.conv_fwd.argtypes = [P, P, P, P, P, P, P, P, I32, I32, P, P]
+        lib.conv_plan.argtypes = [P, P, P, P, P, I32, I32, ctypes.c_char_p, ctypes.c_size_t]
+        lib.conv_debug_force.argtypes = [I32, I32]
+        lib.conv_last_error.restype = ctypes.c_char_p
+        for name in EXPORTS:
+            if name not in ("conv_packed_w_cols", "conv_last_error"):
+                getattr(lib, name).restype = I32
+        _lib = lib
+    return _lib
+
+
+def _check(func: str, status: int) -> None:
+    if status != IGC_OK:
+        raise IgcError(func, status, conv_last_error())
+
+
+def _i64(v, n):
+    v = tuple(int(a) for a in v)
+    if len(v) != n:
+        raise ValueError(f"expected {n} values, got {v}")
+    return (ctypes.c_int64 * n)(*v)
+
+
+def _i32(v):
+    v = tuple(int(a) for a in v)
+    if len(v) != 3:
+        raise ValueError(f"expected 3 values, got {v}")
+    return (ctypes.c_int32 * 3)(*v)
+
+
+def _dev(t) -> int:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must live in GPU memory")
+    return t.data_ptr()
+
+
+def _stream(stream, t) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+
+
+def conv_out_dims(xshape, wshape, stride, pad, dilation):
+    out = (ctypes.c_int64 * 3)()
+    _check("conv_out_dims", load().conv_out_dims(_i64(xshape, 5), _i64(wshape, 5), _i32(stride), _i32(pad),
+                                                 _i32(dilation), out))
+    return tuple(out)
+
+
+def conv_packed_w_cols(wshape, dtype) -> int:
+    v = load().conv_packed_w_cols(_i64(wshape, 5), int(dtype))
+    if v <= 0:
+        raise IgcError("conv_packed_w_cols", int(v), "bad filter shape or dtype")
+    return int(v)
+
+
+def conv_amax(t_bf16, numel, amax_dev, stream=None):
+    _check("conv_amax", load().conv_amax(_dev(t_bf16), int(numel), _dev(amax_dev), _stream(stream, t_bf16)))
+
+
+def conv_fp8_scales(amax_dev, scale_pair_dev, stream=None):
+    _check("conv_fp8_scales", load().conv_fp8_scales(_dev(amax_dev), _dev(scale_pair_dev),
+                                                     _stream(stream, amax_dev)))
+
+
+def conv_pack_x(x_ncdhw_bf16, x_out, xshape, dtype, scale_pair_dev=None, stream=None):
+    _check("conv_pack_x", load().conv_pack_x(_dev(x_ncdhw_bf16), _dev(x_out), _i64(xshape, 5), int(dtype),
+                                             _dev(scale_pair_dev), _stream(stream, x_out)))
+
+
+def conv_pack_w(w_kctrs_bf16, w_packed, wshape, dtype, x_layout, scale_pair_dev=None, stream=None):
+    _check("conv_pack_w", load().conv_pack_w(_dev(w_kctrs_bf16), _dev(w_packed), _i64(wshape, 5), int(dtype),
+                                             int(x_layout), _dev(scale_pair_dev), _stream(stream, w_packed)))
+
+
+def conv_fwd(x, w_packed, y, xshape, wshape, stride, pad, dilation, dtype, x_layout, scales_dev=None, stream=None):
+    _check("conv_fwd", load().conv_fwd(_dev(x), _dev(w_packed), _dev(y), _i64(xshape, 5), _i64(wshape, 5),
+                                       _i32(stride), _i32(pad), _i32(dilation), int(dtype), int(x_layout),
+                                       _dev(scales_dev), _stream(stream, y)))
+
+
+def conv_plan(xshape, wshape, stride, pad, dilation, dtype, x_layout) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check("conv_plan", load().conv_plan(_i64(xshape, 5), _i64(wshape, 5), _i32(stride), _i32(pad),
+                                         _i32(dilation), int(dtype), int(x_layout), buf, 256))
+    return buf.value.decode()
+
+
+def conv_debug_force(path, tile):
+    _check("conv_debug_force", load().conv_debug_force(int(path), int(tile)))
+
+
+def conv_last_error() -> str:
+    return load().conv_last_error().decode()

@@ -1,0 +1,398 @@
+// C-ABI entry points: validation, path and tile selection, launch.
+//
+// Nothing here allocates device memory or synchronises; every launch goes to
+// the caller's stream. Validation finishes before the first launch, so an
+// error return leaves the stream untouched.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "igconv.h"
+#include "igconv_internal.h"
+
+namespace igc {
+hipError_t launch_conv_bf16(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream);
+hipError_t launch_conv_fp8(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream);
+
+hipError_t launch_conv(const ConvParams &p, int tile, Mode mode, Dtype dt, bool big, bool cblock,
+                       hipStream_t stream)
+{
+    return dt == DT_FP8 ? launch_conv_fp8(p, tile, mode, big, cblock, stream)
+                        : launch_conv_bf16(p, tile, mode, big, cblock, stream);
+}
+}  // namespace igc
+
+namespace {
+
+using namespace igc;
+
+thread_local std::string g_err;
+std::atomic<int> g_force_path{IGC_PATH_AUTO};
+std::atomic<int> g_force_tile{-1};
+
+constexpr int64_t kI32Max = 2147483647;
+// Element offsets up to this bound use 32-bit arithmetic in the conv kernel;
+// larger tensors switch to 64-bit offsets (invalid im2col taps may compute an
+// offset up to one tensor beyond the valid range before being masked).
+constexpr int64_t kSmallTensor = int64_t(1) << 30;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok()
+{
+    g_err.clear();
+    return IGC_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Geometry {
+    int64_t N, C, D, H, W, K, T, R, S;
+    int64_t sd, sh, sw, pd, ph, pw, dd, dh, dw;
+    int64_t Do, Ho, Wo;
+};
+
+int check_geometry(const int64_t *xs, const int64_t *ws, const int32_t *st, const int32_t *pad,
+                   const int32_t *dil, Geometry &g)
+{
+    if (!xs || !ws || !st || !pad || !dil)
+        return fail(IGC_ERR_INVALID, "null shape/stride/pad/dilation array");
+    g.N = xs[0]; g.C = xs[1]; g.D = xs[2]; g.H = xs[3]; g.W = xs[4];
+    g.K = ws[0]; g.T = ws[2]; g.R = ws[3]; g.S = ws[4];
+    for (int i = 0; i < 5; ++i) {
+        if (xs[i] < 1 || xs[i] > kI32Max)
+            return fail(IGC_ERR_INVALID, "xshape[%d] = %lld must be in [1, 2^31)", i, (long long)xs[i]);
+        if (ws[i] < 1 || ws[i] > kI32Max)
+            return fail(IGC_ERR_INVALID, "wshape[%d] = %lld must be in [1, 2^31)", i, (long long)ws[i]);
+    }
+    if (ws[1] != xs[1])
+        return fail(IGC_ERR_INVALID, "channel mismatch: x has C=%lld, w has C=%lld", (long long)xs[1],
+                    (long long)ws[1]);
+    for (int i = 0; i < 3; ++i) {
+        if (st[i] < 1)
+            return fail(IGC_ERR_INVALID, "stride[%d] = %d must be >= 1", i, st[i]);
+        if (dil[i] < 1)
+            return fail(IGC_ERR_INVALID, "dilation[%d] = %d must be >= 1", i, dil[i]);
+        if (pad[i] < 0)
+            return fail(IGC_ERR_INVALID, "pad[%d] = %d must be >= 0", i, pad[i]);
+    }
+    g.sd = st[0]; g.sh = st[1]; g.sw = st[2];
+    g.pd = pad[0]; g.ph = pad[1]; g.pw = pad[2];
+    g.dd = dil[0]; g.dh = dil[1]; g.dw = dil[2];
+    const int64_t ed = g.D + 2 * g.pd - g.dd * (g.T - 1) - 1;
+    const int64_t eh = g.H + 2 * g.ph - g.dh * (g.R - 1) - 1;
+    const int64_t ew = g.W + 2 * g.pw - g.dw * (g.S - 1) - 1;
+    if (ed < 0 || eh < 0 || ew < 0)
+        return fail(IGC_ERR_INVALID, "filter (dilated) does not fit the padded input");
+    g.Do = ed / g.sd + 1;
+    g.Ho = eh / g.sh + 1;
+    g.Wo = ew / g.sw + 1;
+    return IGC_OK;
+}
+
+int64_t packed_cols(int64_t rk, int dtype) { return (rk + (dtype == IGC_FP8_E4M3FN ? 127 : 63)) / (dtype == IGC_FP8_E4M3FN ? 128 : 64) * (dtype == IGC_FP8_E4M3FN ? 128 : 64); }
+
+struct Plan {
+    int path;  // IGC_PATH_*
+    int tile;
+    bool big, cblock;
+    ConvParams p;
+};
+
+// Point output (MIOpen PR #10912): stride irrelevant once the input extent
+// equals the filter extent with no padding and unit dilation -- one output
+// position per image, a plain GEMM over the batch.
+bool is_point(const Geometry &g)
+{
+    return g.pd == 0 && g.ph == 0 && g.pw == 0 && g.dd == 1 && g.dh == 1 && g.dw == 1 && g.D == g.T &&
+           g.H == g.R && g.W == g.S;
+}
+
+// Temporal-only filter (FlyDSL PR #860, 3x1x1 fast decode): the (h, w) index
+// of an output position is its input index, only the time axis has taps.
+bool is_temporal(const Geometry &g)
+{
+    return g.R == 1 && g.S == 1 && g.ph == 0 && g.pw == 0 && g.sh == 1 && g.sw == 1;
+}
+
+int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int32_t *pad, const int32_t *dil,
+              int dtype, int x_layout, Plan &pl)
+{
+    Geometry g;
+    int rc = check_geometry(xs, ws, st, pad, dil, g);
+    if (rc)
+        return rc;
+    if (dtype != IGC_BF16 && dtype != IGC_FP8_E4M3FN)
+        return fail(IGC_ERR_INVALID, "dtype %d is neither IGC_BF16 nor IGC_FP8_E4M3FN", dtype);
+    if (x_layout != IGC_NCDHW && x_layout != IGC_NDHWC)
+        return fail(IGC_ERR_INVALID, "x_layout %d is neither IGC_NCDHW nor IGC_NDHWC", x_layout);
+    const int esz = dtype == IGC_FP8_E4M3FN ? 1 : 2;
+    const int chunk = 16 / esz;
+    const int tke = 8 * chunk;
+
+    const int forced = g_force_path.load();
+    int path;
+    if (forced == IGC_PATH_AUTO) {
+        path = is_point(g) ? IGC_PATH_POINT : (is_temporal(g) ? IGC_PATH_TEMPORAL : IGC_PATH_GENERIC);
+    } else {
+        path = forced;
+        if (path == IGC_PATH_POINT && !is_point(g))
+            return fail(IGC_ERR_UNSUPPORTED, "forced point-output path does not apply to this shape");
+        if (path == IGC_PATH_TEMPORAL && !is_temporal(g))
+            return fail(IGC_ERR_UNSUPPORTED, "forced temporal path needs a Tx1x1 filter, h/w stride 1, pad 0");
+        if (path < IGC_PATH_GENERIC || path > IGC_PATH_POINT)
+            return fail(IGC_ERR_INVALID, "forced path %d unknown", path);
+    }
+
+    const int64_t rk = g.C * g.T * g.R * g.S;
+    const int64_t ldw = packed_cols(rk, dtype);
+    const int64_t P = g.Do * g.Ho * g.Wo;
+    const int64_t xnum = g.N * g.C * g.D * g.H * g.W;
+    const int64_t ynum = g.N * g.K * P;
+    if (rk > kI32Max - 256 || ldw * g.K / g.K != ldw)
+        return fail(IGC_ERR_UNSUPPORTED, "reduction length C*T*R*S = %lld too large", (long long)rk);
+    if (g.K * ldw * esz >= (int64_t(1) << 32))
+        return fail(IGC_ERR_UNSUPPORTED, "packed filter of %lld bytes exceeds 2^32", (long long)(g.K * ldw * esz));
+
+    ConvParams &p = pl.p;
+    p = ConvParams{};
+    p.N = (int)g.N; p.C = (int)g.C; p.D = (int)g.D; p.H = (int)g.H; p.W = (int)g.W;
+    p.K = (int)g.K; p.T = (int)g.T; p.R = (int)g.R; p.S = (int)g.S;
+    p.sd = (int)g.sd; p.sh = (int)g.sh; p.sw = (int)g.sw;
+    p.pd = (int)g.pd; p.ph = (int)g.ph; p.pw = (int)g.pw;
+    p.dd = (int)g.dd; p.dh = (int)g.dh; p.dw = (int)g.dw;
+    p.Do = (int)g.Do; p.Ho = (int)g.Ho; p.Wo = (int)g.Wo;
+    p.Rk = (int)rk;
+    p.ldw = (int)ldw;
+
+    if (path == IGC_PATH_POINT) {
+        if ((rk * esz) % 4 != 0)
+            return fail(IGC_ERR_UNSUPPORTED, "point-output path needs image rows of a multiple of 4 bytes (C*T*R*S*%d = %lld)",
+                        esz, (long long)(rk * esz));
+        p.P = 1;
+        p.M = (int)g.K;
+        p.Ncol = (int)g.N;
+        p.nk = (int)(ldw / tke);
+        pl.cblock = false;
+    } else {
+        if (x_layout != IGC_NDHWC)
+            return fail(IGC_ERR_UNSUPPORTED, "im2col paths need NDHWC activations (pack them with conv_pack_x)");
+        if (g.C % chunk != 0)
+            return fail(IGC_ERR_UNSUPPORTED, "im2col paths need C %% %d == 0 for %s (C = %lld)", chunk,
+                        esz == 1 ? "fp8" : "bf16", (long long)g.C);
+        const int64_t M = g.N * P;
+        if (M > kI32Max || P > kI32Max)
+            return fail(IGC_ERR_UNSUPPORTED, "output rows N*Do*Ho*Wo = %lld exceed 2^31", (long long)M);
+        p.P = (int)P;
+        p.M = (int)M;
+        p.Ncol = (int)g.K;
+        pl.cblock = (g.C % tke) == 0;
+        p.nk = pl.cblock ? (int)(g.T * g.R * g.S * (g.C / tke)) : (int)(ldw / tke);
+    }
+    pl.path = path;
+    pl.big = xnum > kSmallTensor || ynum > kSmallTensor;
+
+    // Tile: the largest whose grid still covers the 256 CUs at least twice
+    // (256x256) or once (128x128), else 64x64.
+    auto nblocks = [&](int t) {
+        return ((int64_t)p.M + kTiles[t].bm - 1) / kTiles[t].bm * (((int64_t)p.Ncol + kTiles[t].bn - 1) / kTiles[t].bn);
+    };
+    int tile = g_force_tile.load();
+    if (tile < 0 || tile >= kNumTiles)
+        tile = nblocks(0) >= 512 ? 0 : (nblocks(1) >= 256 ? 1 : 2);
+    pl.tile = tile;
+    const TileShape ts = kTiles[tile];
+    const int64_t tm = ((int64_t)p.M + ts.bm - 1) / ts.bm, tn = ((int64_t)p.Ncol + ts.bn - 1) / ts.bn;
+    if (tm * tn > kI32Max)
+        return fail(IGC_ERR_UNSUPPORTED, "grid of %lld tiles too large", (long long)(tm * tn));
+    p.tiles_m = (int)tm;
+    p.tiles_n = (int)tn;
+    // Workgroups resident on one XCD (32 CUs): one 256x256 or two smaller tiles per CU.
+    const int resident = 32 * (tile == 0 ? 1 : 2);
+    p.group_m = (int)std::max<int64_t>(1, resident / tn);
+    return IGC_OK;
+}
+
+const char *path_name(int path)
+{
+    switch (path) {
+    case IGC_PATH_POINT: return "point";
+    case IGC_PATH_TEMPORAL: return "temporal";
+    default: return "generic";
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int conv_out_dims(const int64_t xshape[5], const int64_t wshape[5], const int32_t stride[3], const int32_t pad[3],
+                  const int32_t dilation[3], int64_t out_dhw[3])
+{
+    Geometry g;
+    int rc = check_geometry(xshape, wshape, stride, pad, dilation, g);
+    if (rc)
+        return rc;
+    if (!out_dhw)
+        return fail(IGC_ERR_INVALID, "null out_dhw");
+    out_dhw[0] = g.Do;
+    out_dhw[1] = g.Ho;
+    out_dhw[2] = g.Wo;
+    return ok();
+}
+
+int64_t conv_packed_w_cols(const int64_t wshape[5], int dtype)
+{
+    if (!wshape || (dtype != IGC_BF16 && dtype != IGC_FP8_E4M3FN))
+        return IGC_ERR_INVALID;
+    for (int i = 1; i < 5; ++i)
+        if (wshape[i] < 1 || wshape[i] > kI32Max)
+            return IGC_ERR_INVALID;
+    const int64_t rk = wshape[1] * wshape[2] * wshape[3] * wshape[4];
+    if (rk > kI32Max - 256)
+        return IGC_ERR_INVALID;
+    return packed_cols(rk, dtype);
+}
+
+int conv_amax(const void *t_bf16, int64_t numel, float *amax_dev, void *stream)
+{
+    if (!t_bf16 || !amax_dev)
+        return fail(IGC_ERR_INVALID, "conv_amax: null pointer");
+    if (numel < 1)
+        return fail(IGC_ERR_INVALID, "conv_amax: numel = %lld must be >= 1", (long long)numel);
+    if (!aligned16(t_bf16))
+        return fail(IGC_ERR_ALIGN, "conv_amax: tensor not 16-byte aligned");
+    if (launch_amax(static_cast<const uint16_t *>(t_bf16), numel, amax_dev, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return fail(IGC_ERR_HIP, "conv_amax: launch failed");
+    return ok();
+}
+
+int conv_fp8_scales(const float *amax_dev, float *scale_pair_dev, void *stream)
+{
+    if (!amax_dev || !scale_pair_dev)
+        return fail(IGC_ERR_INVALID, "conv_fp8_scales: null pointer");
+    if (launch_fp8_scales(amax_dev, scale_pair_dev, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return fail(IGC_ERR_HIP, "conv_fp8_scales: launch failed");
+    return ok();
+}
+
+int conv_pack_x(const void *x_ncdhw_bf16, void *x_out, const int64_t xshape[5], int dtype,
+                const float *scale_pair_dev, void *stream)
+{
+    if (!x_ncdhw_bf16 || !x_out || !xshape)
+        return fail(IGC_ERR_INVALID, "conv_pack_x: null pointer");
+    if (dtype != IGC_BF16 && dtype != IGC_FP8_E4M3FN)
+        return fail(IGC_ERR_INVALID, "conv_pack_x: bad dtype %d", dtype);
+    if (dtype == IGC_FP8_E4M3FN && !scale_pair_dev)
+        return fail(IGC_ERR_INVALID, "conv_pack_x: fp8 needs scale_pair_dev");
+    for (int i = 0; i < 5; ++i)
+        if (xshape[i] < 1 || xshape[i] > kI32Max)
+            return fail(IGC_ERR_INVALID, "conv_pack_x: xshape[%d] = %lld out of range", i, (long long)xshape[i]);
+    if (!aligned16(x_ncdhw_bf16) || !aligned16(x_out))
+        return fail(IGC_ERR_ALIGN, "conv_pack_x: tensors must be 16-byte aligned");
+    const int64_t C = xshape[1], S = xshape[2] * xshape[3] * xshape[4];
+    const int need = dtype == IGC_FP8_E4M3FN ? 16 : 8;
+    if (C % need != 0)
+        return fail(IGC_ERR_UNSUPPORTED, "conv_pack_x: needs C %% %d == 0 (C = %lld)", need, (long long)C);
+    const int64_t blocks = xshape[0] * ((C + 63) / 64) * ((S + 63) / 64);
+    if (blocks > kI32Max)
+        return fail(IGC_ERR_UNSUPPORTED, "conv_pack_x: tensor too large");
+    if (launch_pack_x(static_cast<const uint16_t *>(x_ncdhw_bf16), x_out, xshape[0], C, S,
+                      dtype == IGC_FP8_E4M3FN ? DT_FP8 : DT_BF16, scale_pair_dev,
+                      static_cast<hipStream_t>(stream)) != hipSuccess)
+        return fail(IGC_ERR_HIP, "conv_pack_x: launch failed");
+    return ok();
+}
+
+int conv_pack_w(const void *w_kctrs_bf16, void *w_packed, const int64_t wshape[5], int dtype, int x_layout,
+                const float *scale_pair_dev, void *stream)
+{
+    if (!w_kctrs_bf16 || !w_packed || !wshape)
+        return fail(IGC_ERR_INVALID, "conv_pack_w: null pointer");
+    if (dtype != IGC_BF16 && dtype != IGC_FP8_E4M3FN)
+        return fail(IGC_ERR_INVALID, "conv_pack_w: bad dtype %d", dtype);
+    if (x_layout != IGC_NCDHW && x_layout != IGC_NDHWC)
+        return fail(IGC_ERR_INVALID, "conv_pack_w: bad x_layout %d", x_layout);
+    if (dtype == IGC_FP8_E4M3FN && !scale_pair_dev)
+        return fail(IGC_ERR_INVALID, "conv_pack_w: fp8 needs scale_pair_dev");
+    for (int i = 0; i < 5; ++i)
+        if (wshape[i] < 1 || wshape[i] > kI32Max)
+            return fail(IGC_ERR_INVALID, "conv_pack_w: wshape[%d] = %lld out of range", i, (long long)wshape[i]);
+    if (!aligned16(w_kctrs_bf16) || !aligned16(w_packed))
+        return fail(IGC_ERR_ALIGN, "conv_pack_w: tensors must be 16-byte aligned");
+    const int64_t ldw = conv_packed_w_cols(wshape, dtype);
+    if (ldw <= 0)
+        return fail(IGC_ERR_INVALID, "conv_pack_w: reduction too large");
+    if (launch_pack_w(static_cast<const uint16_t *>(w_kctrs_bf16), w_packed, wshape[0], wshape[1], wshape[2],
+                      wshape[3], wshape[4], ldw, x_layout == IGC_NDHWC, dtype == IGC_FP8_E4M3FN ? DT_FP8 : DT_BF16,
+                      scale_pair_dev, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return fail(IGC_ERR_HIP, "conv_pack_w: launch failed");
+    return ok();
+}
+
+int conv_fwd(const void *x, const void *w_packed, void *y, const int64_t xshape[5], const int64_t wshape[5],
+             const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout,
+             const float *scales_dev, void *stream)
+{
+    Plan pl;
+    int rc = make_plan(xshape, wshape, stride, pad, dilation, dtype, x_layout, pl);
+    if (rc)
+        return rc;
+    if (!x || !w_packed || !y)
+        return fail(IGC_ERR_INVALID, "conv_fwd: null tensor pointer");
+    if (dtype == IGC_FP8_E4M3FN && !scales_dev)
+        return fail(IGC_ERR_INVALID, "conv_fwd: fp8 needs scales_dev = {s_x, inv_x, s_w, inv_w}");
+    if (!aligned16(x) || !aligned16(w_packed) || !aligned16(y))
+        return fail(IGC_ERR_ALIGN, "conv_fwd: x, w_packed and y must be 16-byte aligned");
+    pl.p.x = x;
+    pl.p.w = w_packed;
+    pl.p.y = y;
+    pl.p.scales = dtype == IGC_FP8_E4M3FN ? scales_dev : nullptr;
+    const Mode mode = pl.path == IGC_PATH_POINT ? MODE_POINT : (pl.path == IGC_PATH_TEMPORAL ? MODE_TEMPORAL : MODE_GENERIC);
+    if (launch_conv(pl.p, pl.tile, mode, dtype == IGC_FP8_E4M3FN ? DT_FP8 : DT_BF16, pl.big, pl.cblock,
+                    static_cast<hipStream_t>(stream)) != hipSuccess)
+        return fail(IGC_ERR_HIP, "conv_fwd: kernel launch failed");
+    return ok();
+}
+
+int conv_plan(const int64_t xshape[5], const int64_t wshape[5], const int32_t stride[3], const int32_t pad[3],
+              const int32_t dilation[3], int dtype, int x_layout, char *buf, size_t len)
+{
+    Plan pl;
+    int rc = make_plan(xshape, wshape, stride, pad, dilation, dtype, x_layout, pl);
+    if (rc)
+        return rc;
+    if (buf && len) {
+        const TileShape ts = kTiles[pl.tile];
+        snprintf(buf, len, "path=%s tile=%dx%d waves=%d kstep=%d order=%s big=%d grid=%d group_m=%d nk=%d",
+                 path_name(pl.path), ts.bm, ts.bn, ts.wm * ts.wn, dtype == IGC_FP8_E4M3FN ? 128 : 64,
+                 pl.cblock ? "cblock" : "linear", pl.big ? 1 : 0, pl.p.tiles_m * pl.p.tiles_n, pl.p.group_m, pl.p.nk);
+    }
+    return ok();
+}
+
+int conv_debug_force(int path, int tile)
+{
+    if (path < IGC_PATH_AUTO || path > IGC_PATH_POINT)
+        return fail(IGC_ERR_INVALID, "conv_debug_force: unknown path %d", path);
+    if (tile < -1 || tile >= kNumTiles)
+        return fail(IGC_ERR_INVALID, "conv_debug_force: tile %d not in [-1, %d)", tile, kNumTiles);
+    g_force_path.store(path);
+    g_force_tile.store(tile);
+    return ok();
+}
+
+const char *conv_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

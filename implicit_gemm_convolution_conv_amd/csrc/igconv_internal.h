@@ -1,0 +1,57 @@
+// Internal declarations shared by the host library and the kernel translation
+// units (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace igc {
+
+enum Mode { MODE_GENERIC = 0, MODE_TEMPORAL = 1, MODE_POINT = 2 };
+enum Dtype { DT_BF16 = 0, DT_FP8 = 1 };
+
+// Tile shapes (rows x cols of the GEMM tile, waves along rows x cols). The
+// reduction step is always 128 bytes of k per row: 64 bf16 or 128 fp8.
+struct TileShape {
+    int bm, bn, wm, wn;
+};
+constexpr int kNumTiles = 3;
+constexpr TileShape kTiles[kNumTiles] = {
+    {256, 256, 2, 4},  // 8 waves, 128x64 per wave: large grids
+    {128, 128, 2, 2},  // 4 waves, 64x64 per wave
+    {64, 64, 2, 2},    // 4 waves, 32x32 per wave: small grids
+};
+
+// Everything a conv kernel needs, passed by value as kernel arguments.
+struct ConvParams {
+    const void *x;          // activations (NDHWC for im2col modes; rows of the B operand for point mode)
+    const void *w;          // packed filter, K rows of ldw elements
+    void *y;                // bf16 NCDHW output
+    const float *scales;    // fp8: {s_x, inv_x, s_w, inv_w}; null for bf16
+    int N, C, D, H, W;
+    int K, T, R, S;
+    int sd, sh, sw, pd, ph, pw, dd, dh, dw;
+    int Do, Ho, Wo;
+    int P;                  // Do*Ho*Wo
+    int M;                  // GEMM rows   (im2col: N*P, point: K)
+    int Ncol;               // GEMM cols   (im2col: K,   point: N)
+    int Rk;                 // reduction length C*T*R*S
+    int ldw;                // packed filter row length (crs_pad)
+    int nk;                 // reduction steps
+    int tiles_m, tiles_n;   // grid of output tiles
+    int group_m;            // grouped raster height (tiles along M sharing an L2 working set)
+};
+
+// One launch of the implicit-GEMM kernel selected by (tile, mode, dtype,
+// 64-bit addressing, channel-block-outer reduction order).
+hipError_t launch_conv(const ConvParams &p, int tile, Mode mode, Dtype dt, bool big, bool cblock,
+                       hipStream_t stream);
+
+hipError_t launch_amax(const uint16_t *t, int64_t n, float *amax, hipStream_t stream);
+hipError_t launch_fp8_scales(const float *amax, float *pair, hipStream_t stream);
+hipError_t launch_pack_x(const uint16_t *x, void *out, int64_t N, int64_t C, int64_t S, Dtype dt,
+                         const float *pair, hipStream_t stream);
+hipError_t launch_pack_w(const uint16_t *w, void *out, int64_t K, int64_t C, int64_t T, int64_t R, int64_t S,
+                         int64_t ldw, bool channel_last, Dtype dt, const float *pair, hipStream_t stream);
+
+}  // namespace igc

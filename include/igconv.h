@@ -1,0 +1,174 @@
+/*
+ * igconv -- forward implicit-GEMM convolution for MI355X (gfx950), C ABI.
+ *
+ * What is computed. conv_fwd evaluates 3D forward convolution (a
+ * cross-correlation with zero padding, stride and dilation; 2D and 1D are the
+ * D = T = 1 and H = R = 1 special cases) as one implicit GEMM: rows
+ * M = N*Do*Ho*Wo output positions, columns = K output channels, reduction
+ * C*T*R*S over channel and filter tap, as described for the bf16 and fp8
+ * conv3d kernels of FlyDSL PR #860 ("[Kernel] fp8 conv3d: 8-wave GEMM
+ * pipeline + BIG_IN fix", PR summary and the commits on the async
+ * global->LDS pipeline, the temporal-only 3x1x1 decode, the vec4 epilogue
+ * and the large-tensor rebase). Point-output shapes (stride equal to the
+ * filter, zero padding, unit dilation, input extent equal to the filter
+ * extent, hence a 1x1x1 output) are one plain GEMM over the batch with no
+ * im2col, as in MIOpen PR #10912 (PR body; channel-last is valid because a
+ * batch slice of x and a row of w enumerate C*T*R*S in the same order).
+ *
+ *   y[n,k,od,oh,ow] = sum_{c,t,r,s} x[n,c,od*sd-pd+t*dd, oh*sh-ph+r*dh,
+ *                                      ow*sw-pw+s*dw] * w[k,c,t,r,s]
+ *   Do = (D + 2*pd - dd*(T-1) - 1)/sd + 1   (likewise Ho, Wo)
+ *
+ * Arithmetic: bf16 operands, or fp8 E4M3FN operands with one fp32 scale per
+ * tensor (s = amax/448); fp32 accumulation; y is bf16 (round to nearest even)
+ * of acc, or of acc * (s_x * s_w) for fp8.
+ *
+ * Conventions for every entry point:
+ *  - Shapes are plain arrays: xshape = {N, C, D, H, W} (logical, whatever the
+ *    memory layout), wshape = {K, C, T, R, S}; stride, pad, dilation =
+ *    {d, h, w}. 2D callers pass D = T = 1, pad_d = 0; 1D also H = R = 1.
+ *  - Every pointer argument named *_dev or a tensor (x, w, y, ...) is DEVICE
+ *    memory owned by the caller; the library allocates nothing, keeps no
+ *    pointer after the call returns, never synchronises and enqueues all work
+ *    on `stream` (a hipStream_t; NULL = the null stream) in call order.
+ *  - Tensors must be contiguous in the stated layout and 16-byte aligned.
+ *  - Return value: IGC_OK, or a negative status. All validation runs before any
+ *    GPU work: on error nothing is enqueued and conv_last_error() describes the
+ *    reason. IGC_ERR_HIP reports a failed kernel launch. No C++ exception
+ *    crosses this interface. All entry points are thread-safe; the error text
+ *    is per thread.
+ */
+#ifndef IGCONV_H
+#define IGCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define IGC_API __attribute__((visibility("default")))
+#else
+#define IGC_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status */
+#define IGC_OK 0
+#define IGC_ERR_INVALID (-1)     /* bad pointer, shape or argument */
+#define IGC_ERR_UNSUPPORTED (-2) /* valid convolution this library does not run */
+#define IGC_ERR_ALIGN (-3)       /* pointer not 16-byte aligned */
+#define IGC_ERR_HIP (-4)         /* HIP runtime error while enqueuing */
+
+/* operand type (dtype) */
+#define IGC_BF16 0
+#define IGC_FP8_E4M3FN 1
+
+/* activation memory layout (x_layout) */
+#define IGC_NCDHW 0
+#define IGC_NDHWC 1
+
+/* execution path reported by conv_plan / forced by conv_debug_force */
+#define IGC_PATH_AUTO 0
+#define IGC_PATH_GENERIC 1  /* im2col decode of every tap */
+#define IGC_PATH_TEMPORAL 2 /* T x 1 x 1 filter: one bounds check per row (time axis only) */
+#define IGC_PATH_POINT 3    /* point output: plain GEMM over the batch */
+
+/*
+ * Output extent {Do, Ho, Wo} by the formula above. Host only.
+ * IGC_ERR_INVALID when a size is non-positive, C differs between x and w, a
+ * stride or dilation is < 1, a pad is < 0, or the filter does not fit.
+ */
+IGC_API int conv_out_dims(const int64_t xshape[5], const int64_t wshape[5], const int32_t stride[3],
+                  const int32_t pad[3], const int32_t dilation[3], int64_t out_dhw[3]);
+
+/*
+ * Row length (elements) of the packed filter that conv_pack_w writes and
+ * conv_fwd reads: C*T*R*S rounded up to the reduction step (64 elements for
+ * bf16, 128 for fp8), the zero-padded "crs_pad" of FlyDSL PR #860 (commit
+ * generalising the 8-wave fp8 kernel to N-/K-partial and tiny-K shapes).
+ * The packed filter is K rows of this length. Host only. <= 0 on bad input.
+ */
+IGC_API int64_t conv_packed_w_cols(const int64_t wshape[5], int dtype);
+
+/*
+ * amax_dev[0] = max |t[i]| over `numel` bf16 values (exact; a NaN input makes
+ * it NaN). amax_dev: one device float, overwritten. numel >= 1.
+ * The per-tensor fp8 scale of each operand is derived from this maximum.
+ */
+IGC_API int conv_amax(const void *t_bf16, int64_t numel, float *amax_dev, void *stream);
+
+/*
+ * scale_pair_dev[0..1] = {s, inv} = {amax/448, 448/amax}, each a correctly
+ * rounded fp32 division of amax_dev[0]; {1, 1} when amax is 0.
+ * 448 is the largest finite E4M3FN value (FlyDSL PR #860 runs its fp8 kernel
+ * on E4M3FN operands, PR summary).
+ */
+IGC_API int conv_fp8_scales(const float *amax_dev, float *scale_pair_dev, void *stream);
+
+/*
+ * Activation pack: x (bf16, NCDHW) -> x_out in NDHWC, as bf16 (a pure
+ * transpose, bit-exact) or as fp8 E4M3FN codes q = E4M3FN(fp32(v * inv)),
+ * round to nearest even, saturating at +-448, inv = scale_pair_dev[1].
+ * This is the NCDHW->NDHWC transpose and the bf16->fp8 pack that FlyDSL
+ * PR #860 runs before its conv kernels (large-tensor rebase commit; the fp8
+ * kernel's tiled transpose). Requires C % 8 == 0 (bf16) or C % 16 == 0 (fp8).
+ * scale_pair_dev is ignored (may be NULL) for bf16. x and x_out must not
+ * overlap. Tensors above 2^31 elements are supported.
+ */
+IGC_API int conv_pack_x(const void *x_ncdhw_bf16, void *x_out, const int64_t xshape[5], int dtype,
+                const float *scale_pair_dev, void *stream);
+
+/*
+ * Filter pack: w (bf16, KCTRS) -> w_packed, K rows of conv_packed_w_cols()
+ * elements, columns zero-filled past C*T*R*S. Column order follows the
+ * activation layout conv_fwd will see: (t, r, s, c) with c fastest for
+ * x_layout = IGC_NDHWC, (c, t, r, s) for IGC_NCDHW (point-output only).
+ * fp8: codes of fp32(w * inv), inv = scale_pair_dev[1], as in conv_pack_x.
+ */
+IGC_API int conv_pack_w(const void *w_kctrs_bf16, void *w_packed, const int64_t wshape[5], int dtype, int x_layout,
+                const float *scale_pair_dev, void *stream);
+
+/*
+ * Forward convolution y = conv(x, w).
+ *  x        activations, dtype operands, layout x_layout. The im2col paths
+ *           (generic, temporal) need IGC_NDHWC with C % 8 == 0 (bf16) or
+ *           C % 16 == 0 (fp8); the point-output path takes either layout.
+ *  w_packed filter from conv_pack_w with the same dtype and x_layout.
+ *  y        bf16 output, NCDHW {N, K, Do, Ho, Wo}; every element is written.
+ *  scales_dev  fp8 only: device float[4] = {s_x, inv_x, s_w, inv_w} (the two
+ *           conv_fp8_scales pairs); y = bf16(acc * (s_x * s_w)). NULL for bf16.
+ * Output rows M = N*Do*Ho*Wo must be < 2^31; x, y above 2^31 elements are
+ * addressed with 64-bit offsets. Returns IGC_ERR_UNSUPPORTED for a shape no
+ * path accepts (the message says which requirement failed).
+ */
+IGC_API int conv_fwd(const void *x, const void *w_packed, void *y, const int64_t xshape[5], const int64_t wshape[5],
+             const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout,
+             const float *scales_dev, void *stream);
+
+/*
+ * Describe, without running anything, the path and tile conv_fwd would use
+ * for these arguments: writes a one-line text such as
+ * "path=generic tile=256x256 waves=8 kstep=64 order=cblock big=0 grid=6752"
+ * into buf (NUL-terminated, truncated to len). Same validation and return
+ * codes as conv_fwd. Host only.
+ */
+IGC_API int conv_plan(const int64_t xshape[5], const int64_t wshape[5], const int32_t stride[3], const int32_t pad[3],
+              const int32_t dilation[3], int dtype, int x_layout, char *buf, size_t len);
+
+/*
+ * Testing hook: force the path (IGC_PATH_*) and/or the tile index (-1 = automatic)
+ * for later conv_fwd / conv_plan calls of this process. A forced path that
+ * does not apply to a shape makes conv_fwd return IGC_ERR_UNSUPPORTED.
+ */
+IGC_API int conv_debug_force(int path, int tile);
+
+/* Text of the last error on this thread ("" if none). Valid until the next call. */
+IGC_API const char *conv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IGCONV_H */

@@ -1,0 +1,122 @@
+"""C-ABI library: loads, exports every declared symbol, host-side logic (no GPU work)."""
+
+import os
+import re
+
+import pytest
+
+from implicit_gemm_convolution_conv_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "igconv.h")).read()
+    return sorted(set(re.findall(r"IGC_API\s+[\w\s\*]*?\b(conv_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_header_constants_match_binding():
+    text = open(os.path.join(ROOT, "include", "igconv.h")).read()
+    consts = dict(re.findall(r"#define (IGC_\w+)\s+\(?(-?\d+)\)?", text))
+    for name, value in consts.items():
+        assert getattr(B, name) == int(value), name
+
+
+@pytest.mark.parametrize("geom", [
+    ((2, 3, 4, 5, 6), (2, 3, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),
+    ((1, 3, 5, 4, 7), (4, 3, 2, 3, 1), (1, 2, 1), (0, 1, 0), (1, 1, 1)),
+    ((2, 2, 6, 7, 5), (3, 2, 3, 2, 3), (2, 1, 2), (2, 0, 1), (1, 2, 1)),
+    ((1, 4, 7, 6, 8), (2, 4, 2, 2, 3), (1, 1, 2), (1, 2, 0), (2, 1, 2)),
+])
+def test_out_dims_match_torch(geom):
+    import torch
+    import torch.nn.functional as F
+    xs, ws, st, pd, dl = geom
+    y = F.conv3d(torch.zeros(xs), torch.zeros(ws), stride=st, padding=pd, dilation=dl)
+    assert B.conv_out_dims(xs, ws, st, pd, dl) == tuple(y.shape[2:])
+
+
+def test_packed_cols():
+    assert B.conv_packed_w_cols((64, 64, 3, 3, 3), B.IGC_BF16) == 1728
+    assert B.conv_packed_w_cols((1280, 3, 1, 14, 14), B.IGC_BF16) == 640
+    assert B.conv_packed_w_cols((1280, 3, 1, 14, 14), B.IGC_FP8_E4M3FN) == 640
+    assert B.conv_packed_w_cols((8, 16, 1, 1, 1), B.IGC_FP8_E4M3FN) == 128
+    assert B.conv_packed_w_cols((2048, 2048, 3, 3, 3), B.IGC_FP8_E4M3FN) == 55296
+
+
+def _plan(x, w, st=(1, 1, 1), pd=(0, 0, 0), dl=(1, 1, 1), dt=B.IGC_BF16, lay=B.IGC_NDHWC):
+    return dict(kv.split("=") for kv in B.conv_plan(x, w, st, pd, dl, dt, lay).split())
+
+
+def test_path_selection():
+    assert _plan((9500, 3, 1, 14, 14), (1280, 3, 1, 14, 14), (1, 14, 14), lay=B.IGC_NCDHW)["path"] == "point"
+    assert _plan((2, 16, 1, 14, 14), (32, 16, 1, 14, 14), (1, 14, 14))["path"] == "point"
+    # input larger than the filter: still one output position, but not a plain GEMM over the batch
+    assert _plan((2, 16, 1, 15, 15), (32, 16, 1, 14, 14), (1, 14, 14))["path"] == "generic"
+    p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 1, 1), pd=(1, 0, 0), dt=B.IGC_FP8_E4M3FN)
+    assert p["path"] == "temporal" and p["order"] == "cblock" and p["kstep"] == "128"
+    p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))
+    assert (p["path"], p["tile"], p["grid"], p["nk"]) == ("generic", "256x256", "6752", "864")
+    assert _plan((1, 1024, 240, 160, 90), (1024, 1024, 3, 1, 1), pd=(1, 0, 0))["big"] == "1"
+    assert _plan((1, 64, 4, 16, 16), (64, 64, 3, 3, 3), pd=(1, 1, 1))["tile"] == "64x64"
+    assert _plan((1, 24, 4, 16, 16), (64, 24, 3, 3, 3), pd=(1, 1, 1))["order"] == "linear"
+
+
+def test_forced_path_and_tile():
+    try:
+        B.conv_debug_force(B.IGC_PATH_GENERIC, 1)
+        p = _plan((1, 64, 8, 8, 8), (64, 64, 3, 1, 1), pd=(1, 0, 0))
+        assert (p["path"], p["tile"]) == ("generic", "128x128")
+        B.conv_debug_force(B.IGC_PATH_POINT, -1)
+        with pytest.raises(B.IgcError) as e:
+            _plan((1, 64, 8, 8, 8), (64, 64, 3, 1, 1), pd=(1, 0, 0))
+        assert e.value.status == B.IGC_ERR_UNSUPPORTED
+    finally:
+        B.conv_debug_force(B.IGC_PATH_AUTO, -1)
+
+
+@pytest.mark.parametrize("args,status", [
+    (((1, 64, 4, 4, 4), (64, 32, 3, 3, 3)), B.IGC_ERR_INVALID),          # channel mismatch
+    (((1, 64, 2, 4, 4), (64, 64, 3, 3, 3)), B.IGC_ERR_INVALID),          # filter does not fit (pad 0)
+    (((0, 64, 4, 4, 4), (64, 64, 3, 3, 3)), B.IGC_ERR_INVALID),          # empty batch
+    (((1, 60, 4, 4, 4), (64, 60, 3, 3, 3)), B.IGC_ERR_UNSUPPORTED),      # C % 8 != 0 on the im2col path
+])
+def test_invalid_geometry_is_rejected(args, status):
+    with pytest.raises(B.IgcError) as e:
+        B.conv_plan(args[0], args[1], (1, 1, 1), (0, 0, 0), (1, 1, 1), B.IGC_BF16, B.IGC_NDHWC)
+    assert e.value.status == status
+    assert B.conv_last_error()
+
+
+def test_fp8_channel_requirement_and_layout():
+    with pytest.raises(B.IgcError) as e:
+        B.conv_plan((1, 24, 4, 4, 4), (8, 24, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), B.IGC_FP8_E4M3FN,
+                    B.IGC_NDHWC)
+    assert e.value.status == B.IGC_ERR_UNSUPPORTED
+    with pytest.raises(B.IgcError) as e:  # im2col needs channel-last activations
+        B.conv_plan((1, 64, 4, 4, 4), (8, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), B.IGC_BF16, B.IGC_NCDHW)
+    assert e.value.status == B.IGC_ERR_UNSUPPORTED
+
+
+def test_null_pointers_rejected_before_any_launch():
+    lib = B.load()
+    xs = (B._i64((1, 64, 4, 4, 4), 5), B._i64((64, 64, 3, 3, 3), 5))
+    one = B._i32((1, 1, 1))
+    rc = lib.conv_fwd(None, None, None, xs[0], xs[1], one, one, one, B.IGC_BF16, B.IGC_NDHWC, None, None)
+    assert rc == B.IGC_ERR_INVALID
+    assert lib.conv_amax(None, 10, None, None) == B.IGC_ERR_INVALID
+    assert lib.conv_pack_x(None, None, xs[0], B.IGC_BF16, None, None) == B.IGC_ERR_INVALID
+    rc = lib.conv_fwd(16, 32, 48, xs[0], xs[1], one, one, one, B.IGC_FP8_E4M3FN, B.IGC_NDHWC, None, None)
+    assert rc == B.IGC_ERR_INVALID  # fp8 without scales
+    rc = lib.conv_fwd(8, 32, 48, xs[0], xs[1], one, one, one, B.IGC_BF16, B.IGC_NDHWC, None, None)
+    assert rc == B.IGC_ERR_ALIGN

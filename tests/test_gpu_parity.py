@@ -1,0 +1,243 @@
+"""GPU parity of the HIP path against the CPU oracle at sizes the oracle finishes
+in seconds (several tiles and ragged tails), plus the exact cases.
+
+Every case prints its name before touching the GPU so that a failing run
+names it.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from implicit_gemm_convolution_conv_amd import binding as B
+from implicit_gemm_convolution_conv_amd import inputs as I
+from oracle import oracle as O
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(name):
+    print(f"[case] {name}", flush=True)
+
+
+def _bf16_case(name, xs, ws, st, pd, dl, seed, dist=("uniform", 1.0), x_layout="NDHWC"):
+    _announce(name)
+    g = I.generator(seed, P.DEV)
+    x = I.draw(xs, dist, g, P.DEV)
+    w = I.draw(ws, dist, g, P.DEV)
+    y = P.run_bf16(x, w, st, pd, dl, x_layout=x_layout)
+    ref = O.conv3d(P.bits(x), P.bits(w), st, pd, dl)
+    R = int(np.prod(ws[1:]))
+    P.check_close(P.y_values(y), ref, R, float(x.abs().max()), float(w.abs().max()), name)
+    return x, w, y
+
+
+def test_c1_full_bf16():
+    wl = I.WORKLOADS["c1"]
+    _announce("c1 full")
+    x, w = I.make(wl, P.DEV)
+    y = P.run_bf16(x, w, wl.stride, wl.pad, wl.dil)
+    ref = O.conv3d(P.bits(x), P.bits(w), wl.stride, wl.pad, wl.dil)
+    P.check_close(P.y_values(y), ref, wl.reduction, float(x.abs().max()), float(w.abs().max()), "c1")
+
+
+GEOMS = [
+    # name, x (N,C,D,H,W), w (K,C,T,R,S), stride, pad, dil
+    ("ragged_linear_c24", (2, 24, 5, 7, 9), (40, 24, 3, 3, 3), (1, 2, 1), (1, 1, 2), (1, 1, 2)),
+    ("ragged_c72_k136", (1, 72, 4, 9, 11), (136, 72, 2, 3, 3), (2, 1, 1), (1, 1, 1), (1, 2, 1)),
+    ("c8_tiny", (3, 8, 3, 5, 6), (16, 8, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),
+    ("c128_cblock_multi_tile", (2, 128, 6, 10, 12), (200, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),
+    ("asym_pad_stride2", (1, 64, 7, 13, 10), (72, 64, 3, 5, 1), (2, 2, 1), (0, 2, 0), (1, 1, 1)),
+    ("temporal_3x1x1", (2, 64, 9, 6, 7), (96, 64, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1)),
+    ("temporal_strided_dilated", (1, 32, 11, 5, 9), (48, 32, 3, 1, 1), (2, 1, 1), (2, 0, 0), (2, 1, 1)),
+    ("pointwise_1x1x1", (2, 48, 3, 7, 5), (80, 48, 1, 1, 1), (1, 1, 1), (0, 0, 0), (1, 1, 1)),
+    ("odd_spatial_vec_off", (1, 16, 3, 5, 7), (24, 16, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("case", GEOMS, ids=[g[0] for g in GEOMS])
+def test_bf16_shapes(case):
+    name, xs, ws, st, pd, dl = case
+    _bf16_case(name, xs, ws, st, pd, dl, seed=zlib.crc32(name.encode()) % 1000)
+
+
+@pytest.mark.parametrize("layout", ["NCDHW", "NDHWC"])
+@pytest.mark.parametrize("k", [200, 198])
+def test_point_output_bf16(layout, k):
+    # patch-embed geometry at a reduced batch: 14x14 filter, stride 14, C=3 (R = 588, not a multiple of 64)
+    _bf16_case(f"point_{layout}_k{k}", (300, 3, 1, 14, 14), (k, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1),
+               seed=7, dist=("normal", 1.0), x_layout=layout)
+
+
+def test_2d_and_1d_through_3d():
+    _announce("conv2d / conv1d as D=T=1 (and H=R=1)")
+    g = I.generator(11, P.DEV)
+    x2 = I.draw((2, 16, 1, 12, 10), ("uniform", 1.0), g, P.DEV)
+    w2 = I.draw((24, 16, 1, 3, 3), ("uniform", 1.0), g, P.DEV)
+    y = P.run_bf16(x2, w2, (1, 1, 2), (0, 1, 1), (1, 1, 1))
+    ref = F.conv2d(x2[:, :, 0].double().cpu(), w2[:, :, 0].double().cpu(), stride=(1, 2), padding=1).numpy()
+    P.check_close(P.y_values(y)[:, :, 0], ref, 16 * 9, float(x2.abs().max()), float(w2.abs().max()), "conv2d")
+    x1 = I.draw((3, 32, 1, 1, 40), ("uniform", 1.0), g, P.DEV)
+    w1 = I.draw((8, 32, 1, 1, 5), ("uniform", 1.0), g, P.DEV)
+    y = P.run_bf16(x1, w1, (1, 1, 2), (0, 0, 2), (1, 1, 1))
+    ref = F.conv1d(x1[:, :, 0, 0].double().cpu(), w1[:, :, 0, 0].double().cpu(), stride=2, padding=2).numpy()
+    P.check_close(P.y_values(y)[:, :, 0, 0], ref, 32 * 5, float(x1.abs().max()), float(w1.abs().max()), "conv1d")
+
+
+def test_temporal_path_matches_generic_bitwise():
+    _announce("temporal vs generic, bitwise")
+    g = I.generator(12, P.DEV)
+    xs, ws, st, pd, dl = (2, 64, 9, 6, 7), (96, 64, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1)
+    x = I.draw(xs, ("uniform", 1.0), g, P.DEV)
+    w = I.draw(ws, ("uniform", 1.0), g, P.DEV)
+    assert B.conv_plan(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC).startswith("path=temporal")
+    y_fast = P.run_bf16(x, w, st, pd, dl)
+    try:
+        B.conv_debug_force(B.IGC_PATH_GENERIC, -1)
+        y_gen = P.run_bf16(x, w, st, pd, dl)
+    finally:
+        B.conv_debug_force(B.IGC_PATH_AUTO, -1)
+    assert torch.equal(y_fast.view(torch.int16), y_gen.view(torch.int16))
+
+
+def test_every_tile_gives_identical_bits():
+    # the reduction order over k is the same for every tile shape
+    _announce("tiles 0/1/2 bitwise")
+    g = I.generator(13, P.DEV)
+    xs, ws, st, pd, dl = (1, 64, 5, 18, 20), (136, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)
+    x = I.draw(xs, ("uniform", 1.0), g, P.DEV)
+    w = I.draw(ws, ("uniform", 1.0), g, P.DEV)
+    outs = []
+    try:
+        for tile in range(3):
+            B.conv_debug_force(B.IGC_PATH_AUTO, tile)
+            outs.append(P.run_bf16(x, w, st, pd, dl).clone())
+    finally:
+        B.conv_debug_force(B.IGC_PATH_AUTO, -1)
+    ref = O.conv3d(P.bits(x), P.bits(w), st, pd, dl)
+    P.check_close(P.y_values(outs[0]), ref, 64 * 27, float(x.abs().max()), float(w.abs().max()), "tile0")
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_every_output_written_and_deterministic():
+    _announce("NaN-prefilled output, repeat runs")
+    g = I.generator(14, P.DEV)
+    xs, ws, st, pd, dl = (2, 40, 5, 9, 7), (72, 40, 3, 3, 3), (1, 2, 1), (1, 1, 1), (1, 1, 1)
+    x = I.draw(xs, ("uniform", 1.0), g, P.DEV)
+    w = I.draw(ws, ("uniform", 1.0), g, P.DEV)
+    shape = (2, 72) + B.conv_out_dims(xs, ws, st, pd, dl)
+    y1 = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=P.DEV)
+    y2 = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=P.DEV)
+    P.run_bf16(x, w, st, pd, dl, out=y1)
+    P.run_bf16(x, w, st, pd, dl, out=y2)
+    assert not torch.isnan(y1).any()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+# ------------------------------------------------------------------ exact (integer-valued) cases
+
+def _int_case(xs, ws, st, pd, dl, seed, x_layout="NDHWC"):
+    g = I.generator(seed, P.DEV)
+    x = I.int_valued(xs, -2, 2, g, P.DEV)
+    w = I.sparse_ternary(ws, 128, g, P.DEV)  # |y| <= 2 * 128: every partial sum exact in fp32, y exact in bf16
+    y = P.run_bf16(x, w, st, pd, dl, x_layout=x_layout)
+    ref = O.conv3d(P.bits(x), P.bits(w), st, pd, dl)
+    assert np.array_equal(P.y_values(y), ref)
+
+
+@pytest.mark.parametrize("case", [
+    ((2, 64, 5, 9, 11), (96, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),
+    ((1, 24, 6, 7, 8), (40, 24, 3, 2, 3), (2, 1, 2), (1, 0, 2), (1, 2, 1)),
+    ((2, 128, 7, 5, 6), (64, 128, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1)),
+])
+def test_integer_inputs_bit_exact_bf16(case):
+    _announce(f"integer bf16 {case}")
+    _int_case(*case, seed=21)
+
+
+@pytest.mark.parametrize("layout", ["NCDHW", "NDHWC"])
+def test_integer_inputs_bit_exact_point(layout):
+    _announce(f"integer point {layout}")
+    _int_case((130, 3, 1, 14, 14), (68, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1), seed=22, x_layout=layout)
+
+
+def test_integer_inputs_bit_exact_fp8():
+    # integers |v| <= 2 are exact E4M3FN codes with unit scales, so the fp8 path is exact too
+    _announce("integer fp8, unit scales")
+    g = I.generator(23, P.DEV)
+    xs, ws, st, pd, dl = (1, 64, 5, 9, 11), (80, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)
+    x = I.int_valued(xs, -2, 2, g, P.DEV)
+    w = I.sparse_ternary(ws, 128, g, P.DEV)
+    ones = torch.ones(4, dtype=torch.float32, device=P.DEV)
+    n, c, d, h, wd = xs
+    xq = torch.empty((n, d, h, wd, c), dtype=torch.uint8, device=P.DEV)
+    B.conv_pack_x(x, xq, xs, B.IGC_FP8_E4M3FN, ones[0:2])
+    wq = torch.empty((ws[0], B.conv_packed_w_cols(ws, B.IGC_FP8_E4M3FN)), dtype=torch.uint8, device=P.DEV)
+    B.conv_pack_w(w, wq, ws, B.IGC_FP8_E4M3FN, B.IGC_NDHWC, ones[2:4])
+    y = torch.empty((n, ws[0]) + B.conv_out_dims(xs, ws, st, pd, dl), dtype=torch.bfloat16, device=P.DEV)
+    B.conv_fwd(xq, wq, y, xs, ws, st, pd, dl, B.IGC_FP8_E4M3FN, B.IGC_NDHWC, ones)
+    torch.cuda.synchronize()
+    ref = O.conv3d(P.bits(x), P.bits(w), st, pd, dl)
+    assert np.array_equal(P.y_values(y), ref)
+
+
+# ------------------------------------------------------------------ fp8
+
+FP8_GEOMS = [
+    ("c1_shape_fp8", (1, 64, 4, 16, 16), (64, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),
+    ("fp8_c48_linear", (2, 48, 5, 6, 7), (40, 48, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),
+    ("fp8_c256_k300", (1, 256, 4, 9, 10), (300, 256, 3, 3, 3), (1, 2, 1), (1, 1, 1), (1, 1, 1)),
+    ("fp8_temporal", (1, 128, 8, 9, 10), (136, 128, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1)),
+    ("fp8_c16_tiny", (2, 16, 3, 5, 6), (24, 16, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("case", FP8_GEOMS, ids=[g[0] for g in FP8_GEOMS])
+def test_fp8_shapes(case):
+    name, xs, ws, st, pd, dl = case
+    _announce(name)
+    g = I.generator(31, P.DEV)
+    x = I.draw(xs, ("normal", 1.0), g, P.DEV)
+    w = I.draw(ws, ("normal", 1.0 / np.sqrt(np.prod(ws[1:]))), g, P.DEV)
+    ops = P.Fp8Operands(x, w)
+    y = P.run_fp8(ops, xs, ws, st, pd, dl)
+    sx, sw = float(ops.ref_scales[0]), float(ops.ref_scales[2])
+    ref = O.conv3d(ops.ref_xq, ops.ref_wq, st, pd, dl, sx=sx, sw=sw)
+    mx = float(np.abs(O.e4m3_decode(ops.ref_xq)).max()) * sx
+    mw = float(np.abs(O.e4m3_decode(ops.ref_wq)).max()) * sw
+    P.check_close(P.y_values(y), ref, int(np.prod(ws[1:])), mx, mw, name)
+
+
+def test_pack_bf16_is_a_transpose():
+    _announce("bf16 pack bit-exact, ragged spatial")
+    g = I.generator(41, P.DEV)
+    for xs in [(2, 72, 3, 5, 7), (1, 64, 4, 16, 16), (3, 8, 2, 3, 5)]:
+        x = I.draw(xs, ("normal", 1.0), g, P.DEV)
+        n, c, d, h, wd = xs
+        out = torch.empty((n, d, h, wd, c), dtype=torch.bfloat16, device=P.DEV)
+        B.conv_pack_x(x, out, xs, B.IGC_BF16)
+        torch.cuda.synchronize()
+        assert np.array_equal(P.bits(out), np.moveaxis(P.bits(x), 1, -1))
+
+
+def test_amax_handles_tails_and_zero():
+    _announce("amax tails / zero tensor")
+    g = I.generator(42, P.DEV)
+    amax = torch.empty(1, dtype=torch.float32, device=P.DEV)
+    for n in (1, 7, 8, 9, 1000003):
+        t = I.draw((n,), ("normal", 3.0), g, P.DEV)
+        B.conv_amax(t, n, amax)
+        torch.cuda.synchronize()
+        assert float(amax) == O.amax_bf16(P.bits(t))
+    z = torch.zeros(100, dtype=torch.bfloat16, device=P.DEV)
+    pair = torch.empty(2, dtype=torch.float32, device=P.DEV)
+    B.conv_amax(z, 100, amax)
+    B.conv_fp8_scales(amax, pair)
+    torch.cuda.synchronize()
+    assert pair.tolist() == [1.0, 1.0]
