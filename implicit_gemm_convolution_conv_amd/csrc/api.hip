@@ -208,8 +208,12 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         return ((int64_t)p.M + kTiles[t].bm - 1) / kTiles[t].bm * (((int64_t)p.Ncol + kTiles[t].bn - 1) / kTiles[t].bn);
     };
     int tile = g_force_tile.load();
-    if (tile < 0 || tile >= kNumTiles)
-        tile = nblocks(0) >= 512 ? 0 : (nblocks(1) >= 256 ? 1 : 2);
+    if (tile < 0 || tile >= kNumTiles) {
+        // Measured on MI355X: 16x16 MFMA blocks are faster for bf16 and for the
+        // short-reduction temporal fp8 path, 32x32 blocks for fp8 with full 3D filters.
+        const int base = (dtype == IGC_FP8_E4M3FN && path == IGC_PATH_GENERIC) ? 3 : 0;
+        tile = base + (nblocks(base) >= 512 ? 0 : (nblocks(base + 1) >= 256 ? 1 : 2));
+    }
     pl.tile = tile;
     const TileShape ts = kTiles[tile];
     const int64_t tm = ((int64_t)p.M + ts.bm - 1) / ts.bm, tn = ((int64_t)p.Ncol + ts.bn - 1) / ts.bn;
@@ -218,7 +222,7 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
     p.tiles_m = (int)tm;
     p.tiles_n = (int)tn;
     // Workgroups resident on one XCD (32 CUs): one 256x256 or two smaller tiles per CU.
-    const int resident = 32 * (tile == 0 ? 1 : 2);
+    const int resident = 32 * (ts.bm == 256 ? 1 : 2);
     p.group_m = (int)std::max<int64_t>(1, resident / tn);
     return IGC_OK;
 }
@@ -375,8 +379,8 @@ int conv_plan(const int64_t xshape[5], const int64_t wshape[5], const int32_t st
         return rc;
     if (buf && len) {
         const TileShape ts = kTiles[pl.tile];
-        snprintf(buf, len, "path=%s tile=%dx%d waves=%d kstep=%d order=%s big=%d grid=%d group_m=%d nk=%d",
-                 path_name(pl.path), ts.bm, ts.bn, ts.wm * ts.wn, dtype == IGC_FP8_E4M3FN ? 128 : 64,
+        snprintf(buf, len, "path=%s tile=%dx%d waves=%d mfma=%dx%d kstep=%d order=%s big=%d grid=%d group_m=%d nk=%d",
+                 path_name(pl.path), ts.bm, ts.bn, ts.wm * ts.wn, ts.mf, ts.mf, dtype == IGC_FP8_E4M3FN ? 128 : 64,
                  pl.cblock ? "cblock" : "linear", pl.big ? 1 : 0, pl.p.tiles_m * pl.p.tiles_n, pl.p.group_m, pl.p.nk);
     }
     return ok();

@@ -32,6 +32,28 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // 16-byte load from an address that is only known to be 4-byte aligned.
 typedef int i32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int MF>
+struct AccType {
+    using type = f32x4;
+};
+template <>
+struct AccType<32> {
+    using type = f32x16;
+};
+
+// Quad q (4 consecutive rows of one column) of an accumulator block.
+template <int MF>
+__device__ inline f32x4 quad(const typename AccType<MF>::type &acc, int q)
+{
+    if constexpr (MF == 16) {
+        return acc;
+    } else {
+        return f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    }
+}
+
 template <bool BIG>
 struct OffType {
     using type = int32_t;
@@ -70,7 +92,7 @@ __device__ inline uint32_t f32_to_bf16_rne(float f)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int BM, int BN, int WM, int WN, int DT, int MODE, bool BIG, bool CBLK>
+template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, bool BIG, bool CBLK>
 __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void conv_igemm_kernel(ConvParams p)
 {
@@ -83,11 +105,12 @@ void conv_igemm_kernel(ConvParams p)
     constexpr int AIT = BM / RSTEP;            // A rows loaded per thread
     constexpr int BIT = BN / RSTEP;            // B rows loaded per thread
     constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int FM = WTM / MF, FN = WTN / MF;
     constexpr int STAGE = (BM + BN) * 128;
     static_assert(BM % RSTEP == 0 && BN % RSTEP == 0 && AIT >= 1 && BIT >= 1, "loader split");
     static_assert(RSTEP % 8 == 0, "a thread's rows must share (row & 7)");
-    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "MFMA blocks");
+    static_assert(MF == 16 || MF == 32, "MFMA block size");
+    static_assert(WTM % MF == 0 && WTN % MF == 0, "MFMA blocks");
     static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
     static_assert(MODE != MODE_POINT || !CBLK, "point mode reduces in natural order");
 
@@ -284,51 +307,74 @@ void conv_igemm_kernel(ConvParams p)
     };
 
     // ---------------------------------------------------------------- MFMA
-    f32x4 acc[FM][FN];
+    // MF = 16: 16x16 blocks (bf16 16x16x32, fp8 16x16x128), a lane owns rows
+    //          4*(lane/16) + 0..3 of column lane%16 of each block.
+    // MF = 32: 32x32 blocks (bf16 32x32x16, fp8 32x32x64), a lane owns rows
+    //          8*q + 4*(lane/32) + 0..3 (q = 0..3) of column lane%32.
+    // A lane's operand fragment is one row (column) of its block, lane % MF,
+    // and 16 (bf16) or 32 (fp8) bytes of k; A and B take the same k bytes, so
+    // which bytes a lane holds does not change the product.
+    using AccT = typename AccType<MF>::type;
+    AccT acc[FM][FN];
 #pragma unroll
     for (int a = 0; a < FM; ++a)
 #pragma unroll
         for (int b = 0; b < FN; ++b)
-            acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[a][b] = AccT{};
 
-    const int lrow = lane & 15, lgrp = lane >> 4, lsw = lane & 7;
+    const int lrow = lane & (MF - 1), lgrp = lane / MF, lsw = lane & 7;
     auto compute = [&](const char *st) {
         const char *aw = st + (wm * WTM + lrow) * 128;
         const char *bw = st + BM * 128 + (wn * WTN + lrow) * 128;
-        if constexpr (DT == DT_BF16) {
+        constexpr int GROUPS = 64 / MF;            // lane groups per block (k split)
+        constexpr int CPL = DT == DT_BF16 ? 1 : 2;  // 16-byte chunks per lane per MFMA
+        constexpr int SUB = 8 / (GROUPS * CPL);     // MFMAs per block per reduction step
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int sl = ((lgrp + 4 * h) ^ lsw) * 16;
+        for (int h = 0; h < SUB; ++h) {
+            // chunks of this lane: (h * GROUPS + lgrp) * CPL + 0..CPL-1
+            const int c0 = (h * GROUPS + lgrp) * CPL;
+            const int sl0 = (c0 ^ lsw) * 16;
+            const int sl1 = ((c0 + 1) ^ lsw) * 16;
+            if constexpr (DT == DT_BF16) {
                 bf16x8 bf[FN];
 #pragma unroll
                 for (int b = 0; b < FN; ++b)
-                    bf[b] = *reinterpret_cast<const bf16x8 *>(bw + b * 16 * 128 + sl);
+                    bf[b] = *reinterpret_cast<const bf16x8 *>(bw + b * MF * 128 + sl0);
 #pragma unroll
                 for (int a = 0; a < FM; ++a) {
-                    const bf16x8 af = *reinterpret_cast<const bf16x8 *>(aw + a * 16 * 128 + sl);
+                    const bf16x8 af = *reinterpret_cast<const bf16x8 *>(aw + a * MF * 128 + sl0);
 #pragma unroll
-                    for (int b = 0; b < FN; ++b)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[b], acc[a][b], 0, 0, 0);
+                    for (int b = 0; b < FN; ++b) {
+                        if constexpr (MF == 16)
+                            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[b], acc[a][b], 0, 0, 0);
+                        else
+                            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[b], acc[a][b], 0, 0, 0);
+                    }
                 }
-            }
-        } else {
-            const int sl0 = (lgrp ^ lsw) * 16, sl1 = ((lgrp + 4) ^ lsw) * 16;
-            i32x8 bf[FN];
+            } else {
+                i32x8 bf[FN];
 #pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const i32x4 lo = *reinterpret_cast<const i32x4 *>(bw + b * 16 * 128 + sl0);
-                const i32x4 hi = *reinterpret_cast<const i32x4 *>(bw + b * 16 * 128 + sl1);
-                bf[b] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
+                for (int b = 0; b < FN; ++b) {
+                    const i32x4 lo = *reinterpret_cast<const i32x4 *>(bw + b * MF * 128 + sl0);
+                    const i32x4 hi = *reinterpret_cast<const i32x4 *>(bw + b * MF * 128 + sl1);
+                    bf[b] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
 #pragma unroll
-            for (int a = 0; a < FM; ++a) {
-                const i32x4 lo = *reinterpret_cast<const i32x4 *>(aw + a * 16 * 128 + sl0);
-                const i32x4 hi = *reinterpret_cast<const i32x4 *>(aw + a * 16 * 128 + sl1);
-                const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                for (int a = 0; a < FM; ++a) {
+                    const i32x4 lo = *reinterpret_cast<const i32x4 *>(aw + a * MF * 128 + sl0);
+                    const i32x4 hi = *reinterpret_cast<const i32x4 *>(aw + a * MF * 128 + sl1);
+                    const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-                for (int b = 0; b < FN; ++b)  // operand formats 0/0: both E4M3; scales 127 = 2^0
-                    acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[b], acc[a][b], 0, 0, 0,
-                                                                                 127, 0, 127);
+                    for (int b = 0; b < FN; ++b) {
+                        // operand formats 0/0: both E4M3; zero scale operands select the unscaled MFMA
+                        if constexpr (MF == 16)
+                            acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[b], acc[a][b], 0, 0,
+                                                                                         0, 0, 0, 0);
+                        else
+                            acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[b], acc[a][b], 0, 0,
+                                                                                        0, 0, 0, 0);
+                    }
+                }
             }
         }
     };
@@ -350,62 +396,67 @@ void conv_igemm_kernel(ConvParams p)
     }
 
     // ---------------------------------------------------------------- epilogue
-    // MFMA 16x16 output layout: lane holds rows 4*(lane/16) + 0..3 of column lane%16.
+    // Each lane holds groups of 4 consecutive GEMM rows of one column ("quads").
     float sc = 1.0f;
     if constexpr (DT == DT_FP8)
         sc = p.scales[0] * p.scales[2];
     uint16_t *yb = static_cast<uint16_t *>(p.y);
+    constexpr int QUADS = MF / 16 * (MF / 16);  // 1 (16x16) or 4 (32x32) per block
 #pragma unroll
     for (int a = 0; a < FM; ++a) {
-        const int row = m0 + wm * WTM + a * 16 + 4 * lgrp;  // first of 4 consecutive GEMM rows
-        if constexpr (MODE != MODE_POINT) {
-            int nimg = 0, sp = 0;
-            if (row < p.M) {
-                nimg = row / p.P;
-                sp = row - nimg * p.P;
-            }
-            const bool vec = (p.P & 3) == 0 && row + 3 < p.M;  // 4 rows in one image, 8-byte aligned
 #pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const int col = n0 + wn * WTN + b * 16 + lrow;  // output channel
-                if (row >= p.M || col >= p.K)
-                    continue;
-                const f32x4 v = acc[a][b] * sc;
-                if (vec) {
-                    const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                      f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
-                    *reinterpret_cast<u32x2 *>(yb + ((Off)nimg * p.K + col) * (Off)p.P + sp) = pk;
-                } else {
+        for (int q = 0; q < QUADS; ++q) {
+            // first of the 4 consecutive GEMM rows of this quad
+            const int row = m0 + wm * WTM + a * MF + (MF == 16 ? 4 * lgrp : 8 * q + 4 * lgrp);
+            if constexpr (MODE != MODE_POINT) {
+                int nimg = 0, sp = 0;
+                if (row < p.M) {
+                    nimg = row / p.P;
+                    sp = row - nimg * p.P;
+                }
+                const bool vec = (p.P & 3) == 0 && row + 3 < p.M;  // 4 rows in one image, 8-byte aligned
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int m = row + e;
-                        if (m < p.M) {
-                            const int n2 = m / p.P;
-                            const int sp2 = m - n2 * p.P;
-                            yb[((Off)n2 * p.K + col) * (Off)p.P + sp2] = (uint16_t)f32_to_bf16_rne(v[e]);
+                for (int b = 0; b < FN; ++b) {
+                    const int col = n0 + wn * WTN + b * MF + lrow;  // output channel
+                    if (row >= p.M || col >= p.K)
+                        continue;
+                    const f32x4 v = quad<MF>(acc[a][b], q) * sc;
+                    if (vec) {
+                        const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                          f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+                        *reinterpret_cast<u32x2 *>(yb + ((Off)nimg * p.K + col) * (Off)p.P + sp) = pk;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int m = row + e;
+                            if (m < p.M) {
+                                const int n2 = m / p.P;
+                                const int sp2 = m - n2 * p.P;
+                                yb[((Off)n2 * p.K + col) * (Off)p.P + sp2] = (uint16_t)f32_to_bf16_rne(v[e]);
+                            }
                         }
                     }
                 }
-            }
-        } else {
-            // rows are output channels, columns are images: y[n][k] is contiguous in k
-            const bool vec = (p.K & 3) == 0 && row + 3 < p.M;
+            } else {
+                // rows are output channels, columns are images: y[n][k] is contiguous in k
+                const bool vec = (p.K & 3) == 0 && row + 3 < p.M;
 #pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const int col = n0 + wn * WTN + b * 16 + lrow;  // image
-                if (row >= p.M || col >= p.Ncol)
-                    continue;
-                const f32x4 v = acc[a][b] * sc;
-                uint16_t *dst = yb + (Off)col * p.K + row;
-                if (vec) {
-                    const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                      f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
-                    *reinterpret_cast<u32x2 *>(dst) = pk;
-                } else {
+                for (int b = 0; b < FN; ++b) {
+                    const int col = n0 + wn * WTN + b * MF + lrow;  // image
+                    if (row >= p.M || col >= p.Ncol)
+                        continue;
+                    const f32x4 v = quad<MF>(acc[a][b], q) * sc;
+                    uint16_t *dst = yb + (Off)col * p.K + row;
+                    if (vec) {
+                        const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                          f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+                        *reinterpret_cast<u32x2 *>(dst) = pk;
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (row + e < p.M)
-                            dst[e] = (uint16_t)f32_to_bf16_rne(v[e]);
+                        for (int e = 0; e < 4; ++e)
+                            if (row + e < p.M)
+                                dst[e] = (uint16_t)f32_to_bf16_rne(v[e]);
+                    }
                 }
             }
         }
@@ -417,40 +468,40 @@ template <int DT>
 hipError_t launch_conv_dt(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream)
 {
     const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
-#define IGC_LAUNCH(BM_, BN_, WM_, WN_, MODE_, BIG_, CBLK_)                                                       \
+#define IGC_LAUNCH(BM_, BN_, WM_, WN_, MF_, MODE_, BIG_, CBLK_)                                                  \
     do {                                                                                                       \
-        hipLaunchKernelGGL((conv_igemm_kernel<BM_, BN_, WM_, WN_, DT, MODE_, BIG_, CBLK_>), grid,              \
+        hipLaunchKernelGGL((conv_igemm_kernel<BM_, BN_, WM_, WN_, MF_, DT, MODE_, BIG_, CBLK_>), grid,         \
                            dim3(WM_ * WN_ * 64), 0, stream, p);                                                \
         return hipGetLastError();                                                                              \
     } while (0)
-#define IGC_MODES(BM_, BN_, WM_, WN_)                                                                          \
+#define IGC_MODES(BM_, BN_, WM_, WN_, MF_)                                                                     \
     do {                                                                                                       \
         if (mode == MODE_POINT) {                                                                              \
-            if (big) IGC_LAUNCH(BM_, BN_, WM_, WN_, MODE_POINT, true, false);                                  \
-            IGC_LAUNCH(BM_, BN_, WM_, WN_, MODE_POINT, false, false);                                          \
+            if (big) IGC_LAUNCH(BM_, BN_, WM_, WN_, MF_, MODE_POINT, true, false);                             \
+            IGC_LAUNCH(BM_, BN_, WM_, WN_, MF_, MODE_POINT, false, false);                                     \
         }                                                                                                      \
         if (mode == MODE_TEMPORAL) {                                                                           \
             if (big) {                                                                                         \
-                if (cblock) IGC_LAUNCH(BM_, BN_, WM_, WN_, MODE_TEMPORAL, true, true);                         \
-                IGC_LAUNCH(BM_, BN_, WM_, WN_, MODE_TEMPORAL, true, false);                                    \
+                if (cblock) IGC_LAUNCH(BM_, BN_, WM_, WN_, MF_, MODE_TEMPORAL, true, true);                    \
+                IGC_LAUNCH(BM_, BN_, WM_, WN_, MF_, MODE_TEMPORAL, true, false);                               \
             }                                                                                                  \
-            if (cblock) IGC_LAUNCH(BM_, BN_, WM_, WN_, MODE_TEMPORAL, false, true);                            \
-            IGC_LAUNCH(BM_, BN_, WM_, WN_, MODE_TEMPORAL, false, false);                                       \
+            if (cblock) IGC_LAUNCH(BM_, BN_, WM_, WN_, MF_, MODE_TEMPORAL, false, true);                       \
+            IGC_LAUNCH(BM_, BN_, WM_, WN_, MF_, MODE_TEMPORAL, false, false);                                  \
         }                                                                                                      \
         if (big) {                                                                                             \
-            if (cblock) IGC_LAUNCH(BM_, BN_, WM_, WN_, MODE_GENERIC, true, true);                              \
-            IGC_LAUNCH(BM_, BN_, WM_, WN_, MODE_GENERIC, true, false);                                         \
+            if (cblock) IGC_LAUNCH(BM_, BN_, WM_, WN_, MF_, MODE_GENERIC, true, true);                         \
+            IGC_LAUNCH(BM_, BN_, WM_, WN_, MF_, MODE_GENERIC, true, false);                                    \
         }                                                                                                      \
-        if (cblock) IGC_LAUNCH(BM_, BN_, WM_, WN_, MODE_GENERIC, false, true);                                 \
-        IGC_LAUNCH(BM_, BN_, WM_, WN_, MODE_GENERIC, false, false);                                            \
+        if (cblock) IGC_LAUNCH(BM_, BN_, WM_, WN_, MF_, MODE_GENERIC, false, true);                            \
+        IGC_LAUNCH(BM_, BN_, WM_, WN_, MF_, MODE_GENERIC, false, false);                                       \
     } while (0)
     switch (tile) {
-    case 0:
-        IGC_MODES(256, 256, 2, 4);
-    case 1:
-        IGC_MODES(128, 128, 2, 2);
-    default:
-        IGC_MODES(64, 64, 2, 2);
+    case 0: IGC_MODES(256, 256, 2, 4, 16);
+    case 1: IGC_MODES(128, 128, 2, 2, 16);
+    case 2: IGC_MODES(64, 64, 2, 2, 16);
+    case 3: IGC_MODES(256, 256, 2, 4, 32);
+    case 4: IGC_MODES(128, 128, 2, 2, 32);
+    default: IGC_MODES(64, 64, 2, 2, 32);
     }
 #undef IGC_MODES
 #undef IGC_LAUNCH

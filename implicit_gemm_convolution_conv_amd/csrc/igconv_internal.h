@@ -10,16 +10,21 @@ namespace igc {
 enum Mode { MODE_GENERIC = 0, MODE_TEMPORAL = 1, MODE_POINT = 2 };
 enum Dtype { DT_BF16 = 0, DT_FP8 = 1 };
 
-// Tile shapes (rows x cols of the GEMM tile, waves along rows x cols). The
-// reduction step is always 128 bytes of k per row: 64 bf16 or 128 fp8.
+// Tile shapes: rows x cols of the GEMM tile, waves along rows x cols, MFMA
+// block edge (16: 16x16 blocks; 32: 32x32 blocks, which need fewer operand
+// registers per lane). The reduction step is always 128 bytes of k per row:
+// 64 bf16 or 128 fp8.
 struct TileShape {
-    int bm, bn, wm, wn;
+    int bm, bn, wm, wn, mf;
 };
-constexpr int kNumTiles = 3;
+constexpr int kNumTiles = 6;
 constexpr TileShape kTiles[kNumTiles] = {
-    {256, 256, 2, 4},  // 8 waves, 128x64 per wave: large grids
-    {128, 128, 2, 2},  // 4 waves, 64x64 per wave
-    {64, 64, 2, 2},    // 4 waves, 32x32 per wave: small grids
+    {256, 256, 2, 4, 16},  // 8 waves, 128x64 per wave: large grids
+    {128, 128, 2, 2, 16},  // 4 waves, 64x64 per wave
+    {64, 64, 2, 2, 16},    // 4 waves, 32x32 per wave: small grids
+    {256, 256, 2, 4, 32},
+    {128, 128, 2, 2, 32},
+    {64, 64, 2, 2, 32},
 };
 
 // Everything a conv kernel needs, passed by value as kernel arguments.
