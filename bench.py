@@ -33,8 +33,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # dense MFMA, MI355X published figures
 PEAK_HBM_GBS = 8000.0
+# sources that decide the headline kernel's code and launch configuration
 KERNEL_SOURCES = ["implicit_gemm_convolution_conv_amd/csrc/conv_igemm.h",
-                  "implicit_gemm_convolution_conv_amd/csrc/conv_bf16.hip"]
+                  "implicit_gemm_convolution_conv_amd/csrc/conv_bf16.hip",
+                  "implicit_gemm_convolution_conv_amd/csrc/igconv_internal.h",
+                  "implicit_gemm_convolution_conv_amd/csrc/api.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv_igemm_c3_bf16_traffic.json")
 
 
@@ -204,6 +207,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", default=None, help="comma list of extra workloads (c1,c2,c4,c4t,c5)")
+    ap.add_argument("--profile", action="store_true",
+                    help="counter-collection run: the headline conv `steps` times, then one 1 GiB device copy "
+                         "(the reference for scaling FETCH_SIZE / WRITE_SIZE); prints nothing else")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path (one process, one device).",
@@ -221,6 +227,21 @@ def main():
         sys.exit(2)
     B.load()
     torch.cuda.set_device(0)
+
+    if args.profile:
+        wl = I.WORKLOADS["c3"]
+        x, w = I.make(wl, "cuda")
+        wp = PL.packed_weight(w, "bf16", "NDHWC")
+        y = PL.output(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dil, "cuda")
+        for _ in range(args.steps):
+            B.conv_fwd(x, wp, y, wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)  # 1 GiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] profile run done: {args.steps} conv launches, one {src.numel() * 2} byte copy")
+        return
 
     log(f"[bench] headline c3 bf16, {args.steps} steps after {args.warmup} warm-up")
     head = bench_workload("c3", args.steps, args.warmup, torch, B, I, PL)

@@ -1,0 +1,153 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py times.
+
+Random data: the oracle evaluates sampled output elements one by one (box
+corners, edges, faces and their neighbours, chosen planes and channels, plus
+uniform draws) and the relative-L2 / max-abs tolerance applies over the
+sample. Exact checks at full size: a delta filter (output = shifted copy of
+the input, bit for bit) and all-ones operands (output = C x number of valid
+taps, a closed form), which exercise every address the kernels compute.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from implicit_gemm_convolution_conv_amd import binding as B
+from implicit_gemm_convolution_conv_amd import inputs as I
+from implicit_gemm_convolution_conv_amd import pipeline as PL
+from oracle import oracle as O
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(name):
+    print(f"[case] {name}", flush=True)
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _valid_taps(size, ksz, pad, dev):
+    o = torch.arange(size + 2 * pad - ksz + 1, device=dev)
+    t = torch.arange(ksz, device=dev)
+    pos = o[:, None] - pad + t[None, :]
+    return ((pos >= 0) & (pos < size)).sum(1).to(torch.float64)
+
+
+def test_c2_point_output_full():
+    wl = I.WORKLOADS["c2"]
+    _announce("c2 point-output, all 9500 x 1280 outputs")
+    x, w = I.make(wl, P.DEV)
+    assert B.conv_plan(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dil, B.IGC_BF16,
+                       B.IGC_NCDHW).startswith("path=point")
+    y = P.run_bf16(x, w, wl.stride, wl.pad, wl.dil, x_layout="NCDHW")
+    ref = O.conv3d(P.bits(x), P.bits(w), wl.stride, wl.pad, wl.dil)
+    P.check_close(P.y_values(y), ref, wl.reduction, float(x.abs().max()), float(w.abs().max()), "c2")
+    _free()
+
+
+def test_c3_sampled_and_exact():
+    wl = I.WORKLOADS["c3"]
+    _announce("c3 bf16 sampled")
+    x, w = I.make(wl, P.DEV)  # x drawn NDHWC
+    xs, ws = wl.x_shape, wl.w_shape
+    wp = PL.packed_weight(w, "bf16", "NDHWC")
+    y = PL.output(xs, ws, wl.stride, wl.pad, wl.dil, P.DEV)
+    B.conv_fwd(x, wp, y, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    pts = P.sample_points(1, ws[0], *y.shape[2:], rng, n_random=600, extra_k=(1023, 1024))
+    ref = O.conv3d_points(P.bits(x), P.bits(w), pts, wl.stride, wl.pad, wl.dil, x_layout="NDHWC")
+    P.check_close(P.gather(y, pts), ref, wl.reduction, float(x.abs().max()), float(w.abs().max()), "c3")
+
+    _announce("c3 bf16 delta filter, full size")
+    k, c = ws[0], ws[1]
+    perm = torch.randperm(c, generator=torch.Generator().manual_seed(0))[:k].to(P.DEV)
+    wd = torch.zeros(ws, dtype=torch.bfloat16, device=P.DEV)
+    tap = (2, 0, 1)
+    wd[torch.arange(k, device=P.DEV), perm, tap[0], tap[1], tap[2]] = 1.0
+    wpd = PL.packed_weight(wd, "bf16", "NDHWC")
+    B.conv_fwd(x, wpd, y, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
+    xpad = torch.nn.functional.pad(x, (0, 0, 1, 1, 1, 1, 1, 1))  # zero halo on D, H, W of NDHWC
+    d, h, wdt = xs[2:]
+    shifted = xpad[:, tap[0]:tap[0] + d, tap[1]:tap[1] + h, tap[2]:tap[2] + wdt, :]  # (N, D, H, W, C)
+    expect = shifted[..., perm].permute(0, 4, 1, 2, 3)
+    assert torch.equal(y.view(torch.int16), expect.contiguous().view(torch.int16))
+    del xpad, shifted, expect, wd, wpd
+
+    _announce("c3 bf16 all-ones, full size")
+    x.fill_(1.0)
+    wones = torch.ones(ws, dtype=torch.bfloat16, device=P.DEV)
+    wp = PL.packed_weight(wones, "bf16", "NDHWC")
+    B.conv_fwd(x, wp, y, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
+    cnt = (_valid_taps(d, 3, 1, P.DEV)[:, None, None] * _valid_taps(h, 3, 1, P.DEV)[None, :, None]
+           * _valid_taps(wdt, 3, 1, P.DEV)[None, None, :]) * c
+    assert torch.equal(y.double(), cnt.expand(1, k, d, h, wdt))
+    _free()
+
+
+@pytest.mark.parametrize("name", ["c4", "c4t"])
+def test_fp8_sampled(name):
+    wl = I.WORKLOADS[name]
+    _announce(f"{name} fp8 pack (all codes) and sampled conv")
+    x, w = I.make(wl, P.DEV)  # x drawn NCDHW bf16
+    xs, ws = wl.x_shape, wl.w_shape
+    ops = P.Fp8Operands(x, w, check_codes=True)
+    y = P.run_fp8(ops, xs, ws, wl.stride, wl.pad, wl.dil)
+    rng = np.random.default_rng(4)
+    pts = P.sample_points(1, ws[0], *y.shape[2:], rng, n_random=600)
+    sx, sw = float(ops.ref_scales[0]), float(ops.ref_scales[2])
+    ref = O.conv3d_points(ops.ref_xq, ops.ref_wq, pts, wl.stride, wl.pad, wl.dil, sx=sx, sw=sw)
+    mx = float(np.abs(O.e4m3_decode(ops.ref_xq)).max()) * sx
+    mw = float(np.abs(O.e4m3_decode(ops.ref_wq)).max()) * sw
+    P.check_close(P.gather(y, pts), ref, wl.reduction, mx, mw, name)
+    _free()
+
+
+def test_c5_large_tensor():
+    wl = I.WORKLOADS["c5"]
+    xs, ws = wl.x_shape, wl.w_shape
+    n, c, d, h, wdt = xs
+    k = ws[0]
+    _announce("c5 >2^31 elements: transpose bit-exact")
+    x, w = I.make(wl, P.DEV)  # NCDHW, 3.5e9 elements
+    assert x.numel() > 2 ** 31
+    plan = B.conv_plan(xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
+    assert "path=temporal" in plan and "big=1" in plan
+    xt = PL.packed_input(x, "bf16")
+    torch.cuda.synchronize()
+    for dd in range(0, d, 16):  # compare plane blocks to bound the scratch
+        assert torch.equal(xt[:, dd:dd + 16].view(torch.int16),
+                           x[:, :, dd:dd + 16].permute(0, 2, 3, 4, 1).contiguous().view(torch.int16))
+
+    _announce("c5 sampled vs oracle (planes across the 2^31 / 2^32 offsets)")
+    wp = PL.packed_weight(w, "bf16", "NDHWC")
+    y = PL.output(xs, ws, wl.stride, wl.pad, wl.dil, P.DEV)
+    B.conv_fwd(xt, wp, y, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
+    torch.cuda.synchronize()
+    assert y.numel() > 2 ** 31
+    rng = np.random.default_rng(5)
+    pts = P.sample_points(1, k, *y.shape[2:], rng, n_random=800, extra_d=(145, 146, 147, 238),
+                          extra_k=(621, 622, 1023))
+    xb = P.bits(x)  # 7 GB host copy, NCDHW
+    ref = O.conv3d_points(xb, P.bits(w), pts, wl.stride, wl.pad, wl.dil)
+    del xb
+    P.check_close(P.gather(y, pts), ref, wl.reduction, float(x.abs().max()), float(w.abs().max()), "c5")
+
+    _announce("c5 delta filter, full size (bit-exact)")
+    perm = torch.randperm(c, generator=torch.Generator().manual_seed(1))[:k].to(P.DEV)
+    wd = torch.zeros(ws, dtype=torch.bfloat16, device=P.DEV)
+    wd[torch.arange(k, device=P.DEV), perm, 0, 0, 0] = 1.0  # tap t=0: y[:, k, od] = x[:, perm[k], od - 1]
+    wpd = PL.packed_weight(wd, "bf16", "NDHWC")
+    B.conv_fwd(xt, wpd, y, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
+    torch.cuda.synchronize()
+    del xt
+    assert torch.equal(y[:, :, 0].view(torch.int16), torch.zeros_like(y[:, :, 0]).view(torch.int16))
+    for kk in range(0, k, 128):
+        src = x[:, perm[kk:kk + 128], : d - 1]
+        assert torch.equal(y[:, kk:kk + 128, 1:].view(torch.int16), src.view(torch.int16)), kk
+    _free()
