@@ -56,7 +56,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.conv_pack_w.argtypes = [P, P, P, I32, I32, P, P]
         lib.conv_fwd.argtypes = [P, P, P, P, P, P, P, P, I32, I32, P, P]
         lib.conv_plan.argtypes = [P, P, P, P, P, I32, I32, ctypes.c_char_p, ctypes.c_size_t]
-        lib.conv_debug_force.argtypes = [I32, I32]
+        lib.conv_debug_force.argtypes = [I32, I32, I32]
         lib.conv_last_error.restype = ctypes.c_char_p
         for name in EXPORTS:
             if name not in ("conv_packed_w_cols", "conv_last_error"):
@@ -146,8 +146,8 @@ def conv_plan(xshape, wshape, stride, pad, dilation, dtype, x_layout) -> str:
     return buf.value.decode()
 
 
-def conv_debug_force(path, tile):
-    _check("conv_debug_force", load().conv_debug_force(int(path), int(tile)))
+def conv_debug_force(path, tile, group_m=0):
+    _check("conv_debug_force", load().conv_debug_force(int(path), int(tile), int(group_m)))
 
 
 def conv_last_error() -> str:

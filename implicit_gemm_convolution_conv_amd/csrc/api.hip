@@ -15,9 +15,15 @@ namespace igc {
 hipError_t launch_conv_bf16(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream);
 hipError_t launch_conv_fp8(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream);
 
+hipError_t launch_conv_dma_bf16(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream);
+hipError_t launch_conv_dma_fp8(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream);
+
 hipError_t launch_conv(const ConvParams &p, int tile, Mode mode, Dtype dt, bool big, bool cblock,
                        hipStream_t stream)
 {
+    if (kTiles[tile].stages)
+        return dt == DT_FP8 ? launch_conv_dma_fp8(p, tile, mode, big, cblock, stream)
+                            : launch_conv_dma_bf16(p, tile, mode, big, cblock, stream);
     return dt == DT_FP8 ? launch_conv_fp8(p, tile, mode, big, cblock, stream)
                         : launch_conv_bf16(p, tile, mode, big, cblock, stream);
 }
@@ -30,6 +36,7 @@ using namespace igc;
 thread_local std::string g_err;
 std::atomic<int> g_force_path{IGC_PATH_AUTO};
 std::atomic<int> g_force_tile{-1};
+std::atomic<int> g_force_group_m{0};
 
 constexpr int64_t kI32Max = 2147483647;
 // Element offsets up to this bound use 32-bit arithmetic in the conv kernel;
@@ -138,7 +145,6 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         return fail(IGC_ERR_INVALID, "x_layout %d is neither IGC_NCDHW nor IGC_NDHWC", x_layout);
     const int esz = dtype == IGC_FP8_E4M3FN ? 1 : 2;
     const int chunk = 16 / esz;
-    const int tke = 8 * chunk;
 
     const int forced = g_force_path.load();
     int path;
@@ -182,8 +188,6 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         p.P = 1;
         p.M = (int)g.K;
         p.Ncol = (int)g.N;
-        p.nk = (int)(ldw / tke);
-        pl.cblock = false;
     } else {
         if (x_layout != IGC_NDHWC)
             return fail(IGC_ERR_UNSUPPORTED, "im2col paths need NDHWC activations (pack them with conv_pack_x)");
@@ -196,8 +200,6 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         p.P = (int)P;
         p.M = (int)M;
         p.Ncol = (int)g.K;
-        pl.cblock = (g.C % tke) == 0;
-        p.nk = pl.cblock ? (int)(g.T * g.R * g.S * (g.C / tke)) : (int)(ldw / tke);
     }
     pl.path = path;
     pl.big = xnum > kSmallTensor || ynum > kSmallTensor;
@@ -213,9 +215,22 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         // short-reduction temporal fp8 path, 32x32 blocks for fp8 with full 3D filters.
         const int base = (dtype == IGC_FP8_E4M3FN && path == IGC_PATH_GENERIC) ? 3 : 0;
         tile = base + (nblocks(base) >= 512 ? 0 : (nblocks(base + 1) >= 256 ? 1 : 2));
+    } else {
+        if (kTiles[tile].stages && path == IGC_PATH_POINT)
+            return fail(IGC_ERR_UNSUPPORTED, "tile %d (direct-to-LDS) does not run the point-output path", tile);
+        if (kTiles[tile].stages && kTiles[tile].mf == 16 && esz == 1)
+            return fail(IGC_ERR_UNSUPPORTED, "tile %d: fp8 with 64-byte steps needs 32x32 MFMA blocks", tile);
     }
     pl.tile = tile;
     const TileShape ts = kTiles[tile];
+    const int tke = step_bytes(ts) / esz;  // elements per reduction step
+    if (path == IGC_PATH_POINT) {
+        p.nk = (int)(ldw / tke);
+        pl.cblock = false;
+    } else {
+        pl.cblock = (g.C % tke) == 0;
+        p.nk = pl.cblock ? (int)(g.T * g.R * g.S * (g.C / tke)) : (int)(ldw / tke);
+    }
     const int64_t tm = ((int64_t)p.M + ts.bm - 1) / ts.bm, tn = ((int64_t)p.Ncol + ts.bn - 1) / ts.bn;
     if (tm * tn > kI32Max)
         return fail(IGC_ERR_UNSUPPORTED, "grid of %lld tiles too large", (long long)(tm * tn));
@@ -224,6 +239,8 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
     // Workgroups resident on one XCD (32 CUs): one 256x256 or two smaller tiles per CU.
     const int resident = 32 * (ts.bm == 256 ? 1 : 2);
     p.group_m = (int)std::max<int64_t>(1, resident / tn);
+    if (g_force_group_m.load() > 0)
+        p.group_m = g_force_group_m.load();
     return IGC_OK;
 }
 
@@ -379,21 +396,26 @@ int conv_plan(const int64_t xshape[5], const int64_t wshape[5], const int32_t st
         return rc;
     if (buf && len) {
         const TileShape ts = kTiles[pl.tile];
-        snprintf(buf, len, "path=%s tile=%dx%d waves=%d mfma=%dx%d kstep=%d order=%s big=%d grid=%d group_m=%d nk=%d",
-                 path_name(pl.path), ts.bm, ts.bn, ts.wm * ts.wn, ts.mf, ts.mf, dtype == IGC_FP8_E4M3FN ? 128 : 64,
+        snprintf(buf, len,
+                 "path=%s tile=%dx%d waves=%d mfma=%dx%d stages=%d kstep=%d order=%s big=%d grid=%d group_m=%d nk=%d",
+                 path_name(pl.path), ts.bm, ts.bn, ts.wm * ts.wn, ts.mf, ts.mf, ts.stages ? ts.stages : 2,
+                 step_bytes(ts) / (dtype == IGC_FP8_E4M3FN ? 1 : 2),
                  pl.cblock ? "cblock" : "linear", pl.big ? 1 : 0, pl.p.tiles_m * pl.p.tiles_n, pl.p.group_m, pl.p.nk);
     }
     return ok();
 }
 
-int conv_debug_force(int path, int tile)
+int conv_debug_force(int path, int tile, int group_m)
 {
     if (path < IGC_PATH_AUTO || path > IGC_PATH_POINT)
         return fail(IGC_ERR_INVALID, "conv_debug_force: unknown path %d", path);
     if (tile < -1 || tile >= kNumTiles)
         return fail(IGC_ERR_INVALID, "conv_debug_force: tile %d not in [-1, %d)", tile, kNumTiles);
+    if (group_m < 0)
+        return fail(IGC_ERR_INVALID, "conv_debug_force: group_m %d < 0", group_m);
     g_force_path.store(path);
     g_force_tile.store(tile);
+    g_force_group_m.store(group_m);
     return ok();
 }
 

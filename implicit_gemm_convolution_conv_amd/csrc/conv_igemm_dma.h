@@ -1,0 +1,382 @@
+// Implicit-GEMM forward convolution, im2col paths, with a multi-stage
+// direct-to-LDS pipeline (gfx950 global_load_lds_dwordx4).
+//
+// Same GEMM as conv_igemm_kernel (rows = output positions, columns = output
+// channels, reduction over (t, r, s, c)), but the operand tiles go from global
+// memory straight into LDS without passing through registers, as the async
+// global->LDS pipeline of FlyDSL PR #860 does (async DMA commit). Freed of
+// staging registers, the ring holds S stages of 64 bytes of k per row, so a
+// load is issued S-1 reduction steps before its data are consumed, which
+// hides L2-miss latency that a one-step register prefetch exposes.
+//
+// An LDS-DMA instruction writes lane i's 16 bytes at base + 16 * i: one wave
+// instruction fills 16 consecutive 64-byte rows. The LDS layout (chunk q of
+// row r at slot q ^ ((r >> 1) & 3)) is therefore produced by choosing which
+// chunk each lane fetches. Zero padding: a lane whose tap falls outside the
+// input box (or whose row is past M, or whose reduction index is past
+// C*T*R*S) fetches a 16-byte zero line instead.
+#pragma once
+
+#include "conv_igemm.h"
+
+namespace igc {
+
+// Sixteen zero bytes: the source of every padding chunk.
+__device__ __attribute__((aligned(16))) const int kZeroLine[4] = {0, 0, 0, 0};
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
+template <int N>
+__device__ inline void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, bool BIG, bool CBLK, int S>
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void conv_igemm_dma_kernel(ConvParams p)
+{
+    using Off = typename OffType<BIG>::type;
+    constexpr int NW = WM * WN;                // waves
+    constexpr int ESZ = DT == DT_FP8 ? 1 : 2;  // bytes per element
+    constexpr int CH = 16 / ESZ;               // elements per 16-byte chunk
+    constexpr int KB = 64;                     // bytes of k per row per stage
+    constexpr int TKE = KB / ESZ;              // elements per reduction step
+    constexpr int AIT = BM / (16 * NW);        // A row groups (16 rows each) per wave
+    constexpr int BIT = BN / (16 * NW);
+    constexpr int LPS = AIT + BIT;             // LDS-DMA loads per thread per stage
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / MF, FN = WTN / MF;
+    constexpr int STAGE = (BM + BN) * KB;
+    static_assert(MODE != MODE_POINT, "point mode uses the register-staged kernel");
+    static_assert(AIT >= 1 && BIT >= 1 && BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "loader split");
+    static_assert(MF == 32 || DT == DT_BF16, "fp8 needs 128-byte k per 16x16 MFMA: use 32x32 blocks");
+    static_assert(WTM % MF == 0 && WTN % MF == 0, "MFMA blocks");
+    static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS budget");
+    static_assert(LPS * (S - 2) < 64, "vmcnt range");
+
+    __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave % WM, wn = wave / WM;
+
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // This lane's row within each 16-row group and the chunk it fetches there.
+    const int lr = lane >> 2;
+    const int jc = (lane & 3) ^ ((lane >> 3) & 3);
+
+    const char *xb = static_cast<const char *>(p.x);
+    const char *wb = static_cast<const char *>(p.w);
+    const char *zero = reinterpret_cast<const char *>(kZeroLine);
+
+    // ---------------------------------------------------------------- A rows (im2col origins)
+    int a_id0[AIT], a_ih0[AIT], a_iw0[AIT];
+    Off a_base[AIT];
+    {
+        const int hw = p.Ho * p.Wo;
+#pragma unroll
+        for (int i = 0; i < AIT; ++i) {
+            const int m = m0 + 16 * (wave + i * NW) + lr;
+            if (m < p.M) {
+                const int nimg = m / p.P;
+                const int sp = m - nimg * p.P;
+                const int od = sp / hw;
+                const int rem = sp - od * hw;
+                const int oh = rem / p.Wo;
+                const int ow = rem - oh * p.Wo;
+                a_id0[i] = od * p.sd - p.pd;
+                a_ih0[i] = oh * p.sh - p.ph;
+                a_iw0[i] = ow * p.sw - p.pw;
+                if constexpr (MODE == MODE_TEMPORAL)
+                    a_base[i] = (((Off)nimg * p.D + a_id0[i]) * (Off)(p.H * p.W) + rem) * (Off)p.C;
+                else
+                    a_base[i] = ((((Off)nimg * p.D + a_id0[i]) * p.H + a_ih0[i]) * (Off)p.W + a_iw0[i]) * (Off)p.C;
+            } else {
+                a_id0[i] = a_ih0[i] = a_iw0[i] = -(1 << 29);
+                a_base[i] = 0;
+            }
+        }
+    }
+    // ---------------------------------------------------------------- B rows (filter)
+    const char *b_row[BIT];
+#pragma unroll
+    for (int i = 0; i < BIT; ++i) {
+        const int n = n0 + 16 * (wave + i * NW) + lr;
+        b_row[i] = n < p.Ncol ? wb + (int64_t)n * p.ldw * ESZ : nullptr;
+    }
+
+    // ---------------------------------------------------------------- k position of the next issue
+    int kc, c = 0, t = 0, r = 0, s = 0;
+    bool kval = true;
+    if constexpr (!CBLK) {
+        kc = jc * CH;
+        c = kc % p.C;
+        const int tap = kc / p.C;
+        s = tap % p.S;
+        r = (tap / p.S) % p.R;
+        t = tap / (p.S * p.R);
+        kval = kc < p.Rk;
+    } else {
+        c = jc * CH;
+        kc = c;
+    }
+    Off tapoff = 0;
+    auto update_tapoff = [&]() {
+        if constexpr (MODE == MODE_TEMPORAL)
+            tapoff = (Off)(t * p.dd) * (Off)(p.H * p.W) * (Off)p.C + c;
+        else
+            tapoff = (((Off)(t * p.dd) * p.H + r * p.dh) * (Off)p.W + s * p.dw) * (Off)p.C + c;
+    };
+    update_tapoff();
+    auto advance = [&]() {
+        if constexpr (CBLK) {
+            if (++s == p.S) {
+                s = 0;
+                if (++r == p.R) {
+                    r = 0;
+                    if (++t == p.T) {
+                        t = 0;
+                        c += TKE;
+                    }
+                }
+            }
+            kc = ((t * p.R + r) * p.S + s) * p.C + c;
+        } else {
+            kc += TKE;
+            kval = kc < p.Rk;
+            c += TKE;
+            while (c >= p.C) {
+                c -= p.C;
+                if (++s == p.S) {
+                    s = 0;
+                    if (++r == p.R) {
+                        r = 0;
+                        ++t;
+                    }
+                }
+            }
+        }
+        update_tapoff();
+    };
+
+    // Issue one reduction step into LDS stage st: A then B, one instruction per 16-row group.
+    auto issue = [&](int st) {
+        char *stage = smem + st * STAGE;
+#pragma unroll
+        for (int i = 0; i < AIT; ++i) {
+            bool ok;
+            if constexpr (MODE == MODE_TEMPORAL) {
+                ok = kval && (unsigned)(a_id0[i] + t * p.dd) < (unsigned)p.D;
+            } else {
+                ok = kval && (unsigned)(a_id0[i] + t * p.dd) < (unsigned)p.D &&
+                     (unsigned)(a_ih0[i] + r * p.dh) < (unsigned)p.H &&
+                     (unsigned)(a_iw0[i] + s * p.dw) < (unsigned)p.W;
+            }
+            const char *src = ok ? xb + (a_base[i] + tapoff) * ESZ : zero;
+            __builtin_amdgcn_global_load_lds(
+                src, (__attribute__((address_space(3))) void *)(stage + 16 * (wave + i * NW) * KB), 16, 0, 0);
+        }
+        char *bst = stage + BM * KB;
+#pragma unroll
+        for (int i = 0; i < BIT; ++i) {
+            const char *src = b_row[i] ? b_row[i] + (int64_t)kc * ESZ : zero;
+            __builtin_amdgcn_global_load_lds(
+                src, (__attribute__((address_space(3))) void *)(bst + 16 * (wave + i * NW) * KB), 16, 0, 0);
+        }
+    };
+
+    // ---------------------------------------------------------------- MFMA
+    using AccT = typename AccType<MF>::type;
+    AccT acc[FM][FN];
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b)
+            acc[a][b] = AccT{};
+
+    const int lrow = lane & (MF - 1), lgrp = lane / MF, lsw = (lane >> 1) & 3;
+    auto compute = [&](const char *st) {
+        const char *aw = st + (wm * WTM + lrow) * KB;
+        const char *bw = st + BM * KB + (wn * WTN + lrow) * KB;
+        constexpr int GROUPS = 64 / MF;
+        constexpr int CPL = DT == DT_BF16 ? 1 : 2;
+        constexpr int SUB = (KB / 16) / (GROUPS * CPL);
+        static_assert(SUB >= 1, "step too short for this MFMA");
+#pragma unroll
+        for (int h = 0; h < SUB; ++h) {
+            const int c0 = (h * GROUPS + lgrp) * CPL;
+            const int sl0 = (c0 ^ lsw) * 16;
+            const int sl1 = ((c0 + 1) ^ lsw) * 16;
+            if constexpr (DT == DT_BF16) {
+                bf16x8 bf[FN];
+#pragma unroll
+                for (int b = 0; b < FN; ++b)
+                    bf[b] = *reinterpret_cast<const bf16x8 *>(bw + b * MF * KB + sl0);
+#pragma unroll
+                for (int a = 0; a < FM; ++a) {
+                    const bf16x8 af = *reinterpret_cast<const bf16x8 *>(aw + a * MF * KB + sl0);
+#pragma unroll
+                    for (int b = 0; b < FN; ++b) {
+                        if constexpr (MF == 16)
+                            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[b], acc[a][b], 0, 0, 0);
+                        else
+                            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[b], acc[a][b], 0, 0, 0);
+                    }
+                }
+            } else {
+                i32x8 bf[FN];
+#pragma unroll
+                for (int b = 0; b < FN; ++b) {
+                    const i32x4 lo = *reinterpret_cast<const i32x4 *>(bw + b * MF * KB + sl0);
+                    const i32x4 hi = *reinterpret_cast<const i32x4 *>(bw + b * MF * KB + sl1);
+                    bf[b] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+#pragma unroll
+                for (int a = 0; a < FM; ++a) {
+                    const i32x4 lo = *reinterpret_cast<const i32x4 *>(aw + a * MF * KB + sl0);
+                    const i32x4 hi = *reinterpret_cast<const i32x4 *>(aw + a * MF * KB + sl1);
+                    const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+                    for (int b = 0; b < FN; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[b], acc[a][b], 0, 0, 0, 0,
+                                                                                    0, 0);
+                }
+            }
+        }
+    };
+
+    // ---------------------------------------------------------------- pipeline
+    // Stage ks lives in slot ks % S. Before computing step ks every thread
+    // waits until its own loads of step ks have landed (later steps may stay
+    // in flight), then the barrier makes all threads' data visible and
+    // guarantees that step ks-1's slot is no longer read, so step ks+S-1 can be
+    // issued into it.
+    const int nk = p.nk;
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st) {
+        if (st < nk) {
+            issue(st);
+            if (st + 1 < nk)
+                advance();
+        }
+    }
+    for (int ks = 0; ks < nk; ++ks) {
+        const int ahead = nk - 1 - ks;  // steps issued after ks, capped at S-2
+        if (ahead >= S - 2) {
+            wait_vmcnt<LPS * (S - 2)>();
+        } else if constexpr (S > 3) {
+            if (ahead == 1)
+                wait_vmcnt<LPS>();
+            else
+                wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        asm volatile("s_barrier" ::: "memory");
+        if (ks + S - 1 < nk) {
+            issue((ks + S - 1) % S);
+            if (ks + S < nk)
+                advance();
+        }
+        compute(smem + (ks % S) * STAGE);
+    }
+
+    // ---------------------------------------------------------------- epilogue
+    float sc = 1.0f;
+    if constexpr (DT == DT_FP8)
+        sc = p.scales[0] * p.scales[2];
+    uint16_t *yb = static_cast<uint16_t *>(p.y);
+    constexpr int QUADS = MF / 16 * (MF / 16);
+#pragma unroll
+    for (int a = 0; a < FM; ++a) {
+#pragma unroll
+        for (int q = 0; q < QUADS; ++q) {
+            const int row = m0 + wm * WTM + a * MF + (MF == 16 ? 4 * lgrp : 8 * q + 4 * lgrp);
+            int nimg = 0, sp = 0;
+            if (row < p.M) {
+                nimg = row / p.P;
+                sp = row - nimg * p.P;
+            }
+            const bool vec = (p.P & 3) == 0 && row + 3 < p.M;
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                const int col = n0 + wn * WTN + b * MF + lrow;
+                if (row >= p.M || col >= p.K)
+                    continue;
+                const f32x4 v = quad<MF>(acc[a][b], q) * sc;
+                if (vec) {
+                    const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                      f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+                    *reinterpret_cast<u32x2 *>(yb + ((Off)nimg * p.K + col) * (Off)p.P + sp) = pk;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = row + e;
+                        if (m < p.M) {
+                            const int n2 = m / p.P;
+                            const int sp2 = m - n2 * p.P;
+                            yb[((Off)n2 * p.K + col) * (Off)p.P + sp2] = (uint16_t)f32_to_bf16_rne(v[e]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Launch helper for one dtype: tile index 6.. of kTiles (the direct-to-LDS tiles).
+template <int DT>
+hipError_t launch_conv_dma_dt(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+#define IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_, BIG_, CBLK_)                                              \
+    do {                                                                                                       \
+        hipLaunchKernelGGL((conv_igemm_dma_kernel<BM_, BN_, WM_, WN_, MF_, DT, MODE_, BIG_, CBLK_, S_>), grid, \
+                           dim3(WM_ * WN_ * 64), 0, stream, p);                                                \
+        return hipGetLastError();                                                                              \
+    } while (0)
+#define IGC_DMODES(BM_, BN_, WM_, WN_, MF_, S_)                                                                \
+    do {                                                                                                       \
+        if (mode == MODE_TEMPORAL) {                                                                           \
+            if (big) {                                                                                         \
+                if (cblock) IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_TEMPORAL, true, true);               \
+                IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_TEMPORAL, true, false);                          \
+            }                                                                                                  \
+            if (cblock) IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_TEMPORAL, false, true);                  \
+            IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_TEMPORAL, false, false);                             \
+        }                                                                                                      \
+        if (big) {                                                                                             \
+            if (cblock) IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_GENERIC, true, true);                    \
+            IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_GENERIC, true, false);                               \
+        }                                                                                                      \
+        if (cblock) IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_GENERIC, false, true);                       \
+        IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_GENERIC, false, false);                                  \
+    } while (0)
+    if (mode == MODE_POINT)
+        return hipErrorInvalidValue;
+    if constexpr (DT == DT_BF16) {
+        switch (tile) {
+        case 6: IGC_DMODES(256, 256, 2, 4, 16, 4);
+        case 7: IGC_DMODES(256, 256, 2, 4, 32, 4);
+        case 8: IGC_DMODES(128, 128, 2, 2, 16, 4);
+        case 9: IGC_DMODES(128, 128, 2, 2, 32, 4);
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (tile) {
+        case 7: IGC_DMODES(256, 256, 2, 4, 32, 4);
+        case 9: IGC_DMODES(128, 128, 2, 2, 32, 4);
+        default: return hipErrorInvalidValue;
+        }
+    }
+#undef IGC_DMODES
+#undef IGC_DLAUNCH
+}
+
+}  // namespace igc

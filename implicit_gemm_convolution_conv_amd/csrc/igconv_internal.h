@@ -12,19 +12,25 @@ enum Dtype { DT_BF16 = 0, DT_FP8 = 1 };
 
 // Tile shapes: rows x cols of the GEMM tile, waves along rows x cols, MFMA
 // block edge (16: 16x16 blocks; 32: 32x32 blocks, which need fewer operand
-// registers per lane). The reduction step is always 128 bytes of k per row:
-// 64 bf16 or 128 fp8.
+// registers per lane) and LDS stages. stages == 0: register-staged kernel,
+// two LDS buffers, 128 bytes of k per row per step (64 bf16 / 128 fp8).
+// stages > 0: direct-to-LDS ring of that many stages, 64 bytes of k per row
+// per step (32 bf16 / 64 fp8); fp8 needs 32x32 blocks there.
 struct TileShape {
-    int bm, bn, wm, wn, mf;
+    int bm, bn, wm, wn, mf, stages;
 };
-constexpr int kNumTiles = 6;
+constexpr int kNumTiles = 10;
 constexpr TileShape kTiles[kNumTiles] = {
-    {256, 256, 2, 4, 16},  // 8 waves, 128x64 per wave: large grids
-    {128, 128, 2, 2, 16},  // 4 waves, 64x64 per wave
-    {64, 64, 2, 2, 16},    // 4 waves, 32x32 per wave: small grids
-    {256, 256, 2, 4, 32},
-    {128, 128, 2, 2, 32},
-    {64, 64, 2, 2, 32},
+    {256, 256, 2, 4, 16, 0},  // 8 waves, 128x64 per wave: large grids
+    {128, 128, 2, 2, 16, 0},  // 4 waves, 64x64 per wave
+    {64, 64, 2, 2, 16, 0},    // 4 waves, 32x32 per wave: small grids
+    {256, 256, 2, 4, 32, 0},
+    {128, 128, 2, 2, 32, 0},
+    {64, 64, 2, 2, 32, 0},
+    {256, 256, 2, 4, 16, 4},  // direct-to-LDS, 4 x 32 KB ring
+    {256, 256, 2, 4, 32, 4},
+    {128, 128, 2, 2, 16, 4},  // direct-to-LDS, 4 x 16 KB ring
+    {128, 128, 2, 2, 32, 4},
 };
 
 // Everything a conv kernel needs, passed by value as kernel arguments.
@@ -51,6 +57,8 @@ struct ConvParams {
 // 64-bit addressing, channel-block-outer reduction order).
 hipError_t launch_conv(const ConvParams &p, int tile, Mode mode, Dtype dt, bool big, bool cblock,
                        hipStream_t stream);
+// Reduction step of a tile in bytes of k per row.
+constexpr int step_bytes(const TileShape &t) { return t.stages ? 64 : 128; }
 
 hipError_t launch_amax(const uint16_t *t, int64_t n, float *amax, hipStream_t stream);
 hipError_t launch_fp8_scales(const float *amax, float *pair, hipStream_t stream);

@@ -158,11 +158,12 @@ IGC_API int conv_plan(const int64_t xshape[5], const int64_t wshape[5], const in
               const int32_t dilation[3], int dtype, int x_layout, char *buf, size_t len);
 
 /*
- * Testing hook: force the path (IGC_PATH_*) and/or the tile index (-1 = automatic)
- * for later conv_fwd / conv_plan calls of this process. A forced path that
- * does not apply to a shape makes conv_fwd return IGC_ERR_UNSUPPORTED.
+ * Testing and tuning hook: force the path (IGC_PATH_*), the tile index (-1 =
+ * automatic) and the grouped-raster height in tiles (0 = automatic) for later
+ * conv_fwd / conv_plan calls of this process. A forced path or tile that does
+ * not apply to a shape makes conv_fwd return IGC_ERR_UNSUPPORTED.
  */
-IGC_API int conv_debug_force(int path, int tile);
+IGC_API int conv_debug_force(int path, int tile, int group_m);
 
 /* Text of the last error on this thread ("" if none). Valid until the next call. */
 IGC_API const char *conv_last_error(void);

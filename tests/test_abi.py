@@ -74,15 +74,22 @@ def test_path_selection():
 
 def test_forced_path_and_tile():
     try:
-        B.conv_debug_force(B.IGC_PATH_GENERIC, 1)
+        B.conv_debug_force(B.IGC_PATH_GENERIC, 1, 0)
         p = _plan((1, 64, 8, 8, 8), (64, 64, 3, 1, 1), pd=(1, 0, 0))
         assert (p["path"], p["tile"]) == ("generic", "128x128")
-        B.conv_debug_force(B.IGC_PATH_POINT, -1)
+        B.conv_debug_force(B.IGC_PATH_POINT, -1, 0)
         with pytest.raises(B.IgcError) as e:
             _plan((1, 64, 8, 8, 8), (64, 64, 3, 1, 1), pd=(1, 0, 0))
         assert e.value.status == B.IGC_ERR_UNSUPPORTED
+        B.conv_debug_force(B.IGC_PATH_AUTO, 6, 0)  # direct-to-LDS 16x16 tile cannot run fp8
+        with pytest.raises(B.IgcError) as e:
+            _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1), dt=B.IGC_FP8_E4M3FN)
+        assert e.value.status == B.IGC_ERR_UNSUPPORTED
+        B.conv_debug_force(B.IGC_PATH_AUTO, 7, 5)
+        p = _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1), dt=B.IGC_FP8_E4M3FN)
+        assert (p["stages"], p["kstep"], p["group_m"]) == ("4", "64", "5")
     finally:
-        B.conv_debug_force(B.IGC_PATH_AUTO, -1)
+        B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)
 
 
 @pytest.mark.parametrize("args,status", [

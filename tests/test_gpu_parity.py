@@ -25,6 +25,19 @@ def _announce(name):
     print(f"[case] {name}", flush=True)
 
 
+class forced:
+    """Force a path / tile / raster group for the duration of a with-block."""
+
+    def __init__(self, path=B.IGC_PATH_AUTO, tile=-1, group_m=0):
+        self.args = (path, tile, group_m)
+
+    def __enter__(self):
+        B.conv_debug_force(*self.args)
+
+    def __exit__(self, *exc):
+        B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)
+
+
 def _bf16_case(name, xs, ws, st, pd, dl, seed, dist=("uniform", 1.0), x_layout="NDHWC"):
     _announce(name)
     g = I.generator(seed, P.DEV)
@@ -98,10 +111,10 @@ def test_temporal_path_matches_generic_bitwise():
     assert B.conv_plan(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC).startswith("path=temporal")
     y_fast = P.run_bf16(x, w, st, pd, dl)
     try:
-        B.conv_debug_force(B.IGC_PATH_GENERIC, -1)
+        B.conv_debug_force(B.IGC_PATH_GENERIC, -1, 0)
         y_gen = P.run_bf16(x, w, st, pd, dl)
     finally:
-        B.conv_debug_force(B.IGC_PATH_AUTO, -1)
+        B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)
     assert torch.equal(y_fast.view(torch.int16), y_gen.view(torch.int16))
 
 
@@ -115,10 +128,10 @@ def test_every_tile_gives_identical_bits():
     outs = []
     try:
         for tile in range(3):
-            B.conv_debug_force(B.IGC_PATH_AUTO, tile)
+            B.conv_debug_force(B.IGC_PATH_AUTO, tile, 0)
             outs.append(P.run_bf16(x, w, st, pd, dl).clone())
     finally:
-        B.conv_debug_force(B.IGC_PATH_AUTO, -1)
+        B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)
     ref = O.conv3d(P.bits(x), P.bits(w), st, pd, dl)
     P.check_close(P.y_values(outs[0]), ref, 64 * 27, float(x.abs().max()), float(w.abs().max()), "tile0")
     for o in outs[1:]:
@@ -241,3 +254,57 @@ def test_amax_handles_tails_and_zero():
     B.conv_fp8_scales(amax, pair)
     torch.cuda.synchronize()
     assert pair.tolist() == [1.0, 1.0]
+
+
+# ------------------------------------------------------------------ direct-to-LDS pipeline tiles
+
+DMA_CASES = [g for g in GEOMS if g[0] in ("ragged_linear_c24", "c128_cblock_multi_tile", "asym_pad_stride2",
+                                           "temporal_3x1x1", "temporal_strided_dilated", "c8_tiny")]
+
+
+@pytest.mark.parametrize("tile", [6, 7, 8, 9])
+@pytest.mark.parametrize("case", DMA_CASES, ids=[g[0] for g in DMA_CASES])
+def test_dma_tiles_bf16(tile, case):
+    name, xs, ws, st, pd, dl = case
+    with forced(tile=tile):
+        _bf16_case(f"dma tile {tile} {name}", xs, ws, st, pd, dl, seed=zlib.crc32(name.encode()) % 1000)
+
+
+@pytest.mark.parametrize("tile", [6, 7, 8, 9])
+def test_dma_tiles_integer_bit_exact(tile):
+    _announce(f"dma tile {tile} integer")
+    with forced(tile=tile):
+        _int_case((2, 64, 5, 9, 11), (96, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), seed=24)
+        _int_case((1, 24, 6, 7, 8), (40, 24, 3, 2, 3), (2, 1, 2), (1, 0, 2), (1, 2, 1), seed=25)
+
+
+@pytest.mark.parametrize("tile", [7, 9])
+@pytest.mark.parametrize("case", FP8_GEOMS, ids=[g[0] for g in FP8_GEOMS])
+def test_dma_tiles_fp8(tile, case):
+    name, xs, ws, st, pd, dl = case
+    _announce(f"dma tile {tile} {name}")
+    g = I.generator(32, P.DEV)
+    x = I.draw(xs, ("normal", 1.0), g, P.DEV)
+    w = I.draw(ws, ("normal", 1.0 / np.sqrt(np.prod(ws[1:]))), g, P.DEV)
+    ops = P.Fp8Operands(x, w)
+    with forced(tile=tile):
+        y = P.run_fp8(ops, xs, ws, st, pd, dl)
+    sx, sw = float(ops.ref_scales[0]), float(ops.ref_scales[2])
+    ref = O.conv3d(ops.ref_xq, ops.ref_wq, st, pd, dl, sx=sx, sw=sw)
+    mx = float(np.abs(O.e4m3_decode(ops.ref_xq)).max()) * sx
+    mw = float(np.abs(O.e4m3_decode(ops.ref_wq)).max()) * sw
+    P.check_close(P.y_values(y), ref, int(np.prod(ws[1:])), mx, mw, name)
+
+
+def test_dma_tiles_agree_bitwise():
+    # 16x16-block direct-to-LDS tiles walk the reduction in the same order
+    _announce("dma tiles 6 / 8 bitwise")
+    g = I.generator(15, P.DEV)
+    xs, ws, st, pd, dl = (1, 64, 5, 18, 20), (136, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)
+    x = I.draw(xs, ("uniform", 1.0), g, P.DEV)
+    w = I.draw(ws, ("uniform", 1.0), g, P.DEV)
+    outs = []
+    for tile in (6, 8):
+        with forced(tile=tile):
+            outs.append(P.run_bf16(x, w, st, pd, dl).clone())
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
