@@ -216,28 +216,29 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         const int base = (dtype == IGC_FP8_E4M3FN && path == IGC_PATH_GENERIC) ? 3 : 0;
         tile = base + (nblocks(base) >= 512 ? 0 : (nblocks(base + 1) >= 256 ? 1 : 2));
     } else {
-        if (kTiles[tile].stages && path == IGC_PATH_POINT)
-            return fail(IGC_ERR_UNSUPPORTED, "tile %d (direct-to-LDS) does not run the point-output path", tile);
         if (kTiles[tile].stages && kTiles[tile].mf == 16 && esz == 1)
             return fail(IGC_ERR_UNSUPPORTED, "tile %d: fp8 with 64-byte steps needs 32x32 MFMA blocks", tile);
+        if (esz == 2 && (tile == 12 || tile == 13))
+            return fail(IGC_ERR_UNSUPPORTED, "tile %d is an fp8-only tile", tile);
     }
     pl.tile = tile;
     const TileShape ts = kTiles[tile];
     const int tke = step_bytes(ts) / esz;  // elements per reduction step
     if (path == IGC_PATH_POINT) {
-        p.nk = (int)(ldw / tke);
+        p.nk = (int)((rk + tke - 1) / tke);  // no step made only of the filter's zero padding
         pl.cblock = false;
     } else {
         pl.cblock = (g.C % tke) == 0;
         p.nk = pl.cblock ? (int)(g.T * g.R * g.S * (g.C / tke)) : (int)(ldw / tke);
     }
+    p.pairs = (ts.stages && pl.cblock && (g.C % (2 * tke)) == 0) ? 2 : 1;
     const int64_t tm = ((int64_t)p.M + ts.bm - 1) / ts.bm, tn = ((int64_t)p.Ncol + ts.bn - 1) / ts.bn;
     if (tm * tn > kI32Max)
         return fail(IGC_ERR_UNSUPPORTED, "grid of %lld tiles too large", (long long)(tm * tn));
     p.tiles_m = (int)tm;
     p.tiles_n = (int)tn;
     // Workgroups resident on one XCD (32 CUs): one 256x256 or two smaller tiles per CU.
-    const int resident = 32 * (ts.bm == 256 ? 1 : 2);
+    const int resident = 32 * (ts.bm * ts.bn >= 256 * 256 ? 1 : 2);
     p.group_m = (int)std::max<int64_t>(1, resident / tn);
     if (g_force_group_m.load() > 0)
         p.group_m = g_force_group_m.load();
@@ -397,10 +398,10 @@ int conv_plan(const int64_t xshape[5], const int64_t wshape[5], const int32_t st
     if (buf && len) {
         const TileShape ts = kTiles[pl.tile];
         snprintf(buf, len,
-                 "path=%s tile=%dx%d waves=%d mfma=%dx%d stages=%d kstep=%d order=%s big=%d grid=%d group_m=%d nk=%d",
+                 "path=%s tile=%dx%d waves=%d mfma=%dx%d stages=%d kstep=%d order=%s%s big=%d grid=%d group_m=%d nk=%d",
                  path_name(pl.path), ts.bm, ts.bn, ts.wm * ts.wn, ts.mf, ts.mf, ts.stages ? ts.stages : 2,
                  step_bytes(ts) / (dtype == IGC_FP8_E4M3FN ? 1 : 2),
-                 pl.cblock ? "cblock" : "linear", pl.big ? 1 : 0, pl.p.tiles_m * pl.p.tiles_n, pl.p.group_m, pl.p.nk);
+                 pl.cblock ? "cblock" : "linear", pl.p.pairs == 2 ? "-paired" : "", pl.big ? 1 : 0, pl.p.tiles_m * pl.p.tiles_n, pl.p.group_m, pl.p.nk);
     }
     return ok();
 }

@@ -15,6 +15,12 @@
 // chunk each lane fetches. Zero padding: a lane whose tap falls outside the
 // input box (or whose row is past M, or whose reduction index is past
 // C*T*R*S) fetches a 16-byte zero line instead.
+//
+// Point-output mode (MIOpen PR #10912: one GEMM over the batch) uses the
+// filter as A and the flattened images as B. Image rows end at C*T*R*S
+// elements with no padding and are only 4-byte aligned; the one chunk that
+// straddles a row's end is fetched as zeros by the DMA and then overwritten
+// from registers with its valid bytes before the last step is consumed.
 #pragma once
 
 #include "conv_igemm.h"
@@ -33,8 +39,14 @@ __device__ inline void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Waves per SIMD the register budget is sized for: two for 8-wave tiles and
+// for tiles small enough that two workgroups share a CU, one for the 4-wave
+// 256x256 tile whose 128x128 wave tiles hold 256 fp32 accumulators per lane.
+template <int BM, int BN, int WM, int WN>
+constexpr int dma_waves_per_eu() { return (WM * WN == 4 && BM * BN >= 256 * 256) ? 1 : 2; }
+
 template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, bool BIG, bool CBLK, int S>
-__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN>())))
 void conv_igemm_dma_kernel(ConvParams p)
 {
     using Off = typename OffType<BIG>::type;
@@ -49,7 +61,7 @@ void conv_igemm_dma_kernel(ConvParams p)
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / MF, FN = WTN / MF;
     constexpr int STAGE = (BM + BN) * KB;
-    static_assert(MODE != MODE_POINT, "point mode uses the register-staged kernel");
+    static_assert(MODE != MODE_POINT || !CBLK, "point mode reduces in natural order");
     static_assert(AIT >= 1 && BIT >= 1 && BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "loader split");
     static_assert(MF == 32 || DT == DT_BF16, "fp8 needs 128-byte k per 16x16 MFMA: use 32x32 blocks");
     static_assert(WTM % MF == 0 && WTN % MF == 0, "MFMA blocks");
@@ -75,10 +87,18 @@ void conv_igemm_dma_kernel(ConvParams p)
     const char *wb = static_cast<const char *>(p.w);
     const char *zero = reinterpret_cast<const char *>(kZeroLine);
 
-    // ---------------------------------------------------------------- A rows (im2col origins)
+    // ---------------------------------------------------------------- A rows
+    // im2col modes: input origin of each row; point mode: filter rows.
     int a_id0[AIT], a_ih0[AIT], a_iw0[AIT];
     Off a_base[AIT];
-    {
+    const char *a_row[AIT];
+    if constexpr (MODE == MODE_POINT) {
+#pragma unroll
+        for (int i = 0; i < AIT; ++i) {
+            const int k = m0 + 16 * (wave + i * NW) + lr;
+            a_row[i] = k < p.M ? wb + (int64_t)k * p.ldw * ESZ : nullptr;
+        }
+    } else {
         const int hw = p.Ho * p.Wo;
 #pragma unroll
         for (int i = 0; i < AIT; ++i) {
@@ -108,13 +128,21 @@ void conv_igemm_dma_kernel(ConvParams p)
 #pragma unroll
     for (int i = 0; i < BIT; ++i) {
         const int n = n0 + 16 * (wave + i * NW) + lr;
-        b_row[i] = n < p.Ncol ? wb + (int64_t)n * p.ldw * ESZ : nullptr;
+        if constexpr (MODE == MODE_POINT)  // image n: Rk elements
+            b_row[i] = n < p.Ncol ? xb + (int64_t)n * p.Rk * ESZ : nullptr;
+        else  // filter row n
+            b_row[i] = n < p.Ncol ? wb + (int64_t)n * p.ldw * ESZ : nullptr;
     }
+    // point mode: valid bytes of the chunk that straddles the end of an image row
+    i32x4 tailv[BIT];
+    unsigned tail_mask = 0;
 
     // ---------------------------------------------------------------- k position of the next issue
     int kc, c = 0, t = 0, r = 0, s = 0;
     bool kval = true;
-    if constexpr (!CBLK) {
+    if constexpr (MODE == MODE_POINT) {
+        kc = jc * CH;
+    } else if constexpr (!CBLK) {
         kc = jc * CH;
         c = kc % p.C;
         const int tap = kc / p.C;
@@ -126,26 +154,39 @@ void conv_igemm_dma_kernel(ConvParams p)
         c = jc * CH;
         kc = c;
     }
+    // Channel-block order: channel block (pairs * TKE) outer, tap, then the
+    // `pairs` consecutive TKE-wide halves of each 128-byte line, so the two
+    // halves of a cache line are fetched by consecutive steps.
+    int cbase = 0, half = 0;
     Off tapoff = 0;
     auto update_tapoff = [&]() {
-        if constexpr (MODE == MODE_TEMPORAL)
+        if constexpr (MODE == MODE_POINT)
+            return;
+        else if constexpr (MODE == MODE_TEMPORAL)
             tapoff = (Off)(t * p.dd) * (Off)(p.H * p.W) * (Off)p.C + c;
         else
             tapoff = (((Off)(t * p.dd) * p.H + r * p.dh) * (Off)p.W + s * p.dw) * (Off)p.C + c;
     };
     update_tapoff();
     auto advance = [&]() {
-        if constexpr (CBLK) {
-            if (++s == p.S) {
-                s = 0;
-                if (++r == p.R) {
-                    r = 0;
-                    if (++t == p.T) {
-                        t = 0;
-                        c += TKE;
+        if constexpr (MODE == MODE_POINT) {
+            kc += TKE;
+            return;
+        } else if constexpr (CBLK) {
+            if (++half == p.pairs) {
+                half = 0;
+                if (++s == p.S) {
+                    s = 0;
+                    if (++r == p.R) {
+                        r = 0;
+                        if (++t == p.T) {
+                            t = 0;
+                            cbase += p.pairs * TKE;
+                        }
                     }
                 }
             }
+            c = cbase + half * TKE + jc * CH;
             kc = ((t * p.R + r) * p.S + s) * p.C + c;
         } else {
             kc += TKE;
@@ -170,6 +211,12 @@ void conv_igemm_dma_kernel(ConvParams p)
         char *stage = smem + st * STAGE;
 #pragma unroll
         for (int i = 0; i < AIT; ++i) {
+            if constexpr (MODE == MODE_POINT) {
+                const char *src = a_row[i] ? a_row[i] + (int64_t)kc * ESZ : zero;
+                __builtin_amdgcn_global_load_lds(
+                    src, (__attribute__((address_space(3))) void *)(stage + 16 * (wave + i * NW) * KB), 16, 0, 0);
+                continue;
+            }
             bool ok;
             if constexpr (MODE == MODE_TEMPORAL) {
                 ok = kval && (unsigned)(a_id0[i] + t * p.dd) < (unsigned)p.D;
@@ -185,7 +232,25 @@ void conv_igemm_dma_kernel(ConvParams p)
         char *bst = stage + BM * KB;
 #pragma unroll
         for (int i = 0; i < BIT; ++i) {
-            const char *src = b_row[i] ? b_row[i] + (int64_t)kc * ESZ : zero;
+            const char *src = zero;
+            if constexpr (MODE == MODE_POINT) {
+                if (b_row[i] && kc + CH <= p.Rk) {
+                    src = b_row[i] + (int64_t)kc * ESZ;
+                } else if (b_row[i] && kc < p.Rk) {  // straddles the row end: keep its valid words
+                    const int nwords = (p.Rk - kc) * ESZ / 4;
+                    const int *w4 = reinterpret_cast<const int *>(b_row[i] + (int64_t)kc * ESZ);
+                    i32x4 v = {0, 0, 0, 0};
+#pragma unroll
+                    for (int q = 0; q < 3; ++q)
+                        if (q < nwords)
+                            v[q] = w4[q];
+                    tailv[i] = v;
+                    tail_mask |= 1u << i;
+                }
+            } else {
+                if (b_row[i])
+                    src = b_row[i] + (int64_t)kc * ESZ;
+            }
             __builtin_amdgcn_global_load_lds(
                 src, (__attribute__((address_space(3))) void *)(bst + 16 * (wave + i * NW) * KB), 16, 0, 0);
         }
@@ -279,6 +344,18 @@ void conv_igemm_dma_kernel(ConvParams p)
             wait_vmcnt<0>();
         }
         asm volatile("s_barrier" ::: "memory");
+        if constexpr (MODE == MODE_POINT) {
+            // The straddling chunks belong to the last step (nk = ceil(Rk / TKE)); its
+            // DMA wrote zeros there, which have landed: overwrite them, then publish.
+            if (ks == nk - 1 && (p.Rk % CH) != 0) {
+                char *bst = smem + (ks % S) * STAGE + BM * KB;
+#pragma unroll
+                for (int i = 0; i < BIT; ++i)
+                    if (tail_mask & (1u << i))
+                        *reinterpret_cast<i32x4 *>(bst + 16 * (wave + i * NW) * KB + 16 * lane) = tailv[i];
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            }
+        }
         if (ks + S - 1 < nk) {
             issue((ks + S - 1) % S);
             if (ks + S < nk)
@@ -298,6 +375,29 @@ void conv_igemm_dma_kernel(ConvParams p)
 #pragma unroll
         for (int q = 0; q < QUADS; ++q) {
             const int row = m0 + wm * WTM + a * MF + (MF == 16 ? 4 * lgrp : 8 * q + 4 * lgrp);
+            if constexpr (MODE == MODE_POINT) {
+                // rows are output channels, columns are images: y[n][k] is contiguous in k
+                const bool vec = (p.K & 3) == 0 && row + 3 < p.M;
+#pragma unroll
+                for (int b = 0; b < FN; ++b) {
+                    const int col = n0 + wn * WTN + b * MF + lrow;
+                    if (row >= p.M || col >= p.Ncol)
+                        continue;
+                    const f32x4 v = quad<MF>(acc[a][b], q) * sc;
+                    uint16_t *dst = yb + (Off)col * p.K + row;
+                    if (vec) {
+                        const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                          f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+                        *reinterpret_cast<u32x2 *>(dst) = pk;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (row + e < p.M)
+                                dst[e] = (uint16_t)f32_to_bf16_rne(v[e]);
+                    }
+                }
+                continue;
+            }
             int nimg = 0, sp = 0;
             if (row < p.M) {
                 nimg = row / p.P;
@@ -330,7 +430,7 @@ void conv_igemm_dma_kernel(ConvParams p)
     }
 }
 
-// Launch helper for one dtype: tile index 6.. of kTiles (the direct-to-LDS tiles).
+// Launch helper for one dtype: the direct-to-LDS tiles of kTiles (stages > 0).
 template <int DT>
 hipError_t launch_conv_dma_dt(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream)
 {
@@ -343,6 +443,10 @@ hipError_t launch_conv_dma_dt(const ConvParams &p, int tile, Mode mode, bool big
     } while (0)
 #define IGC_DMODES(BM_, BN_, WM_, WN_, MF_, S_)                                                                \
     do {                                                                                                       \
+        if (mode == MODE_POINT) {                                                                              \
+            if (big) IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_POINT, true, false);                        \
+            IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_POINT, false, false);                                \
+        }                                                                                                      \
         if (mode == MODE_TEMPORAL) {                                                                           \
             if (big) {                                                                                         \
                 if (cblock) IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_TEMPORAL, true, true);               \
@@ -358,20 +462,25 @@ hipError_t launch_conv_dma_dt(const ConvParams &p, int tile, Mode mode, bool big
         if (cblock) IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_GENERIC, false, true);                       \
         IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_GENERIC, false, false);                                  \
     } while (0)
-    if (mode == MODE_POINT)
-        return hipErrorInvalidValue;
     if constexpr (DT == DT_BF16) {
         switch (tile) {
         case 6: IGC_DMODES(256, 256, 2, 4, 16, 4);
         case 7: IGC_DMODES(256, 256, 2, 4, 32, 4);
         case 8: IGC_DMODES(128, 128, 2, 2, 16, 4);
         case 9: IGC_DMODES(128, 128, 2, 2, 32, 4);
+        case 10: IGC_DMODES(128, 128, 2, 2, 16, 8);
+        case 11: IGC_DMODES(64, 64, 2, 2, 16, 4);
+        case 14: IGC_DMODES(256, 256, 2, 2, 16, 4);
+        case 15: IGC_DMODES(256, 256, 2, 2, 32, 4);
         default: return hipErrorInvalidValue;
         }
     } else {
         switch (tile) {
         case 7: IGC_DMODES(256, 256, 2, 4, 32, 4);
         case 9: IGC_DMODES(128, 128, 2, 2, 32, 4);
+        case 12: IGC_DMODES(128, 128, 2, 2, 32, 8);
+        case 13: IGC_DMODES(64, 64, 2, 2, 32, 4);
+        case 15: IGC_DMODES(256, 256, 2, 2, 32, 4);
         default: return hipErrorInvalidValue;
         }
     }

@@ -19,7 +19,7 @@ enum Dtype { DT_BF16 = 0, DT_FP8 = 1 };
 struct TileShape {
     int bm, bn, wm, wn, mf, stages;
 };
-constexpr int kNumTiles = 10;
+constexpr int kNumTiles = 16;
 constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 16, 0},  // 8 waves, 128x64 per wave: large grids
     {128, 128, 2, 2, 16, 0},  // 4 waves, 64x64 per wave
@@ -31,6 +31,12 @@ constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 32, 4},
     {128, 128, 2, 2, 16, 4},  // direct-to-LDS, 4 x 16 KB ring
     {128, 128, 2, 2, 32, 4},
+    {128, 128, 2, 2, 16, 8},  // direct-to-LDS, 8 x 16 KB ring: latency-bound short reductions
+    {64, 64, 2, 2, 16, 4},    // direct-to-LDS, 4 x 8 KB ring, many blocks per CU
+    {128, 128, 2, 2, 32, 8},
+    {64, 64, 2, 2, 32, 4},
+    {256, 256, 2, 2, 16, 4},  // direct-to-LDS, 4 waves of 128x128 (256 accumulators per lane)
+    {256, 256, 2, 2, 32, 4},
 };
 
 // Everything a conv kernel needs, passed by value as kernel arguments.
@@ -51,6 +57,7 @@ struct ConvParams {
     int nk;                 // reduction steps
     int tiles_m, tiles_n;   // grid of output tiles
     int group_m;            // grouped raster height (tiles along M sharing an L2 working set)
+    int pairs;              // direct-to-LDS channel-block order: reduction steps per 128-byte line (1 or 2)
 };
 
 // One launch of the implicit-GEMM kernel selected by (tile, mode, dtype,

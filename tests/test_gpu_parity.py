@@ -262,7 +262,7 @@ DMA_CASES = [g for g in GEOMS if g[0] in ("ragged_linear_c24", "c128_cblock_mult
                                            "temporal_3x1x1", "temporal_strided_dilated", "c8_tiny")]
 
 
-@pytest.mark.parametrize("tile", [6, 7, 8, 9])
+@pytest.mark.parametrize("tile", [6, 7, 8, 9, 14, 15])
 @pytest.mark.parametrize("case", DMA_CASES, ids=[g[0] for g in DMA_CASES])
 def test_dma_tiles_bf16(tile, case):
     name, xs, ws, st, pd, dl = case
@@ -270,7 +270,7 @@ def test_dma_tiles_bf16(tile, case):
         _bf16_case(f"dma tile {tile} {name}", xs, ws, st, pd, dl, seed=zlib.crc32(name.encode()) % 1000)
 
 
-@pytest.mark.parametrize("tile", [6, 7, 8, 9])
+@pytest.mark.parametrize("tile", [6, 7, 8, 9, 14, 15])
 def test_dma_tiles_integer_bit_exact(tile):
     _announce(f"dma tile {tile} integer")
     with forced(tile=tile):
@@ -278,7 +278,7 @@ def test_dma_tiles_integer_bit_exact(tile):
         _int_case((1, 24, 6, 7, 8), (40, 24, 3, 2, 3), (2, 1, 2), (1, 0, 2), (1, 2, 1), seed=25)
 
 
-@pytest.mark.parametrize("tile", [7, 9])
+@pytest.mark.parametrize("tile", [7, 9, 15])
 @pytest.mark.parametrize("case", FP8_GEOMS, ids=[g[0] for g in FP8_GEOMS])
 def test_dma_tiles_fp8(tile, case):
     name, xs, ws, st, pd, dl = case
@@ -298,13 +298,51 @@ def test_dma_tiles_fp8(tile, case):
 
 def test_dma_tiles_agree_bitwise():
     # 16x16-block direct-to-LDS tiles walk the reduction in the same order
-    _announce("dma tiles 6 / 8 bitwise")
+    _announce("dma tiles 6 / 8 / 14 bitwise")
     g = I.generator(15, P.DEV)
     xs, ws, st, pd, dl = (1, 64, 5, 18, 20), (136, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)
     x = I.draw(xs, ("uniform", 1.0), g, P.DEV)
     w = I.draw(ws, ("uniform", 1.0), g, P.DEV)
     outs = []
-    for tile in (6, 8):
+    for tile in (6, 8, 14):
         with forced(tile=tile):
             outs.append(P.run_bf16(x, w, st, pd, dl).clone())
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+@pytest.mark.parametrize("tile", [8, 10, 11])
+@pytest.mark.parametrize("layout", ["NCDHW", "NDHWC"])
+def test_point_output_dma_tiles(tile, layout):
+    with forced(tile=tile):
+        _bf16_case(f"point dma tile {tile} {layout}", (300, 3, 1, 14, 14), (200, 3, 1, 14, 14), (1, 14, 14),
+                   (0, 0, 0), (1, 1, 1), seed=8, dist=("normal", 1.0), x_layout=layout)
+        _bf16_case(f"point dma tile {tile} {layout} k198 odd R", (77, 6, 1, 3, 7), (198, 6, 1, 3, 7), (1, 3, 7),
+                   (0, 0, 0), (1, 1, 1), seed=9, dist=("normal", 1.0), x_layout=layout)
+
+
+@pytest.mark.parametrize("tile", [8, 10, 11])
+def test_point_output_dma_integer_bit_exact(tile):
+    _announce(f"integer point dma tile {tile}")
+    with forced(tile=tile):
+        _int_case((130, 3, 1, 14, 14), (68, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1), seed=26,
+                  x_layout="NCDHW")
+
+
+@pytest.mark.parametrize("tile", [-1, 4, 9, 12, 13])
+def test_point_output_fp8(tile):
+    # channel-last fp8 patch embed: 7x7 filter, stride 7, C=16 (the fp8 pack needs C % 16 == 0)
+    name = f"fp8 point tile {tile}"
+    _announce(name)
+    xs, ws, st, pd, dl = (100, 16, 1, 7, 7), (72, 16, 1, 7, 7), (1, 7, 7), (0, 0, 0), (1, 1, 1)
+    g = I.generator(33, P.DEV)
+    x = I.draw(xs, ("normal", 1.0), g, P.DEV)
+    w = I.draw(ws, ("normal", 1.0 / np.sqrt(np.prod(ws[1:]))), g, P.DEV)
+    ops = P.Fp8Operands(x, w)
+    with forced(tile=tile):
+        assert B.conv_plan(xs, ws, st, pd, dl, B.IGC_FP8_E4M3FN, B.IGC_NDHWC).startswith("path=point")
+        y = P.run_fp8(ops, xs, ws, st, pd, dl)
+    sx, sw = float(ops.ref_scales[0]), float(ops.ref_scales[2])
+    ref = O.conv3d(ops.ref_xq, ops.ref_wq, st, pd, dl, sx=sx, sw=sw)
+    mx = float(np.abs(O.e4m3_decode(ops.ref_xq)).max()) * sx
+    mw = float(np.abs(O.e4m3_decode(ops.ref_wq)).max()) * sw
+    P.check_close(P.y_values(y), ref, int(np.prod(ws[1:])), mx, mw, name)
