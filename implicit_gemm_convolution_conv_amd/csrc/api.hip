@@ -3,7 +3,9 @@
 // Nothing here allocates device memory or synchronises; every launch goes to
 // the caller's stream. Validation finishes before the first launch, so an
 // error return leaves the stream untouched.
+#include <algorithm>
 #include <atomic>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -18,9 +20,14 @@ hipError_t launch_conv_fp8(const ConvParams &p, int tile, Mode mode, bool big, b
 hipError_t launch_conv_dma_bf16(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream);
 hipError_t launch_conv_dma_fp8(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream);
 
+hipError_t launch_conv_win_bf16(const ConvParams &p, int tile, bool big, hipStream_t stream);
+hipError_t launch_conv_win_fp8(const ConvParams &p, int tile, bool big, hipStream_t stream);
+
 hipError_t launch_conv(const ConvParams &p, int tile, Mode mode, Dtype dt, bool big, bool cblock,
                        hipStream_t stream)
 {
+    if (is_window(kTiles[tile]))
+        return dt == DT_FP8 ? launch_conv_win_fp8(p, tile, big, stream) : launch_conv_win_bf16(p, tile, big, stream);
     if (kTiles[tile].stages)
         return dt == DT_FP8 ? launch_conv_dma_fp8(p, tile, mode, big, cblock, stream)
                             : launch_conv_dma_bf16(p, tile, mode, big, cblock, stream);
@@ -211,15 +218,23 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
     };
     int tile = g_force_tile.load();
     if (tile < 0 || tile >= kNumTiles) {
-        // Measured on MI355X: 16x16 MFMA blocks are faster for bf16 and for the
-        // short-reduction temporal fp8 path, 32x32 blocks for fp8 with full 3D filters.
-        const int base = (dtype == IGC_FP8_E4M3FN && path == IGC_PATH_GENERIC) ? 3 : 0;
-        tile = base + (nblocks(base) >= 512 ? 0 : (nblocks(base + 1) >= 256 ? 1 : 2));
+        // Measured on MI355X: the 256x256 direct-to-LDS tile with 128-byte steps
+        // (16x16 MFMA blocks, bf16 and fp8) is the fastest whenever its grid
+        // reaches ~160 workgroups, the point-output GEMM of the patch embed
+        // (190 workgroups) included; smaller grids take the register-staged
+        // 128x128 or 64x64 tiles.
+        tile = nblocks(21) >= 160 ? 21 : (nblocks(1) >= 256 ? 1 : 2);
     } else {
-        if (kTiles[tile].stages && kTiles[tile].mf == 16 && esz == 1)
+        if (kTiles[tile].stages && kTiles[tile].mf == 16 && esz == 1 && kTiles[tile].kb == 64)
             return fail(IGC_ERR_UNSUPPORTED, "tile %d: fp8 with 64-byte steps needs 32x32 MFMA blocks", tile);
         if (esz == 2 && (tile == 12 || tile == 13))
             return fail(IGC_ERR_UNSUPPORTED, "tile %d is an fp8-only tile", tile);
+        if (esz == 1 && tile == 20)
+            return fail(IGC_ERR_UNSUPPORTED, "tile %d is a bf16-only tile", tile);
+        if (is_window(kTiles[tile]) && path != IGC_PATH_GENERIC)
+            return fail(IGC_ERR_UNSUPPORTED, "tile %d (input window) runs the generic im2col path only", tile);
+        if (is_window(kTiles[tile]) && esz == 1 && kTiles[tile].mf == 16)
+            return fail(IGC_ERR_UNSUPPORTED, "tile %d: fp8 with 64-byte steps needs 32x32 MFMA blocks", tile);
     }
     pl.tile = tile;
     const TileShape ts = kTiles[tile];
@@ -231,8 +246,35 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         pl.cblock = (g.C % tke) == 0;
         p.nk = pl.cblock ? (int)(g.T * g.R * g.S * (g.C / tke)) : (int)(ldw / tke);
     }
-    p.pairs = (ts.stages && pl.cblock && (g.C % (2 * tke)) == 0) ? 2 : 1;
-    const int64_t tm = ((int64_t)p.M + ts.bm - 1) / ts.bm, tn = ((int64_t)p.Ncol + ts.bn - 1) / ts.bn;
+    p.pairs = (ts.stages > 0 && ts.kb == 64 && pl.cblock && (g.C % (2 * tke)) == 0) ? 2 : 1;
+    int64_t tm = ((int64_t)p.M + ts.bm - 1) / ts.bm;
+    const int64_t tn = ((int64_t)p.Ncol + ts.bn - 1) / ts.bn;
+    if (is_window(ts)) {
+        // Tiles stay inside one output plane; the input box of a tile spans
+        // the input rows of its output rows plus the filter's reach.
+        if (g.C % tke != 0)
+            return fail(IGC_ERR_UNSUPPORTED, "input-window tile needs C %% %d == 0", tke);
+        const int64_t P2 = g.Ho * g.Wo;
+        const int64_t tpp = (P2 + ts.bm - 1) / ts.bm;
+        int64_t span = 1;
+        for (int64_t j = 0; j < tpp; ++j) {
+            const int64_t qa = j * ts.bm, qb = std::min(qa + ts.bm, P2) - 1;
+            span = std::max(span, qb / g.Wo - qa / g.Wo + 1);
+        }
+        const int64_t wh = (span - 1) * g.sh + (g.R - 1) * g.dh + 1;
+        const int64_t ww = (g.Wo - 1) * g.sw + (g.S - 1) * g.dw + 1;
+        const int64_t bytes = g.T * wh * ww * 64;
+        const int64_t nwi = (bytes + 8 * 1024 - 1) / (8 * 1024);  // 8 waves x 1 KB per instruction
+        if (nwi * 8 * 1024 > 96 * 1024)
+            return fail(IGC_ERR_UNSUPPORTED, "input box of %lld bytes exceeds the 96 KB window", (long long)bytes);
+        p.tpp = (int)tpp;
+        p.win_h = (int)wh;
+        p.win_w = (int)ww;
+        p.win_nwi = (int)nwi;
+        tm = g.N * g.Do * tpp;
+        pl.cblock = true;
+        p.nk = (int)(g.T * g.R * g.S * (g.C / tke));
+    }
     if (tm * tn > kI32Max)
         return fail(IGC_ERR_UNSUPPORTED, "grid of %lld tiles too large", (long long)(tm * tn));
     p.tiles_m = (int)tm;
@@ -399,9 +441,9 @@ int conv_plan(const int64_t xshape[5], const int64_t wshape[5], const int32_t st
         const TileShape ts = kTiles[pl.tile];
         snprintf(buf, len,
                  "path=%s tile=%dx%d waves=%d mfma=%dx%d stages=%d kstep=%d order=%s%s big=%d grid=%d group_m=%d nk=%d",
-                 path_name(pl.path), ts.bm, ts.bn, ts.wm * ts.wn, ts.mf, ts.mf, ts.stages ? ts.stages : 2,
+                 path_name(pl.path), ts.bm, ts.bn, ts.wm * ts.wn, ts.mf, ts.mf, ts.stages ? std::abs(ts.stages) : 2,
                  step_bytes(ts) / (dtype == IGC_FP8_E4M3FN ? 1 : 2),
-                 pl.cblock ? "cblock" : "linear", pl.p.pairs == 2 ? "-paired" : "", pl.big ? 1 : 0, pl.p.tiles_m * pl.p.tiles_n, pl.p.group_m, pl.p.nk);
+                 is_window(ts) ? "window" : (pl.cblock ? "cblock" : "linear"), pl.p.pairs == 2 ? "-paired" : "", pl.big ? 1 : 0, pl.p.tiles_m * pl.p.tiles_n, pl.p.group_m, pl.p.nk);
     }
     return ok();
 }

@@ -45,7 +45,7 @@ __device__ inline void wait_vmcnt()
 template <int BM, int BN, int WM, int WN>
 constexpr int dma_waves_per_eu() { return (WM * WN == 4 && BM * BN >= 256 * 256) ? 1 : 2; }
 
-template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, bool BIG, bool CBLK, int S>
+template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, bool BIG, bool CBLK, int S, int KB = 64>
 __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN>())))
 void conv_igemm_dma_kernel(ConvParams p)
 {
@@ -53,17 +53,19 @@ void conv_igemm_dma_kernel(ConvParams p)
     constexpr int NW = WM * WN;                // waves
     constexpr int ESZ = DT == DT_FP8 ? 1 : 2;  // bytes per element
     constexpr int CH = 16 / ESZ;               // elements per 16-byte chunk
-    constexpr int KB = 64;                     // bytes of k per row per stage
     constexpr int TKE = KB / ESZ;              // elements per reduction step
-    constexpr int AIT = BM / (16 * NW);        // A row groups (16 rows each) per wave
-    constexpr int BIT = BN / (16 * NW);
+    constexpr int RPI = 1024 / KB;             // rows filled by one DMA instruction (64 lanes x 16 B)
+    constexpr int CPR = KB / 16;               // 16-byte chunks per row
+    constexpr int AIT = BM / (RPI * NW);       // A row groups per wave
+    constexpr int BIT = BN / (RPI * NW);
     constexpr int LPS = AIT + BIT;             // LDS-DMA loads per thread per stage
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / MF, FN = WTN / MF;
     constexpr int STAGE = (BM + BN) * KB;
     static_assert(MODE != MODE_POINT || !CBLK, "point mode reduces in natural order");
-    static_assert(AIT >= 1 && BIT >= 1 && BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "loader split");
-    static_assert(MF == 32 || DT == DT_BF16, "fp8 needs 128-byte k per 16x16 MFMA: use 32x32 blocks");
+    static_assert(KB == 64 || KB == 128, "64- or 128-byte steps");
+    static_assert(AIT >= 1 && BIT >= 1 && BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "loader split");
+    static_assert(MF == 32 || DT == DT_BF16 || KB == 128, "fp8 16x16 MFMA needs 128-byte steps");
     static_assert(WTM % MF == 0 && WTN % MF == 0, "MFMA blocks");
     static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS budget");
     static_assert(LPS * (S - 2) < 64, "vmcnt range");
@@ -79,9 +81,10 @@ void conv_igemm_dma_kernel(ConvParams p)
     tile_coords(p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    // This lane's row within each 16-row group and the chunk it fetches there.
-    const int lr = lane >> 2;
-    const int jc = (lane & 3) ^ ((lane >> 3) & 3);
+    // This lane's row within each RPI-row group and the chunk it fetches there:
+    // 128-byte rows keep chunk q at slot q ^ (row & 7), 64-byte rows at q ^ ((row >> 1) & 3).
+    const int lr = lane / CPR;
+    const int jc = KB == 128 ? ((lane & 7) ^ (lane >> 3)) : ((lane & 3) ^ ((lane >> 3) & 3));
 
     const char *xb = static_cast<const char *>(p.x);
     const char *wb = static_cast<const char *>(p.w);
@@ -95,14 +98,14 @@ void conv_igemm_dma_kernel(ConvParams p)
     if constexpr (MODE == MODE_POINT) {
 #pragma unroll
         for (int i = 0; i < AIT; ++i) {
-            const int k = m0 + 16 * (wave + i * NW) + lr;
+            const int k = m0 + RPI * (wave + i * NW) + lr;
             a_row[i] = k < p.M ? wb + (int64_t)k * p.ldw * ESZ : nullptr;
         }
     } else {
         const int hw = p.Ho * p.Wo;
 #pragma unroll
         for (int i = 0; i < AIT; ++i) {
-            const int m = m0 + 16 * (wave + i * NW) + lr;
+            const int m = m0 + RPI * (wave + i * NW) + lr;
             if (m < p.M) {
                 const int nimg = m / p.P;
                 const int sp = m - nimg * p.P;
@@ -127,7 +130,7 @@ void conv_igemm_dma_kernel(ConvParams p)
     const char *b_row[BIT];
 #pragma unroll
     for (int i = 0; i < BIT; ++i) {
-        const int n = n0 + 16 * (wave + i * NW) + lr;
+        const int n = n0 + RPI * (wave + i * NW) + lr;
         if constexpr (MODE == MODE_POINT)  // image n: Rk elements
             b_row[i] = n < p.Ncol ? xb + (int64_t)n * p.Rk * ESZ : nullptr;
         else  // filter row n
@@ -214,7 +217,7 @@ void conv_igemm_dma_kernel(ConvParams p)
             if constexpr (MODE == MODE_POINT) {
                 const char *src = a_row[i] ? a_row[i] + (int64_t)kc * ESZ : zero;
                 __builtin_amdgcn_global_load_lds(
-                    src, (__attribute__((address_space(3))) void *)(stage + 16 * (wave + i * NW) * KB), 16, 0, 0);
+                    src, (__attribute__((address_space(3))) void *)(stage + RPI * (wave + i * NW) * KB), 16, 0, 0);
                 continue;
             }
             bool ok;
@@ -227,7 +230,7 @@ void conv_igemm_dma_kernel(ConvParams p)
             }
             const char *src = ok ? xb + (a_base[i] + tapoff) * ESZ : zero;
             __builtin_amdgcn_global_load_lds(
-                src, (__attribute__((address_space(3))) void *)(stage + 16 * (wave + i * NW) * KB), 16, 0, 0);
+                src, (__attribute__((address_space(3))) void *)(stage + RPI * (wave + i * NW) * KB), 16, 0, 0);
         }
         char *bst = stage + BM * KB;
 #pragma unroll
@@ -252,7 +255,7 @@ void conv_igemm_dma_kernel(ConvParams p)
                     src = b_row[i] + (int64_t)kc * ESZ;
             }
             __builtin_amdgcn_global_load_lds(
-                src, (__attribute__((address_space(3))) void *)(bst + 16 * (wave + i * NW) * KB), 16, 0, 0);
+                src, (__attribute__((address_space(3))) void *)(bst + RPI * (wave + i * NW) * KB), 16, 0, 0);
         }
     };
 
@@ -265,13 +268,13 @@ void conv_igemm_dma_kernel(ConvParams p)
         for (int b = 0; b < FN; ++b)
             acc[a][b] = AccT{};
 
-    const int lrow = lane & (MF - 1), lgrp = lane / MF, lsw = (lane >> 1) & 3;
+    const int lrow = lane & (MF - 1), lgrp = lane / MF, lsw = KB == 128 ? (lane & 7) : ((lane >> 1) & 3);
     auto compute = [&](const char *st) {
         const char *aw = st + (wm * WTM + lrow) * KB;
         const char *bw = st + BM * KB + (wn * WTN + lrow) * KB;
         constexpr int GROUPS = 64 / MF;
         constexpr int CPL = DT == DT_BF16 ? 1 : 2;
-        constexpr int SUB = (KB / 16) / (GROUPS * CPL);
+        constexpr int SUB = CPR / (GROUPS * CPL);
         static_assert(SUB >= 1, "step too short for this MFMA");
 #pragma unroll
         for (int h = 0; h < SUB; ++h) {
@@ -308,9 +311,14 @@ void conv_igemm_dma_kernel(ConvParams p)
                     const i32x4 hi = *reinterpret_cast<const i32x4 *>(aw + a * MF * KB + sl1);
                     const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-                    for (int b = 0; b < FN; ++b)
-                        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[b], acc[a][b], 0, 0, 0, 0,
-                                                                                    0, 0);
+                    for (int b = 0; b < FN; ++b) {
+                        if constexpr (MF == 16)
+                            acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[b], acc[a][b], 0, 0,
+                                                                                         0, 0, 0, 0);
+                        else
+                            acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[b], acc[a][b], 0, 0,
+                                                                                        0, 0, 0, 0);
+                    }
                 }
             }
         }
@@ -352,7 +360,7 @@ void conv_igemm_dma_kernel(ConvParams p)
 #pragma unroll
                 for (int i = 0; i < BIT; ++i)
                     if (tail_mask & (1u << i))
-                        *reinterpret_cast<i32x4 *>(bst + 16 * (wave + i * NW) * KB + 16 * lane) = tailv[i];
+                        *reinterpret_cast<i32x4 *>(bst + RPI * (wave + i * NW) * KB + 16 * lane) = tailv[i];
                 asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             }
         }
@@ -430,15 +438,10 @@ void conv_igemm_dma_kernel(ConvParams p)
     }
 }
 
-// Launch helper for one dtype: the direct-to-LDS tiles of kTiles (stages > 0).
-template <int DT>
-hipError_t launch_conv_dma_dt(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream)
-{
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
 #define IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_, BIG_, CBLK_)                                              \
     do {                                                                                                       \
-        hipLaunchKernelGGL((conv_igemm_dma_kernel<BM_, BN_, WM_, WN_, MF_, DT, MODE_, BIG_, CBLK_, S_>), grid, \
-                           dim3(WM_ * WN_ * 64), 0, stream, p);                                                \
+        hipLaunchKernelGGL((conv_igemm_dma_kernel<BM_, BN_, WM_, WN_, MF_, DT, MODE_, BIG_, CBLK_, S_, KB_>),   \
+                           grid, dim3(WM_ * WN_ * 64), 0, stream, p);                                          \
         return hipGetLastError();                                                                              \
     } while (0)
 #define IGC_DMODES(BM_, BN_, WM_, WN_, MF_, S_)                                                                \
@@ -462,6 +465,25 @@ hipError_t launch_conv_dma_dt(const ConvParams &p, int tile, Mode mode, bool big
         if (cblock) IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_GENERIC, false, true);                       \
         IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_GENERIC, false, false);                                  \
     } while (0)
+// The direct-to-LDS tiles with 128-byte steps (tiles 21, 22).
+template <int DT>
+hipError_t launch_conv_dma128(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+    constexpr int KB_ = 128;
+    switch (tile) {
+    case 21: IGC_DMODES(256, 256, 2, 4, 16, 2);
+    case 22: IGC_DMODES(256, 256, 2, 4, 32, 2);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Launch helper for one dtype: the direct-to-LDS tiles of kTiles (stages > 0).
+template <int DT>
+hipError_t launch_conv_dma_dt(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+    constexpr int KB_ = 64;
     if constexpr (DT == DT_BF16) {
         switch (tile) {
         case 6: IGC_DMODES(256, 256, 2, 4, 16, 4);
@@ -472,7 +494,10 @@ hipError_t launch_conv_dma_dt(const ConvParams &p, int tile, Mode mode, bool big
         case 11: IGC_DMODES(64, 64, 2, 2, 16, 4);
         case 14: IGC_DMODES(256, 256, 2, 2, 16, 4);
         case 15: IGC_DMODES(256, 256, 2, 2, 32, 4);
-        default: return hipErrorInvalidValue;
+        case 18: IGC_DMODES(256, 128, 2, 2, 16, 3);
+        case 19: IGC_DMODES(256, 128, 2, 2, 32, 3);
+        case 20: IGC_DMODES(128, 256, 2, 2, 16, 3);
+        default: break;
         }
     } else {
         switch (tile) {
@@ -481,11 +506,14 @@ hipError_t launch_conv_dma_dt(const ConvParams &p, int tile, Mode mode, bool big
         case 12: IGC_DMODES(128, 128, 2, 2, 32, 8);
         case 13: IGC_DMODES(64, 64, 2, 2, 32, 4);
         case 15: IGC_DMODES(256, 256, 2, 2, 32, 4);
-        default: return hipErrorInvalidValue;
+        case 19: IGC_DMODES(256, 128, 2, 2, 32, 3);
+        default: break;
         }
     }
+    return launch_conv_dma128<DT>(p, tile, mode, big, cblock, stream);
+}
+
 #undef IGC_DMODES
 #undef IGC_DLAUNCH
-}
 
 }  // namespace igc

@@ -12,31 +12,41 @@ enum Dtype { DT_BF16 = 0, DT_FP8 = 1 };
 
 // Tile shapes: rows x cols of the GEMM tile, waves along rows x cols, MFMA
 // block edge (16: 16x16 blocks; 32: 32x32 blocks, which need fewer operand
-// registers per lane) and LDS stages. stages == 0: register-staged kernel,
-// two LDS buffers, 128 bytes of k per row per step (64 bf16 / 128 fp8).
-// stages > 0: direct-to-LDS ring of that many stages, 64 bytes of k per row
-// per step (32 bf16 / 64 fp8); fp8 needs 32x32 blocks there.
+// registers per lane), LDS stages and bytes of k per row per reduction step
+// (kb: 128 = 64 bf16 / 128 fp8, 64 = 32 bf16 / 64 fp8). stages == 0:
+// register-staged kernel, two LDS buffers. stages > 0: direct-to-LDS ring of
+// that many stages; fp8 with 64-byte steps needs 32x32 blocks.
+// stages < 0: input-window kernel: the activations a tile needs for one
+// 64-byte channel block sit in LDS once and serve every filter tap; the
+// filter streams through a ring of -stages stages (64 bytes of k per step).
 struct TileShape {
-    int bm, bn, wm, wn, mf, stages;
+    int bm, bn, wm, wn, mf, stages, kb;
 };
-constexpr int kNumTiles = 16;
+constexpr int kNumTiles = 23;
 constexpr TileShape kTiles[kNumTiles] = {
-    {256, 256, 2, 4, 16, 0},  // 8 waves, 128x64 per wave: large grids
-    {128, 128, 2, 2, 16, 0},  // 4 waves, 64x64 per wave
-    {64, 64, 2, 2, 16, 0},    // 4 waves, 32x32 per wave: small grids
-    {256, 256, 2, 4, 32, 0},
-    {128, 128, 2, 2, 32, 0},
-    {64, 64, 2, 2, 32, 0},
-    {256, 256, 2, 4, 16, 4},  // direct-to-LDS, 4 x 32 KB ring
-    {256, 256, 2, 4, 32, 4},
-    {128, 128, 2, 2, 16, 4},  // direct-to-LDS, 4 x 16 KB ring
-    {128, 128, 2, 2, 32, 4},
-    {128, 128, 2, 2, 16, 8},  // direct-to-LDS, 8 x 16 KB ring: latency-bound short reductions
-    {64, 64, 2, 2, 16, 4},    // direct-to-LDS, 4 x 8 KB ring, many blocks per CU
-    {128, 128, 2, 2, 32, 8},
-    {64, 64, 2, 2, 32, 4},
-    {256, 256, 2, 2, 16, 4},  // direct-to-LDS, 4 waves of 128x128 (256 accumulators per lane)
-    {256, 256, 2, 2, 32, 4},
+    {256, 256, 2, 4, 16, 0, 128},  // 8 waves, 128x64 per wave: large grids
+    {128, 128, 2, 2, 16, 0, 128},  // 4 waves, 64x64 per wave
+    {64, 64, 2, 2, 16, 0, 128},    // 4 waves, 32x32 per wave: small grids
+    {256, 256, 2, 4, 32, 0, 128},
+    {128, 128, 2, 2, 32, 0, 128},
+    {64, 64, 2, 2, 32, 0, 128},
+    {256, 256, 2, 4, 16, 4, 64},   // direct-to-LDS, 4 x 32 KB ring
+    {256, 256, 2, 4, 32, 4, 64},
+    {128, 128, 2, 2, 16, 4, 64},   // direct-to-LDS, 4 x 16 KB ring
+    {128, 128, 2, 2, 32, 4, 64},
+    {128, 128, 2, 2, 16, 8, 64},   // direct-to-LDS, 8 x 16 KB ring: latency-bound short reductions
+    {64, 64, 2, 2, 16, 4, 64},     // direct-to-LDS, 4 x 8 KB ring, many blocks per CU
+    {128, 128, 2, 2, 32, 8, 64},
+    {64, 64, 2, 2, 32, 4, 64},
+    {256, 256, 2, 2, 16, 4, 64},   // direct-to-LDS, 4 waves of 128x128 (256 accumulators per lane)
+    {256, 256, 2, 2, 32, 4, 64},
+    {256, 256, 2, 4, 16, -4, 64},  // input window in LDS + 4-stage filter ring (full 3D filters)
+    {256, 256, 2, 4, 32, -4, 64},
+    {256, 128, 2, 2, 16, 3, 64},   // direct-to-LDS, 3 x 24 KB ring: two workgroups per CU
+    {256, 128, 2, 2, 32, 3, 64},
+    {128, 256, 2, 2, 16, 3, 64},
+    {256, 256, 2, 4, 16, 2, 128},  // direct-to-LDS, 2 x 64 KB ring, 128-byte steps
+    {256, 256, 2, 4, 32, 2, 128},
 };
 
 // Everything a conv kernel needs, passed by value as kernel arguments.
@@ -58,6 +68,10 @@ struct ConvParams {
     int tiles_m, tiles_n;   // grid of output tiles
     int group_m;            // grouped raster height (tiles along M sharing an L2 working set)
     int pairs;              // direct-to-LDS channel-block order: reduction steps per 128-byte line (1 or 2)
+    // input-window kernel: tiles never cross an output plane (n, od)
+    int tpp;                // M tiles per output plane = ceil(Ho*Wo / BM)
+    int win_h, win_w;       // window rows / columns (input pixels) per plane slot
+    int win_nwi;            // window DMA instructions per thread per channel block
 };
 
 // One launch of the implicit-GEMM kernel selected by (tile, mode, dtype,
@@ -65,7 +79,8 @@ struct ConvParams {
 hipError_t launch_conv(const ConvParams &p, int tile, Mode mode, Dtype dt, bool big, bool cblock,
                        hipStream_t stream);
 // Reduction step of a tile in bytes of k per row.
-constexpr int step_bytes(const TileShape &t) { return t.stages ? 64 : 128; }
+constexpr int step_bytes(const TileShape &t) { return t.kb; }
+constexpr bool is_window(const TileShape &t) { return t.stages < 0; }
 
 hipError_t launch_amax(const uint16_t *t, int64_t n, float *amax, hipStream_t stream);
 hipError_t launch_fp8_scales(const float *amax, float *pair, hipStream_t stream);

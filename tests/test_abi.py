@@ -66,7 +66,8 @@ def test_path_selection():
     p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 1, 1), pd=(1, 0, 0), dt=B.IGC_FP8_E4M3FN)
     assert p["path"] == "temporal" and p["order"] == "cblock" and p["kstep"] == "128"
     p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))
-    assert (p["path"], p["tile"], p["grid"], p["nk"]) == ("generic", "256x256", "6752", "864")
+    assert (p["path"], p["tile"], p["grid"], p["nk"], p["stages"]) == ("generic", "256x256", "6752", "864", "2")
+    assert _plan((9500, 3, 1, 14, 14), (1280, 3, 1, 14, 14), (1, 14, 14), lay=B.IGC_NCDHW)["grid"] == "190"
     assert _plan((1, 1024, 240, 160, 90), (1024, 1024, 3, 1, 1), pd=(1, 0, 0))["big"] == "1"
     assert _plan((1, 64, 4, 16, 16), (64, 64, 3, 3, 3), pd=(1, 1, 1))["tile"] == "64x64"
     assert _plan((1, 24, 4, 16, 16), (64, 24, 3, 3, 3), pd=(1, 1, 1))["order"] == "linear"
@@ -127,3 +128,21 @@ def test_null_pointers_rejected_before_any_launch():
     assert rc == B.IGC_ERR_INVALID  # fp8 without scales
     rc = lib.conv_fwd(8, 32, 48, xs[0], xs[1], one, one, one, B.IGC_BF16, B.IGC_NDHWC, None, None)
     assert rc == B.IGC_ERR_ALIGN
+
+
+def test_window_tile_limits():
+    try:
+        B.conv_debug_force(B.IGC_PATH_AUTO, 16, 0)
+        p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))
+        assert (p["order"], p["grid"], p["nk"]) == ("window", str(60 * 15 * 8), str(27 * 64))
+        with pytest.raises(B.IgcError) as e:  # box of 3 planes x 9 rows x 1002 columns exceeds LDS
+            _plan((1, 64, 4, 16, 1000), (64, 64, 3, 3, 3), pd=(1, 1, 1))
+        assert e.value.status == B.IGC_ERR_UNSUPPORTED
+        with pytest.raises(B.IgcError) as e:  # temporal filters take the temporal path
+            _plan((1, 64, 8, 8, 8), (64, 64, 3, 1, 1), pd=(1, 0, 0))
+        assert e.value.status == B.IGC_ERR_UNSUPPORTED
+        with pytest.raises(B.IgcError) as e:  # 64-byte channel blocks
+            _plan((1, 48, 8, 8, 8), (64, 48, 3, 3, 3), pd=(1, 1, 1))
+        assert e.value.status == B.IGC_ERR_UNSUPPORTED
+    finally:
+        B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)

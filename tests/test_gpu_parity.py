@@ -262,7 +262,7 @@ DMA_CASES = [g for g in GEOMS if g[0] in ("ragged_linear_c24", "c128_cblock_mult
                                            "temporal_3x1x1", "temporal_strided_dilated", "c8_tiny")]
 
 
-@pytest.mark.parametrize("tile", [6, 7, 8, 9, 14, 15])
+@pytest.mark.parametrize("tile", [6, 7, 8, 9, 14, 15, 18, 19, 20, 21, 22])
 @pytest.mark.parametrize("case", DMA_CASES, ids=[g[0] for g in DMA_CASES])
 def test_dma_tiles_bf16(tile, case):
     name, xs, ws, st, pd, dl = case
@@ -270,7 +270,7 @@ def test_dma_tiles_bf16(tile, case):
         _bf16_case(f"dma tile {tile} {name}", xs, ws, st, pd, dl, seed=zlib.crc32(name.encode()) % 1000)
 
 
-@pytest.mark.parametrize("tile", [6, 7, 8, 9, 14, 15])
+@pytest.mark.parametrize("tile", [6, 7, 8, 9, 14, 15, 21, 22])
 def test_dma_tiles_integer_bit_exact(tile):
     _announce(f"dma tile {tile} integer")
     with forced(tile=tile):
@@ -278,7 +278,7 @@ def test_dma_tiles_integer_bit_exact(tile):
         _int_case((1, 24, 6, 7, 8), (40, 24, 3, 2, 3), (2, 1, 2), (1, 0, 2), (1, 2, 1), seed=25)
 
 
-@pytest.mark.parametrize("tile", [7, 9, 15])
+@pytest.mark.parametrize("tile", [7, 9, 15, 19, 21, 22])
 @pytest.mark.parametrize("case", FP8_GEOMS, ids=[g[0] for g in FP8_GEOMS])
 def test_dma_tiles_fp8(tile, case):
     name, xs, ws, st, pd, dl = case
@@ -310,7 +310,7 @@ def test_dma_tiles_agree_bitwise():
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
-@pytest.mark.parametrize("tile", [8, 10, 11])
+@pytest.mark.parametrize("tile", [8, 10, 11, 21, 22])
 @pytest.mark.parametrize("layout", ["NCDHW", "NDHWC"])
 def test_point_output_dma_tiles(tile, layout):
     with forced(tile=tile):
@@ -320,7 +320,7 @@ def test_point_output_dma_tiles(tile, layout):
                    (0, 0, 0), (1, 1, 1), seed=9, dist=("normal", 1.0), x_layout=layout)
 
 
-@pytest.mark.parametrize("tile", [8, 10, 11])
+@pytest.mark.parametrize("tile", [8, 10, 11, 21])
 def test_point_output_dma_integer_bit_exact(tile):
     _announce(f"integer point dma tile {tile}")
     with forced(tile=tile):
@@ -340,6 +340,53 @@ def test_point_output_fp8(tile):
     ops = P.Fp8Operands(x, w)
     with forced(tile=tile):
         assert B.conv_plan(xs, ws, st, pd, dl, B.IGC_FP8_E4M3FN, B.IGC_NDHWC).startswith("path=point")
+        y = P.run_fp8(ops, xs, ws, st, pd, dl)
+    sx, sw = float(ops.ref_scales[0]), float(ops.ref_scales[2])
+    ref = O.conv3d(ops.ref_xq, ops.ref_wq, st, pd, dl, sx=sx, sw=sw)
+    mx = float(np.abs(O.e4m3_decode(ops.ref_xq)).max()) * sx
+    mw = float(np.abs(O.e4m3_decode(ops.ref_wq)).max()) * sw
+    P.check_close(P.y_values(y), ref, int(np.prod(ws[1:])), mx, mw, name)
+
+
+# ------------------------------------------------------------------ input-window tiles (16 bf16, 17 bf16/fp8)
+
+WIN_CASES = [
+    ("c1_shape", (1, 64, 4, 16, 16), (64, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),
+    ("c128_multi_plane", (2, 128, 6, 10, 12), (200, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),
+    ("asym_stride2", (1, 64, 7, 13, 10), (72, 64, 3, 5, 1), (2, 2, 1), (0, 2, 0), (1, 1, 1)),
+    ("dilated", (1, 64, 6, 11, 13), (80, 64, 3, 3, 3), (1, 1, 1), (2, 1, 2), (2, 1, 2)),
+    ("wide_rows_partial_tiles", (2, 96, 3, 9, 70), (40, 96, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("tile", [16, 17])
+@pytest.mark.parametrize("case", WIN_CASES, ids=[g[0] for g in WIN_CASES])
+def test_window_tiles_bf16(tile, case):
+    name, xs, ws, st, pd, dl = case
+    with forced(tile=tile):
+        assert "order=window" in B.conv_plan(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC)
+        _bf16_case(f"window tile {tile} {name}", xs, ws, st, pd, dl, seed=zlib.crc32(name.encode()) % 1000)
+
+
+@pytest.mark.parametrize("tile", [16, 17])
+def test_window_tiles_integer_bit_exact(tile):
+    _announce(f"window tile {tile} integer")
+    with forced(tile=tile):
+        _int_case((2, 64, 5, 9, 11), (96, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), seed=27)
+        _int_case((1, 32, 6, 7, 40), (40, 32, 3, 2, 3), (2, 1, 2), (1, 0, 2), (1, 2, 1), seed=28)
+
+
+@pytest.mark.parametrize("case", [g for g in FP8_GEOMS if g[0] in ("c1_shape_fp8", "fp8_c256_k300")] + [
+    ("fp8_c128_dilated", (1, 128, 6, 11, 13), (80, 128, 3, 3, 3), (1, 1, 1), (2, 1, 2), (2, 1, 2))],
+    ids=lambda g: g[0])
+def test_window_tile_fp8(case):
+    name, xs, ws, st, pd, dl = case
+    _announce(f"window tile 17 {name}")
+    g = I.generator(34, P.DEV)
+    x = I.draw(xs, ("normal", 1.0), g, P.DEV)
+    w = I.draw(ws, ("normal", 1.0 / np.sqrt(np.prod(ws[1:]))), g, P.DEV)
+    ops = P.Fp8Operands(x, w)
+    with forced(tile=17):
         y = P.run_fp8(ops, xs, ws, st, pd, dl)
     sx, sw = float(ops.ref_scales[0]), float(ops.ref_scales[2])
     ref = O.conv3d(ops.ref_xq, ops.ref_wq, st, pd, dl, sx=sx, sw=sw)
