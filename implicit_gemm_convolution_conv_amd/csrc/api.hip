@@ -221,9 +221,9 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         // Measured on MI355X: the 256x256 direct-to-LDS tile with 128-byte steps
         // (16x16 MFMA blocks, bf16 and fp8) is the fastest whenever its grid
         // reaches ~160 workgroups, the point-output GEMM of the patch embed
-        // (190 workgroups) included; smaller grids take the register-staged
-        // 128x128 or 64x64 tiles.
-        tile = nblocks(21) >= 160 ? 21 : (nblocks(1) >= 256 ? 1 : 2);
+        // (190 workgroups) included; smaller grids take the 128x128 (two
+        // workgroups per CU) or 64x64 (4-stage ring) direct-to-LDS tiles.
+        tile = nblocks(21) >= 160 ? 21 : (nblocks(24) >= 256 ? 24 : 26);
     } else {
         if (kTiles[tile].stages && kTiles[tile].mf == 16 && esz == 1 && kTiles[tile].kb == 64)
             return fail(IGC_ERR_UNSUPPORTED, "tile %d: fp8 with 64-byte steps needs 32x32 MFMA blocks", tile);

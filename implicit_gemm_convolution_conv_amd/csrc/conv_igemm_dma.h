@@ -465,7 +465,7 @@ void conv_igemm_dma_kernel(ConvParams p)
         if (cblock) IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_GENERIC, false, true);                       \
         IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_GENERIC, false, false);                                  \
     } while (0)
-// The direct-to-LDS tiles with 128-byte steps (tiles 21, 22).
+// The direct-to-LDS tiles with 128-byte steps (tiles 21 and up).
 template <int DT>
 hipError_t launch_conv_dma128(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream)
 {
@@ -474,6 +474,10 @@ hipError_t launch_conv_dma128(const ConvParams &p, int tile, Mode mode, bool big
     switch (tile) {
     case 21: IGC_DMODES(256, 256, 2, 4, 16, 2);
     case 22: IGC_DMODES(256, 256, 2, 4, 32, 2);
+    case 23: IGC_DMODES(128, 128, 2, 2, 16, 4);
+    case 24: IGC_DMODES(128, 128, 2, 2, 16, 2);
+    case 25: IGC_DMODES(256, 128, 2, 4, 16, 2);
+    case 26: IGC_DMODES(64, 64, 2, 2, 16, 4);
     default: return hipErrorInvalidValue;
     }
 }

@@ -22,7 +22,7 @@ enum Dtype { DT_BF16 = 0, DT_FP8 = 1 };
 struct TileShape {
     int bm, bn, wm, wn, mf, stages, kb;
 };
-constexpr int kNumTiles = 23;
+constexpr int kNumTiles = 27;
 constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 16, 0, 128},  // 8 waves, 128x64 per wave: large grids
     {128, 128, 2, 2, 16, 0, 128},  // 4 waves, 64x64 per wave
@@ -47,6 +47,10 @@ constexpr TileShape kTiles[kNumTiles] = {
     {128, 256, 2, 2, 16, 3, 64},
     {256, 256, 2, 4, 16, 2, 128},  // direct-to-LDS, 2 x 64 KB ring, 128-byte steps
     {256, 256, 2, 4, 32, 2, 128},
+    {128, 128, 2, 2, 16, 4, 128},  // direct-to-LDS, 4 x 32 KB ring, 128-byte steps: short reductions
+    {128, 128, 2, 2, 16, 2, 128},  // two workgroups per CU
+    {256, 128, 2, 4, 16, 2, 128},
+    {64, 64, 2, 2, 16, 4, 128},    // small grids
 };
 
 // Everything a conv kernel needs, passed by value as kernel arguments.

@@ -262,7 +262,7 @@ DMA_CASES = [g for g in GEOMS if g[0] in ("ragged_linear_c24", "c128_cblock_mult
                                            "temporal_3x1x1", "temporal_strided_dilated", "c8_tiny")]
 
 
-@pytest.mark.parametrize("tile", [6, 7, 8, 9, 14, 15, 18, 19, 20, 21, 22])
+@pytest.mark.parametrize("tile", [6, 7, 8, 9, 14, 15, 18, 19, 20, 21, 22, 23, 24, 25, 26])
 @pytest.mark.parametrize("case", DMA_CASES, ids=[g[0] for g in DMA_CASES])
 def test_dma_tiles_bf16(tile, case):
     name, xs, ws, st, pd, dl = case
@@ -278,7 +278,7 @@ def test_dma_tiles_integer_bit_exact(tile):
         _int_case((1, 24, 6, 7, 8), (40, 24, 3, 2, 3), (2, 1, 2), (1, 0, 2), (1, 2, 1), seed=25)
 
 
-@pytest.mark.parametrize("tile", [7, 9, 15, 19, 21, 22])
+@pytest.mark.parametrize("tile", [7, 9, 15, 19, 21, 22, 23, 25, 26])
 @pytest.mark.parametrize("case", FP8_GEOMS, ids=[g[0] for g in FP8_GEOMS])
 def test_dma_tiles_fp8(tile, case):
     name, xs, ws, st, pd, dl = case
@@ -310,7 +310,7 @@ def test_dma_tiles_agree_bitwise():
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
-@pytest.mark.parametrize("tile", [8, 10, 11, 21, 22])
+@pytest.mark.parametrize("tile", [8, 10, 11, 21, 22, 23, 24, 25, 26])
 @pytest.mark.parametrize("layout", ["NCDHW", "NDHWC"])
 def test_point_output_dma_tiles(tile, layout):
     with forced(tile=tile):
