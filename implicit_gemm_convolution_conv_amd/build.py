@@ -55,6 +55,11 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
+    # a kernel whose host-side instantiation failed leaves an undefined launch stub behind
+    nm = subprocess.run(["nm", "-C", tmp], capture_output=True, text=True)
+    missing = [l for l in nm.stdout.splitlines() if " U " in l and "__device_stub__" in l]
+    if missing:
+        raise RuntimeError("kernels without a host launch stub:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -23,9 +23,14 @@ hipError_t launch_conv_dma_fp8(const ConvParams &p, int tile, Mode mode, bool bi
 hipError_t launch_conv_win_bf16(const ConvParams &p, int tile, bool big, hipStream_t stream);
 hipError_t launch_conv_win_fp8(const ConvParams &p, int tile, bool big, hipStream_t stream);
 
+hipError_t launch_conv_buf_bf16(const ConvParams &p, int tile, Mode mode, hipStream_t stream);
+hipError_t launch_conv_buf_fp8(const ConvParams &p, int tile, Mode mode, hipStream_t stream);
+
 hipError_t launch_conv(const ConvParams &p, int tile, Mode mode, Dtype dt, bool big, bool cblock,
                        hipStream_t stream)
 {
+    if (is_buffer(kTiles[tile]))
+        return dt == DT_FP8 ? launch_conv_buf_fp8(p, tile, mode, stream) : launch_conv_buf_bf16(p, tile, mode, stream);
     if (is_window(kTiles[tile]))
         return dt == DT_FP8 ? launch_conv_win_fp8(p, tile, big, stream) : launch_conv_win_bf16(p, tile, big, stream);
     if (kTiles[tile].stages)
@@ -187,6 +192,8 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
     p.Do = (int)g.Do; p.Ho = (int)g.Ho; p.Wo = (int)g.Wo;
     p.Rk = (int)rk;
     p.ldw = (int)ldw;
+    p.xbytes = (int)std::min<int64_t>(xnum * esz, kI32Max);
+    p.wbytes = (int)std::min<int64_t>(g.K * ldw * esz, kI32Max);
 
     if (path == IGC_PATH_POINT) {
         if ((rk * esz) % 4 != 0)
@@ -224,6 +231,13 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         // (190 workgroups) included; smaller grids take the 128x128 (two
         // workgroups per CU) or 64x64 (4-stage ring) direct-to-LDS tiles.
         tile = nblocks(21) >= 160 ? 21 : (nblocks(24) >= 256 ? 24 : 26);
+        // Where the whole-channel-block im2col order applies and both operands
+        // fit a 2^31-byte buffer range, the buffer-addressed 256x256 tile with
+        // loads spread over the MFMA rows replaces the large tile.
+        const bool buffer_ok = path != IGC_PATH_POINT && g.C % (128 / esz) == 0 && !pl.big &&
+                               xnum * esz < (int64_t(1) << 31) && g.K * ldw * esz < (int64_t(1) << 31);
+        if (tile == 21 && buffer_ok)
+            tile = 30;
     } else {
         if (kTiles[tile].stages && kTiles[tile].mf == 16 && esz == 1 && kTiles[tile].kb == 64)
             return fail(IGC_ERR_UNSUPPORTED, "tile %d: fp8 with 64-byte steps needs 32x32 MFMA blocks", tile);
@@ -235,6 +249,14 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
             return fail(IGC_ERR_UNSUPPORTED, "tile %d (input window) runs the generic im2col path only", tile);
         if (is_window(kTiles[tile]) && esz == 1 && kTiles[tile].mf == 16)
             return fail(IGC_ERR_UNSUPPORTED, "tile %d: fp8 with 64-byte steps needs 32x32 MFMA blocks", tile);
+        if (is_buffer(kTiles[tile])) {
+            if (path == IGC_PATH_POINT)
+                return fail(IGC_ERR_UNSUPPORTED, "tile %d (buffer-addressed) runs the im2col paths only", tile);
+            if (g.C % (kTiles[tile].kb / esz) != 0)
+                return fail(IGC_ERR_UNSUPPORTED, "tile %d needs C %% %d == 0", tile, kTiles[tile].kb / esz);
+            if (xnum * esz >= (int64_t(1) << 31) || g.K * ldw * esz >= (int64_t(1) << 31) || pl.big)
+                return fail(IGC_ERR_UNSUPPORTED, "tile %d needs x and the packed filter below 2^31 bytes", tile);
+        }
     }
     pl.tile = tile;
     const TileShape ts = kTiles[tile];
@@ -440,10 +462,13 @@ int conv_plan(const int64_t xshape[5], const int64_t wshape[5], const int32_t st
     if (buf && len) {
         const TileShape ts = kTiles[pl.tile];
         snprintf(buf, len,
-                 "path=%s tile=%dx%d waves=%d mfma=%dx%d stages=%d kstep=%d order=%s%s big=%d grid=%d group_m=%d nk=%d",
+                 "path=%s tile=%dx%d waves=%d mfma=%dx%d stages=%d bstages=%d kstep=%d order=%s%s big=%d grid=%d "
+                 "group_m=%d nk=%d loads=%s",
                  path_name(pl.path), ts.bm, ts.bn, ts.wm * ts.wn, ts.mf, ts.mf, ts.stages ? std::abs(ts.stages) : 2,
-                 step_bytes(ts) / (dtype == IGC_FP8_E4M3FN ? 1 : 2),
-                 is_window(ts) ? "window" : (pl.cblock ? "cblock" : "linear"), pl.p.pairs == 2 ? "-paired" : "", pl.big ? 1 : 0, pl.p.tiles_m * pl.p.tiles_n, pl.p.group_m, pl.p.nk);
+                 is_buffer(ts) ? ts.sb : (ts.stages ? std::abs(ts.stages) : 2), step_bytes(ts) / (dtype == IGC_FP8_E4M3FN ? 1 : 2),
+                 is_window(ts) ? "window" : (pl.cblock ? "cblock" : "linear"), pl.p.pairs == 2 ? "-paired" : "",
+                 pl.big ? 1 : 0, pl.p.tiles_m * pl.p.tiles_n, pl.p.group_m, pl.p.nk,
+                 is_buffer(ts) ? "buffer-lds" : (ts.stages > 0 ? "global-lds" : (is_window(ts) ? "window-lds" : "registers")));
     }
     return ok();
 }

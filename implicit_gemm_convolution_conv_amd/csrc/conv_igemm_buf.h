@@ -1,0 +1,390 @@
+// Implicit-GEMM forward convolution, im2col paths in channel-block order, with
+// buffer-addressed direct-to-LDS loads and one LDS ring per operand.
+//
+// Same GEMM and LDS layout as conv_igemm_dma_kernel (rows = output positions,
+// columns = output channels, reduction over (t, r, s, c) with the channel
+// block outermost), with three changes to the load side:
+//
+//  * Loads go through buffer resources (buffer_load_dwordx4 ... lds). An
+//    offset past the end of a buffer reads as zeros without touching memory,
+//    so a padding tap only has to select an out-of-range offset: the address
+//    of a row is one 32-bit add per step and no zero line or branch is needed.
+//    Rows past the end of the GEMM are clamped to the last row; they load real
+//    data whose results are never stored.
+//  * The filter (B) and the activations (A) have rings of their own: the
+//    filter stream is read once per tile and misses L2 far more often than the
+//    activations, which every filter tap re-reads, so B is issued SB-1 steps
+//    ahead and A SA-1 steps ahead (SB >= SA) within the same LDS budget.
+//  * The loads of a step can be spread over the MFMA rows of the step before
+//    (SPREAD rows), so that their address arithmetic issues in the shadow of
+//    the matrix instructions instead of in front of them.
+//
+// Reduction step ks: wait until this thread's loads of step ks have landed,
+// barrier (all loads of step ks visible, step ks-1's slots no longer read),
+// then compute step ks while issuing A(ks+SA-1) and B(ks+SB-1) into the slots
+// step ks-1 used. The multi-stage async global->LDS pipeline follows FlyDSL
+// PR #860 (async DMA commit); the channel-block reduction order and the
+// temporal-only mode follow the same PR's 3D-conv kernels.
+#pragma once
+
+#include <type_traits>
+
+#include "conv_igemm_dma.h"
+
+namespace igc {
+
+// Offset past the end of every buffer the kernel reads (buffers are < 2^31 bytes).
+constexpr unsigned kPastEnd = 0x80000000u;
+
+// Raw buffer resource over [base, base + bytes). Dword 3 = 0x00020000: 32-bit
+// data format, no swizzle, offsets checked against `bytes`.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+// 16 bytes per lane from buffer offset `off` into LDS at lds + 16 * lane.
+__device__ inline void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, char *lds, unsigned off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, int SA, int SB, int KB, int SPREAD>
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN>())))
+void conv_igemm_buf_kernel(ConvParams p)
+{
+    constexpr int NW = WM * WN;                // waves
+    constexpr int ESZ = DT == DT_FP8 ? 1 : 2;  // bytes per element
+    constexpr int TKE = KB / ESZ;              // elements per reduction step
+    constexpr int RPI = 1024 / KB;             // rows filled by one DMA instruction (64 lanes x 16 B)
+    constexpr int CPR = KB / 16;               // 16-byte chunks per row
+    constexpr int AIT = BM / (RPI * NW);       // A row groups per wave
+    constexpr int BIT = BN / (RPI * NW);
+    constexpr int LPS = AIT + BIT;             // DMA instructions per thread per step
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / MF, FN = WTN / MF;
+    constexpr int ASTAGE = BM * KB, BSTAGE = BN * KB;
+    constexpr int GROUPS = 64 / MF;            // lane groups along k in one MFMA operand
+    constexpr int CPL = DT == DT_BF16 ? 1 : 2; // 16-byte chunks per lane per MFMA operand
+    constexpr int SUB = CPR / (GROUPS * CPL);  // MFMA k-slices per step
+    constexpr int ROWS = SUB * FM;             // MFMA rows (FN instructions each) per step
+    static_assert(MODE == MODE_GENERIC || MODE == MODE_TEMPORAL, "im2col modes only");
+    static_assert(KB == 64 || KB == 128, "64- or 128-byte steps");
+    static_assert(AIT >= 1 && BIT >= 1 && BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "loader split");
+    static_assert(SUB >= 1, "step too short for this MFMA");
+    static_assert(SA >= 2 && SB >= SA, "ring depths");
+    static_assert(SA * ASTAGE + SB * BSTAGE <= 160 * 1024, "LDS budget");
+    static_assert(BIT + (SA - 2) * LPS < 64, "vmcnt range");
+    static_assert(SPREAD >= 0 && SPREAD <= ROWS, "spread within one step");
+
+    __shared__ __attribute__((aligned(1024))) char smem[SA * ASTAGE + SB * BSTAGE];
+    char *const as = smem;
+    char *const bs = smem + SA * ASTAGE;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM, wn = wave / WM;
+
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // This lane's row within each RPI-row group and the chunk it fetches there:
+    // 128-byte rows keep chunk q at slot q ^ (row & 7), 64-byte rows at q ^ ((row >> 1) & 3).
+    const int lr = lane / CPR;
+    const int jc = KB == 128 ? ((lane & 7) ^ (lane >> 3)) : ((lane & 3) ^ ((lane >> 3) & 3));
+
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(p.x, p.xbytes);
+    const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(p.w, p.wbytes);
+
+    // ---------------------------------------------------------------- A rows: input origin of each output position
+    int a_d[AIT], a_h[AIT], a_w[AIT];
+    unsigned a_off[AIT];  // byte offset of (origin, channel jc*CH); wraps for padded origins
+    {
+        const int hw = p.Ho * p.Wo;
+#pragma unroll
+        for (int i = 0; i < AIT; ++i) {
+            const int m = min(m0 + RPI * (wave + i * NW) + lr, p.M - 1);
+            const int nimg = m / p.P;
+            const int sp = m - nimg * p.P;
+            const int od = sp / hw;
+            const int rem = sp - od * hw;
+            const int oh = rem / p.Wo;
+            const int ow = rem - oh * p.Wo;
+            a_d[i] = od * p.sd - p.pd;
+            a_h[i] = oh * p.sh - p.ph;
+            a_w[i] = ow * p.sw - p.pw;
+            unsigned pos;
+            if constexpr (MODE == MODE_TEMPORAL)
+                pos = (unsigned)(nimg * p.D + a_d[i]) * (unsigned)(p.H * p.W) + (unsigned)rem;
+            else
+                pos = ((unsigned)(nimg * p.D + a_d[i]) * (unsigned)p.H + (unsigned)a_h[i]) * (unsigned)p.W +
+                      (unsigned)a_w[i];
+            a_off[i] = pos * (unsigned)(p.C * ESZ) + (unsigned)(jc * 16);
+        }
+    }
+    // ---------------------------------------------------------------- B rows: filter rows
+    unsigned b_off[BIT];
+#pragma unroll
+    for (int i = 0; i < BIT; ++i) {
+        const int n = min(n0 + RPI * (wave + i * NW) + lr, p.Ncol - 1);
+        b_off[i] = (unsigned)n * (unsigned)(p.ldw * ESZ) + (unsigned)(jc * 16);
+    }
+
+    // ---------------------------------------------------------------- reduction position (uniform)
+    // Channel block cb (pairs * TKE channels) outer, then tap (t, r, s), then
+    // the `pairs` TKE-wide halves of the block.
+    struct KPos {
+        int half, s, r, t, cb;
+    };
+    auto advance = [&](KPos &k) {
+        const bool hw = ++k.half == p.pairs;
+        k.half = hw ? 0 : k.half;
+        k.s += hw;
+        const bool sw = k.s == p.S;
+        k.s = sw ? 0 : k.s;
+        k.r += sw;
+        const bool rw = k.r == p.R;
+        k.r = rw ? 0 : k.r;
+        k.t += rw;
+        const bool tw = k.t == p.T;
+        k.t = tw ? 0 : k.t;
+        k.cb += tw ? p.pairs * TKE : 0;
+    };
+    auto a_shift = [&](const KPos &k) -> unsigned {  // bytes from a row's origin to this tap and channel block
+        const int c = k.cb + k.half * TKE;
+        if constexpr (MODE == MODE_TEMPORAL)
+            return (unsigned)((k.t * p.dd) * (p.H * p.W) * p.C + c) * ESZ;
+        else
+            return (unsigned)((((k.t * p.dd) * p.H + k.r * p.dh) * p.W + k.s * p.dw) * p.C + c) * ESZ;
+    };
+    auto b_shift = [&](const KPos &k) -> unsigned {
+        return (unsigned)((((k.t * p.R + k.r) * p.S + k.s) * p.C + k.cb + k.half * TKE) * ESZ);
+    };
+
+    // One DMA instruction: A row group i (or B row group i - AIT) of the step at k into ring slot st.
+    auto issue = [&](int j, int st, const KPos &k, unsigned ash, unsigned bsh) {
+        if (j < AIT) {
+            const int i = j;
+            bool ok = (unsigned)(a_d[i] + k.t * p.dd) < (unsigned)p.D;
+            if constexpr (MODE == MODE_GENERIC)
+                ok = ok & ((unsigned)(a_h[i] + k.r * p.dh) < (unsigned)p.H) &
+                     ((unsigned)(a_w[i] + k.s * p.dw) < (unsigned)p.W);
+            const unsigned off = ok ? a_off[i] + ash : kPastEnd;
+            buffer_to_lds16(xr, as + st * ASTAGE + RPI * (wave + i * NW) * KB, off);
+        } else {
+            const int i = j - AIT;
+            buffer_to_lds16(wr, bs + st * BSTAGE + RPI * (wave + i * NW) * KB, b_off[i] + bsh);
+        }
+    };
+
+    // ---------------------------------------------------------------- MFMA
+    using AccT = typename AccType<MF>::type;
+    AccT acc[FM][FN];
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b)
+            acc[a][b] = AccT{};
+
+    const int lrow = lane & (MF - 1), lgrp = lane / MF, lsw = KB == 128 ? (lane & 7) : ((lane >> 1) & 3);
+    using Frag = typename std::conditional<DT == DT_BF16, bf16x8, i32x8>::type;
+    auto frag = [&](const char *rowp, int h) -> Frag {
+        const int c0 = (h * GROUPS + lgrp) * CPL;
+        if constexpr (DT == DT_BF16) {
+            return *reinterpret_cast<const bf16x8 *>(rowp + ((c0 ^ lsw) * 16));
+        } else {
+            const i32x4 lo = *reinterpret_cast<const i32x4 *>(rowp + ((c0 ^ lsw) * 16));
+            const i32x4 hi = *reinterpret_cast<const i32x4 *>(rowp + (((c0 + 1) ^ lsw) * 16));
+            return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+    };
+    auto mfma = [&](const Frag &af, const Frag &bf, AccT &c) {
+        if constexpr (DT == DT_BF16) {
+            if constexpr (MF == 16)
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, c, 0, 0, 0);
+            else
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, c, 0, 0, 0);
+        } else {
+            if constexpr (MF == 16)
+                c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, c, 0, 0, 0, 0, 0, 0);
+            else
+                c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, c, 0, 0, 0, 0, 0, 0);
+        }
+    };
+    // One step from slots (sa, sb); hook(row) runs after MFMA row `row` (0..ROWS-1).
+    auto compute = [&](int sa, int sb, auto &&hook) {
+        const char *aw = as + sa * ASTAGE + (wm * WTM + lrow) * KB;
+        const char *bw = bs + sb * BSTAGE + (wn * WTN + lrow) * KB;
+#pragma unroll
+        for (int h = 0; h < SUB; ++h) {
+            Frag bf[FN];
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                bf[b] = frag(bw + b * MF * KB, h);
+            Frag af[2];
+            af[0] = frag(aw, h);
+#pragma unroll
+            for (int a = 0; a < FM; ++a) {
+                if (a + 1 < FM)
+                    af[(a + 1) & 1] = frag(aw + (a + 1) * MF * KB, h);
+#pragma unroll
+                for (int b = 0; b < FN; ++b)
+                    mfma(af[a & 1], bf[b], acc[a][b]);
+                hook(h * FM + a);
+            }
+        }
+    };
+
+    // ---------------------------------------------------------------- pipeline
+    const int nk = p.nk;
+    KPos ka{0, 0, 0, 0, 0}, kb{0, 0, 0, 0, 0};  // next A and B steps to issue
+    auto issue_a_step = [&](int st) {
+        const unsigned sh = a_shift(ka);
+#pragma unroll
+        for (int j = 0; j < AIT; ++j)
+            issue(j, st, ka, sh, 0);
+        advance(ka);
+    };
+    auto issue_b_step = [&](int st) {
+        const unsigned sh = b_shift(kb);
+#pragma unroll
+        for (int j = AIT; j < LPS; ++j)
+            issue(j, st, kb, 0, sh);
+        advance(kb);
+    };
+    // Prologue: the issues of the virtual steps -(SB-1) .. -1, in steady-state order.
+#pragma unroll
+    for (int j = -(SB - 1); j < 0; ++j) {
+        const int ja = j + SA - 1, jb = j + SB - 1;
+        if (ja >= 0 && ja < nk)
+            issue_a_step(ja % SA);
+        if (jb < nk)
+            issue_b_step(jb % SB);
+    }
+    int ks = 0;
+    // Steady state: every step issues A(ks+SA-1) then B(ks+SB-1). Loads issued
+    // after this thread's last load of step ks: B(ks+SB-SA) of the step that
+    // issued A(ks) when SB > SA, plus SA-2 whole steps.
+    int sa = 0, sb = 0;                  // slots of step ks
+    int ia = SA - 1, ib = SB - 1;        // slots the step's issues go to
+    for (; ks < nk - SB + 1; ++ks) {
+        wait_vmcnt<(SB > SA ? BIT : 0) + (SA - 2) * LPS>();
+        asm volatile("s_barrier" ::: "memory");
+        const unsigned ash = a_shift(ka), bsh = b_shift(kb);
+        const int sta = ia, stb = ib;
+        if constexpr (SPREAD == 0) {
+#pragma unroll
+            for (int j = 0; j < LPS; ++j)
+                issue(j, j < AIT ? sta : stb, j < AIT ? ka : kb, ash, bsh);
+            compute(sa, sb, [](int) {});
+        } else {
+            compute(sa, sb, [&](int row) {
+#pragma unroll
+                for (int j = 0; j < LPS; ++j)
+                    if (j * SPREAD / LPS == row)
+                        issue(j, j < AIT ? sta : stb, j < AIT ? ka : kb, ash, bsh);
+            });
+        }
+        advance(ka);
+        advance(kb);
+        sa = sa + 1 == SA ? 0 : sa + 1;
+        sb = sb + 1 == SB ? 0 : sb + 1;
+        ia = ia + 1 == SA ? 0 : ia + 1;
+        ib = ib + 1 == SB ? 0 : ib + 1;
+    }
+    // Drain: the last SB-1 steps (or all of a short reduction) wait for everything.
+    for (; ks < nk; ++ks) {
+        wait_vmcnt<0>();
+        asm volatile("s_barrier" ::: "memory");
+        if (ks + SA - 1 < nk)
+            issue_a_step(ia);
+        if (ks + SB - 1 < nk)
+            issue_b_step(ib);
+        compute(sa, sb, [](int) {});
+        sa = sa + 1 == SA ? 0 : sa + 1;
+        sb = sb + 1 == SB ? 0 : sb + 1;
+        ia = ia + 1 == SA ? 0 : ia + 1;
+        ib = ib + 1 == SB ? 0 : ib + 1;
+    }
+
+    // ---------------------------------------------------------------- epilogue: bf16 NCDHW
+    float sc = 1.0f;
+    if constexpr (DT == DT_FP8)
+        sc = p.scales[0] * p.scales[2];
+    uint16_t *yb = static_cast<uint16_t *>(p.y);
+    constexpr int QUADS = MF / 16 * (MF / 16);
+#pragma unroll
+    for (int a = 0; a < FM; ++a) {
+#pragma unroll
+        for (int q = 0; q < QUADS; ++q) {
+            const int row = m0 + wm * WTM + a * MF + (MF == 16 ? 4 * lgrp : 8 * q + 4 * lgrp);
+            int nimg = 0, sp = 0;
+            if (row < p.M) {
+                nimg = row / p.P;
+                sp = row - nimg * p.P;
+            }
+            const bool vec = (p.P & 3) == 0 && row + 3 < p.M;
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                const int col = n0 + wn * WTN + b * MF + lrow;
+                if (row >= p.M || col >= p.K)
+                    continue;
+                const f32x4 v = quad<MF>(acc[a][b], q) * sc;
+                if (vec) {
+                    const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                      f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+                    *reinterpret_cast<u32x2 *>(yb + ((int64_t)nimg * p.K + col) * p.P + sp) = pk;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = row + e;
+                        if (m < p.M) {
+                            const int n2 = m / p.P;
+                            const int sp2 = m - n2 * p.P;
+                            yb[((int64_t)n2 * p.K + col) * p.P + sp2] = (uint16_t)f32_to_bf16_rne(v[e]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Launch helper for one dtype: the buffer-addressed tiles of kTiles (sb > 0).
+template <int DT>
+hipError_t launch_conv_buf_dt(const ConvParams &p, int tile, Mode mode, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+#define IGC_BLAUNCH(BM_, BN_, WM_, WN_, MF_, SA_, SB_, KB_, SP_)                                                  \
+    do {                                                                                                       \
+        if (mode == MODE_TEMPORAL)                                                                             \
+            hipLaunchKernelGGL(                                                                                \
+                (conv_igemm_buf_kernel<BM_, BN_, WM_, WN_, MF_, DT, MODE_TEMPORAL, SA_, SB_, KB_, SP_>), grid, \
+                dim3(WM_ * WN_ * 64), 0, stream, p);                                                           \
+        else                                                                                                   \
+            hipLaunchKernelGGL(                                                                                \
+                (conv_igemm_buf_kernel<BM_, BN_, WM_, WN_, MF_, DT, MODE_GENERIC, SA_, SB_, KB_, SP_>), grid,  \
+                dim3(WM_ * WN_ * 64), 0, stream, p);                                                           \
+        return hipGetLastError();                                                                              \
+    } while (0)
+    switch (tile) {
+    case 27: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 3, 128, 0);
+    case 28: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 0);
+    case 29: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 3, 128, 8);
+    case 30: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 8);
+    default: break;
+    }
+    if constexpr (DT == DT_BF16) {  // fp8 16x16 blocks need 128-byte steps
+        switch (tile) {
+        case 31: IGC_BLAUNCH(256, 256, 2, 4, 16, 4, 6, 64, 0);
+        case 32: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 5, 64, 4);
+        default: break;
+        }
+    }
+    return hipErrorInvalidValue;
+#undef IGC_BLAUNCH
+}
+
+}  // namespace igc

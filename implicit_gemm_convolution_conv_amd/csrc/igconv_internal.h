@@ -19,10 +19,13 @@ enum Dtype { DT_BF16 = 0, DT_FP8 = 1 };
 // stages < 0: input-window kernel: the activations a tile needs for one
 // 64-byte channel block sit in LDS once and serve every filter tap; the
 // filter streams through a ring of -stages stages (64 bytes of k per step).
+// sb > 0: buffer-addressed direct-to-LDS kernel (channel-block order, im2col
+// modes): activations in a ring of `stages` stages, filter in a ring of sb.
 struct TileShape {
     int bm, bn, wm, wn, mf, stages, kb;
+    int sb = 0;
 };
-constexpr int kNumTiles = 27;
+constexpr int kNumTiles = 33;
 constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 16, 0, 128},  // 8 waves, 128x64 per wave: large grids
     {128, 128, 2, 2, 16, 0, 128},  // 4 waves, 64x64 per wave
@@ -51,6 +54,12 @@ constexpr TileShape kTiles[kNumTiles] = {
     {128, 128, 2, 2, 16, 2, 128},  // two workgroups per CU
     {256, 128, 2, 4, 16, 2, 128},
     {64, 64, 2, 2, 16, 4, 128},    // small grids
+    {256, 256, 2, 4, 16, 2, 128, 3},  // buffer-addressed: A ring 2 x 32 KB, filter ring 3 x 32 KB
+    {256, 256, 2, 4, 16, 2, 128, 2},
+    {256, 256, 2, 4, 16, 2, 128, 3},  // loads spread over the MFMA rows of the step before
+    {256, 256, 2, 4, 16, 2, 128, 2},
+    {256, 256, 2, 4, 16, 4, 64, 6},   // 64-byte steps: A ring 4 x 16 KB, filter ring 6 x 16 KB
+    {256, 256, 2, 4, 16, 3, 64, 5},
 };
 
 // Everything a conv kernel needs, passed by value as kernel arguments.
@@ -76,6 +85,8 @@ struct ConvParams {
     int tpp;                // M tiles per output plane = ceil(Ho*Wo / BM)
     int win_h, win_w;       // window rows / columns (input pixels) per plane slot
     int win_nwi;            // window DMA instructions per thread per channel block
+    // buffer-addressed kernel: byte extents of x and of the packed filter (< 2^31)
+    int xbytes, wbytes;
 };
 
 // One launch of the implicit-GEMM kernel selected by (tile, mode, dtype,
@@ -85,6 +96,7 @@ hipError_t launch_conv(const ConvParams &p, int tile, Mode mode, Dtype dt, bool 
 // Reduction step of a tile in bytes of k per row.
 constexpr int step_bytes(const TileShape &t) { return t.kb; }
 constexpr bool is_window(const TileShape &t) { return t.stages < 0; }
+constexpr bool is_buffer(const TileShape &t) { return t.sb > 0; }
 
 hipError_t launch_amax(const uint16_t *t, int64_t n, float *amax, hipStream_t stream);
 hipError_t launch_fp8_scales(const float *amax, float *pair, hipStream_t stream);

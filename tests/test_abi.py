@@ -67,6 +67,9 @@ def test_path_selection():
     assert p["path"] == "temporal" and p["order"] == "cblock" and p["kstep"] == "128"
     p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))
     assert (p["path"], p["tile"], p["grid"], p["nk"], p["stages"]) == ("generic", "256x256", "6752", "864", "2")
+    assert p["loads"] == "buffer-lds"
+    p = _plan((1, 1024, 240, 160, 90), (1024, 1024, 3, 1, 1), pd=(1, 0, 0))  # beyond 2^31 bytes: 64-bit global loads
+    assert (p["big"], p["loads"]) == ("1", "global-lds")
     assert _plan((9500, 3, 1, 14, 14), (1280, 3, 1, 14, 14), (1, 14, 14), lay=B.IGC_NCDHW)["grid"] == "190"
     assert _plan((1, 1024, 240, 160, 90), (1024, 1024, 3, 1, 1), pd=(1, 0, 0))["big"] == "1"
     p = _plan((1, 64, 4, 16, 16), (64, 64, 3, 3, 3), pd=(1, 1, 1))
@@ -85,6 +88,17 @@ def test_forced_path_and_tile():
         assert e.value.status == B.IGC_ERR_UNSUPPORTED
         B.conv_debug_force(B.IGC_PATH_AUTO, 6, 0)  # direct-to-LDS 16x16 tile cannot run fp8
         with pytest.raises(B.IgcError) as e:
+            _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1), dt=B.IGC_FP8_E4M3FN)
+        assert e.value.status == B.IGC_ERR_UNSUPPORTED
+        B.conv_debug_force(B.IGC_PATH_AUTO, 27, 0)  # buffer-addressed tiles: im2col paths, whole channel blocks
+        p = _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1))
+        assert (p["loads"], p["stages"], p["bstages"]) == ("buffer-lds", "2", "3")
+        for xs, ws in (((2, 16, 1, 14, 14), (32, 16, 1, 14, 14)), ((1, 96, 4, 4, 4), (8, 96, 3, 3, 3))):
+            with pytest.raises(B.IgcError) as e:
+                _plan(xs, ws, (1, 14, 14) if xs[0] == 2 else (1, 1, 1), pd=(0, 0, 0) if xs[0] == 2 else (1, 1, 1))
+            assert e.value.status == B.IGC_ERR_UNSUPPORTED
+        with pytest.raises(B.IgcError) as e:  # 64-byte fp8 steps need 32x32 blocks
+            B.conv_debug_force(B.IGC_PATH_AUTO, 31, 0)
             _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1), dt=B.IGC_FP8_E4M3FN)
         assert e.value.status == B.IGC_ERR_UNSUPPORTED
         B.conv_debug_force(B.IGC_PATH_AUTO, 7, 5)

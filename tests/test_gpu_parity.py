@@ -348,6 +348,71 @@ def test_point_output_fp8(tile):
     P.check_close(P.y_values(y), ref, int(np.prod(ws[1:])), mx, mw, name)
 
 
+# ------------------------------------------------------------------ buffer-addressed tiles (27..32)
+
+BUF_TILES_BF16 = [27, 28, 29, 30, 31, 32]
+BUF_TILES_FP8 = [27, 28, 29, 30]
+BUF_CASES = [g for g in GEOMS if g[0] in ("c128_cblock_multi_tile", "asym_pad_stride2", "temporal_3x1x1")] + [
+    ("dilated_c64", (1, 64, 6, 11, 13), (80, 64, 3, 3, 3), (1, 1, 1), (2, 1, 2), (2, 1, 2)),
+    ("c192_k300_two_col_tiles", (1, 192, 4, 9, 10), (300, 192, 3, 3, 3), (1, 2, 1), (1, 1, 1), (1, 1, 1)),
+    ("pointwise_c64_one_step", (2, 64, 3, 7, 5), (80, 64, 1, 1, 1), (1, 1, 1), (0, 0, 0), (1, 1, 1)),
+    ("generic_1x1x2_two_steps", (1, 64, 3, 6, 9), (48, 64, 1, 1, 2), (1, 1, 1), (0, 0, 1), (1, 1, 1)),
+    ("temporal_c128_t1", (1, 128, 3, 5, 6), (40, 128, 1, 1, 1), (1, 1, 1), (0, 0, 0), (1, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("tile", BUF_TILES_BF16)
+@pytest.mark.parametrize("case", BUF_CASES, ids=[g[0] for g in BUF_CASES])
+def test_buffer_tiles_bf16(tile, case):
+    name, xs, ws, st, pd, dl = case
+    with forced(tile=tile):
+        assert "loads=buffer-lds" in B.conv_plan(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC)
+        _bf16_case(f"buffer tile {tile} {name}", xs, ws, st, pd, dl, seed=zlib.crc32(name.encode()) % 1000)
+
+
+@pytest.mark.parametrize("tile", BUF_TILES_BF16)
+def test_buffer_tiles_integer_bit_exact(tile):
+    _announce(f"buffer tile {tile} integer")
+    with forced(tile=tile):
+        _int_case((2, 64, 5, 9, 11), (96, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), seed=29)
+        _int_case((1, 128, 6, 7, 8), (40, 128, 3, 2, 3), (2, 1, 2), (1, 0, 2), (1, 2, 1), seed=30)
+
+
+@pytest.mark.parametrize("tile", BUF_TILES_FP8)
+@pytest.mark.parametrize("case", [g for g in FP8_GEOMS if g[0] in ("fp8_c256_k300", "fp8_temporal")],
+                         ids=lambda g: g[0])
+def test_buffer_tiles_fp8(tile, case):
+    name, xs, ws, st, pd, dl = case
+    _announce(f"buffer tile {tile} {name}")
+    g = I.generator(35, P.DEV)
+    x = I.draw(xs, ("normal", 1.0), g, P.DEV)
+    w = I.draw(ws, ("normal", 1.0 / np.sqrt(np.prod(ws[1:]))), g, P.DEV)
+    ops = P.Fp8Operands(x, w)
+    with forced(tile=tile):
+        y = P.run_fp8(ops, xs, ws, st, pd, dl)
+    sx, sw = float(ops.ref_scales[0]), float(ops.ref_scales[2])
+    ref = O.conv3d(ops.ref_xq, ops.ref_wq, st, pd, dl, sx=sx, sw=sw)
+    mx = float(np.abs(O.e4m3_decode(ops.ref_xq)).max()) * sx
+    mw = float(np.abs(O.e4m3_decode(ops.ref_wq)).max()) * sw
+    P.check_close(P.y_values(y), ref, int(np.prod(ws[1:])), mx, mw, name)
+
+
+def test_buffer_tiles_agree_bitwise_with_global_tiles():
+    # same reduction order (channel block outer, 16x16 blocks, k-slices in order): identical bits
+    _announce("buffer tiles vs direct-to-LDS tiles 6 / 21, bitwise")
+    g = I.generator(16, P.DEV)
+    xs, ws, st, pd, dl = (1, 128, 5, 18, 20), (264, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)
+    x = I.draw(xs, ("uniform", 1.0), g, P.DEV)
+    w = I.draw(ws, ("uniform", 1.0), g, P.DEV)
+    outs = {}
+    for tile in [6, 21] + BUF_TILES_BF16:
+        with forced(tile=tile):
+            outs[tile] = P.run_bf16(x, w, st, pd, dl).clone().view(torch.int16)
+    for tile in BUF_TILES_BF16:
+        assert torch.equal(outs[tile], outs[21]), tile
+    assert torch.equal(outs[6], outs[21])
+
+
 # ------------------------------------------------------------------ input-window tiles (16 bf16, 17 bf16/fp8)
 
 WIN_CASES = [
