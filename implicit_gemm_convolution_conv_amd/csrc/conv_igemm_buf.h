@@ -11,10 +11,9 @@
 //    of a row is one 32-bit add per step and no zero line or branch is needed.
 //    Rows past the end of the GEMM are clamped to the last row; they load real
 //    data whose results are never stored.
-//  * The filter (B) and the activations (A) have rings of their own: the
-//    filter stream is read once per tile and misses L2 far more often than the
-//    activations, which every filter tap re-reads, so B is issued SB-1 steps
-//    ahead and A SA-1 steps ahead (SB >= SA) within the same LDS budget.
+//  * The filter (B) and the activations (A) have rings of their own (SB and
+//    SA stages), so the LDS budget can give the operand whose loads take
+//    longer the deeper ring: B is issued SB-1 steps ahead, A SA-1 steps ahead.
 //  * The loads of a step can be spread over the MFMA rows of the step before
 //    (SPREAD rows), so that their address arithmetic issues in the shadow of
 //    the matrix instructions instead of in front of them.
@@ -49,7 +48,8 @@ __device__ inline void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, char *lds, unsi
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, int SA, int SB, int KB, int SPREAD>
+template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, int SA, int SB, int KB, int SPREAD, int PF = 1,
+          bool BPF = false>
 __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN>())))
 void conv_igemm_buf_kernel(ConvParams p)
 {
@@ -72,10 +72,10 @@ void conv_igemm_buf_kernel(ConvParams p)
     static_assert(KB == 64 || KB == 128, "64- or 128-byte steps");
     static_assert(AIT >= 1 && BIT >= 1 && BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "loader split");
     static_assert(SUB >= 1, "step too short for this MFMA");
-    static_assert(SA >= 2 && SB >= SA, "ring depths");
+    static_assert(SA >= 2 && SB >= 2, "ring depths");
     static_assert(SA * ASTAGE + SB * BSTAGE <= 160 * 1024, "LDS budget");
-    static_assert(BIT + (SA - 2) * LPS < 64, "vmcnt range");
     static_assert(SPREAD >= 0 && SPREAD <= ROWS, "spread within one step");
+    static_assert(PF >= 1 && PF <= 3, "A fragment prefetch distance");
 
     __shared__ __attribute__((aligned(1024))) char smem[SA * ASTAGE + SB * BSTAGE];
     char *const as = smem;
@@ -214,32 +214,68 @@ void conv_igemm_buf_kernel(ConvParams p)
         }
     };
     // One step from slots (sa, sb); hook(row) runs after MFMA row `row` (0..ROWS-1).
+    // A fragments are read PF rows ahead of their MFMAs; with BPF the B
+    // fragments of the next k-slice are read while the last rows of this one run.
     auto compute = [&](int sa, int sb, auto &&hook) {
         const char *aw = as + sa * ASTAGE + (wm * WTM + lrow) * KB;
         const char *bw = bs + sb * BSTAGE + (wn * WTN + lrow) * KB;
+        Frag bf[2][FN];
+#pragma unroll
+        for (int b = 0; b < FN; ++b)
+            bf[0][b] = frag(bw + b * MF * KB, 0);
 #pragma unroll
         for (int h = 0; h < SUB; ++h) {
-            Frag bf[FN];
-#pragma unroll
-            for (int b = 0; b < FN; ++b)
-                bf[b] = frag(bw + b * MF * KB, h);
-            Frag af[2];
-            af[0] = frag(aw, h);
-#pragma unroll
-            for (int a = 0; a < FM; ++a) {
-                if (a + 1 < FM)
-                    af[(a + 1) & 1] = frag(aw + (a + 1) * MF * KB, h);
+            const int cb = BPF ? (h & 1) : 0;
+            if (!BPF && h > 0) {
 #pragma unroll
                 for (int b = 0; b < FN; ++b)
-                    mfma(af[a & 1], bf[b], acc[a][b]);
+                    bf[0][b] = frag(bw + b * MF * KB, h);
+            }
+            Frag af[PF + 1];
+#pragma unroll
+            for (int q = 0; q < PF; ++q)
+                if (q < FM)
+                    af[q] = frag(aw + q * MF * KB, h);
+#pragma unroll
+            for (int a = 0; a < FM; ++a) {
+                if (a + PF < FM)
+                    af[(a + PF) % (PF + 1)] = frag(aw + (a + PF) * MF * KB, h);
+                if (BPF && h + 1 < SUB && a == (FM > 2 ? FM - 2 : 0)) {
+#pragma unroll
+                    for (int b = 0; b < FN; ++b)
+                        bf[cb ^ 1][b] = frag(bw + b * MF * KB, h + 1);
+                }
+#pragma unroll
+                for (int b = 0; b < FN; ++b)
+                    mfma(af[a % (PF + 1)], bf[cb][b], acc[a][b]);
                 hook(h * FM + a);
             }
         }
     };
 
     // ---------------------------------------------------------------- pipeline
+    // The operand with the deeper ring (the lead) is issued further ahead; in
+    // each step the other one (the trail) is issued first, so that waiting for
+    // the trail's loads of a step never waits for loads issued after them.
+    constexpr bool A_FIRST = SA <= SB;
+    constexpr int SMIN = SA < SB ? SA : SB, SMAX = SA < SB ? SB : SA;
+    constexpr int FIRST_IT = A_FIRST ? AIT : BIT;
+    // Loads issued after this thread's last load of step ks, in steady state:
+    // the lead's loads of the step that issued the trail's part of ks (when the
+    // rings differ), plus SMIN-2 whole steps.
+    constexpr int AHEAD = (SA == SB ? 0 : LPS - FIRST_IT) + (SMIN - 2) * LPS;
+    static_assert(AHEAD < 64, "vmcnt range");
     const int nk = p.nk;
     KPos ka{0, 0, 0, 0, 0}, kb{0, 0, 0, 0, 0};  // next A and B steps to issue
+    // j-th DMA instruction of a step in issue order (A rows then B rows, or B then A).
+    auto issue_j = [&](int j, int sta, int stb, unsigned ash, unsigned bsh) {
+        const bool is_a = A_FIRST ? j < AIT : j >= BIT;
+        const int row = A_FIRST ? (is_a ? j : j - AIT) : (is_a ? j - BIT : j);
+        if (is_a)
+            issue(row, sta, ka, ash, 0);
+        else
+            issue(AIT + row, stb, kb, 0, bsh);
+    };
     auto issue_a_step = [&](int st) {
         const unsigned sh = a_shift(ka);
 #pragma unroll
@@ -254,37 +290,46 @@ void conv_igemm_buf_kernel(ConvParams p)
             issue(j, st, kb, 0, sh);
         advance(kb);
     };
-    // Prologue: the issues of the virtual steps -(SB-1) .. -1, in steady-state order.
+    // issue the step's parts that exist (A(ks+SA-1) if < nk, B(ks+SB-1) if < nk) in ring order
+    auto issue_parts = [&](int ja, int jb, int sta, int stb) {
+        if (A_FIRST) {
+            if (ja >= 0 && ja < nk)
+                issue_a_step(sta);
+            if (jb >= 0 && jb < nk)
+                issue_b_step(stb);
+        } else {
+            if (jb >= 0 && jb < nk)
+                issue_b_step(stb);
+            if (ja >= 0 && ja < nk)
+                issue_a_step(sta);
+        }
+    };
+    // Prologue: the issues of the virtual steps -(SMAX-1) .. -1, in steady-state order.
 #pragma unroll
-    for (int j = -(SB - 1); j < 0; ++j) {
+    for (int j = -(SMAX - 1); j < 0; ++j) {
         const int ja = j + SA - 1, jb = j + SB - 1;
-        if (ja >= 0 && ja < nk)
-            issue_a_step(ja % SA);
-        if (jb < nk)
-            issue_b_step(jb % SB);
+        issue_parts(ja, jb, ja >= 0 ? ja % SA : 0, jb >= 0 ? jb % SB : 0);
     }
     int ks = 0;
-    // Steady state: every step issues A(ks+SA-1) then B(ks+SB-1). Loads issued
-    // after this thread's last load of step ks: B(ks+SB-SA) of the step that
-    // issued A(ks) when SB > SA, plus SA-2 whole steps.
     int sa = 0, sb = 0;                  // slots of step ks
     int ia = SA - 1, ib = SB - 1;        // slots the step's issues go to
-    for (; ks < nk - SB + 1; ++ks) {
-        wait_vmcnt<(SB > SA ? BIT : 0) + (SA - 2) * LPS>();
+    // Steady state: every step issues both parts.
+    for (; ks < nk - SMAX + 1; ++ks) {
+        wait_vmcnt<AHEAD>();
         asm volatile("s_barrier" ::: "memory");
         const unsigned ash = a_shift(ka), bsh = b_shift(kb);
         const int sta = ia, stb = ib;
         if constexpr (SPREAD == 0) {
 #pragma unroll
             for (int j = 0; j < LPS; ++j)
-                issue(j, j < AIT ? sta : stb, j < AIT ? ka : kb, ash, bsh);
+                issue_j(j, sta, stb, ash, bsh);
             compute(sa, sb, [](int) {});
         } else {
             compute(sa, sb, [&](int row) {
 #pragma unroll
                 for (int j = 0; j < LPS; ++j)
                     if (j * SPREAD / LPS == row)
-                        issue(j, j < AIT ? sta : stb, j < AIT ? ka : kb, ash, bsh);
+                        issue_j(j, sta, stb, ash, bsh);
             });
         }
         advance(ka);
@@ -294,14 +339,11 @@ void conv_igemm_buf_kernel(ConvParams p)
         ia = ia + 1 == SA ? 0 : ia + 1;
         ib = ib + 1 == SB ? 0 : ib + 1;
     }
-    // Drain: the last SB-1 steps (or all of a short reduction) wait for everything.
+    // Drain: the last SMAX-1 steps (or all of a short reduction) wait for everything.
     for (; ks < nk; ++ks) {
         wait_vmcnt<0>();
         asm volatile("s_barrier" ::: "memory");
-        if (ks + SA - 1 < nk)
-            issue_a_step(ia);
-        if (ks + SB - 1 < nk)
-            issue_b_step(ib);
+        issue_parts(ks + SA - 1, ks + SB - 1, ia, ib);
         compute(sa, sb, [](int) {});
         sa = sa + 1 == SA ? 0 : sa + 1;
         sb = sb + 1 == SB ? 0 : sb + 1;
@@ -357,15 +399,15 @@ template <int DT>
 hipError_t launch_conv_buf_dt(const ConvParams &p, int tile, Mode mode, hipStream_t stream)
 {
     const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
-#define IGC_BLAUNCH(BM_, BN_, WM_, WN_, MF_, SA_, SB_, KB_, SP_)                                                  \
+#define IGC_BLAUNCH(BM_, BN_, WM_, WN_, MF_, SA_, SB_, KB_, SP_, ...)                                                  \
     do {                                                                                                       \
         if (mode == MODE_TEMPORAL)                                                                             \
             hipLaunchKernelGGL(                                                                                \
-                (conv_igemm_buf_kernel<BM_, BN_, WM_, WN_, MF_, DT, MODE_TEMPORAL, SA_, SB_, KB_, SP_>), grid, \
+                (conv_igemm_buf_kernel<BM_, BN_, WM_, WN_, MF_, DT, MODE_TEMPORAL, SA_, SB_, KB_, SP_, ##__VA_ARGS__>), grid, \
                 dim3(WM_ * WN_ * 64), 0, stream, p);                                                           \
         else                                                                                                   \
             hipLaunchKernelGGL(                                                                                \
-                (conv_igemm_buf_kernel<BM_, BN_, WM_, WN_, MF_, DT, MODE_GENERIC, SA_, SB_, KB_, SP_>), grid,  \
+                (conv_igemm_buf_kernel<BM_, BN_, WM_, WN_, MF_, DT, MODE_GENERIC, SA_, SB_, KB_, SP_, ##__VA_ARGS__>), grid,  \
                 dim3(WM_ * WN_ * 64), 0, stream, p);                                                           \
         return hipGetLastError();                                                                              \
     } while (0)
@@ -374,12 +416,26 @@ hipError_t launch_conv_buf_dt(const ConvParams &p, int tile, Mode mode, hipStrea
     case 28: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 0);
     case 29: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 3, 128, 8);
     case 30: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 8);
+    case 33: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 4);
+    case 34: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 4, 2, true);
+    case 35: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 8, 2, false);
+    case 36: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 8, 2, true);
+    case 37: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 8, 3, true);
+    case 40: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 8);
+    case 41: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 4);
+    case 42: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 0);
+    case 46: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 8, 2, true);
     default: break;
     }
     if constexpr (DT == DT_BF16) {  // fp8 16x16 blocks need 128-byte steps
         switch (tile) {
         case 31: IGC_BLAUNCH(256, 256, 2, 4, 16, 4, 6, 64, 0);
         case 32: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 5, 64, 4);
+        case 38: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 12, 2, true);
+        case 39: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 16, 2, true);
+        case 43: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 12);
+        case 44: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 16);
+        case 45: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 12, 2, true);
         default: break;
         }
     }

@@ -25,7 +25,7 @@ struct TileShape {
     int bm, bn, wm, wn, mf, stages, kb;
     int sb = 0;
 };
-constexpr int kNumTiles = 33;
+constexpr int kNumTiles = 47;
 constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 16, 0, 128},  // 8 waves, 128x64 per wave: large grids
     {128, 128, 2, 2, 16, 0, 128},  // 4 waves, 64x64 per wave
@@ -60,6 +60,20 @@ constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 16, 2, 128, 2},
     {256, 256, 2, 4, 16, 4, 64, 6},   // 64-byte steps: A ring 4 x 16 KB, filter ring 6 x 16 KB
     {256, 256, 2, 4, 16, 3, 64, 5},
+    {256, 256, 2, 4, 16, 2, 128, 2},  // 33-39: issue spread / fragment prefetch variants of tile 30
+    {256, 256, 2, 4, 16, 2, 128, 2},
+    {256, 256, 2, 4, 16, 2, 128, 2},
+    {256, 256, 2, 4, 16, 2, 128, 2},
+    {256, 256, 2, 4, 16, 2, 128, 2},
+    {256, 256, 2, 4, 16, 2, 128, 2},  // bf16 only
+    {256, 256, 2, 4, 16, 2, 128, 2},  // bf16 only
+    {256, 256, 2, 4, 16, 3, 128, 2},  // 40-46: A ring 3 x 32 KB, filter ring 2 x 32 KB
+    {256, 256, 2, 4, 16, 3, 128, 2},
+    {256, 256, 2, 4, 16, 3, 128, 2},
+    {256, 256, 2, 4, 16, 3, 128, 2},  // bf16 only
+    {256, 256, 2, 4, 16, 3, 128, 2},  // bf16 only
+    {256, 256, 2, 4, 16, 3, 128, 2},  // bf16 only
+    {256, 256, 2, 4, 16, 3, 128, 2},
 };
 
 // Everything a conv kernel needs, passed by value as kernel arguments.

@@ -66,7 +66,7 @@ def test_path_selection():
     p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 1, 1), pd=(1, 0, 0), dt=B.IGC_FP8_E4M3FN)
     assert p["path"] == "temporal" and p["order"] == "cblock" and p["kstep"] == "128"
     p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))
-    assert (p["path"], p["tile"], p["grid"], p["nk"], p["stages"]) == ("generic", "256x256", "6752", "864", "2")
+    assert (p["path"], p["tile"], p["grid"], p["nk"], p["stages"], p["bstages"]) == ("generic", "256x256", "6752", "864", "3", "2")
     assert p["loads"] == "buffer-lds"
     p = _plan((1, 1024, 240, 160, 90), (1024, 1024, 3, 1, 1), pd=(1, 0, 0))  # beyond 2^31 bytes: 64-bit global loads
     assert (p["big"], p["loads"]) == ("1", "global-lds")
