@@ -36,7 +36,8 @@ PEAK_HBM_GBS = 8000.0
 # sources that decide the headline kernel's code and launch configuration
 KERNEL_SOURCES = ["implicit_gemm_convolution_conv_amd/csrc/conv_igemm.h",
                   "implicit_gemm_convolution_conv_amd/csrc/conv_igemm_dma.h",
-                  "implicit_gemm_convolution_conv_amd/csrc/conv_dma_bf16.hip",
+                  "implicit_gemm_convolution_conv_amd/csrc/conv_igemm_buf.h",
+                  "implicit_gemm_convolution_conv_amd/csrc/conv_buf_bf16.hip",
                   "implicit_gemm_convolution_conv_amd/csrc/igconv_internal.h",
                   "implicit_gemm_convolution_conv_amd/csrc/api.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv_igemm_c3_bf16_traffic.json")

@@ -239,13 +239,13 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         const bool buffer_ok = path != IGC_PATH_POINT && g.C % (128 / esz) == 0 && !pl.big &&
                                xnum * esz < (int64_t(1) << 31) && g.K * ldw * esz < (int64_t(1) << 31);
         if (tile == 21 && buffer_ok)
-            tile = 40;
+            tile = 29;
     } else {
         if (kTiles[tile].stages && kTiles[tile].mf == 16 && esz == 1 && kTiles[tile].kb == 64)
             return fail(IGC_ERR_UNSUPPORTED, "tile %d: fp8 with 64-byte steps needs 32x32 MFMA blocks", tile);
         if (esz == 2 && (tile == 12 || tile == 13))
             return fail(IGC_ERR_UNSUPPORTED, "tile %d is an fp8-only tile", tile);
-        if (esz == 1 && (tile == 20 || tile == 38 || tile == 39 || (tile >= 43 && tile <= 45)))
+        if (esz == 1 && (tile == 20 || tile == 30))
             return fail(IGC_ERR_UNSUPPORTED, "tile %d is a bf16-only tile", tile);
         if (is_window(kTiles[tile]) && path != IGC_PATH_GENERIC)
             return fail(IGC_ERR_UNSUPPORTED, "tile %d (input window) runs the generic im2col path only", tile);

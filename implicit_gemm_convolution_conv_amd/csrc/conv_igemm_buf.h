@@ -412,30 +412,16 @@ hipError_t launch_conv_buf_dt(const ConvParams &p, int tile, Mode mode, hipStrea
         return hipGetLastError();                                                                              \
     } while (0)
     switch (tile) {
-    case 27: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 3, 128, 0);
-    case 28: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 0);
-    case 29: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 3, 128, 8);
-    case 30: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 8);
-    case 33: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 4);
-    case 34: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 4, 2, true);
-    case 35: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 8, 2, false);
-    case 36: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 8, 2, true);
-    case 37: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 8, 3, true);
-    case 40: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 8);
-    case 41: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 4);
-    case 42: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 0);
-    case 46: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 8, 2, true);
+    case 27: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 8);
+    case 28: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 3, 128, 8);
+    case 29: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 8);
+    case 31: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 8, 2, true);
     default: break;
     }
-    if constexpr (DT == DT_BF16) {  // fp8 16x16 blocks need 128-byte steps
+    if constexpr (DT == DT_BF16) {  // 16 MFMA rows per step: bf16 only; fp8 16x16 blocks need 128-byte steps
         switch (tile) {
-        case 31: IGC_BLAUNCH(256, 256, 2, 4, 16, 4, 6, 64, 0);
+        case 30: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 16);
         case 32: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 5, 64, 4);
-        case 38: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 12, 2, true);
-        case 39: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 16, 2, true);
-        case 43: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 12);
-        case 44: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 16);
-        case 45: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 12, 2, true);
         default: break;
         }
     }

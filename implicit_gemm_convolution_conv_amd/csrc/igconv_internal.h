@@ -25,7 +25,7 @@ struct TileShape {
     int bm, bn, wm, wn, mf, stages, kb;
     int sb = 0;
 };
-constexpr int kNumTiles = 47;
+constexpr int kNumTiles = 33;
 constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 16, 0, 128},  // 8 waves, 128x64 per wave: large grids
     {128, 128, 2, 2, 16, 0, 128},  // 4 waves, 64x64 per wave
@@ -54,26 +54,12 @@ constexpr TileShape kTiles[kNumTiles] = {
     {128, 128, 2, 2, 16, 2, 128},  // two workgroups per CU
     {256, 128, 2, 4, 16, 2, 128},
     {64, 64, 2, 2, 16, 4, 128},    // small grids
-    {256, 256, 2, 4, 16, 2, 128, 3},  // buffer-addressed: A ring 2 x 32 KB, filter ring 3 x 32 KB
-    {256, 256, 2, 4, 16, 2, 128, 2},
-    {256, 256, 2, 4, 16, 2, 128, 3},  // loads spread over the MFMA rows of the step before
-    {256, 256, 2, 4, 16, 2, 128, 2},
-    {256, 256, 2, 4, 16, 4, 64, 6},   // 64-byte steps: A ring 4 x 16 KB, filter ring 6 x 16 KB
-    {256, 256, 2, 4, 16, 3, 64, 5},
-    {256, 256, 2, 4, 16, 2, 128, 2},  // 33-39: issue spread / fragment prefetch variants of tile 30
-    {256, 256, 2, 4, 16, 2, 128, 2},
-    {256, 256, 2, 4, 16, 2, 128, 2},
-    {256, 256, 2, 4, 16, 2, 128, 2},
-    {256, 256, 2, 4, 16, 2, 128, 2},
-    {256, 256, 2, 4, 16, 2, 128, 2},  // bf16 only
-    {256, 256, 2, 4, 16, 2, 128, 2},  // bf16 only
-    {256, 256, 2, 4, 16, 3, 128, 2},  // 40-46: A ring 3 x 32 KB, filter ring 2 x 32 KB
-    {256, 256, 2, 4, 16, 3, 128, 2},
-    {256, 256, 2, 4, 16, 3, 128, 2},
-    {256, 256, 2, 4, 16, 3, 128, 2},  // bf16 only
-    {256, 256, 2, 4, 16, 3, 128, 2},  // bf16 only
-    {256, 256, 2, 4, 16, 3, 128, 2},  // bf16 only
-    {256, 256, 2, 4, 16, 3, 128, 2},
+    {256, 256, 2, 4, 16, 2, 128, 2},  // buffer-addressed: rings of 2 x 32 KB, loads over 8 of 16 MFMA rows
+    {256, 256, 2, 4, 16, 2, 128, 3},  // filter ring 3 x 32 KB (issued two steps ahead)
+    {256, 256, 2, 4, 16, 3, 128, 2},  // activation ring 3 x 32 KB (two steps ahead): large-grid default
+    {256, 256, 2, 4, 16, 3, 128, 2},  // as 29, loads over all 16 MFMA rows (bf16 only)
+    {256, 256, 2, 4, 16, 3, 128, 2},  // as 29, A fragments two rows ahead, next k-slice's B read early
+    {256, 256, 2, 4, 16, 3, 64, 5},   // 64-byte steps: rings of 3 and 5 x 16 KB (bf16 only)
 };
 
 // Everything a conv kernel needs, passed by value as kernel arguments.

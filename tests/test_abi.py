@@ -92,13 +92,13 @@ def test_forced_path_and_tile():
         assert e.value.status == B.IGC_ERR_UNSUPPORTED
         B.conv_debug_force(B.IGC_PATH_AUTO, 27, 0)  # buffer-addressed tiles: im2col paths, whole channel blocks
         p = _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1))
-        assert (p["loads"], p["stages"], p["bstages"]) == ("buffer-lds", "2", "3")
+        assert (p["loads"], p["stages"], p["bstages"]) == ("buffer-lds", "2", "2")
         for xs, ws in (((2, 16, 1, 14, 14), (32, 16, 1, 14, 14)), ((1, 96, 4, 4, 4), (8, 96, 3, 3, 3))):
             with pytest.raises(B.IgcError) as e:
                 _plan(xs, ws, (1, 14, 14) if xs[0] == 2 else (1, 1, 1), pd=(0, 0, 0) if xs[0] == 2 else (1, 1, 1))
             assert e.value.status == B.IGC_ERR_UNSUPPORTED
         with pytest.raises(B.IgcError) as e:  # 64-byte fp8 steps need 32x32 blocks
-            B.conv_debug_force(B.IGC_PATH_AUTO, 31, 0)
+            B.conv_debug_force(B.IGC_PATH_AUTO, 32, 0)
             _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1), dt=B.IGC_FP8_E4M3FN)
         assert e.value.status == B.IGC_ERR_UNSUPPORTED
         B.conv_debug_force(B.IGC_PATH_AUTO, 7, 5)
