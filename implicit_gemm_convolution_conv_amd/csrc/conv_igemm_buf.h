@@ -48,6 +48,230 @@ __device__ inline void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, char *lds, unsi
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
 }
 
+// Reduction position in channel-block order: channel block cb (pairs * TKE
+// channels) outer, then tap (t, r, s), then the `pairs` TKE-wide halves of
+// the block. Every field is uniform across the workgroup.
+template <int TKE>
+struct KPos {
+    int half = 0, s = 0, r = 0, t = 0, cb = 0;
+    int tap = 0;  // (t * R + r) * S + s
+
+    __device__ void advance(const ConvParams &p)
+    {
+        const bool hw = ++half == p.pairs;
+        half = hw ? 0 : half;
+        tap += hw;
+        s += hw;
+        const bool sw = s == p.S;
+        s = sw ? 0 : s;
+        r += sw;
+        const bool rw = r == p.R;
+        r = rw ? 0 : r;
+        t += rw;
+        const bool tw = t == p.T;
+        t = tw ? 0 : t;
+        tap = tw ? 0 : tap;
+        cb += tw ? p.pairs * TKE : 0;
+    }
+    // Bytes from an input row's origin to this tap and channel block.
+    template <int MODE, int ESZ>
+    __device__ unsigned a_shift(const ConvParams &p) const
+    {
+        const int c = cb + half * TKE;
+        if constexpr (MODE == MODE_TEMPORAL)
+            return (unsigned)((t * p.dd) * (p.H * p.W) * p.C + c) * ESZ;
+        else
+            return (unsigned)((((t * p.dd) * p.H + r * p.dh) * p.W + s * p.dw) * p.C + c) * ESZ;
+    }
+    // Bytes from a packed filter row's start to this reduction step.
+    template <int ESZ>
+    __device__ unsigned b_shift(const ConvParams &p) const
+    {
+        return (unsigned)((((t * p.R + r) * p.S + s) * p.C + cb + half * TKE) * ESZ);
+    }
+};
+
+// N im2col rows of one lane (rows first + i * stride, clamped to M - 1): the
+// input origin (d, h, w) of each and its byte offset at channel chunk `chunk`.
+template <int N, int MODE, int ESZ>
+struct ImRows {
+    int d[N], h[N], w[N];
+    unsigned off[N];  // wraps for padded origins; valid taps land in range
+
+    __device__ void init(const ConvParams &p, int first, int stride, int chunk)
+    {
+        const int hw = p.Ho * p.Wo;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int m = min(first + i * stride, p.M - 1);
+            const int nimg = m / p.P;
+            const int sp = m - nimg * p.P;
+            const int od = sp / hw;
+            const int rem = sp - od * hw;
+            const int oh = rem / p.Wo;
+            const int ow = rem - oh * p.Wo;
+            d[i] = od * p.sd - p.pd;
+            h[i] = oh * p.sh - p.ph;
+            w[i] = ow * p.sw - p.pw;
+            unsigned pos;
+            if constexpr (MODE == MODE_TEMPORAL)
+                pos = (unsigned)(nimg * p.D + d[i]) * (unsigned)(p.H * p.W) + (unsigned)rem;
+            else
+                pos = ((unsigned)(nimg * p.D + d[i]) * (unsigned)p.H + (unsigned)h[i]) * (unsigned)p.W +
+                      (unsigned)w[i];
+            off[i] = pos * (unsigned)(p.C * ESZ) + (unsigned)(chunk * 16);
+        }
+    }
+    // Buffer offset of row i at reduction position k (shift = k.a_shift): past
+    // the end of the buffer when the tap falls outside the input box.
+    template <int TKE>
+    __device__ unsigned at(const ConvParams &p, int i, const KPos<TKE> &k, unsigned shift) const
+    {
+        bool ok = (unsigned)(d[i] + k.t * p.dd) < (unsigned)p.D;
+        if constexpr (MODE == MODE_GENERIC)
+            ok = ok & ((unsigned)(h[i] + k.r * p.dh) < (unsigned)p.H) & ((unsigned)(w[i] + k.s * p.dw) < (unsigned)p.W);
+        return ok ? off[i] + shift : kPastEnd;
+    }
+};
+
+// As ImRows, for filters of at most 32 taps: each row keeps a bit mask of
+// the taps that fall inside the input box instead of its origin (two
+// registers per row instead of four).
+template <int N, int MODE, int ESZ>
+struct ImRowsMasked {
+    unsigned off[N];
+    unsigned valid[N];  // bit (t * R + r) * S + s: that tap reads inside the input box
+
+    __device__ void init(const ConvParams &p, int first, int stride, int chunk)
+    {
+        ImRows<N, MODE, ESZ> rows;
+        rows.init(p, first, stride, chunk);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            off[i] = rows.off[i];
+            unsigned md = 0, mh = 0, mw = 0;  // per-axis validity
+            for (int t = 0; t < p.T; ++t)
+                md |= (unsigned)((unsigned)(rows.d[i] + t * p.dd) < (unsigned)p.D) << t;
+            for (int r = 0; r < p.R; ++r)
+                mh |= (unsigned)(MODE == MODE_TEMPORAL || (unsigned)(rows.h[i] + r * p.dh) < (unsigned)p.H) << r;
+            for (int s = 0; s < p.S; ++s)
+                mw |= (unsigned)(MODE == MODE_TEMPORAL || (unsigned)(rows.w[i] + s * p.dw) < (unsigned)p.W) << s;
+            unsigned v = 0;
+            for (int t = 0; t < p.T; ++t)
+                for (int r = 0; r < p.R; ++r)
+                    if (((md >> t) & (mh >> r)) & 1u)
+                        v |= mw << ((t * p.R + r) * p.S);
+            valid[i] = v;
+        }
+    }
+    template <int TKE>
+    __device__ unsigned at(const ConvParams &, int i, const KPos<TKE> &k, unsigned shift) const
+    {
+        return ((valid[i] >> k.tap) & 1u) ? off[i] + shift : kPastEnd;
+    }
+};
+
+// N packed-filter rows of one lane (rows first + i * stride, clamped to Ncol - 1).
+template <int N, int ESZ>
+struct FilterRows {
+    unsigned off[N];
+
+    __device__ void init(const ConvParams &p, int first, int stride, int chunk)
+    {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int n = min(first + i * stride, p.Ncol - 1);
+            off[i] = (unsigned)n * (unsigned)(p.ldw * ESZ) + (unsigned)(chunk * 16);
+        }
+    }
+};
+
+// MFMA operand fragment of one lane: 8 bf16 or 32 fp8 values along k.
+template <int DT>
+using FragT = typename std::conditional<DT == DT_BF16, bf16x8, i32x8>::type;
+
+// The fragment of k-slice h of the LDS row at rowp (KB-byte rows, chunk q at
+// slot q ^ lsw): lane group lgrp holds chunk(s) (h * GROUPS + lgrp) * CPL.
+template <int DT, int MF>
+__device__ inline FragT<DT> lds_frag(const char *rowp, int h, int lgrp, int lsw)
+{
+    constexpr int GROUPS = 64 / MF, CPL = DT == DT_BF16 ? 1 : 2;
+    const int c0 = (h * GROUPS + lgrp) * CPL;
+    if constexpr (DT == DT_BF16) {
+        return *reinterpret_cast<const bf16x8 *>(rowp + ((c0 ^ lsw) * 16));
+    } else {
+        const i32x4 lo = *reinterpret_cast<const i32x4 *>(rowp + ((c0 ^ lsw) * 16));
+        const i32x4 hi = *reinterpret_cast<const i32x4 *>(rowp + (((c0 + 1) ^ lsw) * 16));
+        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+}
+
+template <int DT, int MF>
+__device__ inline void mfma_acc(const FragT<DT> &af, const FragT<DT> &bf, typename AccType<MF>::type &c)
+{
+    if constexpr (DT == DT_BF16) {
+        if constexpr (MF == 16)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, c, 0, 0, 0);
+        else
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, c, 0, 0, 0);
+    } else {
+        if constexpr (MF == 16)
+            c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, c, 0, 0, 0, 0, 0, 0);
+        else
+            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, c, 0, 0, 0, 0, 0, 0);
+    }
+}
+
+// Epilogue: one wave's FM x FN MFMA blocks of the tile at (row0, col0) to bf16
+// NCDHW y, scaled by s_x * s_w for fp8. Four consecutive rows of one column
+// go out as one 8-byte store when they share an image and P % 4 == 0.
+template <int MF, int FM, int FN, int DT>
+__device__ inline void store_tile_ncdhw(const typename AccType<MF>::type (&acc)[FM][FN], const ConvParams &p,
+                                        int row0, int col0, int lane)
+{
+    const int lrow = lane & (MF - 1), lgrp = lane / MF;
+    float sc = 1.0f;
+    if constexpr (DT == DT_FP8)
+        sc = p.scales[0] * p.scales[2];
+    uint16_t *yb = static_cast<uint16_t *>(p.y);
+    constexpr int QUADS = MF / 16 * (MF / 16);
+#pragma unroll
+    for (int a = 0; a < FM; ++a) {
+#pragma unroll
+        for (int q = 0; q < QUADS; ++q) {
+            const int row = row0 + a * MF + (MF == 16 ? 4 * lgrp : 8 * q + 4 * lgrp);
+            int nimg = 0, sp = 0;
+            if (row < p.M) {
+                nimg = row / p.P;
+                sp = row - nimg * p.P;
+            }
+            const bool vec = (p.P & 3) == 0 && row + 3 < p.M;
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                const int col = col0 + b * MF + lrow;
+                if (row >= p.M || col >= p.K)
+                    continue;
+                const f32x4 v = quad<MF>(acc[a][b], q) * sc;
+                if (vec) {
+                    const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                      f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+                    *reinterpret_cast<u32x2 *>(yb + ((int64_t)nimg * p.K + col) * p.P + sp) = pk;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = row + e;
+                        if (m < p.M) {
+                            const int n2 = m / p.P;
+                            const int sp2 = m - n2 * p.P;
+                            yb[((int64_t)n2 * p.K + col) * p.P + sp2] = (uint16_t)f32_to_bf16_rne(v[e]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, int SA, int SB, int KB, int SPREAD, int PF = 1,
           bool BPF = false>
 __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN>())))
@@ -98,89 +322,22 @@ void conv_igemm_buf_kernel(ConvParams p)
     const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(p.x, p.xbytes);
     const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(p.w, p.wbytes);
 
-    // ---------------------------------------------------------------- A rows: input origin of each output position
-    int a_d[AIT], a_h[AIT], a_w[AIT];
-    unsigned a_off[AIT];  // byte offset of (origin, channel jc*CH); wraps for padded origins
-    {
-        const int hw = p.Ho * p.Wo;
-#pragma unroll
-        for (int i = 0; i < AIT; ++i) {
-            const int m = min(m0 + RPI * (wave + i * NW) + lr, p.M - 1);
-            const int nimg = m / p.P;
-            const int sp = m - nimg * p.P;
-            const int od = sp / hw;
-            const int rem = sp - od * hw;
-            const int oh = rem / p.Wo;
-            const int ow = rem - oh * p.Wo;
-            a_d[i] = od * p.sd - p.pd;
-            a_h[i] = oh * p.sh - p.ph;
-            a_w[i] = ow * p.sw - p.pw;
-            unsigned pos;
-            if constexpr (MODE == MODE_TEMPORAL)
-                pos = (unsigned)(nimg * p.D + a_d[i]) * (unsigned)(p.H * p.W) + (unsigned)rem;
-            else
-                pos = ((unsigned)(nimg * p.D + a_d[i]) * (unsigned)p.H + (unsigned)a_h[i]) * (unsigned)p.W +
-                      (unsigned)a_w[i];
-            a_off[i] = pos * (unsigned)(p.C * ESZ) + (unsigned)(jc * 16);
-        }
-    }
-    // ---------------------------------------------------------------- B rows: filter rows
-    unsigned b_off[BIT];
-#pragma unroll
-    for (int i = 0; i < BIT; ++i) {
-        const int n = min(n0 + RPI * (wave + i * NW) + lr, p.Ncol - 1);
-        b_off[i] = (unsigned)n * (unsigned)(p.ldw * ESZ) + (unsigned)(jc * 16);
-    }
-
-    // ---------------------------------------------------------------- reduction position (uniform)
-    // Channel block cb (pairs * TKE channels) outer, then tap (t, r, s), then
-    // the `pairs` TKE-wide halves of the block.
-    struct KPos {
-        int half, s, r, t, cb;
-    };
-    auto advance = [&](KPos &k) {
-        const bool hw = ++k.half == p.pairs;
-        k.half = hw ? 0 : k.half;
-        k.s += hw;
-        const bool sw = k.s == p.S;
-        k.s = sw ? 0 : k.s;
-        k.r += sw;
-        const bool rw = k.r == p.R;
-        k.r = rw ? 0 : k.r;
-        k.t += rw;
-        const bool tw = k.t == p.T;
-        k.t = tw ? 0 : k.t;
-        k.cb += tw ? p.pairs * TKE : 0;
-    };
-    auto a_shift = [&](const KPos &k) -> unsigned {  // bytes from a row's origin to this tap and channel block
-        const int c = k.cb + k.half * TKE;
-        if constexpr (MODE == MODE_TEMPORAL)
-            return (unsigned)((k.t * p.dd) * (p.H * p.W) * p.C + c) * ESZ;
-        else
-            return (unsigned)((((k.t * p.dd) * p.H + k.r * p.dh) * p.W + k.s * p.dw) * p.C + c) * ESZ;
-    };
-    auto b_shift = [&](const KPos &k) -> unsigned {
-        return (unsigned)((((k.t * p.R + k.r) * p.S + k.s) * p.C + k.cb + k.half * TKE) * ESZ);
-    };
+    ImRows<AIT, MODE, ESZ> arows;
+    arows.init(p, m0 + RPI * wave + lr, RPI * NW, jc);
+    FilterRows<BIT, ESZ> brows;
+    brows.init(p, n0 + RPI * wave + lr, RPI * NW, jc);
 
     // One DMA instruction: A row group i (or B row group i - AIT) of the step at k into ring slot st.
-    auto issue = [&](int j, int st, const KPos &k, unsigned ash, unsigned bsh) {
-        if (j < AIT) {
-            const int i = j;
-            bool ok = (unsigned)(a_d[i] + k.t * p.dd) < (unsigned)p.D;
-            if constexpr (MODE == MODE_GENERIC)
-                ok = ok & ((unsigned)(a_h[i] + k.r * p.dh) < (unsigned)p.H) &
-                     ((unsigned)(a_w[i] + k.s * p.dw) < (unsigned)p.W);
-            const unsigned off = ok ? a_off[i] + ash : kPastEnd;
-            buffer_to_lds16(xr, as + st * ASTAGE + RPI * (wave + i * NW) * KB, off);
-        } else {
-            const int i = j - AIT;
-            buffer_to_lds16(wr, bs + st * BSTAGE + RPI * (wave + i * NW) * KB, b_off[i] + bsh);
-        }
+    auto issue = [&](int j, int st, const KPos<TKE> &k, unsigned ash, unsigned bsh) {
+        if (j < AIT)
+            buffer_to_lds16(xr, as + st * ASTAGE + RPI * (wave + j * NW) * KB, arows.at(p, j, k, ash));
+        else
+            buffer_to_lds16(wr, bs + st * BSTAGE + RPI * (wave + (j - AIT) * NW) * KB, brows.off[j - AIT] + bsh);
     };
 
     // ---------------------------------------------------------------- MFMA
     using AccT = typename AccType<MF>::type;
+    using Frag = FragT<DT>;
     AccT acc[FM][FN];
 #pragma unroll
     for (int a = 0; a < FM; ++a)
@@ -189,30 +346,7 @@ void conv_igemm_buf_kernel(ConvParams p)
             acc[a][b] = AccT{};
 
     const int lrow = lane & (MF - 1), lgrp = lane / MF, lsw = KB == 128 ? (lane & 7) : ((lane >> 1) & 3);
-    using Frag = typename std::conditional<DT == DT_BF16, bf16x8, i32x8>::type;
-    auto frag = [&](const char *rowp, int h) -> Frag {
-        const int c0 = (h * GROUPS + lgrp) * CPL;
-        if constexpr (DT == DT_BF16) {
-            return *reinterpret_cast<const bf16x8 *>(rowp + ((c0 ^ lsw) * 16));
-        } else {
-            const i32x4 lo = *reinterpret_cast<const i32x4 *>(rowp + ((c0 ^ lsw) * 16));
-            const i32x4 hi = *reinterpret_cast<const i32x4 *>(rowp + (((c0 + 1) ^ lsw) * 16));
-            return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-    };
-    auto mfma = [&](const Frag &af, const Frag &bf, AccT &c) {
-        if constexpr (DT == DT_BF16) {
-            if constexpr (MF == 16)
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, c, 0, 0, 0);
-            else
-                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, c, 0, 0, 0);
-        } else {
-            if constexpr (MF == 16)
-                c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, c, 0, 0, 0, 0, 0, 0);
-            else
-                c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, c, 0, 0, 0, 0, 0, 0);
-        }
-    };
+    auto frag = [&](const char *rowp, int h) -> Frag { return lds_frag<DT, MF>(rowp, h, lgrp, lsw); };
     // One step from slots (sa, sb); hook(row) runs after MFMA row `row` (0..ROWS-1).
     // A fragments are read PF rows ahead of their MFMAs; with BPF the B
     // fragments of the next k-slice are read while the last rows of this one run.
@@ -247,7 +381,7 @@ void conv_igemm_buf_kernel(ConvParams p)
                 }
 #pragma unroll
                 for (int b = 0; b < FN; ++b)
-                    mfma(af[a % (PF + 1)], bf[cb][b], acc[a][b]);
+                    mfma_acc<DT, MF>(af[a % (PF + 1)], bf[cb][b], acc[a][b]);
                 hook(h * FM + a);
             }
         }
@@ -266,7 +400,7 @@ void conv_igemm_buf_kernel(ConvParams p)
     constexpr int AHEAD = (SA == SB ? 0 : LPS - FIRST_IT) + (SMIN - 2) * LPS;
     static_assert(AHEAD < 64, "vmcnt range");
     const int nk = p.nk;
-    KPos ka{0, 0, 0, 0, 0}, kb{0, 0, 0, 0, 0};  // next A and B steps to issue
+    KPos<TKE> ka, kb;  // next A and B steps to issue
     // j-th DMA instruction of a step in issue order (A rows then B rows, or B then A).
     auto issue_j = [&](int j, int sta, int stb, unsigned ash, unsigned bsh) {
         const bool is_a = A_FIRST ? j < AIT : j >= BIT;
@@ -277,18 +411,18 @@ void conv_igemm_buf_kernel(ConvParams p)
             issue(AIT + row, stb, kb, 0, bsh);
     };
     auto issue_a_step = [&](int st) {
-        const unsigned sh = a_shift(ka);
+        const unsigned sh = ka.template a_shift<MODE, ESZ>(p);
 #pragma unroll
         for (int j = 0; j < AIT; ++j)
             issue(j, st, ka, sh, 0);
-        advance(ka);
+        ka.advance(p);
     };
     auto issue_b_step = [&](int st) {
-        const unsigned sh = b_shift(kb);
+        const unsigned sh = kb.template b_shift<ESZ>(p);
 #pragma unroll
         for (int j = AIT; j < LPS; ++j)
             issue(j, st, kb, 0, sh);
-        advance(kb);
+        kb.advance(p);
     };
     // issue the step's parts that exist (A(ks+SA-1) if < nk, B(ks+SB-1) if < nk) in ring order
     auto issue_parts = [&](int ja, int jb, int sta, int stb) {
@@ -317,7 +451,7 @@ void conv_igemm_buf_kernel(ConvParams p)
     for (; ks < nk - SMAX + 1; ++ks) {
         wait_vmcnt<AHEAD>();
         asm volatile("s_barrier" ::: "memory");
-        const unsigned ash = a_shift(ka), bsh = b_shift(kb);
+        const unsigned ash = ka.template a_shift<MODE, ESZ>(p), bsh = kb.template b_shift<ESZ>(p);
         const int sta = ia, stb = ib;
         if constexpr (SPREAD == 0) {
 #pragma unroll
@@ -332,8 +466,8 @@ void conv_igemm_buf_kernel(ConvParams p)
                         issue_j(j, sta, stb, ash, bsh);
             });
         }
-        advance(ka);
-        advance(kb);
+        ka.advance(p);
+        kb.advance(p);
         sa = sa + 1 == SA ? 0 : sa + 1;
         sb = sb + 1 == SB ? 0 : sb + 1;
         ia = ia + 1 == SA ? 0 : ia + 1;
@@ -351,47 +485,7 @@ void conv_igemm_buf_kernel(ConvParams p)
         ib = ib + 1 == SB ? 0 : ib + 1;
     }
 
-    // ---------------------------------------------------------------- epilogue: bf16 NCDHW
-    float sc = 1.0f;
-    if constexpr (DT == DT_FP8)
-        sc = p.scales[0] * p.scales[2];
-    uint16_t *yb = static_cast<uint16_t *>(p.y);
-    constexpr int QUADS = MF / 16 * (MF / 16);
-#pragma unroll
-    for (int a = 0; a < FM; ++a) {
-#pragma unroll
-        for (int q = 0; q < QUADS; ++q) {
-            const int row = m0 + wm * WTM + a * MF + (MF == 16 ? 4 * lgrp : 8 * q + 4 * lgrp);
-            int nimg = 0, sp = 0;
-            if (row < p.M) {
-                nimg = row / p.P;
-                sp = row - nimg * p.P;
-            }
-            const bool vec = (p.P & 3) == 0 && row + 3 < p.M;
-#pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const int col = n0 + wn * WTN + b * MF + lrow;
-                if (row >= p.M || col >= p.K)
-                    continue;
-                const f32x4 v = quad<MF>(acc[a][b], q) * sc;
-                if (vec) {
-                    const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                      f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
-                    *reinterpret_cast<u32x2 *>(yb + ((int64_t)nimg * p.K + col) * p.P + sp) = pk;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int m = row + e;
-                        if (m < p.M) {
-                            const int n2 = m / p.P;
-                            const int sp2 = m - n2 * p.P;
-                            yb[((int64_t)n2 * p.K + col) * p.P + sp2] = (uint16_t)f32_to_bf16_rne(v[e]);
-                        }
-                    }
-                }
-            }
-        }
-    }
+    store_tile_ncdhw<MF, FM, FN, DT>(acc, p, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
 // Launch helper for one dtype: the buffer-addressed tiles of kTiles (sb > 0).
@@ -399,17 +493,17 @@ template <int DT>
 hipError_t launch_conv_buf_dt(const ConvParams &p, int tile, Mode mode, hipStream_t stream)
 {
     const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
-#define IGC_BLAUNCH(BM_, BN_, WM_, WN_, MF_, SA_, SB_, KB_, SP_, ...)                                                  \
-    do {                                                                                                       \
-        if (mode == MODE_TEMPORAL)                                                                             \
-            hipLaunchKernelGGL(                                                                                \
-                (conv_igemm_buf_kernel<BM_, BN_, WM_, WN_, MF_, DT, MODE_TEMPORAL, SA_, SB_, KB_, SP_, ##__VA_ARGS__>), grid, \
-                dim3(WM_ * WN_ * 64), 0, stream, p);                                                           \
-        else                                                                                                   \
-            hipLaunchKernelGGL(                                                                                \
-                (conv_igemm_buf_kernel<BM_, BN_, WM_, WN_, MF_, DT, MODE_GENERIC, SA_, SB_, KB_, SP_, ##__VA_ARGS__>), grid,  \
-                dim3(WM_ * WN_ * 64), 0, stream, p);                                                           \
-        return hipGetLastError();                                                                              \
+#define IGC_BLAUNCH(BM_, BN_, WM_, WN_, MF_, SA_, SB_, KB_, SP_, ...)                                          \
+    do {                                                                                                   \
+        if (mode == MODE_TEMPORAL)                                                                         \
+            hipLaunchKernelGGL((conv_igemm_buf_kernel<BM_, BN_, WM_, WN_, MF_, DT, MODE_TEMPORAL, SA_, SB_, KB_, \
+                                                      SP_, ##__VA_ARGS__>),                                  \
+                               grid, dim3(WM_ * WN_ * 64), 0, stream, p);                                  \
+        else                                                                                               \
+            hipLaunchKernelGGL((conv_igemm_buf_kernel<BM_, BN_, WM_, WN_, MF_, DT, MODE_GENERIC, SA_, SB_, KB_,  \
+                                                      SP_, ##__VA_ARGS__>),                                  \
+                               grid, dim3(WM_ * WN_ * 64), 0, stream, p);                                  \
+        return hipGetLastError();                                                                          \
     } while (0)
     switch (tile) {
     case 27: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 8);

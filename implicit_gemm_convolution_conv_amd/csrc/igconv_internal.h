@@ -25,7 +25,7 @@ struct TileShape {
     int bm, bn, wm, wn, mf, stages, kb;
     int sb = 0;
 };
-constexpr int kNumTiles = 33;
+constexpr int kNumTiles = 34;
 constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 16, 0, 128},  // 8 waves, 128x64 per wave: large grids
     {128, 128, 2, 2, 16, 0, 128},  // 4 waves, 64x64 per wave
@@ -60,6 +60,7 @@ constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 16, 3, 128, 2},  // as 29, loads over all 16 MFMA rows (bf16 only)
     {256, 256, 2, 4, 16, 3, 128, 2},  // as 29, A fragments two rows ahead, next k-slice's B read early
     {256, 256, 2, 4, 16, 3, 64, 5},   // 64-byte steps: rings of 3 and 5 x 16 KB (bf16 only)
+    {256, 256, 2, 4, 16, 3, 128, 2},  // as 29, ping-pong wave groups (compute / memory phases)
 };
 
 // Everything a conv kernel needs, passed by value as kernel arguments.

@@ -65,6 +65,8 @@ def test_path_selection():
     assert _plan((2, 16, 1, 15, 15), (32, 16, 1, 14, 14), (1, 14, 14))["path"] == "generic"
     p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 1, 1), pd=(1, 0, 0), dt=B.IGC_FP8_E4M3FN)
     assert p["path"] == "temporal" and p["order"] == "cblock" and p["kstep"] == "128"
+    assert p["schedule"] == "pingpong"  # fp8 default: ping-pong wave groups
+    assert _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))["schedule"] == "lockstep"
     p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))
     assert (p["path"], p["tile"], p["grid"], p["nk"], p["stages"], p["bstages"]) == ("generic", "256x256", "6752", "864", "3", "2")
     assert p["loads"] == "buffer-lds"
@@ -97,6 +99,11 @@ def test_forced_path_and_tile():
             with pytest.raises(B.IgcError) as e:
                 _plan(xs, ws, (1, 14, 14) if xs[0] == 2 else (1, 1, 1), pd=(0, 0, 0) if xs[0] == 2 else (1, 1, 1))
             assert e.value.status == B.IGC_ERR_UNSUPPORTED
+        B.conv_debug_force(B.IGC_PATH_AUTO, 33, 0)  # ping-pong tile: tap masks of 32 bits
+        assert _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1))["loads"] == "buffer-lds"
+        with pytest.raises(B.IgcError) as e:
+            _plan((1, 64, 8, 8, 8), (64, 64, 4, 3, 3), pd=(1, 1, 1))
+        assert e.value.status == B.IGC_ERR_UNSUPPORTED
         with pytest.raises(B.IgcError) as e:  # 64-byte fp8 steps need 32x32 blocks
             B.conv_debug_force(B.IGC_PATH_AUTO, 32, 0)
             _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1), dt=B.IGC_FP8_E4M3FN)

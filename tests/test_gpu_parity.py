@@ -350,8 +350,8 @@ def test_point_output_fp8(tile):
 
 # ------------------------------------------------------------------ buffer-addressed tiles (27..32)
 
-BUF_TILES_BF16 = [27, 28, 29, 30, 31, 32]
-BUF_TILES_FP8 = [27, 28, 29, 31]
+BUF_TILES_BF16 = [27, 28, 29, 30, 31, 32, 33]
+BUF_TILES_FP8 = [27, 28, 29, 31, 33]
 BUF_CASES = [g for g in GEOMS if g[0] in ("c128_cblock_multi_tile", "asym_pad_stride2", "temporal_3x1x1")] + [
     ("dilated_c64", (1, 64, 6, 11, 13), (80, 64, 3, 3, 3), (1, 1, 1), (2, 1, 2), (2, 1, 2)),
     ("c192_k300_two_col_tiles", (1, 192, 4, 9, 10), (300, 192, 3, 3, 3), (1, 2, 1), (1, 1, 1), (1, 1, 1)),
