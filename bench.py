@@ -38,6 +38,7 @@ KERNEL_SOURCES = ["implicit_gemm_convolution_conv_amd/csrc/conv_igemm.h",
                   "implicit_gemm_convolution_conv_amd/csrc/conv_igemm_dma.h",
                   "implicit_gemm_convolution_conv_amd/csrc/conv_igemm_buf.h",
                   "implicit_gemm_convolution_conv_amd/csrc/conv_igemm_pp.h",
+                  "implicit_gemm_convolution_conv_amd/csrc/conv_igemm_ppw.h",
                   "implicit_gemm_convolution_conv_amd/csrc/conv_buf_bf16.hip",
                   "implicit_gemm_convolution_conv_amd/csrc/igconv_internal.h",
                   "implicit_gemm_convolution_conv_amd/csrc/api.hip"]

@@ -262,6 +262,16 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
             if (tile == 33 && g.T * g.R * g.S > 32)
                 return fail(IGC_ERR_UNSUPPORTED, "tile %d keeps a 32-bit tap mask per row: at most 32 filter taps",
                             tile);
+            if (tile == 34) {
+                const int64_t cols = (g.Wo - 1) * g.sw + (g.S - 1) * g.dw + 1;
+                const int64_t rows = (255 / g.Wo + 2) * cols;
+                if (path != IGC_PATH_GENERIC || g.S < 2 || g.T * g.R > 16 || rows > 352)
+                    return fail(IGC_ERR_UNSUPPORTED,
+                                "tile %d needs the generic path, S >= 2, T*R <= 16 and a window of at most 352 "
+                                "pixels (here %lld)", tile, (long long)rows);
+                p.win_cols = (int)cols;
+                p.win_rows = (int)rows;
+            }
         }
     }
     pl.tile = tile;
@@ -469,13 +479,13 @@ int conv_plan(const int64_t xshape[5], const int64_t wshape[5], const int32_t st
         const TileShape ts = kTiles[pl.tile];
         snprintf(buf, len,
                  "path=%s tile=%dx%d waves=%d mfma=%dx%d stages=%d bstages=%d kstep=%d order=%s%s big=%d grid=%d "
-                 "group_m=%d nk=%d loads=%s schedule=%s",
+                 "group_m=%d nk=%d loads=%s schedule=%s areuse=%s",
                  path_name(pl.path), ts.bm, ts.bn, ts.wm * ts.wn, ts.mf, ts.mf, ts.stages ? std::abs(ts.stages) : 2,
                  is_buffer(ts) ? ts.sb : (ts.stages ? std::abs(ts.stages) : 2), step_bytes(ts) / (dtype == IGC_FP8_E4M3FN ? 1 : 2),
                  is_window(ts) ? "window" : (pl.cblock ? "cblock" : "linear"), pl.p.pairs == 2 ? "-paired" : "",
                  pl.big ? 1 : 0, pl.p.tiles_m * pl.p.tiles_n, pl.p.group_m, pl.p.nk,
                  is_buffer(ts) ? "buffer-lds" : (ts.stages > 0 ? "global-lds" : (is_window(ts) ? "window-lds" : "registers")),
-                 pl.tile == 33 ? "pingpong" : "lockstep");
+                 pl.tile == 33 || pl.tile == 34 ? "pingpong" : "lockstep", pl.tile == 34 ? "taps" : "none");
     }
     return ok();
 }

@@ -25,7 +25,7 @@ struct TileShape {
     int bm, bn, wm, wn, mf, stages, kb;
     int sb = 0;
 };
-constexpr int kNumTiles = 34;
+constexpr int kNumTiles = 35;
 constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 16, 0, 128},  // 8 waves, 128x64 per wave: large grids
     {128, 128, 2, 2, 16, 0, 128},  // 4 waves, 64x64 per wave
@@ -61,6 +61,7 @@ constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 16, 3, 128, 2},  // as 29, A fragments two rows ahead, next k-slice's B read early
     {256, 256, 2, 4, 16, 3, 64, 5},   // 64-byte steps: rings of 3 and 5 x 16 KB (bf16 only)
     {256, 256, 2, 4, 16, 3, 128, 2},  // as 29, ping-pong wave groups (compute / memory phases)
+    {256, 256, 2, 4, 16, 2, 128, 2},  // as 33, activation windows shared by the S taps of a filter row
 };
 
 // Everything a conv kernel needs, passed by value as kernel arguments.
@@ -88,6 +89,8 @@ struct ConvParams {
     int win_nwi;            // window DMA instructions per thread per channel block
     // buffer-addressed kernel: byte extents of x and of the packed filter (< 2^31)
     int xbytes, wbytes;
+    // tap-shared activation windows: input pixels per output row, rows per window
+    int win_cols, win_rows;
 };
 
 // One launch of the implicit-GEMM kernel selected by (tile, mode, dtype,

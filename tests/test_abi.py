@@ -104,6 +104,15 @@ def test_forced_path_and_tile():
         with pytest.raises(B.IgcError) as e:
             _plan((1, 64, 8, 8, 8), (64, 64, 4, 3, 3), pd=(1, 1, 1))
         assert e.value.status == B.IGC_ERR_UNSUPPORTED
+        B.conv_debug_force(B.IGC_PATH_AUTO, 34, 0)  # tap-shared activation windows
+        p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))
+        assert (p["areuse"], p["schedule"], p["nk"]) == ("taps", "pingpong", "864")
+        for xs, ws, pad in (((1, 64, 8, 8, 8), (64, 64, 3, 1, 1), (1, 0, 0)),        # temporal path
+                            ((1, 64, 8, 8, 8), (64, 64, 3, 3, 1), (1, 1, 0)),        # S = 1: nothing to share
+                            ((1, 64, 4, 4, 400), (64, 64, 3, 3, 3), (1, 1, 1))):     # window above 352 pixels
+            with pytest.raises(B.IgcError) as e:
+                _plan(xs, ws, pd=pad)
+            assert e.value.status == B.IGC_ERR_UNSUPPORTED
         with pytest.raises(B.IgcError) as e:  # 64-byte fp8 steps need 32x32 blocks
             B.conv_debug_force(B.IGC_PATH_AUTO, 32, 0)
             _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1), dt=B.IGC_FP8_E4M3FN)
