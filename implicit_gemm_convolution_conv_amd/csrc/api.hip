@@ -119,12 +119,33 @@ int check_geometry(const int64_t *xs, const int64_t *ws, const int32_t *st, cons
     return IGC_OK;
 }
 
+// Upper bound on the bytes between a tile's x base (the first input plane its
+// first row can read, see tile_x_base) and the end of the last input plane any
+// of its 256 rows, or of the window rows of the tap-shared kernel, can read.
+int64_t buffer_x_span(const Geometry &g, int esz)
+{
+    const int64_t plane = g.H * g.W * g.C * esz;
+    const int64_t hw = g.Ho * g.Wo;
+    const int64_t k = 255 / hw + 2;                          // output planes past the first one
+    int64_t planes = k * g.sd + (g.T - 1) * g.dd + 1;        // tile inside one image
+    if (g.N > 1) {
+        const int64_t P = g.Do * hw;
+        if (P <= 256 + 2 * hw)                               // a tile can hold whole images
+            planes = std::max(planes, (256 / P + 3) * g.D);
+        else                                                 // the tail of one image, the head of the next
+            planes = std::max(planes, g.D - std::min(g.D - 1, std::max<int64_t>(0, (g.Do - 1 - k) * g.sd - g.pd)) +
+                                          std::min(g.D, k * g.sd + (g.T - 1) * g.dd + 1));
+    }
+    return planes * plane;
+}
+
 int64_t packed_cols(int64_t rk, int dtype) { return (rk + (dtype == IGC_FP8_E4M3FN ? 127 : 63)) / (dtype == IGC_FP8_E4M3FN ? 128 : 64) * (dtype == IGC_FP8_E4M3FN ? 128 : 64); }
 
 struct Plan {
     int path;  // IGC_PATH_*
     int tile;
     bool big, cblock;
+    int64_t xspan;  // bound on a tile's reach into x from its buffer base
     ConvParams p;
 };
 
@@ -192,7 +213,7 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
     p.Do = (int)g.Do; p.Ho = (int)g.Ho; p.Wo = (int)g.Wo;
     p.Rk = (int)rk;
     p.ldw = (int)ldw;
-    p.xbytes = (int)std::min<int64_t>(xnum * esz, kI32Max);
+    p.xbytes = xnum * esz;
     p.wbytes = (int)std::min<int64_t>(g.K * ldw * esz, kI32Max);
 
     if (path == IGC_PATH_POINT) {
@@ -217,6 +238,7 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
     }
     pl.path = path;
     pl.big = xnum > kSmallTensor || ynum > kSmallTensor;
+    pl.xspan = buffer_x_span(g, esz);
 
     // Tile: the largest whose grid still covers the 256 CUs at least twice
     // (256x256) or once (128x128), else 64x64.
@@ -231,14 +253,15 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         // (190 workgroups) included; smaller grids take the 128x128 (two
         // workgroups per CU) or 64x64 (4-stage ring) direct-to-LDS tiles.
         tile = nblocks(21) >= 160 ? 21 : (nblocks(24) >= 256 ? 24 : 26);
-        // Where the whole-channel-block im2col order applies and both operands
-        // fit a 2^31-byte buffer range, a buffer-addressed 256x256 tile
+        // Where the whole-channel-block im2col order applies and each tile's
+        // reach into x (and the whole packed filter) fits a 2^31-byte buffer
+        // range, a buffer-addressed 256x256 tile
         // replaces the large tile: activations issued two steps ahead (3 x 32 KB
         // ring), the filter one step ahead (2 x 32 KB). bf16 takes tile 29
         // (loads spread over the first half of each step's MFMA rows); fp8 the
         // ping-pong wave groups of tile 33 (1-2 % faster there, 10 % slower on bf16).
-        const bool buffer_ok = path != IGC_PATH_POINT && g.C % (128 / esz) == 0 && !pl.big &&
-                               xnum * esz < (int64_t(1) << 31) && g.K * ldw * esz < (int64_t(1) << 31);
+        const bool buffer_ok = path != IGC_PATH_POINT && g.C % (128 / esz) == 0 &&
+                               buffer_x_span(g, esz) < 0x7ffffff0 && g.K * ldw * esz < (int64_t(1) << 31);
         if (tile == 21 && buffer_ok)
             tile = (esz == 1 && g.T * g.R * g.S <= 32) ? 33 : 29;
     } else {
@@ -257,8 +280,9 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
                 return fail(IGC_ERR_UNSUPPORTED, "tile %d (buffer-addressed) runs the im2col paths only", tile);
             if (g.C % (kTiles[tile].kb / esz) != 0)
                 return fail(IGC_ERR_UNSUPPORTED, "tile %d needs C %% %d == 0", tile, kTiles[tile].kb / esz);
-            if (xnum * esz >= (int64_t(1) << 31) || g.K * ldw * esz >= (int64_t(1) << 31) || pl.big)
-                return fail(IGC_ERR_UNSUPPORTED, "tile %d needs x and the packed filter below 2^31 bytes", tile);
+            if (buffer_x_span(g, esz) >= 0x7ffffff0 || g.K * ldw * esz >= (int64_t(1) << 31))
+                return fail(IGC_ERR_UNSUPPORTED,
+                            "tile %d needs each tile's reach into x and the packed filter below 2^31 bytes", tile);
             if (tile == 33 && g.T * g.R * g.S > 32)
                 return fail(IGC_ERR_UNSUPPORTED, "tile %d keeps a 32-bit tap mask per row: at most 32 filter taps",
                             tile);
@@ -479,13 +503,14 @@ int conv_plan(const int64_t xshape[5], const int64_t wshape[5], const int32_t st
         const TileShape ts = kTiles[pl.tile];
         snprintf(buf, len,
                  "path=%s tile=%dx%d waves=%d mfma=%dx%d stages=%d bstages=%d kstep=%d order=%s%s big=%d grid=%d "
-                 "group_m=%d nk=%d loads=%s schedule=%s areuse=%s",
+                 "group_m=%d nk=%d loads=%s schedule=%s areuse=%s xspan=%lld",
                  path_name(pl.path), ts.bm, ts.bn, ts.wm * ts.wn, ts.mf, ts.mf, ts.stages ? std::abs(ts.stages) : 2,
                  is_buffer(ts) ? ts.sb : (ts.stages ? std::abs(ts.stages) : 2), step_bytes(ts) / (dtype == IGC_FP8_E4M3FN ? 1 : 2),
                  is_window(ts) ? "window" : (pl.cblock ? "cblock" : "linear"), pl.p.pairs == 2 ? "-paired" : "",
                  pl.big ? 1 : 0, pl.p.tiles_m * pl.p.tiles_n, pl.p.group_m, pl.p.nk,
                  is_buffer(ts) ? "buffer-lds" : (ts.stages > 0 ? "global-lds" : (is_window(ts) ? "window-lds" : "registers")),
-                 pl.tile == 33 || pl.tile == 34 ? "pingpong" : "lockstep", pl.tile == 34 ? "taps" : "none");
+                 pl.tile == 33 || pl.tile == 34 ? "pingpong" : "lockstep", pl.tile == 34 ? "taps" : "none",
+                 pl.path == IGC_PATH_POINT ? 0LL : (long long)pl.xspan);
     }
     return ok();
 }

@@ -42,6 +42,27 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int bytes
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
 
+// Byte offset in x of the first input plane that any row of the tile starting
+// at output row m0 can read: plane od*sd - pd of the row's image, clamped to
+// [0, D-1]. Every valid tap of rows m0.. lies at or above it (later rows have
+// later planes or later images); the plan checks that they lie below it + 2^31.
+template <int ESZ>
+__device__ inline int64_t tile_x_base(const ConvParams &p, int m0)
+{
+    const int nimg = m0 / p.P;
+    const int od = (m0 - nimg * p.P) / (p.Ho * p.Wo);
+    const int id = min(max(0, od * p.sd - p.pd), p.D - 1);
+    return ((int64_t)nimg * p.D + id) * ((int64_t)p.H * p.W) * p.C * ESZ;
+}
+
+// Buffer over x seen from the tile's base: at most 2^31 - 16 bytes, so the
+// out-of-range offset kPastEnd is always past it.
+__device__ inline __amdgpu_buffer_rsrc_t tile_x_rsrc(const ConvParams &p, int64_t xbase)
+{
+    const int64_t left = p.xbytes - xbase;
+    return buffer_rsrc(static_cast<const char *>(p.x) + xbase, (int)(left < 0x7ffffff0 ? left : 0x7ffffff0));
+}
+
 // 16 bytes per lane from buffer offset `off` into LDS at lds + 16 * lane.
 __device__ inline void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, char *lds, unsigned off)
 {
@@ -92,13 +113,14 @@ struct KPos {
 };
 
 // N im2col rows of one lane (rows first + i * stride, clamped to M - 1): the
-// input origin (d, h, w) of each and its byte offset at channel chunk `chunk`.
+// input origin (d, h, w) of each and its byte offset from xbase at channel
+// chunk `chunk`.
 template <int N, int MODE, int ESZ>
 struct ImRows {
     int d[N], h[N], w[N];
     unsigned off[N];  // wraps for padded origins; valid taps land in range
 
-    __device__ void init(const ConvParams &p, int first, int stride, int chunk)
+    __device__ void init(const ConvParams &p, int first, int stride, int chunk, int64_t xbase)
     {
         const int hw = p.Ho * p.Wo;
 #pragma unroll
@@ -113,13 +135,12 @@ struct ImRows {
             d[i] = od * p.sd - p.pd;
             h[i] = oh * p.sh - p.ph;
             w[i] = ow * p.sw - p.pw;
-            unsigned pos;
+            int64_t pos;
             if constexpr (MODE == MODE_TEMPORAL)
-                pos = (unsigned)(nimg * p.D + d[i]) * (unsigned)(p.H * p.W) + (unsigned)rem;
+                pos = ((int64_t)nimg * p.D + d[i]) * ((int64_t)p.H * p.W) + rem;
             else
-                pos = ((unsigned)(nimg * p.D + d[i]) * (unsigned)p.H + (unsigned)h[i]) * (unsigned)p.W +
-                      (unsigned)w[i];
-            off[i] = pos * (unsigned)(p.C * ESZ) + (unsigned)(chunk * 16);
+                pos = (((int64_t)nimg * p.D + d[i]) * p.H + h[i]) * (int64_t)p.W + w[i];
+            off[i] = (unsigned)(pos * p.C * ESZ - xbase) + (unsigned)(chunk * 16);
         }
     }
     // Buffer offset of row i at reduction position k (shift = k.a_shift): past
@@ -142,10 +163,10 @@ struct ImRowsMasked {
     unsigned off[N];
     unsigned valid[N];  // bit (t * R + r) * S + s: that tap reads inside the input box
 
-    __device__ void init(const ConvParams &p, int first, int stride, int chunk)
+    __device__ void init(const ConvParams &p, int first, int stride, int chunk, int64_t xbase)
     {
         ImRows<N, MODE, ESZ> rows;
-        rows.init(p, first, stride, chunk);
+        rows.init(p, first, stride, chunk, xbase);
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             off[i] = rows.off[i];
@@ -319,11 +340,12 @@ void conv_igemm_buf_kernel(ConvParams p)
     const int lr = lane / CPR;
     const int jc = KB == 128 ? ((lane & 7) ^ (lane >> 3)) : ((lane & 3) ^ ((lane >> 3) & 3));
 
-    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(p.x, p.xbytes);
+    const int64_t xbase = tile_x_base<ESZ>(p, m0);
+    const __amdgpu_buffer_rsrc_t xr = tile_x_rsrc(p, xbase);
     const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(p.w, p.wbytes);
 
     ImRows<AIT, MODE, ESZ> arows;
-    arows.init(p, m0 + RPI * wave + lr, RPI * NW, jc);
+    arows.init(p, m0 + RPI * wave + lr, RPI * NW, jc, xbase);
     FilterRows<BIT, ESZ> brows;
     brows.init(p, n0 + RPI * wave + lr, RPI * NW, jc);
 

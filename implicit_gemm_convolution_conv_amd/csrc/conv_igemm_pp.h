@@ -80,11 +80,12 @@ void conv_igemm_pp_kernel(ConvParams p)
     // group 1 loads activation rows, group 0 filter rows: RPI * (wl + 4 i) + lr
     ImRowsMasked<IT, MODE, ESZ> arows;  // the plan keeps T * R * S <= 32 on this kernel
     FilterRows<IT, ESZ> brows;
+    const int64_t xbase = tile_x_base<ESZ>(p, m0);
     if (g)
-        arows.init(p, m0 + RPI * wl + lr, RPI * 4, jc);
+        arows.init(p, m0 + RPI * wl + lr, RPI * 4, jc, xbase);
     else
         brows.init(p, n0 + RPI * wl + lr, RPI * 4, jc);
-    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(p.x, p.xbytes);
+    const __amdgpu_buffer_rsrc_t xr = tile_x_rsrc(p, xbase);
     const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(p.w, p.wbytes);
     KPos<TKE> ka, kb;  // next activation / filter step to issue
 

@@ -38,7 +38,7 @@ struct WinRows {
     unsigned off[N];              // wraps for rows above or left of the input
     unsigned valid[(N + 1) / 2];  // row i: bits 16 * (i & 1) + t * R + r
 
-    __device__ void init(const ConvParams &p, int g0, int first, int stride, int chunk)
+    __device__ void init(const ConvParams &p, int g0, int first, int stride, int chunk, int64_t xbase)
     {
         const int glast = p.N * p.Do * p.Ho - 1;
 #pragma unroll
@@ -55,8 +55,7 @@ struct WinRows {
             const int od = q % p.Do;
             const int n = q / p.Do;
             const int id0 = od * p.sd - p.pd, ih0 = oh * p.sh - p.ph, iw = col - p.pw;
-            off[i] = ((((unsigned)(n * p.D + id0)) * (unsigned)p.H + (unsigned)ih0) * (unsigned)p.W + (unsigned)iw) *
-                         (unsigned)(p.C * ESZ) +
+            off[i] = (unsigned)(((((int64_t)n * p.D + id0) * p.H + ih0) * (int64_t)p.W + iw) * p.C * ESZ - xbase) +
                      (unsigned)(chunk * 16);
             const bool colok = (unsigned)iw < (unsigned)p.W && wr < p.win_rows && g0 + j <= glast;
             unsigned v = 0;
@@ -128,11 +127,12 @@ void conv_igemm_ppw_kernel(ConvParams p)
 
     WinRows<IW, ESZ> wrows;
     FilterRows<IT, ESZ> brows;
+    const int64_t xbase = tile_x_base<ESZ>(p, m0);
     if (g)
-        wrows.init(p, g0, RPI * wl + lr, RPI * 4, jc);
+        wrows.init(p, g0, RPI * wl + lr, RPI * 4, jc, xbase);
     else
         brows.init(p, n0 + RPI * wl + lr, RPI * 4, jc);
-    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(p.x, p.xbytes);
+    const __amdgpu_buffer_rsrc_t xr = tile_x_rsrc(p, xbase);
     const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(p.w, p.wbytes);
     KPos<TKE> kb;
     WPos<TKE> kw;

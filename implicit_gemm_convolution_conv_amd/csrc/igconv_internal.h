@@ -87,8 +87,10 @@ struct ConvParams {
     int tpp;                // M tiles per output plane = ceil(Ho*Wo / BM)
     int win_h, win_w;       // window rows / columns (input pixels) per plane slot
     int win_nwi;            // window DMA instructions per thread per channel block
-    // buffer-addressed kernel: byte extents of x and of the packed filter (< 2^31)
-    int xbytes, wbytes;
+    // buffer-addressed kernels: byte size of x (any size: each tile rebases its
+    // buffer at the first input plane it can read) and of the packed filter (< 2^31)
+    int64_t xbytes;
+    int wbytes;
     // tap-shared activation windows: input pixels per output row, rows per window
     int win_cols, win_rows;
 };

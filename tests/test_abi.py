@@ -70,7 +70,11 @@ def test_path_selection():
     p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))
     assert (p["path"], p["tile"], p["grid"], p["nk"], p["stages"], p["bstages"]) == ("generic", "256x256", "6752", "864", "3", "2")
     assert p["loads"] == "buffer-lds"
-    p = _plan((1, 1024, 240, 160, 90), (1024, 1024, 3, 1, 1), pd=(1, 0, 0))  # beyond 2^31 bytes: 64-bit global loads
+    # beyond 2^31 bytes: each tile rebases its buffer at the first input plane it reads (4 planes = 118 MB here)
+    p = _plan((1, 1024, 240, 160, 90), (1024, 1024, 3, 1, 1), pd=(1, 0, 0))
+    assert (p["big"], p["loads"]) == ("1", "buffer-lds")
+    # a single input plane of 2 GB cannot fit one buffer window: 64-bit global-address loads
+    p = _plan((1, 128, 3, 4096, 2049), (128, 128, 3, 3, 3), pd=(1, 1, 1))
     assert (p["big"], p["loads"]) == ("1", "global-lds")
     assert _plan((9500, 3, 1, 14, 14), (1280, 3, 1, 14, 14), (1, 14, 14), lay=B.IGC_NCDHW)["grid"] == "190"
     assert _plan((1, 1024, 240, 160, 90), (1024, 1024, 3, 1, 1), pd=(1, 0, 0))["big"] == "1"
@@ -177,3 +181,50 @@ def test_window_tile_limits():
         assert e.value.status == B.IGC_ERR_UNSUPPORTED
     finally:
         B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)
+
+
+def _tile_reach(xs, ws, st, pd, dl, esz, bm=256):
+    """Brute force over every 256-row tile: the byte range its valid im2col reads (and the window rows of the
+    tap-shared kernel: every input pixel of every output row the tile touches, plus one more output row) cover,
+    relative to the tile's buffer base, the first input plane its first row can read."""
+    n_, c, d, h, w = xs
+    _, _, t_, r_, s_ = ws
+    do = (d + 2 * pd[0] - dl[0] * (t_ - 1) - 1) // st[0] + 1
+    ho = (h + 2 * pd[1] - dl[1] * (r_ - 1) - 1) // st[1] + 1
+    wo = (w + 2 * pd[2] - dl[2] * (s_ - 1) - 1) // st[2] + 1
+    P, M, rows_total = do * ho * wo, n_ * do * ho * wo, n_ * do * ho
+    pix = c * esz
+    worst_lo, worst_hi = 0, 0
+    for m0 in range(0, M, bm):
+        n0, od0 = m0 // P, (m0 % P) // (ho * wo)
+        base = (n0 * d + min(max(0, od0 * st[0] - pd[0]), d - 1)) * h * w * pix
+        g0, g1 = m0 // wo, min(rows_total - 1, (min(m0 + bm, M) - 1) // wo + 1)
+        for g in range(g0, g1 + 1):  # output rows (n, od, oh); every column of each
+            n, od, oh = g // (do * ho), (g // ho) % do, g % ho
+            for t in range(t_):
+                idd = od * st[0] - pd[0] + t * dl[0]
+                for r in range(r_):
+                    ih = oh * st[1] - pd[1] + r * dl[1]
+                    if not (0 <= idd < d and 0 <= ih < h):
+                        continue
+                    row = ((n * d + idd) * h + ih) * w * pix
+                    worst_lo = min(worst_lo, row - base)
+                    worst_hi = max(worst_hi, row + w * pix - base)
+    return worst_lo, worst_hi
+
+
+@pytest.mark.parametrize("geom", [
+    ((1, 8, 9, 6, 7), (8, 8, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),
+    ((3, 8, 5, 6, 7), (8, 8, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),     # tiles hold whole images
+    ((2, 8, 9, 12, 30), (8, 8, 3, 3, 3), (2, 1, 1), (2, 1, 1), (2, 1, 1)),   # crossing into the next image
+    ((4, 8, 7, 5, 5), (8, 8, 2, 1, 1), (1, 1, 1), (1, 0, 0), (3, 1, 1)),     # temporal, dilated
+    ((2, 8, 11, 20, 20), (8, 8, 3, 3, 3), (2, 2, 2), (0, 1, 1), (1, 2, 2)),
+    ((5, 8, 3, 4, 3), (8, 8, 3, 2, 2), (1, 2, 1), (2, 0, 1), (1, 1, 1)),
+    ((3, 8, 4, 5, 6), (8, 8, 2, 2, 2), (1, 1, 1), (3, 1, 1), (1, 1, 1)),     # padding beyond the filter's reach
+])
+def test_buffer_span_bound_covers_every_tile(geom):
+    xs, ws, st, pd, dl = geom
+    lo, hi = _tile_reach(xs, ws, st, pd, dl, esz=2)
+    p = _plan(xs, ws, st, pd, dl)
+    assert lo >= 0, "a valid read lies below the tile's buffer base"
+    assert hi <= int(p["xspan"]), (hi, p["xspan"])

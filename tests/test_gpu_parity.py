@@ -362,6 +362,8 @@ BUF_CASES = [g for g in GEOMS if g[0] in ("c128_cblock_multi_tile", "asym_pad_st
     ("windows_cross_planes_images", (3, 64, 3, 5, 21), (72, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),
     ("windows_stride2_dilated", (1, 64, 7, 12, 37), (64, 64, 2, 3, 3), (2, 2, 1), (1, 2, 2), (2, 2, 2)),
     ("windows_2d_5x5", (2, 128, 1, 19, 37), (96, 128, 1, 5, 5), (1, 1, 1), (0, 2, 2), (1, 1, 1)),
+    # time padding beyond the filter's reach: a tile's first input plane clamps to its image's last plane
+    ("pad_beyond_reach_images", (3, 64, 4, 5, 6), (40, 64, 2, 2, 2), (1, 1, 1), (3, 1, 1), (1, 1, 1)),
 ]
 
 
