@@ -39,6 +39,7 @@ KERNEL_SOURCES = ["implicit_gemm_convolution_conv_amd/csrc/conv_igemm.h",
                   "implicit_gemm_convolution_conv_amd/csrc/conv_igemm_buf.h",
                   "implicit_gemm_convolution_conv_amd/csrc/conv_igemm_pp.h",
                   "implicit_gemm_convolution_conv_amd/csrc/conv_igemm_ppw.h",
+                  "implicit_gemm_convolution_conv_amd/csrc/conv_pw.hip",
                   "implicit_gemm_convolution_conv_amd/csrc/conv_buf_bf16.hip",
                   "implicit_gemm_convolution_conv_amd/csrc/igconv_internal.h",
                   "implicit_gemm_convolution_conv_amd/csrc/api.hip"]
@@ -96,7 +97,7 @@ def bench_workload(name, steps, warmup, torch, B, I, PL):
     y = PL.output(xshape, wshape, wl.stride, wl.pad, wl.dil, "cuda")
     res = {"workload": wl.note, "flop": flops}
     if wl.dtype == "bf16":
-        if name == "c2":  # point output: x read as is (NCHW), filter in (c, r, s) order
+        if name in ("c2", "pw"):  # point output / 1x1x1: x read as is (NCDHW), filter in (c, t, r, s) order
             wp = PL.packed_weight(w, "bf16", "NCDHW")
             lay, xk = B.IGC_NCDHW, x
         else:
@@ -111,7 +112,10 @@ def bench_workload(name, steps, warmup, torch, B, I, PL):
         wall, ev = time_launches(step, steps, warmup, torch)
         res.update(ms=wall, kernel_ms=ev, tflops=flops / (wall * 1e-3) / 1e12,
                    kernel_tflops=flops / (ev * 1e-3) / 1e12)
-        if name != "c2" and wl.x_layout != "NDHWC":  # also the bf16 transpose that feeds it
+        if name == "pw":  # HBM-bound: x and y once, the filter per 64 output channels
+            nbytes = 2 * (x.numel() + y.numel() + w.numel())
+            res.update(kernel_gbs=nbytes / (ev * 1e-3) / 1e9, hbm_frac=nbytes / (ev * 1e-3) / 1e9 / PEAK_HBM_GBS)
+        if name not in ("c2", "pw") and wl.x_layout != "NDHWC":  # also the bf16 transpose that feeds it
             xt = torch.empty((xshape[0],) + tuple(xshape[2:]) + (xshape[1],), dtype=torch.bfloat16, device="cuda")
             _, ev_t = time_launches(lambda: B.conv_pack_x(x, xt, xshape, B.IGC_BF16), steps, warmup, torch)
             nbytes = 4 * x.numel()
@@ -210,7 +214,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", default=None, help="comma list of extra workloads (c1,c2,c4,c4t,c5)")
+    ap.add_argument("--only", default=None, help="comma list of extra workloads (c1,c2,c4,c4t,c5,pw)")
     ap.add_argument("--profile", action="store_true",
                     help="counter-collection run: the headline conv `steps` times, then one 1 GiB device copy "
                          "(the reference for scaling FETCH_SIZE / WRITE_SIZE); prints nothing else")
@@ -253,7 +257,7 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        names = args.only.split(",") if args.only else ["c1", "c2", "c4", "c4t", "c5"]
+        names = args.only.split(",") if args.only else ["c1", "c2", "c4", "c4t", "c5", "pw"]
         for name in names:
             log(f"[bench] extra workload {name}")
             extra[name] = bench_workload(name, max(5, args.steps // 2), args.warmup, torch, B, I, PL)

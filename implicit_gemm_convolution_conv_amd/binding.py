@@ -24,7 +24,7 @@ IGC_OK = 0
 IGC_ERR_INVALID, IGC_ERR_UNSUPPORTED, IGC_ERR_ALIGN, IGC_ERR_HIP = -1, -2, -3, -4
 IGC_BF16, IGC_FP8_E4M3FN = 0, 1
 IGC_NCDHW, IGC_NDHWC = 0, 1
-IGC_PATH_AUTO, IGC_PATH_GENERIC, IGC_PATH_TEMPORAL, IGC_PATH_POINT = 0, 1, 2, 3
+IGC_PATH_AUTO, IGC_PATH_GENERIC, IGC_PATH_TEMPORAL, IGC_PATH_POINT, IGC_PATH_POINTWISE = 0, 1, 2, 3, 4
 
 EXPORTS = ("conv_out_dims", "conv_packed_w_cols", "conv_amax", "conv_fp8_scales", "conv_pack_x", "conv_pack_w",
            "conv_fwd", "conv_plan", "conv_debug_force", "conv_last_error")

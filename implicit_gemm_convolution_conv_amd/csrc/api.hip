@@ -29,6 +29,8 @@ hipError_t launch_conv_buf_fp8(const ConvParams &p, int tile, Mode mode, hipStre
 hipError_t launch_conv(const ConvParams &p, int tile, Mode mode, Dtype dt, bool big, bool cblock,
                        hipStream_t stream)
 {
+    if (is_pointwise_tile(tile))
+        return launch_conv_pw(p, tile - kPointwiseFirst, stream);
     if (is_buffer(kTiles[tile]))
         return dt == DT_FP8 ? launch_conv_buf_fp8(p, tile, mode, stream) : launch_conv_buf_bf16(p, tile, mode, stream);
     if (is_window(kTiles[tile]))
@@ -158,6 +160,16 @@ bool is_point(const Geometry &g)
            g.H == g.R && g.W == g.S;
 }
 
+// 1x1x1 filter with unit stride and no padding (dilation is irrelevant): y of
+// image n is W (K x C) times x_n (C x D*H*W), so NCDHW activations need no
+// transpose (FlyDSL PR #860 sends this shape to a plain matmul for that reason,
+// PR description "Performance").
+bool is_pointwise(const Geometry &g)
+{
+    return g.T == 1 && g.R == 1 && g.S == 1 && g.sd == 1 && g.sh == 1 && g.sw == 1 && g.pd == 0 && g.ph == 0 &&
+           g.pw == 0;
+}
+
 // Temporal-only filter (FlyDSL PR #860, 3x1x1 fast decode): the (h, w) index
 // of an output position is its input index, only the time axis has taps.
 bool is_temporal(const Geometry &g)
@@ -180,16 +192,21 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
     const int chunk = 16 / esz;
 
     const int forced = g_force_path.load();
+    const bool pointwise_ok = is_pointwise(g) && x_layout == IGC_NCDHW && dtype == IGC_BF16;
     int path;
     if (forced == IGC_PATH_AUTO) {
-        path = is_point(g) ? IGC_PATH_POINT : (is_temporal(g) ? IGC_PATH_TEMPORAL : IGC_PATH_GENERIC);
+        path = is_point(g) ? IGC_PATH_POINT
+                           : (pointwise_ok ? IGC_PATH_POINTWISE : (is_temporal(g) ? IGC_PATH_TEMPORAL : IGC_PATH_GENERIC));
     } else {
         path = forced;
         if (path == IGC_PATH_POINT && !is_point(g))
             return fail(IGC_ERR_UNSUPPORTED, "forced point-output path does not apply to this shape");
         if (path == IGC_PATH_TEMPORAL && !is_temporal(g))
             return fail(IGC_ERR_UNSUPPORTED, "forced temporal path needs a Tx1x1 filter, h/w stride 1, pad 0");
-        if (path < IGC_PATH_GENERIC || path > IGC_PATH_POINT)
+        if (path == IGC_PATH_POINTWISE && !pointwise_ok)
+            return fail(IGC_ERR_UNSUPPORTED,
+                        "forced pointwise path needs a 1x1x1 filter, unit stride, no padding, NCDHW bf16 activations");
+        if (path < IGC_PATH_GENERIC || path > IGC_PATH_POINTWISE)
             return fail(IGC_ERR_INVALID, "forced path %d unknown", path);
     }
 
@@ -216,6 +233,37 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
     p.xbytes = xnum * esz;
     p.wbytes = (int)std::min<int64_t>(g.K * ldw * esz, kI32Max);
 
+    if (path == IGC_PATH_POINTWISE) {
+        const int64_t S = g.D * g.H * g.W;
+        const int ft = g_force_tile.load();
+        if (ft >= 0 && !is_pointwise_tile(ft))
+            return fail(IGC_ERR_UNSUPPORTED, "the pointwise path runs tiles %d..%d only (forced %d)", kPointwiseFirst,
+                        kPointwiseLast, ft);
+        // measured on the 14 GB 512->48 shape: 512 positions, 32-channel steps, 4 stages (tile 37) is fastest
+        const int pt = ft >= 0 ? ft : kPointwiseFirst + 2;
+        const int bm = kTiles[pt].bm;
+        if (S % 8 != 0)
+            return fail(IGC_ERR_UNSUPPORTED, "pointwise path needs D*H*W %% 8 == 0 (16-byte rows), D*H*W = %lld",
+                        (long long)S);
+        if (g.N * S > kI32Max || S > kI32Max)
+            return fail(IGC_ERR_UNSUPPORTED, "output rows N*D*H*W = %lld exceed 2^31", (long long)(g.N * S));
+        const int64_t tiles = g.N * ((S + bm - 1) / bm) * ((g.K + 63) / 64);
+        if (tiles > kI32Max)
+            return fail(IGC_ERR_UNSUPPORTED, "grid of %lld tiles too large", (long long)tiles);
+        p.P = (int)S;
+        p.M = (int)(g.N * S);
+        p.Ncol = (int)g.K;
+        p.nk = (int)((g.C + kTiles[pt].kb / 2 - 1) / (kTiles[pt].kb / 2));  // kb bytes = kb/2 channels per step
+        p.tiles_m = (int)(g.N * ((S + bm - 1) / bm));
+        p.tiles_n = (int)((g.K + 63) / 64);
+        p.group_m = 1;
+        pl.path = path;
+        pl.tile = pt;
+        pl.big = xnum > kSmallTensor || ynum > kSmallTensor;
+        pl.cblock = false;
+        pl.xspan = 0;
+        return IGC_OK;
+    }
     if (path == IGC_PATH_POINT) {
         if ((rk * esz) % 4 != 0)
             return fail(IGC_ERR_UNSUPPORTED, "point-output path needs image rows of a multiple of 4 bytes (C*T*R*S*%d = %lld)",
@@ -246,6 +294,8 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         return ((int64_t)p.M + kTiles[t].bm - 1) / kTiles[t].bm * (((int64_t)p.Ncol + kTiles[t].bn - 1) / kTiles[t].bn);
     };
     int tile = g_force_tile.load();
+    if (is_pointwise_tile(tile))
+        return fail(IGC_ERR_UNSUPPORTED, "tile %d is a pointwise path kernel", tile);
     if (tile < 0 || tile >= kNumTiles) {
         // Measured on MI355X: the 256x256 direct-to-LDS tile with 128-byte steps
         // (16x16 MFMA blocks, bf16 and fp8) is the fastest whenever its grid
@@ -352,6 +402,7 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
 const char *path_name(int path)
 {
     switch (path) {
+    case IGC_PATH_POINTWISE: return "pointwise";
     case IGC_PATH_POINT: return "point";
     case IGC_PATH_TEMPORAL: return "temporal";
     default: return "generic";

@@ -25,7 +25,10 @@ struct TileShape {
     int bm, bn, wm, wn, mf, stages, kb;
     int sb = 0;
 };
-constexpr int kNumTiles = 35;
+constexpr int kNumTiles = 40;
+// tiles 35..39: the NCDHW 1x1x1 kernel (conv_pw.hip), chosen by its path only
+constexpr int kPointwiseFirst = 35, kPointwiseLast = 39;
+constexpr bool is_pointwise_tile(int t) { return t >= kPointwiseFirst && t <= kPointwiseLast; }
 constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 16, 0, 128},  // 8 waves, 128x64 per wave: large grids
     {128, 128, 2, 2, 16, 0, 128},  // 4 waves, 64x64 per wave
@@ -62,6 +65,11 @@ constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 16, 3, 64, 5},   // 64-byte steps: rings of 3 and 5 x 16 KB (bf16 only)
     {256, 256, 2, 4, 16, 3, 128, 2},  // as 29, ping-pong wave groups (compute / memory phases)
     {256, 256, 2, 4, 16, 2, 128, 2},  // as 33, activation windows shared by the S taps of a filter row
+    {256, 64, 4, 1, 16, 3, 128},      // 1x1x1 on NCDHW x: 256 positions x 64 output channels, 64-channel steps
+    {256, 64, 4, 1, 16, 2, 128},      // 2 stages of 40 KB: two workgroups per CU
+    {512, 64, 4, 1, 16, 4, 64},       // 512 positions (1 KB per channel row), 32-channel steps, 4 x 36 KB
+    {512, 64, 4, 1, 16, 2, 64},       // two workgroups per CU
+    {256, 64, 4, 1, 16, 4, 64},       // 256 positions, 32-channel steps, 4 x 20 KB: two workgroups per CU
 };
 
 // Everything a conv kernel needs, passed by value as kernel arguments.
@@ -103,6 +111,11 @@ hipError_t launch_conv(const ConvParams &p, int tile, Mode mode, Dtype dt, bool 
 constexpr int step_bytes(const TileShape &t) { return t.kb; }
 constexpr bool is_window(const TileShape &t) { return t.stages < 0; }
 constexpr bool is_buffer(const TileShape &t) { return t.sb > 0; }
+
+// 1x1x1 filter, unit stride, no padding, NCDHW bf16 x: one GEMM per image
+// over the D*H*W positions, reading x untransposed (tiles of 256 positions x
+// 64 output channels: tiles_m = N * ceil(P / 256), tiles_n = ceil(K / 64)).
+hipError_t launch_conv_pw(const ConvParams &p, int variant, hipStream_t stream);
 
 hipError_t launch_amax(const uint16_t *t, int64_t n, float *amax, hipStream_t stream);
 hipError_t launch_fp8_scales(const float *amax, float *pair, hipStream_t stream);

@@ -22,6 +22,10 @@ them; the draws themselves are synthetic):
 * ``c5``  large conv3d bf16 (x and y above 2^31 elements): N=1 C=1024 D=240
   H=160 W=90, K=1024, 3x1x1, pad (1, 0, 0); x ~ U(-1, 1),
   w ~ N(0, 1/sqrt(3C)).
+* ``pw``  1x1x1 conv3d bf16 on NCDHW activations, C=512 -> K=48 over
+  D=240 H=320 W=180 (14 GB of activations): the shape the FlyDSL page's
+  1x1x1 measurement implies (its description gives the 14 GB A operand and
+  K=48); x ~ N(0, 1), w ~ N(0, 1/sqrt(C)).
 
 "N(0, 1/sqrt(R))" is read as standard deviation 1/sqrt(R).
 """
@@ -78,6 +82,9 @@ WORKLOADS = {
     "c5": Workload("c5", (1, 1024, 240, 160, 90), (1024, 1024, 3, 1, 1), pad=(1, 0, 0),
                    x_dist=("uniform", 1.0), w_dist=("normal", 1.0 / math.sqrt(_R(1024, 3, 1, 1))), seed=5,
                    note="large conv3d fwd bf16 N=1 C=1024 D=240 H=160 W=90 K=1024 3x1x1 pad (1,0,0)"),
+    "pw": Workload("pw", (1, 512, 240, 320, 180), (48, 512, 1, 1, 1),
+                   x_dist=("normal", 1.0), w_dist=("normal", 1.0 / math.sqrt(512)), seed=6,
+                   note="1x1x1 conv3d fwd bf16 NCDHW (no transpose) N=1 C=512 D=240 H=320 W=180 K=48"),
 }
 
 _CHUNK = 1 << 27  # draw large tensors in 128 Mi-element pieces to bound fp32 scratch

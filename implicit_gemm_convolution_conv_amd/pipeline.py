@@ -58,17 +58,17 @@ def conv3d(x_ncdhw: torch.Tensor, w_kctrs: torch.Tensor, stride=(1, 1, 1), pad=(
            dtype="bf16", stream=None):
     """y = conv3d(x, w) from bf16 NCDHW x and bf16 KCTRS w, all on the GPU.
 
-    Point-output shapes read x as is; other shapes pack x to NDHWC first. fp8
-    quantises both operands with per-tensor amax/448 scales."""
+    Point-output shapes and bf16 1x1x1 filters read x as is; other shapes pack
+    x to NDHWC first. fp8 quantises both operands with per-tensor amax/448
+    scales."""
     dt = _code(dtype)
     xshape, wshape = tuple(x_ncdhw.shape), tuple(w_kctrs.shape)
-    plan = B.conv_plan(xshape, wshape, stride, pad, dil, dt, B.IGC_NCDHW) if _is_point(xshape, wshape, pad, dil) \
-        else ""
+    direct = dt == B.IGC_BF16 and direct_ncdhw(xshape, wshape, stride, pad, dil)
     scales = fp8_scales(x_ncdhw, w_kctrs, stream) if dt == B.IGC_FP8_E4M3FN else None
     sx = scales[0:2] if scales is not None else None
     sw = scales[2:4] if scales is not None else None
     y = output(xshape, wshape, stride, pad, dil, x_ncdhw.device)
-    if plan.startswith("path=point") and dt == B.IGC_BF16:
+    if direct:
         wp = packed_weight(w_kctrs, dt, "NCDHW", sw, stream)
         B.conv_fwd(x_ncdhw, wp, y, xshape, wshape, stride, pad, dil, dt, B.IGC_NCDHW, scales, stream)
         return y
@@ -78,5 +78,11 @@ def conv3d(x_ncdhw: torch.Tensor, w_kctrs: torch.Tensor, stride=(1, 1, 1), pad=(
     return y
 
 
-def _is_point(xshape, wshape, pad, dil):
-    return tuple(pad) == (0, 0, 0) and tuple(dil) == (1, 1, 1) and tuple(xshape[2:]) == tuple(wshape[2:])
+def direct_ncdhw(xshape, wshape, stride, pad, dil) -> bool:
+    """True when the library reads bf16 NCDHW x as it is for this shape (point output, or the 1x1x1 pointwise
+    path) instead of needing the NDHWC pack."""
+    try:
+        plan = B.conv_plan(xshape, wshape, stride, pad, dil, B.IGC_BF16, B.IGC_NCDHW)
+    except B.IgcError:
+        return False
+    return plan.startswith("path=point")

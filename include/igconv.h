@@ -74,6 +74,7 @@ extern "C" {
 #define IGC_PATH_GENERIC 1  /* im2col decode of every tap */
 #define IGC_PATH_TEMPORAL 2 /* T x 1 x 1 filter: one bounds check per row (time axis only) */
 #define IGC_PATH_POINT 3    /* point output: plain GEMM over the batch */
+#define IGC_PATH_POINTWISE 4 /* 1x1x1 filter on NCDHW bf16 activations: per-image GEMM, no transpose */
 
 /*
  * Output extent {Do, Ho, Wo} by the formula above. Host only.
@@ -135,6 +136,12 @@ IGC_API int conv_pack_w(const void *w_kctrs_bf16, void *w_packed, const int64_t 
  *  x        activations, dtype operands, layout x_layout. The im2col paths
  *           (generic, temporal) need IGC_NDHWC with C % 8 == 0 (bf16) or
  *           C % 16 == 0 (fp8); the point-output path takes either layout.
+ *           A 1x1x1 filter with unit stride and no padding on IGC_NCDHW bf16
+ *           activations with D*H*W % 8 == 0 runs as one GEMM per image that
+ *           reads x as it is (IGC_PATH_POINTWISE): the route FlyDSL PR #860
+ *           takes for 1x1x1 filters to avoid the NCDHW->NDHWC transpose
+ *           (PR description, "Performance"). w_packed then comes from
+ *           conv_pack_w with x_layout = IGC_NCDHW.
  *  w_packed filter from conv_pack_w with the same dtype and x_layout.
  *  y        bf16 output, NCDHW {N, K, Do, Ho, Wo}; every element is written.
  *  scales_dev  fp8 only: device float[4] = {s_x, inv_x, s_w, inv_w} (the two

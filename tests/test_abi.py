@@ -81,6 +81,16 @@ def test_path_selection():
     p = _plan((1, 64, 4, 16, 16), (64, 64, 3, 3, 3), pd=(1, 1, 1))
     assert (p["tile"], p["stages"]) == ("64x64", "4")
     assert _plan((1, 24, 4, 16, 16), (64, 24, 3, 3, 3), pd=(1, 1, 1))["order"] == "linear"
+    # 1x1x1 filters on NCDHW bf16 activations: one GEMM per image, no transpose
+    p = _plan((1, 512, 240, 320, 180), (48, 512, 1, 1, 1), lay=B.IGC_NCDHW)
+    assert (p["path"], p["tile"], p["nk"], p["grid"]) == ("pointwise", "512x64", "16", str(240 * 320 * 180 // 512))
+    assert _plan((2, 64, 4, 6, 10), (48, 64, 1, 1, 1))["path"] == "temporal"   # NDHWC: the flat GEMM of the temporal path
+    with pytest.raises(B.IgcError) as e:  # D*H*W % 8 != 0: NCDHW activations need the pack
+        _plan((2, 64, 3, 5, 7), (48, 64, 1, 1, 1), lay=B.IGC_NCDHW)
+    assert e.value.status == B.IGC_ERR_UNSUPPORTED
+    with pytest.raises(B.IgcError) as e:  # fp8 operands come from the NDHWC pack
+        _plan((1, 64, 4, 6, 10), (48, 64, 1, 1, 1), dt=B.IGC_FP8_E4M3FN, lay=B.IGC_NCDHW)
+    assert e.value.status == B.IGC_ERR_UNSUPPORTED
 
 
 def test_forced_path_and_tile():

@@ -435,6 +435,57 @@ def test_buffer_tiles_agree_bitwise_with_global_tiles():
     assert torch.equal(outs[6], outs[21])
 
 
+# ------------------------------------------------------------------ 1x1x1 filters on NCDHW activations (no transpose)
+
+PW_CASES = [
+    ("pw_c64_k48_two_position_tiles", (1, 64, 4, 8, 16), (48, 64, 1, 1, 1)),
+    ("pw_c40_k100_ragged", (2, 40, 3, 5, 8), (100, 40, 1, 1, 1)),      # C < 64, two channel tiles, S = 120
+    ("pw_c512_k48_three_images", (3, 512, 2, 6, 20), (48, 512, 1, 1, 1)),  # 8 reduction steps
+    ("pw_c200_k64_tail", (1, 200, 5, 7, 24), (64, 200, 1, 1, 1)),      # C % 64 != 0, S = 840
+    ("pw_c8_k16_tiny", (1, 8, 1, 1, 8), (16, 8, 1, 1, 1)),
+    ("pw_2d", (2, 96, 1, 12, 30), (72, 96, 1, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("case", PW_CASES, ids=[c[0] for c in PW_CASES])
+def test_pointwise_ncdhw(case):
+    name, xs, ws = case
+    one, zero = (1, 1, 1), (0, 0, 0)
+    assert B.conv_plan(xs, ws, one, zero, one, B.IGC_BF16, B.IGC_NCDHW).startswith("path=pointwise")
+    _bf16_case(f"pointwise {name}", xs, ws, one, zero, one, seed=zlib.crc32(name.encode()) % 1000,
+               dist=("normal", 1.0), x_layout="NCDHW")
+
+
+@pytest.mark.parametrize("tile", [35, 36, 37, 38, 39])
+def test_pointwise_tiles(tile):
+    one, zero = (1, 1, 1), (0, 0, 0)
+    with forced(tile=tile):
+        for name, xs, ws in (PW_CASES[1], PW_CASES[2], PW_CASES[3]):
+            _bf16_case(f"pointwise tile {tile} {name}", xs, ws, one, zero, one, seed=tile, dist=("normal", 1.0),
+                       x_layout="NCDHW")
+        _int_case((2, 72, 3, 4, 10), (80, 72, 1, 1, 1), one, zero, one, seed=32, x_layout="NCDHW")
+
+
+def test_pointwise_integer_bit_exact():
+    _announce("pointwise integer")
+    _int_case((2, 72, 3, 4, 10), (80, 72, 1, 1, 1), (1, 1, 1), (0, 0, 0), (1, 1, 1), seed=31, x_layout="NCDHW")
+
+
+def test_pointwise_matches_transposed_path_bitwise():
+    # same reduction order as the NDHWC temporal path (64-channel steps, two 32-channel MFMA slices), same bits;
+    # the NaN-prefilled output checks that every element is written
+    _announce("pointwise vs pack + temporal path, bitwise")
+    g = I.generator(17, P.DEV)
+    xs, ws, one, zero = (2, 192, 3, 10, 24), (88, 192, 1, 1, 1), (1, 1, 1), (0, 0, 0)
+    x = I.draw(xs, ("normal", 1.0), g, P.DEV)
+    w = I.draw(ws, ("normal", 0.1), g, P.DEV)
+    y1 = torch.full((xs[0], ws[0]) + xs[2:], float("nan"), dtype=torch.bfloat16, device=P.DEV)
+    P.run_bf16(x, w, one, zero, one, x_layout="NCDHW", out=y1)
+    y2 = P.run_bf16(x, w, one, zero, one, x_layout="NDHWC")
+    assert not torch.isnan(y1).any()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
 # ------------------------------------------------------------------ input-window tiles (16 bf16, 17 bf16/fp8)
 
 WIN_CASES = [

@@ -151,3 +151,38 @@ def test_c5_large_tensor():
         src = x[:, perm[kk:kk + 128], : d - 1]
         assert torch.equal(y[:, kk:kk + 128, 1:].view(torch.int16), src.view(torch.int16)), kk
     _free()
+
+
+def test_pointwise_ncdhw_page_workload():
+    """1x1x1 conv on 14 GB of NCDHW activations, read without a transpose: sampled positions against the oracle
+    (a 1x1x1 conv of the gathered columns), then a one-hot filter that must copy channels bit for bit."""
+    wl = I.WORKLOADS["pw"]
+    xs, ws = wl.x_shape, wl.w_shape
+    n, c, d, h, wdt = xs
+    k = ws[0]
+    one, zero = (1, 1, 1), (0, 0, 0)
+    _announce("pw 1x1x1 NCDHW, 14 GB: sampled vs oracle")
+    assert B.conv_plan(xs, ws, one, zero, one, B.IGC_BF16, B.IGC_NCDHW).startswith("path=pointwise")
+    x, w = I.make(wl, P.DEV)
+    wp = PL.packed_weight(w, "bf16", "NCDHW")
+    y = PL.output(xs, ws, one, zero, one, P.DEV)
+    B.conv_fwd(x, wp, y, xs, ws, one, zero, one, B.IGC_BF16, B.IGC_NCDHW)
+    torch.cuda.synchronize()
+    S = d * h * wdt
+    rng = np.random.default_rng(6)
+    pos = np.unique(np.concatenate([rng.integers(0, S, 2000), [0, 1, 255, 256, S - 256, S - 1]]))
+    pos_t = torch.as_tensor(pos, device=P.DEV)
+    cols = x.view(n, c, S)[:, :, pos_t].contiguous().view(n, c, 1, 1, len(pos))
+    ref = O.conv3d(P.bits(cols), P.bits(w), one, zero, one)            # (n, k, 1, 1, len(pos))
+    got = y.view(n, k, S)[:, :, pos_t].contiguous().view(n, k, 1, 1, len(pos))
+    P.check_close(P.y_values(got), ref, c, float(x.abs().max()), float(w.abs().max()), "pw")
+
+    _announce("pw one-hot filter, full size (bit-exact)")
+    perm = torch.randperm(c, generator=torch.Generator().manual_seed(2))[:k].to(P.DEV)
+    wd = torch.zeros(ws, dtype=torch.bfloat16, device=P.DEV)
+    wd[torch.arange(k, device=P.DEV), perm, 0, 0, 0] = 1.0
+    B.conv_fwd(x, PL.packed_weight(wd, "bf16", "NCDHW"), y, xs, ws, one, zero, one, B.IGC_BF16, B.IGC_NCDHW)
+    torch.cuda.synchronize()
+    for kk in range(k):
+        assert torch.equal(y[:, kk].view(torch.int16), x[:, perm[kk]].view(torch.int16)), kk
+    _free()
