@@ -68,10 +68,12 @@ def kernel_hash():
     return h.hexdigest()[:16]
 
 
-def time_launches(fn, steps, warmup, torch):
+def time_launches(fn, steps, warmup, torch, stats=None, between=None):
     """Run fn warmup times, then `steps` times with an event pair around each call
     on the current stream (the one the library launches on). Returns (wall ms per
-    step, mean event ms per call)."""
+    step, mean event ms per call); `stats`, if a dict, also receives the median
+    and minimum event ms. `between`, if given, runs before every timed call
+    outside its events (the cold-cache figure evicts the caches with it)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -79,12 +81,19 @@ def time_launches(fn, steps, warmup, torch):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for a, b in evs:
+        if between is not None:
+            between()
         a.record(stream)
         fn()
         b.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    ev = sum(a.elapsed_time(b) for a, b in evs) / steps
+    times = sorted(a.elapsed_time(b) for a, b in evs)
+    ev = sum(times) / steps
+    if stats is not None:
+        stats["median"] = times[len(times) // 2] if len(times) % 2 else 0.5 * (times[len(times) // 2 - 1] +
+                                                                                times[len(times) // 2])
+        stats["min"] = times[0]
     return wall, ev
 
 
@@ -109,9 +118,16 @@ def bench_workload(name, steps, warmup, torch, B, I, PL):
         def step():
             B.conv_fwd(xk, wp, y, xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay)
 
-        wall, ev = time_launches(step, steps, warmup, torch)
-        res.update(ms=wall, kernel_ms=ev, tflops=flops / (wall * 1e-3) / 1e12,
-                   kernel_tflops=flops / (ev * 1e-3) / 1e12)
+        st = {}
+        wall, ev = time_launches(step, steps, warmup, torch, st)
+        res.update(ms=wall, kernel_ms=ev, kernel_ms_median=st["median"], kernel_ms_min=st["min"],
+                   tflops=flops / (wall * 1e-3) / 1e12, kernel_tflops=flops / (ev * 1e-3) / 1e12)
+        if name in ("c1", "c2"):  # working set fits the MALL: also with the caches evicted before every call
+            scratch = torch.empty(1 << 28, dtype=torch.int16, device="cuda")  # 512 MB
+            cst = {}
+            time_launches(step, steps, warmup, torch, cst, between=lambda: scratch.fill_(1))
+            res.update(cold_kernel_ms_median=cst["median"], cold_kernel_ms_min=cst["min"])
+            del scratch
         if name == "pw":  # HBM-bound: x and y once, the filter per 64 output channels
             nbytes = 2 * (x.numel() + y.numel() + w.numel())
             res.update(kernel_gbs=nbytes / (ev * 1e-3) / 1e9, hbm_frac=nbytes / (ev * 1e-3) / 1e9 / PEAK_HBM_GBS)
@@ -141,7 +157,9 @@ def bench_workload(name, steps, warmup, torch, B, I, PL):
             prep()
             conv()
 
-        _, ev_k = time_launches(conv, steps, warmup, torch)
+        st = {}
+        _, ev_k = time_launches(conv, steps, warmup, torch, st)
+        res.update(kernel_ms_median=st["median"], kernel_ms_min=st["min"])
         wall_e, ev_e = time_launches(e2e, steps, warmup, torch)
         _, ev_p = time_launches(lambda: B.conv_pack_x(x, xq, xshape, B.IGC_FP8_E4M3FN, scales[0:2]), steps,
                                 warmup, torch)
@@ -285,7 +303,9 @@ def main():
         "data": "synthetic (seeded; x ~ N(0,1), w ~ N(0, 1/sqrt(C*27)), bf16)",
         "config": {"workload": "conv3d fwd bf16 NDHWC N=1 C=2048 D=60 H=80 W=45 K=2048 3x3x3 stride 1 pad 1",
                    "gemm_m": 216000, "gemm_n": 2048, "reduction": 55296, "flop_per_step": head["flop"],
-                   "plan": head["plan"]},
+                   "plan": head["plan"], "kernel_ms_mean": round(head["kernel_ms"], 4),
+                   "kernel_ms_median": round(head["kernel_ms_median"], 4),
+                   "kernel_ms_min": round(head["kernel_ms_min"], 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
                      "traffic": traffic_bytes()},
