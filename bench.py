@@ -128,6 +128,21 @@ def bench_workload(name, steps, warmup, torch, B, I, PL):
             time_launches(step, steps, warmup, torch, cst, between=lambda: scratch.fill_(1))
             res.update(cold_kernel_ms_median=cst["median"], cold_kernel_ms_min=cst["min"])
             del scratch
+        nws = B.conv_fwd_workspace_bytes(xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay)
+        if nws > 0:  # under-filled grid: the split reduction through conv_fwd_ws (conv kernel + reduction pass)
+            wsb = torch.empty(nws // 4, dtype=torch.float32, device="cuda")
+            res["split_plan"] = B.conv_plan_ws(xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay, nws)
+
+            def split_step():
+                B.conv_fwd_ws(xk, wp, y, xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay, workspace=wsb)
+
+            sst, cst = {}, {}
+            _, sev = time_launches(split_step, steps, warmup, torch, sst)
+            scratch = torch.empty(1 << 28, dtype=torch.int16, device="cuda")
+            time_launches(split_step, steps, warmup, torch, cst, between=lambda: scratch.fill_(1))
+            res.update(split_kernel_ms=sev, split_kernel_ms_median=sst["median"], split_kernel_ms_min=sst["min"],
+                       split_cold_kernel_ms_median=cst["median"], split_cold_kernel_ms_min=cst["min"])
+            del scratch, wsb
         if name == "pw":  # HBM-bound: x and y once, the filter per 64 output channels
             nbytes = 2 * (x.numel() + y.numel() + w.numel())
             res.update(kernel_gbs=nbytes / (ev * 1e-3) / 1e9, hbm_frac=nbytes / (ev * 1e-3) / 1e9 / PEAK_HBM_GBS)

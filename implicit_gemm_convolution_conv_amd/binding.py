@@ -27,7 +27,8 @@ IGC_NCDHW, IGC_NDHWC = 0, 1
 IGC_PATH_AUTO, IGC_PATH_GENERIC, IGC_PATH_TEMPORAL, IGC_PATH_POINT, IGC_PATH_POINTWISE = 0, 1, 2, 3, 4
 
 EXPORTS = ("conv_out_dims", "conv_packed_w_cols", "conv_amax", "conv_fp8_scales", "conv_pack_x", "conv_pack_w",
-           "conv_fwd", "conv_plan", "conv_debug_force", "conv_last_error")
+           "conv_fwd", "conv_fwd_ws", "conv_fwd_workspace_bytes", "conv_plan", "conv_plan_ws", "conv_debug_force",
+           "conv_debug_force_splits", "conv_last_error")
 
 
 class IgcError(RuntimeError):
@@ -56,10 +57,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.conv_pack_w.argtypes = [P, P, P, I32, I32, P, P]
         lib.conv_fwd.argtypes = [P, P, P, P, P, P, P, P, I32, I32, P, P]
         lib.conv_plan.argtypes = [P, P, P, P, P, I32, I32, ctypes.c_char_p, ctypes.c_size_t]
+        lib.conv_fwd_ws.argtypes = [P, P, P, P, P, P, P, P, I32, I32, P, P, ctypes.c_size_t, P]
+        lib.conv_fwd_workspace_bytes.argtypes = [P, P, P, P, P, I32, I32]
+        lib.conv_fwd_workspace_bytes.restype = I64
+        lib.conv_plan_ws.argtypes = [P, P, P, P, P, I32, I32, ctypes.c_size_t, ctypes.c_char_p, ctypes.c_size_t]
         lib.conv_debug_force.argtypes = [I32, I32, I32]
+        lib.conv_debug_force_splits.argtypes = [I32]
         lib.conv_last_error.restype = ctypes.c_char_p
         for name in EXPORTS:
-            if name not in ("conv_packed_w_cols", "conv_last_error"):
+            if name not in ("conv_packed_w_cols", "conv_fwd_workspace_bytes", "conv_last_error"):
                 getattr(lib, name).restype = I32
         _lib = lib
     return _lib
@@ -139,15 +145,48 @@ def conv_fwd(x, w_packed, y, xshape, wshape, stride, pad, dilation, dtype, x_lay
                                        _dev(scales_dev), _stream(stream, y)))
 
 
+def conv_fwd_ws(x, w_packed, y, xshape, wshape, stride, pad, dilation, dtype, x_layout, scales_dev=None,
+                workspace=None, workspace_bytes=None, stream=None):
+    """conv_fwd with a device workspace (a torch tensor; its whole size unless workspace_bytes says less)."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace_bytes is not None:
+        if int(workspace_bytes) > nbytes:
+            raise ValueError(f"workspace_bytes {workspace_bytes} exceeds the workspace tensor ({nbytes} bytes)")
+        nbytes = int(workspace_bytes)
+    _check("conv_fwd_ws", load().conv_fwd_ws(_dev(x), _dev(w_packed), _dev(y), _i64(xshape, 5), _i64(wshape, 5),
+                                             _i32(stride), _i32(pad), _i32(dilation), int(dtype), int(x_layout),
+                                             _dev(scales_dev), _dev(workspace), nbytes, _stream(stream, y)))
+
+
+def conv_fwd_workspace_bytes(xshape, wshape, stride, pad, dilation, dtype, x_layout) -> int:
+    n = load().conv_fwd_workspace_bytes(_i64(xshape, 5), _i64(wshape, 5), _i32(stride), _i32(pad), _i32(dilation),
+                                        int(dtype), int(x_layout))
+    if n < 0:
+        raise IgcError("conv_fwd_workspace_bytes", int(n), conv_last_error())
+    return int(n)
+
+
 def conv_plan(xshape, wshape, stride, pad, dilation, dtype, x_layout) -> str:
-    buf = ctypes.create_string_buffer(256)
+    buf = ctypes.create_string_buffer(512)
     _check("conv_plan", load().conv_plan(_i64(xshape, 5), _i64(wshape, 5), _i32(stride), _i32(pad),
-                                         _i32(dilation), int(dtype), int(x_layout), buf, 256))
+                                         _i32(dilation), int(dtype), int(x_layout), buf, 512))
+    return buf.value.decode()
+
+
+def conv_plan_ws(xshape, wshape, stride, pad, dilation, dtype, x_layout, workspace_bytes) -> str:
+    buf = ctypes.create_string_buffer(512)
+    _check("conv_plan_ws", load().conv_plan_ws(_i64(xshape, 5), _i64(wshape, 5), _i32(stride), _i32(pad),
+                                               _i32(dilation), int(dtype), int(x_layout), int(workspace_bytes),
+                                               buf, 512))
     return buf.value.decode()
 
 
 def conv_debug_force(path, tile, group_m=0):
     _check("conv_debug_force", load().conv_debug_force(int(path), int(tile), int(group_m)))
+
+
+def conv_debug_force_splits(splits):
+    _check("conv_debug_force_splits", load().conv_debug_force_splits(int(splits)))
 
 
 def conv_last_error() -> str:

@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <string>
 
@@ -51,6 +52,7 @@ thread_local std::string g_err;
 std::atomic<int> g_force_path{IGC_PATH_AUTO};
 std::atomic<int> g_force_tile{-1};
 std::atomic<int> g_force_group_m{0};
+std::atomic<int> g_force_splits{0};
 
 constexpr int64_t kI32Max = 2147483647;
 // Element offsets up to this bound use 32-bit arithmetic in the conv kernel;
@@ -222,6 +224,7 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
 
     ConvParams &p = pl.p;
     p = ConvParams{};
+    p.splits = 1;
     p.N = (int)g.N; p.C = (int)g.C; p.D = (int)g.D; p.H = (int)g.H; p.W = (int)g.W;
     p.K = (int)g.K; p.T = (int)g.T; p.R = (int)g.R; p.S = (int)g.S;
     p.sd = (int)g.sd; p.sh = (int)g.sh; p.sw = (int)g.sw;
@@ -257,6 +260,7 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         p.tiles_m = (int)(g.N * ((S + bm - 1) / bm));
         p.tiles_n = (int)((g.K + 63) / 64);
         p.group_m = 1;
+        p.ksplit = p.nk;
         pl.path = path;
         pl.tile = pt;
         pl.big = xnum > kSmallTensor || ynum > kSmallTensor;
@@ -396,7 +400,48 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
     p.group_m = (int)std::max<int64_t>(1, resident / tn);
     if (g_force_group_m.load() > 0)
         p.group_m = g_force_group_m.load();
+    p.ksplit = p.nk;
     return IGC_OK;
+}
+
+// Split reduction (split-K). FlyDSL PR #860 splits the reduction only when the
+// grid of output tiles under-fills the GPU (its split-K selection rule: the
+// under-fill test decides, a long reduction alone does not). Here: the
+// direct-to-LDS kernels, grids below 128 tiles (half the CUs), and at least 5
+// reduction steps per split (about the ring depth: shorter splits are mostly
+// pipeline fill); enough splits to reach about 256 workgroups, at most 32, and
+// no more than the workspace holds (splits * elements of y fp32 values).
+// Measured on MI355X (bf16, 64x64 tiles): the 1024x64x1728 GEMM of a
+// 64-channel 3x3x3 conv on 4x16x16 goes from 19.0 to 11.7 us, a 512-channel
+// 3x3 conv on 7x7 from 42 to 15 us. Returns the split count (1 = none) with
+// p.ksplit set, or a negative status for a forced split the tile cannot run.
+bool splits_tile(int tile)
+{
+    const TileShape &t = kTiles[tile];
+    return t.stages > 0 && !is_buffer(t) && !is_pointwise_tile(tile);
+}
+
+int plan_splits(Plan &pl, size_t ws_bytes)
+{
+    ConvParams &p = pl.p;
+    const int64_t ynum = (int64_t)p.M * p.Ncol;
+    const int64_t cap = std::min<int64_t>(ws_bytes / 4 / ynum, 64);
+    const int forced = g_force_splits.load();
+    int splits = 1;
+    if (forced > 0) {
+        if (forced > 1 && !splits_tile(pl.tile))
+            return fail(IGC_ERR_UNSUPPORTED, "tile %d does not split the reduction (direct-to-LDS tiles only)",
+                        pl.tile);
+        splits = (int)std::min<int64_t>(std::min(forced, p.nk), cap);
+    } else if (splits_tile(pl.tile)) {
+        const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+        if (grid < 128)
+            splits = (int)std::min<int64_t>(std::min<int64_t>(std::min<int64_t>(256 / grid, p.nk / 5), 32), cap);
+    }
+    splits = std::max(splits, 1);
+    p.ksplit = (p.nk + splits - 1) / splits;
+    p.splits = (p.nk + p.ksplit - 1) / p.ksplit;  // every split holds at least one step
+    return p.splits;
 }
 
 const char *path_name(int path)
@@ -518,9 +563,9 @@ int conv_pack_w(const void *w_kctrs_bf16, void *w_packed, const int64_t wshape[5
     return ok();
 }
 
-int conv_fwd(const void *x, const void *w_packed, void *y, const int64_t xshape[5], const int64_t wshape[5],
-             const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout,
-             const float *scales_dev, void *stream)
+int conv_fwd_ws(const void *x, const void *w_packed, void *y, const int64_t xshape[5], const int64_t wshape[5],
+                const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout,
+                const float *scales_dev, void *workspace_dev, size_t workspace_bytes, void *stream)
 {
     Plan pl;
     int rc = make_plan(xshape, wshape, stride, pad, dilation, dtype, x_layout, pl);
@@ -532,43 +577,86 @@ int conv_fwd(const void *x, const void *w_packed, void *y, const int64_t xshape[
         return fail(IGC_ERR_INVALID, "conv_fwd: fp8 needs scales_dev = {s_x, inv_x, s_w, inv_w}");
     if (!aligned16(x) || !aligned16(w_packed) || !aligned16(y))
         return fail(IGC_ERR_ALIGN, "conv_fwd: x, w_packed and y must be 16-byte aligned");
+    if (workspace_bytes && !workspace_dev)
+        return fail(IGC_ERR_INVALID, "conv_fwd_ws: null workspace with workspace_bytes = %zu", workspace_bytes);
+    if (workspace_dev && !aligned16(workspace_dev))
+        return fail(IGC_ERR_ALIGN, "conv_fwd_ws: workspace must be 16-byte aligned");
+    rc = plan_splits(pl, workspace_dev ? workspace_bytes : 0);
+    if (rc < 0)
+        return rc;
     pl.p.x = x;
     pl.p.w = w_packed;
     pl.p.y = y;
     pl.p.scales = dtype == IGC_FP8_E4M3FN ? scales_dev : nullptr;
+    pl.p.part = pl.p.splits > 1 ? static_cast<float *>(workspace_dev) : nullptr;
     const Mode mode = pl.path == IGC_PATH_POINT ? MODE_POINT : (pl.path == IGC_PATH_TEMPORAL ? MODE_TEMPORAL : MODE_GENERIC);
-    if (launch_conv(pl.p, pl.tile, mode, dtype == IGC_FP8_E4M3FN ? DT_FP8 : DT_BF16, pl.big, pl.cblock,
-                    static_cast<hipStream_t>(stream)) != hipSuccess)
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (launch_conv(pl.p, pl.tile, mode, dtype == IGC_FP8_E4M3FN ? DT_FP8 : DT_BF16, pl.big, pl.cblock, st) !=
+        hipSuccess)
         return fail(IGC_ERR_HIP, "conv_fwd: kernel launch failed");
+    if (pl.p.splits > 1 &&
+        launch_splitk_reduce(pl.p.part, pl.p.splits, (int64_t)pl.p.M * pl.p.Ncol, pl.p.scales, y, st) != hipSuccess)
+        return fail(IGC_ERR_HIP, "conv_fwd_ws: split reduction launch failed");
     return ok();
 }
 
-int conv_plan(const int64_t xshape[5], const int64_t wshape[5], const int32_t stride[3], const int32_t pad[3],
-              const int32_t dilation[3], int dtype, int x_layout, char *buf, size_t len)
+int conv_fwd(const void *x, const void *w_packed, void *y, const int64_t xshape[5], const int64_t wshape[5],
+             const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout,
+             const float *scales_dev, void *stream)
+{
+    return conv_fwd_ws(x, w_packed, y, xshape, wshape, stride, pad, dilation, dtype, x_layout, scales_dev, nullptr, 0,
+                       stream);
+}
+
+int64_t conv_fwd_workspace_bytes(const int64_t xshape[5], const int64_t wshape[5], const int32_t stride[3],
+                                 const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout)
 {
     Plan pl;
     int rc = make_plan(xshape, wshape, stride, pad, dilation, dtype, x_layout, pl);
     if (rc)
         return rc;
+    rc = plan_splits(pl, SIZE_MAX);
+    if (rc < 0)
+        return rc;
+    ok();
+    return rc > 1 ? (int64_t)rc * pl.p.M * pl.p.Ncol * 4 : 0;
+}
+
+int conv_plan_ws(const int64_t xshape[5], const int64_t wshape[5], const int32_t stride[3], const int32_t pad[3],
+                 const int32_t dilation[3], int dtype, int x_layout, size_t workspace_bytes, char *buf, size_t len)
+{
+    Plan pl;
+    int rc = make_plan(xshape, wshape, stride, pad, dilation, dtype, x_layout, pl);
+    if (rc)
+        return rc;
+    rc = plan_splits(pl, workspace_bytes);
+    if (rc < 0)
+        return rc;
     if (buf && len) {
         const TileShape ts = kTiles[pl.tile];
         snprintf(buf, len,
                  "path=%s tile=%dx%d waves=%d mfma=%dx%d stages=%d bstages=%d kstep=%d order=%s%s big=%d grid=%d "
-                 "group_m=%d nk=%d loads=%s schedule=%s areuse=%s xspan=%lld",
+                 "group_m=%d nk=%d loads=%s schedule=%s areuse=%s xspan=%lld splits=%d ksplit=%d",
                  path_name(pl.path), ts.bm, ts.bn, ts.wm * ts.wn, ts.mf, ts.mf, ts.stages ? std::abs(ts.stages) : 2,
                  is_buffer(ts) ? ts.sb : (ts.stages ? std::abs(ts.stages) : 2), step_bytes(ts) / (dtype == IGC_FP8_E4M3FN ? 1 : 2),
                  is_window(ts) ? "window" : (pl.cblock ? "cblock" : "linear"), pl.p.pairs == 2 ? "-paired" : "",
                  pl.big ? 1 : 0, pl.p.tiles_m * pl.p.tiles_n, pl.p.group_m, pl.p.nk,
                  is_buffer(ts) ? "buffer-lds" : (ts.stages > 0 ? "global-lds" : (is_window(ts) ? "window-lds" : "registers")),
                  pl.tile == 33 || pl.tile == 34 ? "pingpong" : "lockstep", pl.tile == 34 ? "taps" : "none",
-                 pl.path == IGC_PATH_POINT ? 0LL : (long long)pl.xspan);
+                 pl.path == IGC_PATH_POINT ? 0LL : (long long)pl.xspan, pl.p.splits, pl.p.ksplit);
     }
     return ok();
 }
 
+int conv_plan(const int64_t xshape[5], const int64_t wshape[5], const int32_t stride[3], const int32_t pad[3],
+              const int32_t dilation[3], int dtype, int x_layout, char *buf, size_t len)
+{
+    return conv_plan_ws(xshape, wshape, stride, pad, dilation, dtype, x_layout, 0, buf, len);
+}
+
 int conv_debug_force(int path, int tile, int group_m)
 {
-    if (path < IGC_PATH_AUTO || path > IGC_PATH_POINT)
+    if (path < IGC_PATH_AUTO || path > IGC_PATH_POINTWISE)
         return fail(IGC_ERR_INVALID, "conv_debug_force: unknown path %d", path);
     if (tile < -1 || tile >= kNumTiles)
         return fail(IGC_ERR_INVALID, "conv_debug_force: tile %d not in [-1, %d)", tile, kNumTiles);
@@ -577,6 +665,14 @@ int conv_debug_force(int path, int tile, int group_m)
     g_force_path.store(path);
     g_force_tile.store(tile);
     g_force_group_m.store(group_m);
+    return ok();
+}
+
+int conv_debug_force_splits(int splits)
+{
+    if (splits < 0)
+        return fail(IGC_ERR_INVALID, "conv_debug_force_splits: splits %d < 0", splits);
+    g_force_splits.store(splits);
     return ok();
 }
 

@@ -67,10 +67,9 @@ struct OffType<true> {
 // so block b runs on XCD b % 8; renumber so that consecutive logical tiles
 // share an XCD (and its L2), then walk the tiles in groups of group_m tile
 // rows, all columns of a group before the next group.
-__device__ inline void tile_coords(const ConvParams &p, int &tm, int &tn)
+__device__ inline void tile_coords(const ConvParams &p, int bid, int &tm, int &tn)
 {
     const int nblk = p.tiles_m * p.tiles_n;
-    const int bid = blockIdx.x;
     const int xcd = bid & 7, idx = bid >> 3;
     const int q = nblk >> 3, r = nblk & 7;
     const int lin = xcd * q + min(xcd, r) + idx;
@@ -82,6 +81,8 @@ __device__ inline void tile_coords(const ConvParams &p, int &tm, int &tn)
     tm = first + in % rows;
     tn = in / rows;
 }
+
+__device__ inline void tile_coords(const ConvParams &p, int &tm, int &tn) { tile_coords(p, blockIdx.x, tm, tn); }
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
 __device__ inline uint32_t f32_to_bf16_rne(float f)

@@ -21,6 +21,13 @@
 // elements with no padding and are only 4-byte aligned; the one chunk that
 // straddles a row's end is fetched as zeros by the DMA and then overwritten
 // from registers with its valid bytes before the last step is consumed.
+//
+// Split reduction (split-K, for grids of output tiles too small to occupy the
+// GPU; FlyDSL PR #860 chooses it only when the tile grid under-fills the
+// device): with p.splits > 1 the grid holds p.splits workgroups per tile, each
+// runs a contiguous range of reduction steps from its own start position and
+// stores unscaled fp32 sums; launch_splitk_reduce adds the slices in split
+// order, scales and rounds to bf16.
 #pragma once
 
 #include "conv_igemm.h"
@@ -77,8 +84,12 @@ void conv_igemm_dma_kernel(ConvParams p)
     const int wave = tid >> 6;
     const int wm = wave % WM, wn = wave / WM;
 
+    // Split reduction: workgroups [j * tiles, (j + 1) * tiles) run split j of every tile.
+    const int ntiles = p.tiles_m * p.tiles_n;
+    const int split = p.splits > 1 ? (int)blockIdx.x / ntiles : 0;
+    const int kbeg = split * p.ksplit;  // first reduction step of this workgroup
     int tm, tn;
-    tile_coords(p, tm, tn);
+    tile_coords(p, (int)blockIdx.x - split * ntiles, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     // This lane's row within each RPI-row group and the chunk it fetches there:
@@ -141,12 +152,17 @@ void conv_igemm_dma_kernel(ConvParams p)
     unsigned tail_mask = 0;
 
     // ---------------------------------------------------------------- k position of the next issue
+    // Channel-block order: channel block (pairs * TKE) outer, tap, then the
+    // `pairs` consecutive TKE-wide halves of each 128-byte line, so the two
+    // halves of a cache line are fetched by consecutive steps. The position
+    // starts at step kbeg.
     int kc, c = 0, t = 0, r = 0, s = 0;
     bool kval = true;
+    int cbase = 0, half = 0;
     if constexpr (MODE == MODE_POINT) {
-        kc = jc * CH;
+        kc = kbeg * TKE + jc * CH;
     } else if constexpr (!CBLK) {
-        kc = jc * CH;
+        kc = kbeg * TKE + jc * CH;
         c = kc % p.C;
         const int tap = kc / p.C;
         s = tap % p.S;
@@ -154,13 +170,17 @@ void conv_igemm_dma_kernel(ConvParams p)
         t = tap / (p.S * p.R);
         kval = kc < p.Rk;
     } else {
-        c = jc * CH;
-        kc = c;
+        const int taps = p.T * p.R * p.S;
+        const int q = kbeg / p.pairs;  // step = (channel block * taps + tap) * pairs + half
+        const int tap = q % taps;
+        half = kbeg - q * p.pairs;
+        cbase = q / taps * p.pairs * TKE;
+        s = tap % p.S;
+        r = (tap / p.S) % p.R;
+        t = tap / (p.S * p.R);
+        c = cbase + half * TKE + jc * CH;
+        kc = ((t * p.R + r) * p.S + s) * p.C + c;
     }
-    // Channel-block order: channel block (pairs * TKE) outer, tap, then the
-    // `pairs` consecutive TKE-wide halves of each 128-byte line, so the two
-    // halves of a cache line are fetched by consecutive steps.
-    int cbase = 0, half = 0;
     Off tapoff = 0;
     auto update_tapoff = [&]() {
         if constexpr (MODE == MODE_POINT)
@@ -330,7 +350,7 @@ void conv_igemm_dma_kernel(ConvParams p)
     // in flight), then the barrier makes all threads' data visible and
     // guarantees that step ks-1's slot is no longer read, so step ks+S-1 can be
     // issued into it.
-    const int nk = p.nk;
+    const int nk = p.splits > 1 ? min(p.nk - kbeg, p.ksplit) : p.nk;  // steps of this workgroup
 #pragma unroll
     for (int st = 0; st < S - 1; ++st) {
         if (st < nk) {
@@ -353,9 +373,9 @@ void conv_igemm_dma_kernel(ConvParams p)
         }
         asm volatile("s_barrier" ::: "memory");
         if constexpr (MODE == MODE_POINT) {
-            // The straddling chunks belong to the last step (nk = ceil(Rk / TKE)); its
+            // The straddling chunks belong to the last step (p.nk = ceil(Rk / TKE)); its
             // DMA wrote zeros there, which have landed: overwrite them, then publish.
-            if (ks == nk - 1 && (p.Rk % CH) != 0) {
+            if (kbeg + ks == p.nk - 1 && (p.Rk % CH) != 0) {
                 char *bst = smem + (ks % S) * STAGE + BM * KB;
 #pragma unroll
                 for (int i = 0; i < BIT; ++i)
@@ -373,10 +393,30 @@ void conv_igemm_dma_kernel(ConvParams p)
     }
 
     // ---------------------------------------------------------------- epilogue
+    // y = bf16(acc * scale); a split workgroup stores its fp32 sums unscaled
+    // at the same element offsets of its slice of the partial buffer.
+    const bool partial = p.splits > 1;
     float sc = 1.0f;
     if constexpr (DT == DT_FP8)
-        sc = p.scales[0] * p.scales[2];
+        if (!partial)
+            sc = p.scales[0] * p.scales[2];
     uint16_t *yb = static_cast<uint16_t *>(p.y);
+    float *pb = partial ? p.part + (int64_t)split * ((int64_t)p.M * p.Ncol) : nullptr;
+    auto put4 = [&](Off off, const f32x4 &v) {  // 4 consecutive elements, 16-byte aligned partials
+        if (partial) {
+            *reinterpret_cast<f32x4 *>(pb + off) = v;
+        } else {
+            const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                              f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+            *reinterpret_cast<u32x2 *>(yb + off) = pk;
+        }
+    };
+    auto put1 = [&](Off off, float v) {
+        if (partial)
+            pb[off] = v;
+        else
+            yb[off] = (uint16_t)f32_to_bf16_rne(v);
+    };
     constexpr int QUADS = MF / 16 * (MF / 16);
 #pragma unroll
     for (int a = 0; a < FM; ++a) {
@@ -392,16 +432,14 @@ void conv_igemm_dma_kernel(ConvParams p)
                     if (row >= p.M || col >= p.Ncol)
                         continue;
                     const f32x4 v = quad<MF>(acc[a][b], q) * sc;
-                    uint16_t *dst = yb + (Off)col * p.K + row;
+                    const Off dst = (Off)col * p.K + row;
                     if (vec) {
-                        const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                          f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
-                        *reinterpret_cast<u32x2 *>(dst) = pk;
+                        put4(dst, v);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             if (row + e < p.M)
-                                dst[e] = (uint16_t)f32_to_bf16_rne(v[e]);
+                                put1(dst + e, v[e]);
                     }
                 }
                 continue;
@@ -419,9 +457,7 @@ void conv_igemm_dma_kernel(ConvParams p)
                     continue;
                 const f32x4 v = quad<MF>(acc[a][b], q) * sc;
                 if (vec) {
-                    const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                      f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
-                    *reinterpret_cast<u32x2 *>(yb + ((Off)nimg * p.K + col) * (Off)p.P + sp) = pk;
+                    put4(((Off)nimg * p.K + col) * (Off)p.P + sp, v);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -429,7 +465,7 @@ void conv_igemm_dma_kernel(ConvParams p)
                         if (m < p.M) {
                             const int n2 = m / p.P;
                             const int sp2 = m - n2 * p.P;
-                            yb[((Off)n2 * p.K + col) * (Off)p.P + sp2] = (uint16_t)f32_to_bf16_rne(v[e]);
+                            put1(((Off)n2 * p.K + col) * (Off)p.P + sp2, v[e]);
                         }
                     }
                 }
@@ -469,7 +505,7 @@ void conv_igemm_dma_kernel(ConvParams p)
 template <int DT>
 hipError_t launch_conv_dma128(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream)
 {
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n * p.splits));
     constexpr int KB_ = 128;
     switch (tile) {
     case 21: IGC_DMODES(256, 256, 2, 4, 16, 2);
@@ -486,7 +522,7 @@ hipError_t launch_conv_dma128(const ConvParams &p, int tile, Mode mode, bool big
 template <int DT>
 hipError_t launch_conv_dma_dt(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream)
 {
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n * p.splits));
     constexpr int KB_ = 64;
     if constexpr (DT == DT_BF16) {
         switch (tile) {

@@ -101,6 +101,12 @@ struct ConvParams {
     int wbytes;
     // tap-shared activation windows: input pixels per output row, rows per window
     int win_cols, win_rows;
+    // split reduction (direct-to-LDS kernels): `splits` workgroups per output
+    // tile, split j runs reduction steps [j * ksplit, min(nk, (j + 1) * ksplit))
+    // and stores its unscaled fp32 sums at part + j * (elements of y), indexed
+    // like y; splits == 1: no split, y written directly
+    int splits, ksplit;
+    float *part;
 };
 
 // One launch of the implicit-GEMM kernel selected by (tile, mode, dtype,
@@ -116,6 +122,11 @@ constexpr bool is_buffer(const TileShape &t) { return t.sb > 0; }
 // over the D*H*W positions, reading x untransposed (tiles of 256 positions x
 // 64 output channels: tiles_m = N * ceil(P / 256), tiles_n = ceil(K / 64)).
 hipError_t launch_conv_pw(const ConvParams &p, int variant, hipStream_t stream);
+
+// y[i] = bf16(sum over j < splits of part[j * ynum + i], in order j = 0, 1, ...),
+// times s_x * s_w for fp8 (scales non-null)
+hipError_t launch_splitk_reduce(const float *part, int splits, int64_t ynum, const float *scales, void *y,
+                                hipStream_t stream);
 
 hipError_t launch_amax(const uint16_t *t, int64_t n, float *amax, hipStream_t stream);
 hipError_t launch_fp8_scales(const float *amax, float *pair, hipStream_t stream);

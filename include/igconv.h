@@ -155,6 +155,39 @@ IGC_API int conv_fwd(const void *x, const void *w_packed, void *y, const int64_t
              const float *scales_dev, void *stream);
 
 /*
+ * Forward convolution with a caller-provided device workspace, for output-tile
+ * grids too small to occupy the GPU (few output positions and channels, long
+ * reductions). Same arguments, layouts, result and errors as conv_fwd, plus:
+ *  workspace_dev    device memory owned by the caller, 16-byte aligned, or
+ *                   NULL (then workspace_bytes must be 0); only read and
+ *                   written by work enqueued on `stream` by this call.
+ *  workspace_bytes  its size. When the plan splits the reduction (split-K)
+ *                   into `splits` ranges, each range's fp32 sums take
+ *                   4 * N*K*Do*Ho*Wo bytes; the split count is lowered to what
+ *                   fits, and with room for fewer than two ranges the call
+ *                   runs exactly as conv_fwd.
+ * A split run enqueues two kernels: the conv kernel (one workgroup per tile
+ * and range, unscaled fp32 sums into the workspace) and a pass that adds the
+ * ranges in a fixed order, scales (fp8) and rounds to bf16 into y. Results
+ * are deterministic but may differ from conv_fwd's in the last bit (another
+ * summation order). The split is chosen only where the grid of output tiles
+ * under-fills the GPU, as FlyDSL PR #860's split-K selection does (its rule
+ * that the under-fill test alone decides).
+ */
+IGC_API int conv_fwd_ws(const void *x, const void *w_packed, void *y, const int64_t xshape[5],
+                const int64_t wshape[5], const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3],
+                int dtype, int x_layout, const float *scales_dev, void *workspace_dev, size_t workspace_bytes,
+                void *stream);
+
+/*
+ * Workspace bytes conv_fwd_ws would use for these arguments with unlimited
+ * room: splits * 4 * N*K*Do*Ho*Wo when it splits the reduction, else 0.
+ * Negative status (as conv_fwd) for invalid arguments. Host only.
+ */
+IGC_API int64_t conv_fwd_workspace_bytes(const int64_t xshape[5], const int64_t wshape[5], const int32_t stride[3],
+                const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout);
+
+/*
  * Describe, without running anything, the path and tile conv_fwd would use
  * for these arguments: writes a one-line text such as
  * "path=generic tile=256x256 waves=8 kstep=64 order=cblock big=0 grid=6752"
@@ -164,6 +197,12 @@ IGC_API int conv_fwd(const void *x, const void *w_packed, void *y, const int64_t
 IGC_API int conv_plan(const int64_t xshape[5], const int64_t wshape[5], const int32_t stride[3], const int32_t pad[3],
               const int32_t dilation[3], int dtype, int x_layout, char *buf, size_t len);
 
+/* As conv_plan, for conv_fwd_ws with a workspace of workspace_bytes (the text
+ * ends with the split count and reduction steps per split). Host only. */
+IGC_API int conv_plan_ws(const int64_t xshape[5], const int64_t wshape[5], const int32_t stride[3],
+                 const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout, size_t workspace_bytes,
+                 char *buf, size_t len);
+
 /*
  * Testing and tuning hook: force the path (IGC_PATH_*), the tile index (-1 =
  * automatic) and the grouped-raster height in tiles (0 = automatic) for later
@@ -171,6 +210,11 @@ IGC_API int conv_plan(const int64_t xshape[5], const int64_t wshape[5], const in
  * not apply to a shape makes conv_fwd return IGC_ERR_UNSUPPORTED.
  */
 IGC_API int conv_debug_force(int path, int tile, int group_m);
+
+/* Testing hook: force the split count of conv_fwd_ws / conv_plan_ws (0 =
+ * automatic, 1 = never split; more is capped by the reduction steps and the
+ * workspace). A split on a tile that cannot split returns IGC_ERR_UNSUPPORTED. */
+IGC_API int conv_debug_force_splits(int splits);
 
 /* Text of the last error on this thread ("" if none). Valid until the next call. */
 IGC_API const char *conv_last_error(void);

@@ -84,8 +84,9 @@ class Fp8Operands:
         assert np.array_equal(self.wq.cpu().numpy(), ref_packed), "fp8 filter codes differ"
 
 
-def run_bf16(x_ncdhw, w, stride, pad, dil, x_layout="NDHWC", out=None):
-    """HIP path for bf16: pack (if needed) + conv, returns y (bf16, GPU)."""
+def run_bf16(x_ncdhw, w, stride, pad, dil, x_layout="NDHWC", out=None, workspace=None):
+    """HIP path for bf16: pack (if needed) + conv, returns y (bf16, GPU). With a
+    workspace tensor the conv goes through conv_fwd_ws (split reduction)."""
     xshape, wshape = tuple(x_ncdhw.shape), tuple(w.shape)
     if out is None:
         out = torch.empty((xshape[0], wshape[0]) + B.conv_out_dims(xshape, wshape, stride, pad, dil),
@@ -102,16 +103,23 @@ def run_bf16(x_ncdhw, w, stride, pad, dil, x_layout="NDHWC", out=None):
         xp = x_ncdhw.permute(0, 2, 3, 4, 1).contiguous()
     else:
         xp = x_ncdhw
-    B.conv_fwd(xp, wp, out, xshape, wshape, stride, pad, dil, B.IGC_BF16, lay)
+    if workspace is None:
+        B.conv_fwd(xp, wp, out, xshape, wshape, stride, pad, dil, B.IGC_BF16, lay)
+    else:
+        B.conv_fwd_ws(xp, wp, out, xshape, wshape, stride, pad, dil, B.IGC_BF16, lay, workspace=workspace)
     torch.cuda.synchronize()
     return out
 
 
-def run_fp8(ops: Fp8Operands, xshape, wshape, stride, pad, dil, out=None):
+def run_fp8(ops: Fp8Operands, xshape, wshape, stride, pad, dil, out=None, workspace=None):
     if out is None:
         out = torch.empty((xshape[0], wshape[0]) + B.conv_out_dims(xshape, wshape, stride, pad, dil),
                           dtype=torch.bfloat16, device=DEV)
-    B.conv_fwd(ops.xq, ops.wq, out, xshape, wshape, stride, pad, dil, B.IGC_FP8_E4M3FN, B.IGC_NDHWC, ops.scales)
+    if workspace is None:
+        B.conv_fwd(ops.xq, ops.wq, out, xshape, wshape, stride, pad, dil, B.IGC_FP8_E4M3FN, B.IGC_NDHWC, ops.scales)
+    else:
+        B.conv_fwd_ws(ops.xq, ops.wq, out, xshape, wshape, stride, pad, dil, B.IGC_FP8_E4M3FN, B.IGC_NDHWC,
+                      ops.scales, workspace=workspace)
     torch.cuda.synchronize()
     return out
 

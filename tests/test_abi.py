@@ -238,3 +238,72 @@ def test_buffer_span_bound_covers_every_tile(geom):
     p = _plan(xs, ws, st, pd, dl)
     assert lo >= 0, "a valid read lies below the tile's buffer base"
     assert hi <= int(p["xspan"]), (hi, p["xspan"])
+
+
+def _plan_ws(x, w, nbytes, st=(1, 1, 1), pd=(1, 1, 1), dl=(1, 1, 1), dt=B.IGC_BF16, lay=B.IGC_NDHWC):
+    return dict(kv.split("=") for kv in B.conv_plan_ws(x, w, st, pd, dl, dt, lay, nbytes).split())
+
+
+def test_split_reduction_plan():
+    c1x, c1w = (1, 64, 4, 16, 16), (64, 64, 3, 3, 3)
+    ynum = 1024 * 64
+    nbytes = B.conv_fwd_workspace_bytes(c1x, c1w, (1, 1, 1), (1, 1, 1), (1, 1, 1), B.IGC_BF16, B.IGC_NDHWC)
+    p = _plan_ws(c1x, c1w, nbytes)
+    # 16 tiles of 64x64, 27 steps: splits of >= 5 steps, at most about 256 workgroups
+    assert (p["tile"], p["grid"], p["nk"]) == ("64x64", "16", "27")
+    s, k = int(p["splits"]), int(p["ksplit"])
+    assert (s, k) == (5, 6) and nbytes == s * ynum * 4
+    assert s * 16 <= 256
+    # conv_fwd (no workspace) never splits; conv_plan describes it
+    assert _plan(c1x, c1w, pd=(1, 1, 1))["splits"] == "1"
+    assert _plan_ws(c1x, c1w, 0)["splits"] == "1"
+    # a workspace for two slices gives two splits, one byte short of two gives none
+    assert _plan_ws(c1x, c1w, 2 * ynum * 4)["splits"] == "2"
+    assert _plan_ws(c1x, c1w, 2 * ynum * 4 - 1)["splits"] == "1"
+    # full grids do not split, and need no workspace
+    big = ((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3))
+    assert B.conv_fwd_workspace_bytes(*big, (1, 1, 1), (1, 1, 1), (1, 1, 1), B.IGC_BF16, B.IGC_NDHWC) == 0
+    assert _plan_ws(*big, 1 << 40)["splits"] == "1"
+    # few reduction steps: no split (temporal c1-like, 3 steps)
+    assert B.conv_fwd_workspace_bytes((1, 64, 4, 16, 16), (64, 64, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1),
+                                      B.IGC_BF16, B.IGC_NDHWC) == 0
+    with pytest.raises(B.IgcError):
+        B.conv_fwd_workspace_bytes((1, 64, 4, 4, 4), (64, 32, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1),
+                                   B.IGC_BF16, B.IGC_NDHWC)
+
+
+def test_forced_splits():
+    c1x, c1w = (1, 64, 4, 16, 16), (64, 64, 3, 3, 3)
+    try:
+        B.conv_debug_force_splits(5)
+        p = _plan_ws(c1x, c1w, 1 << 30)
+        assert (p["splits"], p["ksplit"]) == ("5", "6")  # ceil(27 / 5) = 6 steps, ceil(27 / 6) = 5 splits
+        B.conv_debug_force_splits(4)
+        p = _plan_ws(c1x, c1w, 1 << 30)
+        assert (p["splits"], p["ksplit"]) == ("4", "7")
+        B.conv_debug_force_splits(100)  # capped at one step per split
+        p = _plan_ws(c1x, c1w, 1 << 30)
+        assert (p["splits"], p["ksplit"]) == ("27", "1")
+        B.conv_debug_force_splits(1)
+        assert B.conv_fwd_workspace_bytes(c1x, c1w, (1, 1, 1), (1, 1, 1), (1, 1, 1), B.IGC_BF16, B.IGC_NDHWC) == 0
+        B.conv_debug_force_splits(3)
+        B.conv_debug_force(B.IGC_PATH_AUTO, 29, 0)  # buffer-addressed tile: no split
+        with pytest.raises(B.IgcError) as e:
+            _plan_ws(c1x, c1w, 1 << 30)
+        assert e.value.status == B.IGC_ERR_UNSUPPORTED
+        with pytest.raises(B.IgcError) as e:
+            B.conv_debug_force_splits(-1)
+        assert e.value.status == B.IGC_ERR_INVALID
+    finally:
+        B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)
+        B.conv_debug_force_splits(0)
+
+
+def test_workspace_arguments_checked_before_any_launch():
+    lib = B.load()
+    xs = (B._i64((1, 64, 4, 16, 16), 5), B._i64((64, 64, 3, 3, 3), 5))
+    one = B._i32((1, 1, 1))
+    rc = lib.conv_fwd_ws(16, 32, 48, xs[0], xs[1], one, one, one, B.IGC_BF16, B.IGC_NDHWC, None, None, 64, None)
+    assert rc == B.IGC_ERR_INVALID  # bytes without a workspace
+    rc = lib.conv_fwd_ws(16, 32, 48, xs[0], xs[1], one, one, one, B.IGC_BF16, B.IGC_NDHWC, None, 8, 64, None)
+    assert rc == B.IGC_ERR_ALIGN
