@@ -166,8 +166,19 @@ def out_dims(x_shape, w_shape, stride=(1, 1, 1), pad=(0, 0, 0), dil=(1, 1, 1), x
     return tuple(int(v) for v in out)
 
 
-def conv3d(x, w, stride=(1, 1, 1), pad=(0, 0, 0), dil=(1, 1, 1), x_layout="NCDHW", sx=1.0, sw=1.0):
-    """Full output y (N, K, Do, Ho, Wo) in float64."""
+def _bias64(bias, k):
+    """Per-output-channel bias as float64 (fp32 values widen exactly), or None."""
+    if bias is None:
+        return None
+    b = np.asarray(bias)
+    assert b.shape == (k,), (b.shape, k)
+    return b.astype(np.float64)
+
+
+def conv3d(x, w, stride=(1, 1, 1), pad=(0, 0, 0), dil=(1, 1, 1), x_layout="NCDHW", sx=1.0, sw=1.0, bias=None):
+    """Full output y (N, K, Do, Ho, Wo) in float64. With ``bias`` (K values) each
+    output channel k gets bias[k] added, the bias term of a convolution layer
+    (FlyDSL PR #860 tests its fp8 conv with one, gemm8w test cases)."""
     x = np.ascontiguousarray(x)
     w = np.ascontiguousarray(w)
     assert x.ndim == 5 and w.ndim == 5
@@ -178,12 +189,16 @@ def conv3d(x, w, stride=(1, 1, 1), pad=(0, 0, 0), dil=(1, 1, 1), x_layout="NCDHW
                                _ptr(xs), _ptr(ws), _ptr(st), _ptr(pd), _ptr(dl), _ptr(y))
     if rc:
         raise ValueError(f"oracle_conv3d failed ({rc})")
+    b = _bias64(bias, int(ws[0]))
+    if b is not None:
+        y += b[None, :, None, None, None]
     return y
 
 
 def conv3d_points(x, w, points, stride=(1, 1, 1), pad=(0, 0, 0), dil=(1, 1, 1), x_layout="NCDHW",
-                  sx=1.0, sw=1.0):
-    """y at sampled positions: points is (P, 5) of (n, k, od, oh, ow); returns (P,) float64."""
+                  sx=1.0, sw=1.0, bias=None):
+    """y at sampled positions: points is (P, 5) of (n, k, od, oh, ow); returns (P,) float64
+    (plus bias[k] with a bias, as conv3d)."""
     x = np.ascontiguousarray(x)
     w = np.ascontiguousarray(w)
     pts = _c(points, np.int64).reshape(-1, 5)
@@ -194,6 +209,9 @@ def conv3d_points(x, w, points, stride=(1, 1, 1), pad=(0, 0, 0), dil=(1, 1, 1), 
                                       pts.shape[0], _ptr(y))
     if rc:
         raise ValueError(f"oracle_conv3d_points failed ({rc})")
+    b = _bias64(bias, int(ws[0]))
+    if b is not None:
+        y += b[pts[:, 1]]
     return y
 
 

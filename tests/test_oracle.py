@@ -154,6 +154,36 @@ def test_linearity():
     assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("geom", GEOMS[:4])
+def test_bias_matches_torch(geom):
+    # the bias term of a convolution layer: torch's conv3d with bias (an independent implementation)
+    xs, ws, st, pd, dl = geom
+    x, w = _rand(xs, 12), _rand(ws, 13)
+    b = _rand((ws[0],), 14).astype(np.float32)
+    ref = F.conv3d(torch.from_numpy(x), torch.from_numpy(w), torch.from_numpy(b.astype(np.float64)), stride=st,
+                   padding=pd, dilation=dl).numpy()
+    assert np.allclose(O.conv3d(x, w, st, pd, dl, bias=b), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_bias_closed_forms():
+    xs, ws, st, pd, dl = GEOMS[2]
+    x = _rand(xs, 15)
+    b = np.array([0.5, -3.0, 1.0e3], np.float32)
+    # zero filter: y is the bias of its channel, everywhere, exactly
+    y = O.conv3d(x, np.zeros(ws), st, pd, dl, bias=b)
+    assert np.array_equal(y, np.broadcast_to(b.astype(np.float64)[None, :, None, None, None], y.shape))
+    # with a filter: exactly bias[k] more than without (integer-valued data, every sum exact)
+    xi = np.random.default_rng(16).integers(-2, 3, xs).astype(np.float64)
+    wi = np.random.default_rng(17).integers(-1, 2, ws).astype(np.float64)
+    d = O.conv3d(xi, wi, st, pd, dl, bias=b) - O.conv3d(xi, wi, st, pd, dl)
+    assert np.array_equal(d, np.broadcast_to(b.astype(np.float64)[None, :, None, None, None], d.shape))
+    # sampled points carry the same bias
+    pts = np.array([[0, 0, 0, 0, 0], [1, 2, 1, 3, 1], [1, 1, 0, 2, 2]], np.int64)
+    full = O.conv3d(xi, wi, st, pd, dl, bias=b)
+    got = O.conv3d_points(xi, wi, pts, st, pd, dl, bias=b)
+    assert np.array_equal(got, full[tuple(pts.T)])
+
+
 @pytest.mark.parametrize("layout", ["NCDHW", "NDHWC"])
 def test_point_output_equals_matmul(layout):
     # patch-embed geometry (stride == kernel, pad 0, input == filter extent): y = X . W^T
