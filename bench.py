@@ -189,6 +189,40 @@ def bench_workload(name, steps, warmup, torch, B, I, PL):
     return res
 
 
+def bench_epilogue(steps, warmup, torch, B, I, PL):
+    """The headline conv with the fused epilogue extras (bias + amax of y, conv_fwd_ex)
+    against the plain conv followed by a separate amax pass over y."""
+    wl = I.WORKLOADS["c3"]
+    x, w = I.make(wl, "cuda")
+    xs, ws = wl.x_shape, wl.w_shape
+    y = PL.output(xs, ws, wl.stride, wl.pad, wl.dil, "cuda")
+    wp = PL.packed_weight(w, "bf16", "NDHWC")
+    bias = torch.randn(ws[0], generator=I.generator(33, "cuda"), device="cuda", dtype=torch.float32)
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    args = (xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
+
+    def fused():
+        B.conv_fwd_ex(x, wp, y, *args, bias=bias, y_amax=amax)
+
+    def plain():
+        B.conv_fwd(x, wp, y, *args)
+
+    def separate():
+        plain()
+        B.conv_amax(y, y.numel(), amax)
+
+    res = {"workload": wl.note + " + bias + amax(y)"}
+    for key, fn in (("fused", fused), ("plain", plain), ("separate", separate)):
+        st = {}
+        _, ev = time_launches(fn, steps, warmup, torch, st)
+        res.update({f"{key}_ms": ev, f"{key}_ms_median": st["median"]})
+    _, ev_a = time_launches(lambda: B.conv_amax(y, y.numel(), amax), steps, warmup, torch)
+    res.update(amax_pass_ms=ev_a, amax_pass_gbs=2 * y.numel() / (ev_a * 1e-3) / 1e9)
+    del x, w, y, wp
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(seconds: float, I):
     """The fp64 oracle on a bounded random sample of the headline workload's outputs."""
     import numpy as np
@@ -247,7 +281,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", default=None, help="comma list of extra workloads (c1,c2,c4,c4t,c5,pw)")
+    ap.add_argument("--only", default=None, help="comma list of extra workloads (c1,c2,c4,c4t,c5,pw,c3ex)")
     ap.add_argument("--profile", action="store_true",
                     help="counter-collection run: the headline conv `steps` times, then one 1 GiB device copy "
                          "(the reference for scaling FETCH_SIZE / WRITE_SIZE); prints nothing else")
@@ -290,10 +324,13 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        names = args.only.split(",") if args.only else ["c1", "c2", "c4", "c4t", "c5", "pw"]
+        names = args.only.split(",") if args.only else ["c1", "c2", "c4", "c4t", "c5", "pw", "c3ex"]
         for name in names:
             log(f"[bench] extra workload {name}")
-            extra[name] = bench_workload(name, max(5, args.steps // 2), args.warmup, torch, B, I, PL)
+            if name == "c3ex":
+                extra[name] = bench_epilogue(max(5, args.steps // 2), args.warmup, torch, B, I, PL)
+            else:
+                extra[name] = bench_workload(name, max(5, args.steps // 2), args.warmup, torch, B, I, PL)
             log(f"[bench] {name}: {json.dumps(extra[name])}")
 
     cpu = None

@@ -27,7 +27,7 @@ IGC_NCDHW, IGC_NDHWC = 0, 1
 IGC_PATH_AUTO, IGC_PATH_GENERIC, IGC_PATH_TEMPORAL, IGC_PATH_POINT, IGC_PATH_POINTWISE = 0, 1, 2, 3, 4
 
 EXPORTS = ("conv_out_dims", "conv_packed_w_cols", "conv_amax", "conv_fp8_scales", "conv_pack_x", "conv_pack_w",
-           "conv_fwd", "conv_fwd_ws", "conv_fwd_workspace_bytes", "conv_plan", "conv_plan_ws", "conv_debug_force",
+           "conv_fwd", "conv_fwd_ws", "conv_fwd_ex", "conv_fwd_workspace_bytes", "conv_plan", "conv_plan_ws", "conv_debug_force",
            "conv_debug_force_splits", "conv_last_error")
 
 
@@ -58,6 +58,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.conv_fwd.argtypes = [P, P, P, P, P, P, P, P, I32, I32, P, P]
         lib.conv_plan.argtypes = [P, P, P, P, P, I32, I32, ctypes.c_char_p, ctypes.c_size_t]
         lib.conv_fwd_ws.argtypes = [P, P, P, P, P, P, P, P, I32, I32, P, P, ctypes.c_size_t, P]
+        lib.conv_fwd_ex.argtypes = [P, P, P, P, P, P, P, P, I32, I32, P, P, P, P, ctypes.c_size_t, P]
         lib.conv_fwd_workspace_bytes.argtypes = [P, P, P, P, P, I32, I32]
         lib.conv_fwd_workspace_bytes.restype = I64
         lib.conv_plan_ws.argtypes = [P, P, P, P, P, I32, I32, ctypes.c_size_t, ctypes.c_char_p, ctypes.c_size_t]
@@ -156,6 +157,20 @@ def conv_fwd_ws(x, w_packed, y, xshape, wshape, stride, pad, dilation, dtype, x_
     _check("conv_fwd_ws", load().conv_fwd_ws(_dev(x), _dev(w_packed), _dev(y), _i64(xshape, 5), _i64(wshape, 5),
                                              _i32(stride), _i32(pad), _i32(dilation), int(dtype), int(x_layout),
                                              _dev(scales_dev), _dev(workspace), nbytes, _stream(stream, y)))
+
+
+def conv_fwd_ex(x, w_packed, y, xshape, wshape, stride, pad, dilation, dtype, x_layout, scales_dev=None,
+                bias=None, y_amax=None, workspace=None, workspace_bytes=None, stream=None):
+    """conv_fwd with fused extras: fp32 bias[K] before rounding, max |y| into y_amax (fp32[1])."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace_bytes is not None:
+        if int(workspace_bytes) > nbytes:
+            raise ValueError(f"workspace_bytes {workspace_bytes} exceeds the workspace tensor ({nbytes} bytes)")
+        nbytes = int(workspace_bytes)
+    _check("conv_fwd_ex", load().conv_fwd_ex(_dev(x), _dev(w_packed), _dev(y), _i64(xshape, 5), _i64(wshape, 5),
+                                             _i32(stride), _i32(pad), _i32(dilation), int(dtype), int(x_layout),
+                                             _dev(scales_dev), _dev(bias), _dev(y_amax), _dev(workspace), nbytes,
+                                             _stream(stream, y)))
 
 
 def conv_fwd_workspace_bytes(xshape, wshape, stride, pad, dilation, dtype, x_layout) -> int:

@@ -563,9 +563,10 @@ int conv_pack_w(const void *w_kctrs_bf16, void *w_packed, const int64_t wshape[5
     return ok();
 }
 
-int conv_fwd_ws(const void *x, const void *w_packed, void *y, const int64_t xshape[5], const int64_t wshape[5],
+int conv_fwd_ex(const void *x, const void *w_packed, void *y, const int64_t xshape[5], const int64_t wshape[5],
                 const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout,
-                const float *scales_dev, void *workspace_dev, size_t workspace_bytes, void *stream)
+                const float *scales_dev, const float *bias_dev, float *y_amax_dev, void *workspace_dev,
+                size_t workspace_bytes, void *stream)
 {
     Plan pl;
     int rc = make_plan(xshape, wshape, stride, pad, dilation, dtype, x_layout, pl);
@@ -581,6 +582,8 @@ int conv_fwd_ws(const void *x, const void *w_packed, void *y, const int64_t xsha
         return fail(IGC_ERR_INVALID, "conv_fwd_ws: null workspace with workspace_bytes = %zu", workspace_bytes);
     if (workspace_dev && !aligned16(workspace_dev))
         return fail(IGC_ERR_ALIGN, "conv_fwd_ws: workspace must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(bias_dev) | reinterpret_cast<uintptr_t>(y_amax_dev)) & 3u)
+        return fail(IGC_ERR_ALIGN, "conv_fwd_ex: bias and amax must be 4-byte aligned fp32");
     rc = plan_splits(pl, workspace_dev ? workspace_bytes : 0);
     if (rc < 0)
         return rc;
@@ -589,15 +592,26 @@ int conv_fwd_ws(const void *x, const void *w_packed, void *y, const int64_t xsha
     pl.p.y = y;
     pl.p.scales = dtype == IGC_FP8_E4M3FN ? scales_dev : nullptr;
     pl.p.part = pl.p.splits > 1 ? static_cast<float *>(workspace_dev) : nullptr;
+    pl.p.bias = bias_dev;
+    pl.p.amax = reinterpret_cast<unsigned *>(y_amax_dev);
     const Mode mode = pl.path == IGC_PATH_POINT ? MODE_POINT : (pl.path == IGC_PATH_TEMPORAL ? MODE_TEMPORAL : MODE_GENERIC);
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (y_amax_dev && launch_amax_zero(y_amax_dev, st) != hipSuccess)
+        return fail(IGC_ERR_HIP, "conv_fwd_ex: amax clear launch failed");
     if (launch_conv(pl.p, pl.tile, mode, dtype == IGC_FP8_E4M3FN ? DT_FP8 : DT_BF16, pl.big, pl.cblock, st) !=
         hipSuccess)
         return fail(IGC_ERR_HIP, "conv_fwd: kernel launch failed");
-    if (pl.p.splits > 1 &&
-        launch_splitk_reduce(pl.p.part, pl.p.splits, (int64_t)pl.p.M * pl.p.Ncol, pl.p.scales, y, st) != hipSuccess)
+    if (pl.p.splits > 1 && launch_splitk_reduce(pl.p, st) != hipSuccess)
         return fail(IGC_ERR_HIP, "conv_fwd_ws: split reduction launch failed");
     return ok();
+}
+
+int conv_fwd_ws(const void *x, const void *w_packed, void *y, const int64_t xshape[5], const int64_t wshape[5],
+                const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout,
+                const float *scales_dev, void *workspace_dev, size_t workspace_bytes, void *stream)
+{
+    return conv_fwd_ex(x, w_packed, y, xshape, wshape, stride, pad, dilation, dtype, x_layout, scales_dev, nullptr,
+                       nullptr, workspace_dev, workspace_bytes, stream);
 }
 
 int conv_fwd(const void *x, const void *w_packed, void *y, const int64_t xshape[5], const int64_t wshape[5],

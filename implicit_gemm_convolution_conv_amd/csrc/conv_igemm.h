@@ -93,6 +93,70 @@ __device__ inline uint32_t f32_to_bf16_rne(float f)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Output transform of every epilogue: y = bf16(acc * scale + bias[k]), the
+// scale s_x * s_w for fp8 and 1 for bf16, the bias (fp32, one per output
+// channel) only when given. With p.amax set it also keeps the running maximum
+// of |y| over the values this lane stores (non-negative floats order like
+// their bits, so the maximum of bf16 bits & 0x7fff) and flush() merges the
+// wave's maximum into *p.amax as fp32 bits.
+struct Epilogue {
+    float sc;
+    const float *bias;
+    unsigned *amax;
+    unsigned m = 0;
+
+    __device__ Epilogue(const ConvParams &p, bool fp8)
+        : sc(fp8 ? p.scales[0] * p.scales[2] : 1.0f), bias(p.bias), amax(p.amax) {}
+
+    // bf16 bits of the output of channel k
+    __device__ uint32_t one(float acc, int k)
+    {
+        float v = acc * sc;
+        if (bias)
+            v += bias[k];
+        const uint32_t r = f32_to_bf16_rne(v);
+        if (amax)
+            m = max(m, r & 0x7fffu);
+        return r;
+    }
+    // four outputs of channel k, packed for one 8-byte store
+    __device__ u32x2 four(const f32x4 &acc, int k)
+    {
+        const float b = bias ? bias[k] : 0.0f;
+        uint32_t r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v = acc[e] * sc;
+            if (bias)
+                v += b;
+            r[e] = f32_to_bf16_rne(v);
+            if (amax)
+                m = max(m, r[e] & 0x7fffu);
+        }
+        return u32x2{r[0] | (r[1] << 16), r[2] | (r[3] << 16)};
+    }
+    // four outputs of channels k .. k + 3 (point output: channels are the rows)
+    __device__ u32x2 four_channels(const f32x4 &acc, int k)
+    {
+        uint32_t r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            r[e] = one(acc[e], k + e);
+        return u32x2{r[0] | (r[1] << 16), r[2] | (r[3] << 16)};
+    }
+    // every lane of the wave calls this once, after its last store
+    __device__ void flush()
+    {
+        if (!amax)
+            return;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            m = max(m, (unsigned)__shfl_xor((int)m, off));
+        if ((threadIdx.x & 63) == 0)
+            atomicMax(amax, m << 16);
+    }
+};
+
 template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, bool BIG, bool CBLK>
 __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void conv_igemm_kernel(ConvParams p)
@@ -398,9 +462,7 @@ void conv_igemm_kernel(ConvParams p)
 
     // ---------------------------------------------------------------- epilogue
     // Each lane holds groups of 4 consecutive GEMM rows of one column ("quads").
-    float sc = 1.0f;
-    if constexpr (DT == DT_FP8)
-        sc = p.scales[0] * p.scales[2];
+    Epilogue ep(p, DT == DT_FP8);
     uint16_t *yb = static_cast<uint16_t *>(p.y);
     constexpr int QUADS = MF / 16 * (MF / 16);  // 1 (16x16) or 4 (32x32) per block
 #pragma unroll
@@ -421,11 +483,9 @@ void conv_igemm_kernel(ConvParams p)
                     const int col = n0 + wn * WTN + b * MF + lrow;  // output channel
                     if (row >= p.M || col >= p.K)
                         continue;
-                    const f32x4 v = quad<MF>(acc[a][b], q) * sc;
+                    const f32x4 v = quad<MF>(acc[a][b], q);
                     if (vec) {
-                        const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                          f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
-                        *reinterpret_cast<u32x2 *>(yb + ((Off)nimg * p.K + col) * (Off)p.P + sp) = pk;
+                        *reinterpret_cast<u32x2 *>(yb + ((Off)nimg * p.K + col) * (Off)p.P + sp) = ep.four(v, col);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -433,7 +493,7 @@ void conv_igemm_kernel(ConvParams p)
                             if (m < p.M) {
                                 const int n2 = m / p.P;
                                 const int sp2 = m - n2 * p.P;
-                                yb[((Off)n2 * p.K + col) * (Off)p.P + sp2] = (uint16_t)f32_to_bf16_rne(v[e]);
+                                yb[((Off)n2 * p.K + col) * (Off)p.P + sp2] = (uint16_t)ep.one(v[e], col);
                             }
                         }
                     }
@@ -446,22 +506,21 @@ void conv_igemm_kernel(ConvParams p)
                     const int col = n0 + wn * WTN + b * MF + lrow;  // image
                     if (row >= p.M || col >= p.Ncol)
                         continue;
-                    const f32x4 v = quad<MF>(acc[a][b], q) * sc;
+                    const f32x4 v = quad<MF>(acc[a][b], q);
                     uint16_t *dst = yb + (Off)col * p.K + row;
                     if (vec) {
-                        const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                          f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
-                        *reinterpret_cast<u32x2 *>(dst) = pk;
+                        *reinterpret_cast<u32x2 *>(dst) = ep.four_channels(v, row);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             if (row + e < p.M)
-                                dst[e] = (uint16_t)f32_to_bf16_rne(v[e]);
+                                dst[e] = (uint16_t)ep.one(v[e], row + e);
                     }
                 }
             }
         }
     }
+    ep.flush();
 }
 
 // Launch helper for one dtype: picks the instantiation for (tile, mode, big, cblock).

@@ -244,16 +244,15 @@ __device__ inline void mfma_acc(const FragT<DT> &af, const FragT<DT> &bf, typena
 }
 
 // Epilogue: one wave's FM x FN MFMA blocks of the tile at (row0, col0) to bf16
-// NCDHW y, scaled by s_x * s_w for fp8. Four consecutive rows of one column
-// go out as one 8-byte store when they share an image and P % 4 == 0.
+// NCDHW y through Epilogue (scale s_x * s_w for fp8, bias, amax). Four
+// consecutive rows of one column go out as one 8-byte store when they share
+// an image and P % 4 == 0.
 template <int MF, int FM, int FN, int DT>
 __device__ inline void store_tile_ncdhw(const typename AccType<MF>::type (&acc)[FM][FN], const ConvParams &p,
                                         int row0, int col0, int lane)
 {
     const int lrow = lane & (MF - 1), lgrp = lane / MF;
-    float sc = 1.0f;
-    if constexpr (DT == DT_FP8)
-        sc = p.scales[0] * p.scales[2];
+    Epilogue ep(p, DT == DT_FP8);
     uint16_t *yb = static_cast<uint16_t *>(p.y);
     constexpr int QUADS = MF / 16 * (MF / 16);
 #pragma unroll
@@ -272,11 +271,9 @@ __device__ inline void store_tile_ncdhw(const typename AccType<MF>::type (&acc)[
                 const int col = col0 + b * MF + lrow;
                 if (row >= p.M || col >= p.K)
                     continue;
-                const f32x4 v = quad<MF>(acc[a][b], q) * sc;
+                const f32x4 v = quad<MF>(acc[a][b], q);
                 if (vec) {
-                    const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                      f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
-                    *reinterpret_cast<u32x2 *>(yb + ((int64_t)nimg * p.K + col) * p.P + sp) = pk;
+                    *reinterpret_cast<u32x2 *>(yb + ((int64_t)nimg * p.K + col) * p.P + sp) = ep.four(v, col);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -284,13 +281,14 @@ __device__ inline void store_tile_ncdhw(const typename AccType<MF>::type (&acc)[
                         if (m < p.M) {
                             const int n2 = m / p.P;
                             const int sp2 = m - n2 * p.P;
-                            yb[((int64_t)n2 * p.K + col) * p.P + sp2] = (uint16_t)f32_to_bf16_rne(v[e]);
+                            yb[((int64_t)n2 * p.K + col) * p.P + sp2] = (uint16_t)ep.one(v[e], col);
                         }
                     }
                 }
             }
         }
     }
+    ep.flush();
 }
 
 template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, int SA, int SB, int KB, int SPREAD, int PF = 1,

@@ -393,29 +393,28 @@ void conv_igemm_dma_kernel(ConvParams p)
     }
 
     // ---------------------------------------------------------------- epilogue
-    // y = bf16(acc * scale); a split workgroup stores its fp32 sums unscaled
-    // at the same element offsets of its slice of the partial buffer.
+    // y = bf16(acc * scale + bias) (Epilogue); a split workgroup stores its
+    // raw fp32 sums at the same element offsets of its slice of the partial
+    // buffer, and the reduction pass applies scale, bias and amax.
     const bool partial = p.splits > 1;
-    float sc = 1.0f;
-    if constexpr (DT == DT_FP8)
-        if (!partial)
-            sc = p.scales[0] * p.scales[2];
+    Epilogue ep(p, DT == DT_FP8 && !partial);
     uint16_t *yb = static_cast<uint16_t *>(p.y);
     float *pb = partial ? p.part + (int64_t)split * ((int64_t)p.M * p.Ncol) : nullptr;
-    auto put4 = [&](Off off, const f32x4 &v) {  // 4 consecutive elements, 16-byte aligned partials
-        if (partial) {
+    // 4 consecutive elements from off (16-byte aligned partials): 4 positions of
+    // channel k, or channels k .. k + 3 in point mode
+    auto put4 = [&](Off off, const f32x4 &v, int k) {
+        if (partial)
             *reinterpret_cast<f32x4 *>(pb + off) = v;
-        } else {
-            const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                              f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
-            *reinterpret_cast<u32x2 *>(yb + off) = pk;
-        }
+        else if constexpr (MODE == MODE_POINT)
+            *reinterpret_cast<u32x2 *>(yb + off) = ep.four_channels(v, k);
+        else
+            *reinterpret_cast<u32x2 *>(yb + off) = ep.four(v, k);
     };
-    auto put1 = [&](Off off, float v) {
+    auto put1 = [&](Off off, float v, int k) {
         if (partial)
             pb[off] = v;
         else
-            yb[off] = (uint16_t)f32_to_bf16_rne(v);
+            yb[off] = (uint16_t)ep.one(v, k);
     };
     constexpr int QUADS = MF / 16 * (MF / 16);
 #pragma unroll
@@ -431,15 +430,15 @@ void conv_igemm_dma_kernel(ConvParams p)
                     const int col = n0 + wn * WTN + b * MF + lrow;
                     if (row >= p.M || col >= p.Ncol)
                         continue;
-                    const f32x4 v = quad<MF>(acc[a][b], q) * sc;
+                    const f32x4 v = quad<MF>(acc[a][b], q);
                     const Off dst = (Off)col * p.K + row;
                     if (vec) {
-                        put4(dst, v);
+                        put4(dst, v, row);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             if (row + e < p.M)
-                                put1(dst + e, v[e]);
+                                put1(dst + e, v[e], row + e);
                     }
                 }
                 continue;
@@ -455,9 +454,9 @@ void conv_igemm_dma_kernel(ConvParams p)
                 const int col = n0 + wn * WTN + b * MF + lrow;
                 if (row >= p.M || col >= p.K)
                     continue;
-                const f32x4 v = quad<MF>(acc[a][b], q) * sc;
+                const f32x4 v = quad<MF>(acc[a][b], q);
                 if (vec) {
-                    put4(((Off)nimg * p.K + col) * (Off)p.P + sp, v);
+                    put4(((Off)nimg * p.K + col) * (Off)p.P + sp, v, col);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -465,13 +464,15 @@ void conv_igemm_dma_kernel(ConvParams p)
                         if (m < p.M) {
                             const int n2 = m / p.P;
                             const int sp2 = m - n2 * p.P;
-                            put1(((Off)n2 * p.K + col) * (Off)p.P + sp2, v[e]);
+                            put1(((Off)n2 * p.K + col) * (Off)p.P + sp2, v[e], col);
                         }
                     }
                 }
             }
         }
     }
+    if (!partial)
+        ep.flush();
 }
 
 #define IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_, BIG_, CBLK_)                                              \

@@ -233,9 +233,7 @@ void conv_win_kernel(ConvParams p)
     }
 
     // ---------------------------------------------------------------- epilogue
-    float sc = 1.0f;
-    if constexpr (DT == DT_FP8)
-        sc = p.scales[0] * p.scales[2];
+    Epilogue ep(p, DT == DT_FP8);
     uint16_t *yb = static_cast<uint16_t *>(p.y);
     constexpr int QUADS = MF / 16 * (MF / 16);
     const Off ybase = ((Off)nimg * p.K) * (Off)p.P + (Off)od * P2;  // + k * P + q
@@ -250,21 +248,20 @@ void conv_win_kernel(ConvParams p)
                 const int col = n0 + wn * WTN + b * MF + lrow;
                 if (q >= qend || col >= p.K)
                     continue;
-                const f32x4 v = quad<MF>(acc[a][b], qd) * sc;
+                const f32x4 v = quad<MF>(acc[a][b], qd);
                 uint16_t *dst = yb + ybase + (Off)col * p.P + q;
                 if (vec) {
-                    const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                      f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
-                    *reinterpret_cast<u32x2 *>(dst) = pk;
+                    *reinterpret_cast<u32x2 *>(dst) = ep.four(v, col);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         if (q + e < qend)
-                            dst[e] = (uint16_t)f32_to_bf16_rne(v[e]);
+                            dst[e] = (uint16_t)ep.one(v[e], col);
                 }
             }
         }
     }
+    ep.flush();
 }
 
 template <int DT>

@@ -168,6 +168,7 @@ __global__ __launch_bounds__(256) void conv_pw_ncdhw_kernel(ConvParams p)
     }
 
     // y[n][k][s]: lane holds positions 4*lgrp..+3 of each 16-row block for output channel lrow of each column block
+    Epilogue ep(p, false);
     uint16_t *yb = static_cast<uint16_t *>(p.y);
 #pragma unroll
     for (int b = 0; b < SB; ++b) {
@@ -179,12 +180,10 @@ __global__ __launch_bounds__(256) void conv_pw_ncdhw_kernel(ConvParams p)
             const int k = k0 + 16 * kb + lrow;
             if (k >= K)
                 continue;
-            const f32x4 v = acc[b][kb];
-            const u32x2 pk = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                              f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
-            *reinterpret_cast<u32x2 *>(yb + ((int64_t)n * K + k) * S + s) = pk;
+            *reinterpret_cast<u32x2 *>(yb + ((int64_t)n * K + k) * S + s) = ep.four(acc[b][kb], k);
         }
     }
+    ep.flush();
 }
 
 }  // namespace

@@ -107,6 +107,11 @@ struct ConvParams {
     // like y; splits == 1: no split, y written directly
     int splits, ksplit;
     float *part;
+    // fused epilogue extras (null = off): fp32 bias per output channel added
+    // before rounding; max |y| merged into *amax as fp32 bits (zeroed before
+    // the launch)
+    const float *bias;
+    unsigned *amax;
 };
 
 // One launch of the implicit-GEMM kernel selected by (tile, mode, dtype,
@@ -123,10 +128,12 @@ constexpr bool is_buffer(const TileShape &t) { return t.sb > 0; }
 // 64 output channels: tiles_m = N * ceil(P / 256), tiles_n = ceil(K / 64)).
 hipError_t launch_conv_pw(const ConvParams &p, int variant, hipStream_t stream);
 
-// y[i] = bf16(sum over j < splits of part[j * ynum + i], in order j = 0, 1, ...),
-// times s_x * s_w for fp8 (scales non-null)
-hipError_t launch_splitk_reduce(const float *part, int splits, int64_t ynum, const float *scales, void *y,
-                                hipStream_t stream);
+// y[i] = bf16(sum over j < splits of part[j * ynum + i], in order j = 0, 1, ...
+// times s_x * s_w for fp8 (scales non-null) plus the bias of i's channel),
+// ynum = M * Ncol; the amax of y as in the conv epilogues;
+// in point-output layout (y[n][k], K per row) channel = i % K, else (i / P) % K
+hipError_t launch_splitk_reduce(const ConvParams &p, hipStream_t stream);
+hipError_t launch_amax_zero(float *amax, hipStream_t stream);
 
 hipError_t launch_amax(const uint16_t *t, int64_t n, float *amax, hipStream_t stream);
 hipError_t launch_fp8_scales(const float *amax, float *pair, hipStream_t stream);

@@ -180,6 +180,25 @@ IGC_API int conv_fwd_ws(const void *x, const void *w_packed, void *y, const int6
                 void *stream);
 
 /*
+ * Forward convolution with fused epilogue extras; otherwise as conv_fwd_ws
+ * (workspace_dev NULL and workspace_bytes 0: as conv_fwd).
+ *  bias_dev    NULL, or device fp32[K]: y = bf16(acc * (s_x * s_w) + bias[k])
+ *              (bf16: bf16(acc + bias[k])), the bias added in fp32 before the
+ *              one rounding. FlyDSL PR #860 tests its fp8 conv with a bias
+ *              (PR summary, the gemm8w test cases).
+ *  y_amax_dev  NULL, or device fp32[1]: receives max |y| over the bf16 values
+ *              written to y (the per-tensor amax conv_amax would compute on
+ *              y, as the input of a next fp8 convolution's conv_fp8_scales),
+ *              without a second pass over y. It is cleared on `stream` first.
+ * Both must be 4-byte aligned. The amax is merged with atomic maxima of
+ * fp32 bit patterns: calls that share y_amax_dev must not overlap.
+ */
+IGC_API int conv_fwd_ex(const void *x, const void *w_packed, void *y, const int64_t xshape[5],
+                const int64_t wshape[5], const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3],
+                int dtype, int x_layout, const float *scales_dev, const float *bias_dev, float *y_amax_dev,
+                void *workspace_dev, size_t workspace_bytes, void *stream);
+
+/*
  * Workspace bytes conv_fwd_ws would use for these arguments with unlimited
  * room: splits * 4 * N*K*Do*Ho*Wo when it splits the reduction, else 0.
  * Negative status (as conv_fwd) for invalid arguments. Host only.

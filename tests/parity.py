@@ -84,9 +84,10 @@ class Fp8Operands:
         assert np.array_equal(self.wq.cpu().numpy(), ref_packed), "fp8 filter codes differ"
 
 
-def run_bf16(x_ncdhw, w, stride, pad, dil, x_layout="NDHWC", out=None, workspace=None):
+def run_bf16(x_ncdhw, w, stride, pad, dil, x_layout="NDHWC", out=None, workspace=None, bias=None, amax=None):
     """HIP path for bf16: pack (if needed) + conv, returns y (bf16, GPU). With a
-    workspace tensor the conv goes through conv_fwd_ws (split reduction)."""
+    workspace tensor the conv goes through conv_fwd_ws (split reduction), with a
+    bias (fp32 [K]) or an amax output (fp32 [1]) through conv_fwd_ex."""
     xshape, wshape = tuple(x_ncdhw.shape), tuple(w.shape)
     if out is None:
         out = torch.empty((xshape[0], wshape[0]) + B.conv_out_dims(xshape, wshape, stride, pad, dil),
@@ -103,7 +104,10 @@ def run_bf16(x_ncdhw, w, stride, pad, dil, x_layout="NDHWC", out=None, workspace
         xp = x_ncdhw.permute(0, 2, 3, 4, 1).contiguous()
     else:
         xp = x_ncdhw
-    if workspace is None:
+    if bias is not None or amax is not None:
+        B.conv_fwd_ex(xp, wp, out, xshape, wshape, stride, pad, dil, B.IGC_BF16, lay, bias=bias, y_amax=amax,
+                      workspace=workspace)
+    elif workspace is None:
         B.conv_fwd(xp, wp, out, xshape, wshape, stride, pad, dil, B.IGC_BF16, lay)
     else:
         B.conv_fwd_ws(xp, wp, out, xshape, wshape, stride, pad, dil, B.IGC_BF16, lay, workspace=workspace)
@@ -111,11 +115,14 @@ def run_bf16(x_ncdhw, w, stride, pad, dil, x_layout="NDHWC", out=None, workspace
     return out
 
 
-def run_fp8(ops: Fp8Operands, xshape, wshape, stride, pad, dil, out=None, workspace=None):
+def run_fp8(ops: Fp8Operands, xshape, wshape, stride, pad, dil, out=None, workspace=None, bias=None, amax=None):
     if out is None:
         out = torch.empty((xshape[0], wshape[0]) + B.conv_out_dims(xshape, wshape, stride, pad, dil),
                           dtype=torch.bfloat16, device=DEV)
-    if workspace is None:
+    if bias is not None or amax is not None:
+        B.conv_fwd_ex(ops.xq, ops.wq, out, xshape, wshape, stride, pad, dil, B.IGC_FP8_E4M3FN, B.IGC_NDHWC,
+                      ops.scales, bias=bias, y_amax=amax, workspace=workspace)
+    elif workspace is None:
         B.conv_fwd(ops.xq, ops.wq, out, xshape, wshape, stride, pad, dil, B.IGC_FP8_E4M3FN, B.IGC_NDHWC, ops.scales)
     else:
         B.conv_fwd_ws(ops.xq, ops.wq, out, xshape, wshape, stride, pad, dil, B.IGC_FP8_E4M3FN, B.IGC_NDHWC,
