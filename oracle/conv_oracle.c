@@ -19,6 +19,14 @@
  *                                          ow*sw-pw+s*dw) * W(k,c,t,r,s)
  *    with X = 0 outside the input box. Seven nested loops, fp64 accumulation,
  *    int64 indices.
+ *  - the two gradients of that map, which MIOpen PR #10912 turns into one GEMM
+ *    each for point-output shapes (backward data and backward weights, PR
+ *    body): with y = conv(x, w) and an incoming gradient dy of y's shape,
+ *        dx[n,c,d,h,w] = sum of dy[n,k,od,oh,ow] * W(k,c,t,r,s) over every
+ *                        (k, od, oh, ow, t, r, s) whose tap reads (d, h, w)
+ *        dw[k,c,t,r,s] = sum over (n, od, oh, ow) of dy[n,k,od,oh,ow] *
+ *                        X(n,c,od*sd-pd+t*dd, oh*sh-ph+r*dh, ow*sw-pw+s*dw)
+ *    (the adjoints of the forward map in x and in w), fp64, for any geometry.
  *  - the operand encodings the pages use: bf16 (top half of binary32, round to
  *    nearest even) and OCP fp8 E4M3FN (sign, 4-bit exponent with bias 7, 3-bit
  *    mantissa, subnormals, no infinities, S.1111.111 = NaN, max finite 448),
@@ -305,6 +313,102 @@ int oracle_conv3d_points(int xkind, const void *x, int xlayout, double sx, int w
         const int64_t *q = pts + 5 * i;
         y[i] = conv_point(&p, q[0], q[1], q[2], q[3], q[4]);
     }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gradients                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* dy element (NCDHW, N x K x Do x Ho x Wo) */
+static double dy_at(const conv_problem *p, int dykind, const void *dy, int64_t n, int64_t k, int64_t od, int64_t oh,
+                    int64_t ow)
+{
+    return operand(dykind, dy, (((n * p->K + k) * p->Do + od) * p->Ho + oh) * p->Wo + ow, 1.0);
+}
+
+/* Output index o that a tap at offset tap*dil reads input index i from: o*st - pad + tap*dil == i. */
+static int64_t tap_source(int64_t i, int64_t tap, int64_t st, int64_t pad, int64_t dil, int64_t out)
+{
+    int64_t num = i + pad - tap * dil;
+    if (num < 0 || num % st != 0 || num / st >= out)
+        return -1;
+    return num / st;
+}
+
+/*
+ * Gradient with respect to x: dx (N, C, D, H, W) in the layout xlayout. Every
+ * input element gathers the dy elements whose receptive field reads it.
+ */
+int oracle_conv3d_bwd_data(int dykind, const void *dy, int wkind, const void *w, int xlayout, const int64_t xs[5],
+                           const int64_t ws[5], const int32_t st[3], const int32_t pad[3], const int32_t dil[3],
+                           double *dx)
+{
+    conv_problem p;
+    if (setup(&p, ORACLE_F64, 0, xlayout, 1.0, wkind, w, 1.0, xs, ws, st, pad, dil))
+        return -1;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t n = 0; n < p.N; ++n)
+        for (int64_t c = 0; c < p.C; ++c)
+            for (int64_t d = 0; d < p.D; ++d)
+                for (int64_t h = 0; h < p.H; ++h)
+                    for (int64_t x = 0; x < p.W; ++x) {
+                        double acc = 0.0;
+                        for (int64_t k = 0; k < p.K; ++k)
+                            for (int64_t t = 0; t < p.T; ++t) {
+                                int64_t od = tap_source(d, t, p.sd, p.pd, p.dd, p.Do);
+                                if (od < 0)
+                                    continue;
+                                for (int64_t r = 0; r < p.R; ++r) {
+                                    int64_t oh = tap_source(h, r, p.sh, p.ph, p.dh, p.Ho);
+                                    if (oh < 0)
+                                        continue;
+                                    for (int64_t s = 0; s < p.S; ++s) {
+                                        int64_t ow = tap_source(x, s, p.sw_, p.pw, p.dw, p.Wo);
+                                        if (ow < 0)
+                                            continue;
+                                        int64_t wi = (((k * p.C + c) * p.T + t) * p.R + r) * p.S + s;
+                                        acc += dy_at(&p, dykind, dy, n, k, od, oh, ow) * operand(p.wkind, w, wi, 1.0);
+                                    }
+                                }
+                            }
+                        dx[x_index(&p, n, c, d, h, x)] = acc;
+                    }
+    return 0;
+}
+
+/*
+ * Gradient with respect to w: dw (K, C, T, R, S). Every filter element sums
+ * dy times the input element its tap reads, over images and output positions.
+ */
+int oracle_conv3d_bwd_weight(int xkind, const void *x, int xlayout, int dykind, const void *dy, const int64_t xs[5],
+                             const int64_t ws[5], const int32_t st[3], const int32_t pad[3], const int32_t dil[3],
+                             double *dw)
+{
+    conv_problem p;
+    if (setup(&p, xkind, x, xlayout, 1.0, ORACLE_F64, 0, 1.0, xs, ws, st, pad, dil))
+        return -1;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t k = 0; k < p.K; ++k)
+        for (int64_t c = 0; c < p.C; ++c)
+            for (int64_t t = 0; t < p.T; ++t)
+                for (int64_t r = 0; r < p.R; ++r)
+                    for (int64_t s = 0; s < p.S; ++s) {
+                        double acc = 0.0;
+                        for (int64_t n = 0; n < p.N; ++n)
+                            for (int64_t od = 0; od < p.Do; ++od)
+                                for (int64_t oh = 0; oh < p.Ho; ++oh)
+                                    for (int64_t ow = 0; ow < p.Wo; ++ow) {
+                                        int64_t id = od * p.sd - p.pd + t * p.dd;
+                                        int64_t ih = oh * p.sh - p.ph + r * p.dh;
+                                        int64_t iw = ow * p.sw_ - p.pw + s * p.dw;
+                                        if (id < 0 || id >= p.D || ih < 0 || ih >= p.H || iw < 0 || iw >= p.W)
+                                            continue; /* zero padding */
+                                        acc += dy_at(&p, dykind, dy, n, k, od, oh, ow) *
+                                               operand(p.xkind, x, x_index(&p, n, c, id, ih, iw), 1.0);
+                                    }
+                        dw[(((k * p.C + c) * p.T + t) * p.R + r) * p.S + s] = acc;
+                    }
     return 0;
 }
 

@@ -7,8 +7,10 @@ links or runs it, and it imports nothing from the product package.
 It is a ctypes wrapper over ``conv_oracle.c`` (plain C, fp64): the seven-loop
 definition of 3D cross-correlation with zero padding that FlyDSL PR #860
 checks its implicit-GEMM conv kernels against (torch ``conv3d``, commit adding
-the large_shape regression test), the bf16 and OCP E4M3FN encodings, and the
-per-tensor ``amax / 448`` fp8 scaling. Operands are numpy arrays:
+the large_shape regression test), its two gradients (with respect to x and to
+w, the backward-data and backward-weights problems that MIOpen PR #10912 maps
+to one GEMM each for point-output shapes), the bf16 and OCP E4M3FN encodings,
+and the per-tensor ``amax / 448`` fp8 scaling. Operands are numpy arrays:
 
 * ``float64``  -- plain values,
 * ``uint16``   -- bf16 bit patterns,
@@ -63,6 +65,8 @@ def _load():
         lib.oracle_out_dims.argtypes = [p, p, p, p, p, p]
         lib.oracle_conv3d.argtypes = [i32, p, i32, f64, i32, p, f64, p, p, p, p, p, p]
         lib.oracle_conv3d_points.argtypes = [i32, p, i32, f64, i32, p, f64, p, p, p, p, p, p, i64, p]
+        lib.oracle_conv3d_bwd_data.argtypes = [i32, p, i32, p, i32, p, p, p, p, p, p]
+        lib.oracle_conv3d_bwd_weight.argtypes = [i32, p, i32, i32, p, p, p, p, p, p, p]
         lib.oracle_set_threads.argtypes = [i32]
         lib.oracle_get_threads.restype = i32
         _lib = lib
@@ -213,6 +217,40 @@ def conv3d_points(x, w, points, stride=(1, 1, 1), pad=(0, 0, 0), dil=(1, 1, 1), 
     if b is not None:
         y += b[pts[:, 1]]
     return y
+
+
+def conv3d_bwd_data(dy, w, x_shape, stride=(1, 1, 1), pad=(0, 0, 0), dil=(1, 1, 1), x_layout="NCDHW"):
+    """Gradient of conv3d with respect to x for the incoming gradient dy (N, K, Do, Ho, Wo):
+    dx of logical shape x_shape = (N, C, D, H, W), returned in x_layout, float64. MIOpen
+    PR #10912 computes it as one GEMM for point-output shapes (backward data)."""
+    dy = np.ascontiguousarray(dy)
+    w = np.ascontiguousarray(w)
+    xs, ws, st, pd, dl = _geom(x_shape, w.shape, stride, pad, dil, "NCDHW")
+    assert dy.shape == (int(xs[0]), int(ws[0])) + out_dims(x_shape, w.shape, stride, pad, dil), dy.shape
+    n, c, d, h, wd = (int(v) for v in xs)
+    dx = np.empty((n, c, d, h, wd) if x_layout == "NCDHW" else (n, d, h, wd, c), np.float64)
+    rc = _load().oracle_conv3d_bwd_data(_kind(dy), _ptr(dy), _kind(w), _ptr(w), _LAYOUTS[x_layout], _ptr(xs),
+                                        _ptr(ws), _ptr(st), _ptr(pd), _ptr(dl), _ptr(dx))
+    if rc:
+        raise ValueError(f"oracle_conv3d_bwd_data failed ({rc})")
+    return dx
+
+
+def conv3d_bwd_weight(x, dy, w_shape, stride=(1, 1, 1), pad=(0, 0, 0), dil=(1, 1, 1), x_layout="NCDHW"):
+    """Gradient of conv3d with respect to w for the incoming gradient dy: dw (K, C, T, R, S)
+    float64. MIOpen PR #10912 computes it as one GEMM for point-output shapes (backward
+    weights)."""
+    x = np.ascontiguousarray(x)
+    dy = np.ascontiguousarray(dy)
+    xs, ws, st, pd, dl = _geom(x.shape, w_shape, stride, pad, dil, x_layout)
+    x_logical = tuple(int(v) for v in xs)
+    assert dy.shape == (x_logical[0], int(ws[0])) + out_dims(x_logical, w_shape, stride, pad, dil), dy.shape
+    dw = np.empty(tuple(int(v) for v in ws), np.float64)
+    rc = _load().oracle_conv3d_bwd_weight(_kind(x), _ptr(x), _LAYOUTS[x_layout], _kind(dy), _ptr(dy), _ptr(xs),
+                                          _ptr(ws), _ptr(st), _ptr(pd), _ptr(dl), _ptr(dw))
+    if rc:
+        raise ValueError(f"oracle_conv3d_bwd_weight failed ({rc})")
+    return dw
 
 
 def set_threads(n: int) -> None:

@@ -354,3 +354,70 @@ def test_fp8_conv_is_conv_of_dequantised_values():
     wd = torch.from_numpy(wq).view(torch.float8_e4m3fn).double() * float(sw)
     ref = F.conv3d(xd, wd, padding=(1, 0, 1)).numpy()
     assert np.abs(y - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+# ------------------------------------------------------------------ gradients
+
+@pytest.mark.parametrize("geom", GEOMS)
+def test_gradients_match_torch_autograd(geom):
+    # torch's autograd of conv3d in float64 is an independent implementation of both adjoints
+    xs, ws, st, pd, dl = geom
+    x, w = _rand(xs, 20), _rand(ws, 21)
+    xt = torch.from_numpy(x).requires_grad_()
+    wt = torch.from_numpy(w).requires_grad_()
+    y = F.conv3d(xt, wt, stride=st, padding=pd, dilation=dl)
+    dy = _rand(tuple(y.shape), 22)
+    gx, gw = torch.autograd.grad(y, (xt, wt), torch.from_numpy(dy))
+    assert np.allclose(O.conv3d_bwd_data(dy, w, xs, st, pd, dl), gx.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(O.conv3d_bwd_weight(x, dy, ws, st, pd, dl), gw.numpy(), rtol=1e-12, atol=1e-12)
+    # channel-last x: the same gradients, dx laid out NDHWC
+    xl = np.ascontiguousarray(np.moveaxis(x, 1, -1))
+    assert np.allclose(O.conv3d_bwd_data(dy, w, xs, st, pd, dl, x_layout="NDHWC"),
+                       np.moveaxis(gx.numpy(), 1, -1), rtol=1e-12, atol=1e-12)
+    assert np.allclose(O.conv3d_bwd_weight(xl, dy, ws, st, pd, dl, x_layout="NDHWC"), gw.numpy(),
+                       rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("geom", GEOMS)
+def test_gradients_are_the_adjoints(geom):
+    # <conv(x, w), dy> = <x, dgrad(dy, w)> = <w, wgrad(x, dy)>; integer data keeps every sum exact
+    xs, ws, st, pd, dl = geom
+    rng = np.random.default_rng(23)
+    x = rng.integers(-3, 4, xs).astype(np.float64)
+    w = rng.integers(-3, 4, ws).astype(np.float64)
+    y = O.conv3d(x, w, st, pd, dl)
+    dy = rng.integers(-3, 4, y.shape).astype(np.float64)
+    lhs = float(np.sum(y * dy))
+    assert float(np.sum(x * O.conv3d_bwd_data(dy, w, xs, st, pd, dl))) == lhs
+    assert float(np.sum(w * O.conv3d_bwd_weight(x, dy, ws, st, pd, dl))) == lhs
+
+
+@pytest.mark.parametrize("layout", ["NCDHW", "NDHWC"])
+def test_point_output_gradients_are_gemms(layout):
+    # point output (input extent == filter extent, stride == filter): both gradients are one GEMM over the
+    # batch in the layout's own element order (MIOpen PR #10912, PR body)
+    xs, ws, st = (7, 3, 2, 4, 4), (5, 3, 2, 4, 4), (2, 4, 4)
+    x, w = _rand(xs, 24), _rand(ws, 25)
+    dy = _rand((7, 5, 1, 1, 1), 26)
+    n, k = 7, 5
+    if layout == "NDHWC":
+        xl = np.ascontiguousarray(np.moveaxis(x, 1, -1))
+        wl = np.moveaxis(w, 1, -1).reshape(k, -1)
+    else:
+        xl, wl = x, w.reshape(k, -1)
+    dx = O.conv3d_bwd_data(dy, w, xs, st, x_layout=layout)
+    assert np.allclose(dx.reshape(n, -1), dy.reshape(n, k) @ wl, rtol=1e-12, atol=1e-12)
+    dw = O.conv3d_bwd_weight(xl, dy, ws, st, x_layout=layout)
+    dwl = np.moveaxis(dw, 1, -1).reshape(k, -1) if layout == "NDHWC" else dw.reshape(k, -1)
+    assert np.allclose(dwl, dy.reshape(n, k).T @ xl.reshape(n, -1), rtol=1e-12, atol=1e-12)
+
+
+def test_gradients_of_bf16_operands_are_exact_values():
+    # bf16 bit patterns widen exactly: gradients of the bit patterns equal gradients of their values
+    xs, ws, st, pd, dl = GEOMS[0]
+    xb = O.bf16_round(_rand(xs, 27).astype(np.float32))
+    wb = O.bf16_round(_rand(ws, 28).astype(np.float32))
+    dyb = O.bf16_round(_rand((2, 2, 4, 5, 6), 29).astype(np.float32))
+    xv, wv, dyv = O.bf16_value(xb), O.bf16_value(wb), O.bf16_value(dyb)
+    assert np.array_equal(O.conv3d_bwd_data(dyb, wb, xs, st, pd, dl), O.conv3d_bwd_data(dyv, wv, xs, st, pd, dl))
+    assert np.array_equal(O.conv3d_bwd_weight(xb, dyb, ws, st, pd, dl), O.conv3d_bwd_weight(xv, dyv, ws, st, pd, dl))
