@@ -223,6 +223,36 @@ def bench_epilogue(steps, warmup, torch, B, I, PL):
     return res
 
 
+def bench_grad(steps, warmup, torch, B, I, PL):
+    """Gradients of the point-output patch embed (c2 shape): backward data and backward weights."""
+    wl = I.WORKLOADS["c2"]
+    x, w = I.make(wl, "cuda")
+    xs, ws = wl.x_shape, wl.w_shape
+    st, pd, dl = wl.stride, wl.pad, wl.dil
+    dy = torch.randn((xs[0], ws[0], 1, 1, 1), generator=I.generator(34, "cuda"), device="cuda").to(torch.bfloat16)
+    wt = torch.empty((int(w[0].numel()), B.conv_packed_w_t_cols(ws)), dtype=torch.bfloat16, device="cuda")
+    B.conv_pack_w_t(w, wt, ws, B.IGC_NCDHW)
+    dx = torch.empty_like(x)
+    dw = torch.empty_like(w)
+    nws = B.conv_bwd_weight_workspace_bytes(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NCDHW)
+    wsb = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    flops = 2 * xs[0] * ws[0] * int(w[0].numel())
+    res = {"workload": wl.note + ": backward data and backward weights", "flop": flops, "workspace_bytes": nws}
+    for key, fn in (("dgrad", lambda: B.conv_bwd_data(dy, wt, dx, xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NCDHW)),
+                    ("wgrad", lambda: B.conv_bwd_weight(x, dy, dw, xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NCDHW,
+                                                       wsb))):
+        stt, cst = {}, {}
+        _, ev = time_launches(fn, steps, warmup, torch, stt)
+        scratch = torch.empty(1 << 28, dtype=torch.int16, device="cuda")
+        time_launches(fn, steps, warmup, torch, cst, between=lambda: scratch.fill_(1))
+        del scratch
+        res.update({f"{key}_ms": ev, f"{key}_ms_median": stt["median"], f"{key}_ms_min": stt["min"],
+                    f"{key}_cold_ms_median": cst["median"], f"{key}_tflops": flops / (stt["median"] * 1e-3) / 1e12})
+    del x, w, dy, wt, dx, dw, wsb
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(seconds: float, I):
     """The fp64 oracle on a bounded random sample of the headline workload's outputs."""
     import numpy as np
@@ -281,7 +311,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", default=None, help="comma list of extra workloads (c1,c2,c4,c4t,c5,pw,c3ex)")
+    ap.add_argument("--only", default=None, help="comma list of extra workloads (c1,c2,c4,c4t,c5,pw,c3ex,c2grad)")
     ap.add_argument("--profile", action="store_true",
                     help="counter-collection run: the headline conv `steps` times, then one 1 GiB device copy "
                          "(the reference for scaling FETCH_SIZE / WRITE_SIZE); prints nothing else")
@@ -324,11 +354,13 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        names = args.only.split(",") if args.only else ["c1", "c2", "c4", "c4t", "c5", "pw", "c3ex"]
+        names = args.only.split(",") if args.only else ["c1", "c2", "c4", "c4t", "c5", "pw", "c3ex", "c2grad"]
         for name in names:
             log(f"[bench] extra workload {name}")
             if name == "c3ex":
                 extra[name] = bench_epilogue(max(5, args.steps // 2), args.warmup, torch, B, I, PL)
+            elif name == "c2grad":
+                extra[name] = bench_grad(max(20, args.steps), args.warmup, torch, B, I, PL)
             else:
                 extra[name] = bench_workload(name, max(5, args.steps // 2), args.warmup, torch, B, I, PL)
             log(f"[bench] {name}: {json.dumps(extra[name])}")

@@ -28,7 +28,8 @@ IGC_PATH_AUTO, IGC_PATH_GENERIC, IGC_PATH_TEMPORAL, IGC_PATH_POINT, IGC_PATH_POI
 
 EXPORTS = ("conv_out_dims", "conv_packed_w_cols", "conv_amax", "conv_fp8_scales", "conv_pack_x", "conv_pack_w",
            "conv_fwd", "conv_fwd_ws", "conv_fwd_ex", "conv_fwd_workspace_bytes", "conv_plan", "conv_plan_ws", "conv_debug_force",
-           "conv_debug_force_splits", "conv_last_error")
+           "conv_debug_force_splits", "conv_packed_w_t_cols", "conv_pack_w_t", "conv_bwd_data",
+           "conv_bwd_weight_workspace_bytes", "conv_bwd_weight", "conv_last_error")
 
 
 class IgcError(RuntimeError):
@@ -62,11 +63,19 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.conv_fwd_workspace_bytes.argtypes = [P, P, P, P, P, I32, I32]
         lib.conv_fwd_workspace_bytes.restype = I64
         lib.conv_plan_ws.argtypes = [P, P, P, P, P, I32, I32, ctypes.c_size_t, ctypes.c_char_p, ctypes.c_size_t]
+        lib.conv_packed_w_t_cols.argtypes = [P]
+        lib.conv_packed_w_t_cols.restype = I64
+        lib.conv_pack_w_t.argtypes = [P, P, P, I32, P]
+        lib.conv_bwd_data.argtypes = [P, P, P, P, P, P, P, P, I32, I32, P]
+        lib.conv_bwd_weight_workspace_bytes.argtypes = [P, P, P, P, P, I32, I32]
+        lib.conv_bwd_weight_workspace_bytes.restype = I64
+        lib.conv_bwd_weight.argtypes = [P, P, P, P, P, P, P, P, I32, I32, P, ctypes.c_size_t, P]
         lib.conv_debug_force.argtypes = [I32, I32, I32]
         lib.conv_debug_force_splits.argtypes = [I32]
         lib.conv_last_error.restype = ctypes.c_char_p
         for name in EXPORTS:
-            if name not in ("conv_packed_w_cols", "conv_fwd_workspace_bytes", "conv_last_error"):
+            if name not in ("conv_packed_w_cols", "conv_fwd_workspace_bytes", "conv_packed_w_t_cols",
+                            "conv_bwd_weight_workspace_bytes", "conv_last_error"):
                 getattr(lib, name).restype = I32
         _lib = lib
     return _lib
@@ -198,6 +207,44 @@ def conv_plan_ws(xshape, wshape, stride, pad, dilation, dtype, x_layout, workspa
 
 def conv_debug_force(path, tile, group_m=0):
     _check("conv_debug_force", load().conv_debug_force(int(path), int(tile), int(group_m)))
+
+
+def conv_packed_w_t_cols(wshape) -> int:
+    n = load().conv_packed_w_t_cols(_i64(wshape, 5))
+    if n < 0:
+        raise IgcError("conv_packed_w_t_cols", int(n), "bad wshape")
+    return int(n)
+
+
+def conv_pack_w_t(w_kctrs_bf16, w_t, wshape, x_layout, stream=None):
+    _check("conv_pack_w_t", load().conv_pack_w_t(_dev(w_kctrs_bf16), _dev(w_t), _i64(wshape, 5), int(x_layout),
+                                                 _stream(stream, w_t)))
+
+
+def conv_bwd_data(dy, w_t, dx, xshape, wshape, stride, pad, dilation, dtype, x_layout, stream=None):
+    _check("conv_bwd_data", load().conv_bwd_data(_dev(dy), _dev(w_t), _dev(dx), _i64(xshape, 5), _i64(wshape, 5),
+                                                 _i32(stride), _i32(pad), _i32(dilation), int(dtype), int(x_layout),
+                                                 _stream(stream, dx)))
+
+
+def conv_bwd_weight_workspace_bytes(xshape, wshape, stride, pad, dilation, dtype, x_layout) -> int:
+    n = load().conv_bwd_weight_workspace_bytes(_i64(xshape, 5), _i64(wshape, 5), _i32(stride), _i32(pad),
+                                               _i32(dilation), int(dtype), int(x_layout))
+    if n < 0:
+        raise IgcError("conv_bwd_weight_workspace_bytes", int(n), conv_last_error())
+    return int(n)
+
+
+def conv_bwd_weight(x, dy, dw, xshape, wshape, stride, pad, dilation, dtype, x_layout, workspace,
+                    workspace_bytes=None, stream=None):
+    nbytes = workspace.numel() * workspace.element_size()
+    if workspace_bytes is not None:
+        if int(workspace_bytes) > nbytes:
+            raise ValueError(f"workspace_bytes {workspace_bytes} exceeds the workspace tensor ({nbytes} bytes)")
+        nbytes = int(workspace_bytes)
+    _check("conv_bwd_weight", load().conv_bwd_weight(_dev(x), _dev(dy), _dev(dw), _i64(xshape, 5), _i64(wshape, 5),
+                                                     _i32(stride), _i32(pad), _i32(dilation), int(dtype),
+                                                     int(x_layout), _dev(workspace), nbytes, _stream(stream, dw)))
 
 
 def conv_debug_force_splits(splits):

@@ -444,6 +444,98 @@ int plan_splits(Plan &pl, size_t ws_bytes)
     return p.splits;
 }
 
+// One point-mode GEMM, out[col][row] = sum_r A[row][r] * B[col][r] with A rows
+// of ldw elements (zero from Rk on), B rows of Rk elements (4-byte aligned) and
+// out rows of ldo elements: the backward GEMMs of point-output shapes (the
+// forward point path is the case A = filter, B = images, ldo = K). The tile
+// follows the forward rule for grids of this size; a forced tile applies if it
+// is a register or global-address direct-to-LDS tile.
+int plan_point_gemm(int64_t M, int64_t Ncol, int64_t Rk, int64_t ldw, int64_t ldo, Plan &pl)
+{
+    if (M > kI32Max || Ncol > kI32Max || Rk > kI32Max - 256 || ldw > kI32Max || ldo > kI32Max ||
+        M * ldo > (int64_t(1) << 62) / 2)
+        return fail(IGC_ERR_UNSUPPORTED, "GEMM of %lld x %lld over %lld too large", (long long)M, (long long)Ncol,
+                    (long long)Rk);
+    ConvParams &p = pl.p;
+    p = ConvParams{};
+    p.splits = 1;
+    p.N = 1;
+    p.K = (int)ldo;
+    p.M = (int)M;
+    p.Ncol = (int)Ncol;
+    p.Rk = (int)Rk;
+    p.ldw = (int)ldw;
+    p.P = 1;
+    p.Do = p.Ho = p.Wo = 1;
+    auto nblocks = [&](int t) {
+        return (M + kTiles[t].bm - 1) / kTiles[t].bm * ((Ncol + kTiles[t].bn - 1) / kTiles[t].bn);
+    };
+    int tile = g_force_tile.load();
+    if (tile < 0 || tile >= kNumTiles || is_buffer(kTiles[tile]) || is_window(kTiles[tile]) ||
+        is_pointwise_tile(tile) || tile == 12 || tile == 13)
+        tile = nblocks(21) >= 160 ? 21 : (nblocks(24) >= 256 ? 24 : 26);
+    const TileShape ts = kTiles[tile];
+    const int tke = step_bytes(ts) / 2;
+    p.nk = (int)((Rk + tke - 1) / tke);
+    p.ksplit = p.nk;
+    p.pairs = 1;
+    const int64_t tm = (M + ts.bm - 1) / ts.bm, tn = (Ncol + ts.bn - 1) / ts.bn;
+    if (tm * tn > kI32Max)
+        return fail(IGC_ERR_UNSUPPORTED, "grid of %lld tiles too large", (long long)(tm * tn));
+    p.tiles_m = (int)tm;
+    p.tiles_n = (int)tn;
+    const int resident = 32 * (ts.bm * ts.bn >= 256 * 256 ? 1 : 2);
+    p.group_m = (int)std::max<int64_t>(1, resident / tn);
+    if (g_force_group_m.load() > 0)
+        p.group_m = g_force_group_m.load();
+    pl.path = IGC_PATH_POINT;
+    pl.tile = tile;
+    pl.big = Ncol * ldo > kSmallTensor;  // 64-bit output offsets
+    pl.cblock = false;
+    pl.xspan = 0;
+    return IGC_OK;
+}
+
+// Shared checks of the point-output gradient entry points: a point-output
+// geometry (input extent = filter extent, no padding, unit dilation), bf16.
+int check_point_grad(const char *fn, const int64_t *xs, const int64_t *ws, const int32_t *st, const int32_t *pad,
+                     const int32_t *dil, int dtype, int x_layout, Geometry &g)
+{
+    int rc = check_geometry(xs, ws, st, pad, dil, g);
+    if (rc)
+        return rc;
+    if (dtype != IGC_BF16)
+        return fail(dtype == IGC_FP8_E4M3FN ? IGC_ERR_UNSUPPORTED : IGC_ERR_INVALID, "%s: bf16 only (dtype %d)", fn,
+                    dtype);
+    if (x_layout != IGC_NCDHW && x_layout != IGC_NDHWC)
+        return fail(IGC_ERR_INVALID, "%s: x_layout %d is neither IGC_NCDHW nor IGC_NDHWC", fn, x_layout);
+    if (!is_point(g))
+        return fail(IGC_ERR_UNSUPPORTED,
+                    "%s: needs a point-output shape (input extent equal to the filter extent, no padding, unit "
+                    "dilation)", fn);
+    return IGC_OK;
+}
+
+int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Backward weights workspace: x^T [R][ldn] and dy^T [K][ldn] (bf16), each
+// 256-byte aligned, then the split slices (fp32, K * R each).
+struct WgradLayout {
+    int64_t ldn, xt_off, dyt_off, part_off, base_bytes;
+};
+
+WgradLayout wgrad_layout(const Geometry &g)
+{
+    WgradLayout L;
+    const int64_t rk = g.C * g.T * g.R * g.S;
+    L.ldn = align_up(g.N, 64);
+    L.xt_off = 0;
+    L.dyt_off = align_up(rk * L.ldn * 2, 256);
+    L.part_off = L.dyt_off + align_up(g.K * L.ldn * 2, 256);
+    L.base_bytes = L.part_off;
+    return L;
+}
+
 const char *path_name(int path)
 {
     switch (path) {
@@ -679,6 +771,142 @@ int conv_debug_force(int path, int tile, int group_m)
     g_force_path.store(path);
     g_force_tile.store(tile);
     g_force_group_m.store(group_m);
+    return ok();
+}
+
+int64_t conv_packed_w_t_cols(const int64_t wshape[5])
+{
+    if (!wshape)
+        return IGC_ERR_INVALID;
+    for (int i = 0; i < 5; ++i)
+        if (wshape[i] < 1 || wshape[i] > kI32Max)
+            return IGC_ERR_INVALID;
+    return align_up(wshape[0], 64);
+}
+
+int conv_pack_w_t(const void *w_kctrs_bf16, void *w_t, const int64_t wshape[5], int x_layout, void *stream)
+{
+    if (!w_kctrs_bf16 || !w_t || !wshape)
+        return fail(IGC_ERR_INVALID, "conv_pack_w_t: null pointer");
+    if (x_layout != IGC_NCDHW && x_layout != IGC_NDHWC)
+        return fail(IGC_ERR_INVALID, "conv_pack_w_t: bad x_layout %d", x_layout);
+    for (int i = 0; i < 5; ++i)
+        if (wshape[i] < 1 || wshape[i] > kI32Max)
+            return fail(IGC_ERR_INVALID, "conv_pack_w_t: wshape[%d] = %lld out of range", i, (long long)wshape[i]);
+    if (!aligned16(w_kctrs_bf16) || !aligned16(w_t))
+        return fail(IGC_ERR_ALIGN, "conv_pack_w_t: tensors must be 16-byte aligned");
+    const int64_t ldk = align_up(wshape[0], 64), rk = wshape[1] * wshape[2] * wshape[3] * wshape[4];
+    if (rk > kI32Max || rk * ldk * 2 >= (int64_t(1) << 32))
+        return fail(IGC_ERR_UNSUPPORTED, "conv_pack_w_t: transposed filter of %lld x %lld too large", (long long)rk,
+                    (long long)ldk);
+    if (launch_pack_w_t(static_cast<const uint16_t *>(w_kctrs_bf16), static_cast<uint16_t *>(w_t), wshape[0],
+                        wshape[1], wshape[2], wshape[3], wshape[4], ldk, x_layout == IGC_NDHWC,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+        return fail(IGC_ERR_HIP, "conv_pack_w_t: launch failed");
+    return ok();
+}
+
+int conv_bwd_data(const void *dy, const void *w_t, void *dx, const int64_t xshape[5], const int64_t wshape[5],
+                  const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout,
+                  void *stream)
+{
+    Geometry g;
+    int rc = check_point_grad("conv_bwd_data", xshape, wshape, stride, pad, dilation, dtype, x_layout, g);
+    if (rc)
+        return rc;
+    if (!dy || !w_t || !dx)
+        return fail(IGC_ERR_INVALID, "conv_bwd_data: null tensor pointer");
+    if (!aligned16(dy) || !aligned16(w_t) || !aligned16(dx))
+        return fail(IGC_ERR_ALIGN, "conv_bwd_data: dy, w_t and dx must be 16-byte aligned");
+    if (g.K % 2 != 0)
+        return fail(IGC_ERR_UNSUPPORTED, "conv_bwd_data: dy rows of K = %lld bf16 must be 4-byte aligned (K even)",
+                    (long long)g.K);
+    const int64_t rk = g.C * g.T * g.R * g.S;
+    Plan pl;
+    // dx[n][j] = sum_k w_t[j][k] * dy[n][k]: A = w_t (rows j, ldk), B = dy rows (K elements), dx rows of rk
+    rc = plan_point_gemm(rk, g.N, g.K, align_up(g.K, 64), rk, pl);
+    if (rc)
+        return rc;
+    pl.p.x = dy;
+    pl.p.w = w_t;
+    pl.p.y = dx;
+    if (launch_conv(pl.p, pl.tile, MODE_POINT, DT_BF16, pl.big, false, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return fail(IGC_ERR_HIP, "conv_bwd_data: kernel launch failed");
+    return ok();
+}
+
+// Shared by conv_bwd_weight and its workspace query: the GEMM plan, its split
+// count for `room` bytes of slices, and the workspace layout.
+int plan_wgrad(const int64_t *xs, const int64_t *ws, const int32_t *st, const int32_t *pad, const int32_t *dil,
+               int dtype, int x_layout, size_t room, Plan &pl, WgradLayout &L)
+{
+    Geometry g;
+    int rc = check_point_grad("conv_bwd_weight", xs, ws, st, pad, dil, dtype, x_layout, g);
+    if (rc)
+        return rc;
+    L = wgrad_layout(g);
+    const int64_t rk = g.C * g.T * g.R * g.S;
+    if (L.ldn > kI32Max - 256 || rk * L.ldn * 2 >= (int64_t(1) << 32) || g.K * L.ldn * 2 >= (int64_t(1) << 32))
+        return fail(IGC_ERR_UNSUPPORTED, "conv_bwd_weight: transposed operands above 2^32 bytes");
+    // dw[k][j] = sum_n xt[j][n] * dyt[k][n]: A = x^T (rows j), B = dy^T (rows k), both rows of ldn (zeros past N)
+    rc = plan_point_gemm(rk, g.K, L.ldn, L.ldn, rk, pl);
+    if (rc)
+        return rc;
+    rc = plan_splits(pl, room);
+    return rc < 0 ? rc : IGC_OK;
+}
+
+int64_t conv_bwd_weight_workspace_bytes(const int64_t xshape[5], const int64_t wshape[5], const int32_t stride[3],
+                                        const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout)
+{
+    Plan pl;
+    WgradLayout L;
+    int rc = plan_wgrad(xshape, wshape, stride, pad, dilation, dtype, x_layout, SIZE_MAX, pl, L);
+    if (rc)
+        return rc;
+    ok();
+    return L.base_bytes + (pl.p.splits > 1 ? (int64_t)pl.p.splits * pl.p.M * pl.p.Ncol * 4 : 0);
+}
+
+int conv_bwd_weight(const void *x, const void *dy, void *dw, const int64_t xshape[5], const int64_t wshape[5],
+                    const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout,
+                    void *workspace_dev, size_t workspace_bytes, void *stream)
+{
+    Plan pl;
+    WgradLayout L;
+    Geometry g;
+    int rc = check_point_grad("conv_bwd_weight", xshape, wshape, stride, pad, dilation, dtype, x_layout, g);
+    if (rc)
+        return rc;
+    if (!x || !dy || !dw || !workspace_dev)
+        return fail(IGC_ERR_INVALID, "conv_bwd_weight: null pointer");
+    if (!aligned16(x) || !aligned16(dy) || !aligned16(dw) || !aligned16(workspace_dev))
+        return fail(IGC_ERR_ALIGN, "conv_bwd_weight: x, dy, dw and the workspace must be 16-byte aligned");
+    L = wgrad_layout(g);
+    if ((int64_t)workspace_bytes < L.base_bytes)
+        return fail(IGC_ERR_INVALID, "conv_bwd_weight: workspace of %zu bytes, needs at least %lld", workspace_bytes,
+                    (long long)L.base_bytes);
+    rc = plan_wgrad(xshape, wshape, stride, pad, dilation, dtype, x_layout, workspace_bytes - L.base_bytes, pl, L);
+    if (rc)
+        return rc;
+    char *wsb = static_cast<char *>(workspace_dev);
+    uint16_t *xt = reinterpret_cast<uint16_t *>(wsb + L.xt_off);
+    uint16_t *dyt = reinterpret_cast<uint16_t *>(wsb + L.dyt_off);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t rk = g.C * g.T * g.R * g.S;
+    // x is [N][rk] in either layout (a point-output image is rk contiguous elements), dy is [N][K]
+    if (launch_transpose_pad(static_cast<const uint16_t *>(x), xt, g.N, rk, L.ldn, st) != hipSuccess ||
+        launch_transpose_pad(static_cast<const uint16_t *>(dy), dyt, g.N, g.K, L.ldn, st) != hipSuccess)
+        return fail(IGC_ERR_HIP, "conv_bwd_weight: transpose launch failed");
+    pl.p.x = dyt;
+    pl.p.w = xt;
+    pl.p.y = dw;
+    pl.p.part = pl.p.splits > 1 ? reinterpret_cast<float *>(wsb + L.part_off) : nullptr;
+    if (launch_conv(pl.p, pl.tile, MODE_POINT, DT_BF16, pl.big, false, st) != hipSuccess)
+        return fail(IGC_ERR_HIP, "conv_bwd_weight: kernel launch failed");
+    if (pl.p.splits > 1 && launch_splitk_reduce(pl.p, st) != hipSuccess)
+        return fail(IGC_ERR_HIP, "conv_bwd_weight: split reduction launch failed");
     return ok();
 }
 

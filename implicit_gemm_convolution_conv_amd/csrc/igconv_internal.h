@@ -135,6 +135,13 @@ hipError_t launch_conv_pw(const ConvParams &p, int variant, hipStream_t stream);
 hipError_t launch_splitk_reduce(const ConvParams &p, hipStream_t stream);
 hipError_t launch_amax_zero(float *amax, hipStream_t stream);
 
+// dst[c][r] = src[r][c] (src rows of `cols` bf16), dst rows of ld >= rows elements, zero past rows
+hipError_t launch_transpose_pad(const uint16_t *src, uint16_t *dst, int64_t rows, int64_t cols, int64_t ld,
+                                hipStream_t stream);
+// w_t[j][k]: the filter transposed, j in the activation layout's (c, t, r, s) or (t, r, s, c) order
+hipError_t launch_pack_w_t(const uint16_t *w, uint16_t *wt, int64_t K, int64_t C, int64_t T, int64_t R, int64_t S,
+                           int64_t ldk, bool channel_last, hipStream_t stream);
+
 hipError_t launch_amax(const uint16_t *t, int64_t n, float *amax, hipStream_t stream);
 hipError_t launch_fp8_scales(const float *amax, float *pair, hipStream_t stream);
 hipError_t launch_pack_x(const uint16_t *x, void *out, int64_t N, int64_t C, int64_t S, Dtype dt,

@@ -207,6 +207,44 @@ IGC_API int64_t conv_fwd_workspace_bytes(const int64_t xshape[5], const int64_t 
                 const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout);
 
 /*
+ * Gradients of point-output convolutions (input extent equal to the filter
+ * extent, no padding, unit dilation: one output position per image), each one
+ * GEMM over the batch as in MIOpen PR #10912 (PR body: backward data and
+ * backward weights for patch-embedding shapes). bf16 operands, fp32
+ * accumulation, one bf16 rounding. An image of x (and of dx) is then the
+ * C*T*R*S elements in the layout's order: (c, t, r, s) for IGC_NCDHW, (t, r,
+ * s, c) for IGC_NDHWC; dy is {N, K, 1, 1, 1}, i.e. [N][K]. Other geometries
+ * return IGC_ERR_UNSUPPORTED, fp8 too.
+ *
+ * conv_packed_w_t_cols: row length of the transposed filter, K rounded up to 64.
+ * conv_pack_w_t: w_t[j][k] = w[k][c][t][r][s] for the backward-data GEMM, j in
+ *   x_layout's element order, rows of conv_packed_w_t_cols elements with zeros
+ *   from K on (a one-time, per-filter preparation).
+ * conv_bwd_data: dx[n][j] = sum_k dy[n][k] * w[k][j]; dx has x's shape and
+ *   layout, every element written. Needs K even (4-byte aligned dy rows).
+ * conv_bwd_weight: dw[k][j] = sum_n dy[n][k] * x[n][j], written as bf16 in
+ *   filter order: KCTRS for IGC_NCDHW, K x (T, R, S, C) for IGC_NDHWC. The
+ *   reduction runs over n, the slow index of x and dy, so both are first
+ *   transposed into the workspace (x^T and dy^T, rows padded to a multiple of
+ *   64 images with zeros); where the grid of output tiles under-fills the GPU
+ *   the batch is also split as in conv_fwd_ws, fp32 slices in the workspace.
+ *   The workspace must hold at least the two transposes; the split count is
+ *   lowered to what the rest holds.
+ * conv_bwd_weight_workspace_bytes: the bytes conv_bwd_weight uses with
+ *   unlimited room (negative status for invalid arguments). Host only.
+ */
+IGC_API int64_t conv_packed_w_t_cols(const int64_t wshape[5]);
+IGC_API int conv_pack_w_t(const void *w_kctrs_bf16, void *w_t, const int64_t wshape[5], int x_layout, void *stream);
+IGC_API int conv_bwd_data(const void *dy, const void *w_t, void *dx, const int64_t xshape[5],
+                const int64_t wshape[5], const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3],
+                int dtype, int x_layout, void *stream);
+IGC_API int64_t conv_bwd_weight_workspace_bytes(const int64_t xshape[5], const int64_t wshape[5],
+                const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout);
+IGC_API int conv_bwd_weight(const void *x, const void *dy, void *dw, const int64_t xshape[5],
+                const int64_t wshape[5], const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3],
+                int dtype, int x_layout, void *workspace_dev, size_t workspace_bytes, void *stream);
+
+/*
  * Describe, without running anything, the path and tile conv_fwd would use
  * for these arguments: writes a one-line text such as
  * "path=generic tile=256x256 waves=8 kstep=64 order=cblock big=0 grid=6752"

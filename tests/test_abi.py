@@ -307,3 +307,40 @@ def test_workspace_arguments_checked_before_any_launch():
     assert rc == B.IGC_ERR_INVALID  # bytes without a workspace
     rc = lib.conv_fwd_ws(16, 32, 48, xs[0], xs[1], one, one, one, B.IGC_BF16, B.IGC_NDHWC, None, 8, 64, None)
     assert rc == B.IGC_ERR_ALIGN
+
+
+def test_point_gradient_entry_points():
+    xs, ws, st = (9500, 3, 1, 14, 14), (1280, 3, 1, 14, 14), (1, 14, 14)
+    z, one = (0, 0, 0), (1, 1, 1)
+    assert B.conv_packed_w_t_cols(ws) == 1280
+    assert B.conv_packed_w_t_cols((18, 5, 1, 3, 7)) == 64
+    ldn = 9536  # 9500 images rounded up to 64
+    base = (588 * ldn * 2 + 255) // 256 * 256 + (1280 * ldn * 2 + 255) // 256 * 256
+    # 64x64 tiles over 588 x 1280: 200 tiles, no split
+    assert B.conv_bwd_weight_workspace_bytes(xs, ws, st, z, one, B.IGC_BF16, B.IGC_NCDHW) == base
+    # 37 images of 5 x 3 x 7 -> 18 channels: one reduction step over 64 (padded) images, too short to split
+    small = B.conv_bwd_weight_workspace_bytes((37, 5, 1, 3, 7), (18, 5, 1, 3, 7), (1, 3, 7), z, one, B.IGC_BF16,
+                                              B.IGC_NDHWC)
+    assert small == 13568 + 2304  # x^T 105 x 64 and dy^T 18 x 64 bf16, each rounded up to 256 bytes
+    # a long batch on a small grid splits: 4000 images, 2 tiles, 63 steps of 64 images
+    split = B.conv_bwd_weight_workspace_bytes((4000, 5, 1, 3, 7), (18, 5, 1, 3, 7), (1, 3, 7), z, one, B.IGC_BF16,
+                                              B.IGC_NCDHW)
+    ldn = 4032
+    tr = (105 * ldn * 2 + 255) // 256 * 256 + (18 * ldn * 2 + 255) // 256 * 256
+    assert split > tr and (split - tr) % (18 * 105 * 4) == 0 and (split - tr) // (18 * 105 * 4) > 1
+    for fn in (lambda: B.conv_bwd_weight_workspace_bytes((1, 3, 4, 14, 14), ws, st, z, one, B.IGC_BF16,
+                                                         B.IGC_NCDHW),  # input deeper than the filter
+               lambda: B.conv_bwd_weight_workspace_bytes(xs, ws, st, (0, 1, 1), one, B.IGC_BF16, B.IGC_NCDHW),
+               lambda: B.conv_bwd_weight_workspace_bytes(xs, ws, st, z, one, B.IGC_FP8_E4M3FN, B.IGC_NCDHW)):
+        with pytest.raises(B.IgcError) as e:
+            fn()
+        assert e.value.status == B.IGC_ERR_UNSUPPORTED
+    lib = B.load()
+    a, b = B._i64(xs, 5), B._i64(ws, 5)
+    odd = B._i64((9500, 3, 1, 14, 14), 5), B._i64((1279, 3, 1, 14, 14), 5)
+    rc = lib.conv_bwd_data(16, 32, 48, odd[0], odd[1], B._i32(st), B._i32(z), B._i32(one), B.IGC_BF16,
+                           B.IGC_NCDHW, None)
+    assert rc == B.IGC_ERR_UNSUPPORTED  # dy rows of an odd K are not 4-byte aligned
+    rc = lib.conv_bwd_weight(16, 32, 48, a, b, B._i32(st), B._i32(z), B._i32(one), B.IGC_BF16, B.IGC_NCDHW, 64,
+                             base - 1, None)
+    assert rc == B.IGC_ERR_INVALID  # workspace below the two transposes
