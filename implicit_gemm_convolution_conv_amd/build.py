@@ -46,8 +46,9 @@ def _compile(src: str) -> str:
 
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2) // 2), 8)
+    # the kernel-instantiation units take minutes each, the rest seconds: start those first
+    srcs = sorted(sources(), key=lambda s: not os.path.basename(s).startswith(("conv_dma_", "conv_bf16", "conv_fp8")))
+    jobs = jobs or min(len(srcs), max(1, os.cpu_count() or 2), 8)
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"

@@ -409,8 +409,9 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
 // under-fill test decides, a long reduction alone does not). Here: the
 // direct-to-LDS kernels, grids below 128 tiles (half the CUs), and at least 5
 // reduction steps per split (about the ring depth: shorter splits are mostly
-// pipeline fill); enough splits to reach about 256 workgroups, at most 32, and
-// no more than the workspace holds (splits * elements of y fp32 values).
+// pipeline fill); enough splits to fill the GPU once (256 workgroups of 256x256,
+// 512 of the smaller tiles, which pair on a CU), at most 32, and no more than
+// the workspace holds (splits * elements of y fp32 values).
 // Measured on MI355X (bf16, 64x64 tiles): the 1024x64x1728 GEMM of a
 // 64-channel 3x3x3 conv on 4x16x16 goes from 19.0 to 11.7 us, a 512-channel
 // 3x3 conv on 7x7 from 42 to 15 us. Returns the split count (1 = none) with
@@ -435,8 +436,10 @@ int plan_splits(Plan &pl, size_t ws_bytes)
         splits = (int)std::min<int64_t>(std::min(forced, p.nk), cap);
     } else if (splits_tile(pl.tile)) {
         const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+        const TileShape &t = kTiles[pl.tile];
+        const int64_t slots = t.bm * t.bn >= 256 * 256 ? 256 : 512;  // workgroups the GPU holds at once
         if (grid < 128)
-            splits = (int)std::min<int64_t>(std::min<int64_t>(std::min<int64_t>(256 / grid, p.nk / 5), 32), cap);
+            splits = (int)std::min<int64_t>(std::min<int64_t>(std::min<int64_t>(slots / grid, p.nk / 5), 32), cap);
     }
     splits = std::max(splits, 1);
     p.ksplit = (p.nk + splits - 1) / splits;
@@ -450,7 +453,7 @@ int plan_splits(Plan &pl, size_t ws_bytes)
 // forward point path is the case A = filter, B = images, ldo = K). The tile
 // follows the forward rule for grids of this size; a forced tile applies if it
 // is a register or global-address direct-to-LDS tile.
-int plan_point_gemm(int64_t M, int64_t Ncol, int64_t Rk, int64_t ldw, int64_t ldo, Plan &pl)
+int plan_point_gemm(int64_t M, int64_t Ncol, int64_t Rk, int64_t ldw, int64_t ldo, Plan &pl, bool long_split = false)
 {
     if (M > kI32Max || Ncol > kI32Max || Rk > kI32Max - 256 || ldw > kI32Max || ldo > kI32Max ||
         M * ldo > (int64_t(1) << 62) / 2)
@@ -472,8 +475,14 @@ int plan_point_gemm(int64_t M, int64_t Ncol, int64_t Rk, int64_t ldw, int64_t ld
     };
     int tile = g_force_tile.load();
     if (tile < 0 || tile >= kNumTiles || is_buffer(kTiles[tile]) || is_window(kTiles[tile]) ||
-        is_pointwise_tile(tile) || tile == 12 || tile == 13)
+        is_pointwise_tile(tile) || tile == 12 || tile == 13) {
         tile = nblocks(21) >= 160 ? 21 : (nblocks(24) >= 256 ? 24 : 26);
+        // A long reduction that will be split (backward weights over the batch): 128x128 tiles, then
+        // enough splits to fill the GPU; measured on the 9500-image patch embed (588 x 1280 over 9536):
+        // 128x128 with 8 splits 51.5 us, 64x64 with 4-10 splits 61-64 us.
+        if (long_split && tile == 26 && Rk >= 32 * 64)
+            tile = 24;
+    }
     const TileShape ts = kTiles[tile];
     const int tke = step_bytes(ts) / 2;
     p.nk = (int)((Rk + tke - 1) / tke);
@@ -850,7 +859,7 @@ int plan_wgrad(const int64_t *xs, const int64_t *ws, const int32_t *st, const in
     if (L.ldn > kI32Max - 256 || rk * L.ldn * 2 >= (int64_t(1) << 32) || g.K * L.ldn * 2 >= (int64_t(1) << 32))
         return fail(IGC_ERR_UNSUPPORTED, "conv_bwd_weight: transposed operands above 2^32 bytes");
     // dw[k][j] = sum_n xt[j][n] * dyt[k][n]: A = x^T (rows j), B = dy^T (rows k), both rows of ldn (zeros past N)
-    rc = plan_point_gemm(rk, g.K, L.ldn, L.ldn, rk, pl);
+    rc = plan_point_gemm(rk, g.K, L.ldn, L.ldn, rk, pl, room > 0);
     if (rc)
         return rc;
     rc = plan_splits(pl, room);

@@ -98,7 +98,10 @@ __device__ inline uint32_t f32_to_bf16_rne(float f)
 // channel) only when given. With p.amax set it also keeps the running maximum
 // of |y| over the values this lane stores (non-negative floats order like
 // their bits, so the maximum of bf16 bits & 0x7fff) and flush() merges the
-// wave's maximum into *p.amax as fp32 bits.
+// wave's maximum into *p.amax as fp32 bits. EXTRAS = false compiles the bias
+// and amax out: kernels pick the instance once per launch (with_epilogue), so
+// a call without extras runs the plain epilogue with no per-element tests.
+template <bool EXTRAS>
 struct Epilogue {
     float sc;
     const float *bias;
@@ -109,34 +112,44 @@ struct Epilogue {
         : sc(fp8 ? p.scales[0] * p.scales[2] : 1.0f), bias(p.bias), amax(p.amax) {}
 
     // bf16 bits of the output of channel k
-    __device__ uint32_t one(float acc, int k)
+    __device__ __attribute__((always_inline)) uint32_t one(float acc, int k)
     {
         float v = acc * sc;
-        if (bias)
-            v += bias[k];
+        if constexpr (EXTRAS) {
+            if (bias)
+                v += bias[k];
+        }
         const uint32_t r = f32_to_bf16_rne(v);
-        if (amax)
-            m = max(m, r & 0x7fffu);
+        if constexpr (EXTRAS) {
+            if (amax)
+                m = max(m, r & 0x7fffu);
+        }
         return r;
     }
     // four outputs of channel k, packed for one 8-byte store
-    __device__ u32x2 four(const f32x4 &acc, int k)
+    __device__ __attribute__((always_inline)) u32x2 four(const f32x4 &acc, int k)
     {
-        const float b = bias ? bias[k] : 0.0f;
+        float b = 0.0f;
+        if constexpr (EXTRAS)
+            b = bias ? bias[k] : 0.0f;
         uint32_t r[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float v = acc[e] * sc;
-            if (bias)
-                v += b;
+            if constexpr (EXTRAS) {
+                if (bias)
+                    v += b;
+            }
             r[e] = f32_to_bf16_rne(v);
-            if (amax)
-                m = max(m, r[e] & 0x7fffu);
+            if constexpr (EXTRAS) {
+                if (amax)
+                    m = max(m, r[e] & 0x7fffu);
+            }
         }
         return u32x2{r[0] | (r[1] << 16), r[2] | (r[3] << 16)};
     }
     // four outputs of channels k .. k + 3 (point output: channels are the rows)
-    __device__ u32x2 four_channels(const f32x4 &acc, int k)
+    __device__ __attribute__((always_inline)) u32x2 four_channels(const f32x4 &acc, int k)
     {
         uint32_t r[4];
 #pragma unroll
@@ -145,17 +158,33 @@ struct Epilogue {
         return u32x2{r[0] | (r[1] << 16), r[2] | (r[3] << 16)};
     }
     // every lane of the wave calls this once, after its last store
-    __device__ void flush()
+    __device__ __attribute__((always_inline)) void flush()
     {
-        if (!amax)
-            return;
+        if constexpr (EXTRAS) {
+            if (!amax)
+                return;
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-            m = max(m, (unsigned)__shfl_xor((int)m, off));
-        if ((threadIdx.x & 63) == 0)
-            atomicMax(amax, m << 16);
+            for (int off = 32; off > 0; off >>= 1)
+                m = max(m, (unsigned)__shfl_xor((int)m, off));
+            if ((threadIdx.x & 63) == 0)
+                atomicMax(amax, m << 16);
+        }
     }
 };
+
+// Run body(ep) with the epilogue instance this launch needs.
+template <typename F>
+__device__ __attribute__((always_inline)) inline void with_epilogue(const ConvParams &p, bool fp8, F &&body)
+{
+    if (p.bias || p.amax) {
+        Epilogue<true> ep(p, fp8);
+        body(ep);
+        ep.flush();
+    } else {
+        Epilogue<false> ep(p, fp8);
+        body(ep);
+    }
+}
 
 template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, bool BIG, bool CBLK>
 __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
@@ -462,65 +491,65 @@ void conv_igemm_kernel(ConvParams p)
 
     // ---------------------------------------------------------------- epilogue
     // Each lane holds groups of 4 consecutive GEMM rows of one column ("quads").
-    Epilogue ep(p, DT == DT_FP8);
     uint16_t *yb = static_cast<uint16_t *>(p.y);
-    constexpr int QUADS = MF / 16 * (MF / 16);  // 1 (16x16) or 4 (32x32) per block
+    with_epilogue(p, DT == DT_FP8, [&](auto &ep) __attribute__((always_inline)) {
+        constexpr int QUADS = MF / 16 * (MF / 16);  // 1 (16x16) or 4 (32x32) per block
 #pragma unroll
-    for (int a = 0; a < FM; ++a) {
+        for (int a = 0; a < FM; ++a) {
 #pragma unroll
-        for (int q = 0; q < QUADS; ++q) {
-            // first of the 4 consecutive GEMM rows of this quad
-            const int row = m0 + wm * WTM + a * MF + (MF == 16 ? 4 * lgrp : 8 * q + 4 * lgrp);
-            if constexpr (MODE != MODE_POINT) {
-                int nimg = 0, sp = 0;
-                if (row < p.M) {
-                    nimg = row / p.P;
-                    sp = row - nimg * p.P;
-                }
-                const bool vec = (p.P & 3) == 0 && row + 3 < p.M;  // 4 rows in one image, 8-byte aligned
+            for (int q = 0; q < QUADS; ++q) {
+                // first of the 4 consecutive GEMM rows of this quad
+                const int row = m0 + wm * WTM + a * MF + (MF == 16 ? 4 * lgrp : 8 * q + 4 * lgrp);
+                if constexpr (MODE != MODE_POINT) {
+                    int nimg = 0, sp = 0;
+                    if (row < p.M) {
+                        nimg = row / p.P;
+                        sp = row - nimg * p.P;
+                    }
+                    const bool vec = (p.P & 3) == 0 && row + 3 < p.M;  // 4 rows in one image, 8-byte aligned
 #pragma unroll
-                for (int b = 0; b < FN; ++b) {
-                    const int col = n0 + wn * WTN + b * MF + lrow;  // output channel
-                    if (row >= p.M || col >= p.K)
-                        continue;
-                    const f32x4 v = quad<MF>(acc[a][b], q);
-                    if (vec) {
-                        *reinterpret_cast<u32x2 *>(yb + ((Off)nimg * p.K + col) * (Off)p.P + sp) = ep.four(v, col);
-                    } else {
+                    for (int b = 0; b < FN; ++b) {
+                        const int col = n0 + wn * WTN + b * MF + lrow;  // output channel
+                        if (row >= p.M || col >= p.K)
+                            continue;
+                        const f32x4 v = quad<MF>(acc[a][b], q);
+                        if (vec) {
+                            *reinterpret_cast<u32x2 *>(yb + ((Off)nimg * p.K + col) * (Off)p.P + sp) = ep.four(v, col);
+                        } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int m = row + e;
-                            if (m < p.M) {
-                                const int n2 = m / p.P;
-                                const int sp2 = m - n2 * p.P;
-                                yb[((Off)n2 * p.K + col) * (Off)p.P + sp2] = (uint16_t)ep.one(v[e], col);
+                            for (int e = 0; e < 4; ++e) {
+                                const int m = row + e;
+                                if (m < p.M) {
+                                    const int n2 = m / p.P;
+                                    const int sp2 = m - n2 * p.P;
+                                    yb[((Off)n2 * p.K + col) * (Off)p.P + sp2] = (uint16_t)ep.one(v[e], col);
+                                }
                             }
                         }
                     }
-                }
-            } else {
-                // rows are output channels, columns are images: y[n][k] is contiguous in k
-                const bool vec = (p.K & 3) == 0 && row + 3 < p.M;
+                } else {
+                    // rows are output channels, columns are images: y[n][k] is contiguous in k
+                    const bool vec = (p.K & 3) == 0 && row + 3 < p.M;
 #pragma unroll
-                for (int b = 0; b < FN; ++b) {
-                    const int col = n0 + wn * WTN + b * MF + lrow;  // image
-                    if (row >= p.M || col >= p.Ncol)
-                        continue;
-                    const f32x4 v = quad<MF>(acc[a][b], q);
-                    uint16_t *dst = yb + (Off)col * p.K + row;
-                    if (vec) {
-                        *reinterpret_cast<u32x2 *>(dst) = ep.four_channels(v, row);
-                    } else {
+                    for (int b = 0; b < FN; ++b) {
+                        const int col = n0 + wn * WTN + b * MF + lrow;  // image
+                        if (row >= p.M || col >= p.Ncol)
+                            continue;
+                        const f32x4 v = quad<MF>(acc[a][b], q);
+                        uint16_t *dst = yb + (Off)col * p.K + row;
+                        if (vec) {
+                            *reinterpret_cast<u32x2 *>(dst) = ep.four_channels(v, row);
+                        } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (row + e < p.M)
-                                dst[e] = (uint16_t)ep.one(v[e], row + e);
+                            for (int e = 0; e < 4; ++e)
+                                if (row + e < p.M)
+                                    dst[e] = (uint16_t)ep.one(v[e], row + e);
+                        }
                     }
                 }
             }
         }
-    }
-    ep.flush();
+    });
 }
 
 // Launch helper for one dtype: picks the instantiation for (tile, mode, big, cblock).

@@ -120,7 +120,7 @@ struct ImRows {
     int d[N], h[N], w[N];
     unsigned off[N];  // wraps for padded origins; valid taps land in range
 
-    __device__ void init(const ConvParams &p, int first, int stride, int chunk, int64_t xbase)
+    __device__ __attribute__((always_inline)) void init(const ConvParams &p, int first, int stride, int chunk, int64_t xbase)
     {
         const int hw = p.Ho * p.Wo;
 #pragma unroll
@@ -163,7 +163,7 @@ struct ImRowsMasked {
     unsigned off[N];
     unsigned valid[N];  // bit (t * R + r) * S + s: that tap reads inside the input box
 
-    __device__ void init(const ConvParams &p, int first, int stride, int chunk, int64_t xbase)
+    __device__ __attribute__((always_inline)) void init(const ConvParams &p, int first, int stride, int chunk, int64_t xbase)
     {
         ImRows<N, MODE, ESZ> rows;
         rows.init(p, first, stride, chunk, xbase);
@@ -197,7 +197,7 @@ template <int N, int ESZ>
 struct FilterRows {
     unsigned off[N];
 
-    __device__ void init(const ConvParams &p, int first, int stride, int chunk)
+    __device__ __attribute__((always_inline)) void init(const ConvParams &p, int first, int stride, int chunk)
     {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
@@ -248,47 +248,47 @@ __device__ inline void mfma_acc(const FragT<DT> &af, const FragT<DT> &bf, typena
 // consecutive rows of one column go out as one 8-byte store when they share
 // an image and P % 4 == 0.
 template <int MF, int FM, int FN, int DT>
-__device__ inline void store_tile_ncdhw(const typename AccType<MF>::type (&acc)[FM][FN], const ConvParams &p,
+__device__ __attribute__((always_inline)) inline void store_tile_ncdhw(const typename AccType<MF>::type (&acc)[FM][FN], const ConvParams &p,
                                         int row0, int col0, int lane)
 {
     const int lrow = lane & (MF - 1), lgrp = lane / MF;
-    Epilogue ep(p, DT == DT_FP8);
     uint16_t *yb = static_cast<uint16_t *>(p.y);
-    constexpr int QUADS = MF / 16 * (MF / 16);
+    with_epilogue(p, DT == DT_FP8, [&](auto &ep) __attribute__((always_inline)) {
+        constexpr int QUADS = MF / 16 * (MF / 16);
 #pragma unroll
-    for (int a = 0; a < FM; ++a) {
+        for (int a = 0; a < FM; ++a) {
 #pragma unroll
-        for (int q = 0; q < QUADS; ++q) {
-            const int row = row0 + a * MF + (MF == 16 ? 4 * lgrp : 8 * q + 4 * lgrp);
-            int nimg = 0, sp = 0;
-            if (row < p.M) {
-                nimg = row / p.P;
-                sp = row - nimg * p.P;
-            }
-            const bool vec = (p.P & 3) == 0 && row + 3 < p.M;
+            for (int q = 0; q < QUADS; ++q) {
+                const int row = row0 + a * MF + (MF == 16 ? 4 * lgrp : 8 * q + 4 * lgrp);
+                int nimg = 0, sp = 0;
+                if (row < p.M) {
+                    nimg = row / p.P;
+                    sp = row - nimg * p.P;
+                }
+                const bool vec = (p.P & 3) == 0 && row + 3 < p.M;
 #pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const int col = col0 + b * MF + lrow;
-                if (row >= p.M || col >= p.K)
-                    continue;
-                const f32x4 v = quad<MF>(acc[a][b], q);
-                if (vec) {
-                    *reinterpret_cast<u32x2 *>(yb + ((int64_t)nimg * p.K + col) * p.P + sp) = ep.four(v, col);
-                } else {
+                for (int b = 0; b < FN; ++b) {
+                    const int col = col0 + b * MF + lrow;
+                    if (row >= p.M || col >= p.K)
+                        continue;
+                    const f32x4 v = quad<MF>(acc[a][b], q);
+                    if (vec) {
+                        *reinterpret_cast<u32x2 *>(yb + ((int64_t)nimg * p.K + col) * p.P + sp) = ep.four(v, col);
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int m = row + e;
-                        if (m < p.M) {
-                            const int n2 = m / p.P;
-                            const int sp2 = m - n2 * p.P;
-                            yb[((int64_t)n2 * p.K + col) * p.P + sp2] = (uint16_t)ep.one(v[e], col);
+                        for (int e = 0; e < 4; ++e) {
+                            const int m = row + e;
+                            if (m < p.M) {
+                                const int n2 = m / p.P;
+                                const int sp2 = m - n2 * p.P;
+                                yb[((int64_t)n2 * p.K + col) * p.P + sp2] = (uint16_t)ep.one(v[e], col);
+                            }
                         }
                     }
                 }
             }
         }
-    }
-    ep.flush();
+    });
 }
 
 template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, int SA, int SB, int KB, int SPREAD, int PF = 1,

@@ -393,86 +393,85 @@ void conv_igemm_dma_kernel(ConvParams p)
     }
 
     // ---------------------------------------------------------------- epilogue
-    // y = bf16(acc * scale + bias) (Epilogue); a split workgroup stores its
-    // raw fp32 sums at the same element offsets of its slice of the partial
-    // buffer, and the reduction pass applies scale, bias and amax.
-    const bool partial = p.splits > 1;
-    Epilogue ep(p, DT == DT_FP8 && !partial);
-    uint16_t *yb = static_cast<uint16_t *>(p.y);
-    float *pb = partial ? p.part + (int64_t)split * ((int64_t)p.M * p.Ncol) : nullptr;
-    // 4 consecutive elements from off (16-byte aligned partials): 4 positions of
-    // channel k, or channels k .. k + 3 in point mode
-    auto put4 = [&](Off off, const f32x4 &v, int k) {
-        if (partial)
-            *reinterpret_cast<f32x4 *>(pb + off) = v;
-        else if constexpr (MODE == MODE_POINT)
-            *reinterpret_cast<u32x2 *>(yb + off) = ep.four_channels(v, k);
-        else
-            *reinterpret_cast<u32x2 *>(yb + off) = ep.four(v, k);
-    };
-    auto put1 = [&](Off off, float v, int k) {
-        if (partial)
-            pb[off] = v;
-        else
-            yb[off] = (uint16_t)ep.one(v, k);
-    };
-    constexpr int QUADS = MF / 16 * (MF / 16);
+    // emit(put4, put1) walks this lane's outputs: put4(off, v, k) for 4
+    // consecutive elements from element offset off (4 positions of channel k,
+    // or channels k .. k + 3 in point mode), put1 for single ones.
+    auto emit = [&](auto &&put4, auto &&put1) __attribute__((always_inline)) {
+        constexpr int QUADS = MF / 16 * (MF / 16);
 #pragma unroll
-    for (int a = 0; a < FM; ++a) {
+        for (int a = 0; a < FM; ++a) {
 #pragma unroll
-        for (int q = 0; q < QUADS; ++q) {
-            const int row = m0 + wm * WTM + a * MF + (MF == 16 ? 4 * lgrp : 8 * q + 4 * lgrp);
-            if constexpr (MODE == MODE_POINT) {
-                // rows are output channels, columns are images: y[n][k] is contiguous in k
-                const bool vec = (p.K & 3) == 0 && row + 3 < p.M;
+            for (int q = 0; q < QUADS; ++q) {
+                const int row = m0 + wm * WTM + a * MF + (MF == 16 ? 4 * lgrp : 8 * q + 4 * lgrp);
+                if constexpr (MODE == MODE_POINT) {
+                    // rows are output channels, columns are images: y[n][k] is contiguous in k
+                    const bool vec = (p.K & 3) == 0 && row + 3 < p.M;
+#pragma unroll
+                    for (int b = 0; b < FN; ++b) {
+                        const int col = n0 + wn * WTN + b * MF + lrow;
+                        if (row >= p.M || col >= p.Ncol)
+                            continue;
+                        const f32x4 v = quad<MF>(acc[a][b], q);
+                        const Off dst = (Off)col * p.K + row;
+                        if (vec) {
+                            put4(dst, v, row);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (row + e < p.M)
+                                    put1(dst + e, v[e], row + e);
+                        }
+                    }
+                    continue;
+                }
+                int nimg = 0, sp = 0;
+                if (row < p.M) {
+                    nimg = row / p.P;
+                    sp = row - nimg * p.P;
+                }
+                const bool vec = (p.P & 3) == 0 && row + 3 < p.M;
 #pragma unroll
                 for (int b = 0; b < FN; ++b) {
                     const int col = n0 + wn * WTN + b * MF + lrow;
-                    if (row >= p.M || col >= p.Ncol)
+                    if (row >= p.M || col >= p.K)
                         continue;
                     const f32x4 v = quad<MF>(acc[a][b], q);
-                    const Off dst = (Off)col * p.K + row;
                     if (vec) {
-                        put4(dst, v, row);
+                        put4(((Off)nimg * p.K + col) * (Off)p.P + sp, v, col);
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (row + e < p.M)
-                                put1(dst + e, v[e], row + e);
-                    }
-                }
-                continue;
-            }
-            int nimg = 0, sp = 0;
-            if (row < p.M) {
-                nimg = row / p.P;
-                sp = row - nimg * p.P;
-            }
-            const bool vec = (p.P & 3) == 0 && row + 3 < p.M;
-#pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const int col = n0 + wn * WTN + b * MF + lrow;
-                if (row >= p.M || col >= p.K)
-                    continue;
-                const f32x4 v = quad<MF>(acc[a][b], q);
-                if (vec) {
-                    put4(((Off)nimg * p.K + col) * (Off)p.P + sp, v, col);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int m = row + e;
-                        if (m < p.M) {
-                            const int n2 = m / p.P;
-                            const int sp2 = m - n2 * p.P;
-                            put1(((Off)n2 * p.K + col) * (Off)p.P + sp2, v[e], col);
+                        for (int e = 0; e < 4; ++e) {
+                            const int m = row + e;
+                            if (m < p.M) {
+                                const int n2 = m / p.P;
+                                const int sp2 = m - n2 * p.P;
+                                put1(((Off)n2 * p.K + col) * (Off)p.P + sp2, v[e], col);
+                            }
                         }
                     }
                 }
             }
         }
+    };
+    if (p.splits > 1) {
+        // a split workgroup stores its raw fp32 sums at the same element offsets of its slice of
+        // the partial buffer (16-byte aligned runs); the reduction pass applies the epilogue
+        float *pb = p.part + (int64_t)split * ((int64_t)p.M * p.Ncol);
+        emit([&](Off off, const f32x4 &v, int) __attribute__((always_inline)) { *reinterpret_cast<f32x4 *>(pb + off) = v; },
+             [&](Off off, float v, int) __attribute__((always_inline)) { pb[off] = v; });
+    } else {
+        uint16_t *yb = static_cast<uint16_t *>(p.y);
+        with_epilogue(p, DT == DT_FP8, [&](auto &ep) __attribute__((always_inline)) {
+            emit(
+                [&](Off off, const f32x4 &v, int k) __attribute__((always_inline)) {
+                    if constexpr (MODE == MODE_POINT)
+                        *reinterpret_cast<u32x2 *>(yb + off) = ep.four_channels(v, k);
+                    else
+                        *reinterpret_cast<u32x2 *>(yb + off) = ep.four(v, k);
+                },
+                [&](Off off, float v, int k) __attribute__((always_inline)) { yb[off] = (uint16_t)ep.one(v, k); });
+        });
     }
-    if (!partial)
-        ep.flush();
 }
 
 #define IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_, BIG_, CBLK_)                                              \
@@ -502,57 +501,25 @@ void conv_igemm_dma_kernel(ConvParams p)
         if (cblock) IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_GENERIC, false, true);                       \
         IGC_DLAUNCH(BM_, BN_, WM_, WN_, MF_, S_, MODE_GENERIC, false, false);                                  \
     } while (0)
-// The direct-to-LDS tiles with 128-byte steps (tiles 21 and up).
-template <int DT>
-hipError_t launch_conv_dma128(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream)
+// Launch of one direct-to-LDS tile shape (kTiles[TILE], stages > 0) for one
+// dtype, every (mode, 64-bit offsets, channel-block order) variant. Each
+// conv_dma_*.hip unit instantiates a few tiles (IGC_DMA_INSTANTIATE) so that
+// the units compile in parallel; conv_dma.hip dispatches on the tile index.
+template <int DT, int TILE>
+hipError_t launch_conv_dma_tile(const ConvParams &p, Mode mode, bool big, bool cblock, hipStream_t stream)
 {
+    constexpr TileShape T = kTiles[TILE];
+    static_assert(T.stages > 0 && T.sb == 0, "direct-to-LDS tiles only");
     const dim3 grid((unsigned)(p.tiles_m * p.tiles_n * p.splits));
-    constexpr int KB_ = 128;
-    switch (tile) {
-    case 21: IGC_DMODES(256, 256, 2, 4, 16, 2);
-    case 22: IGC_DMODES(256, 256, 2, 4, 32, 2);
-    case 23: IGC_DMODES(128, 128, 2, 2, 16, 4);
-    case 24: IGC_DMODES(128, 128, 2, 2, 16, 2);
-    case 25: IGC_DMODES(256, 128, 2, 4, 16, 2);
-    case 26: IGC_DMODES(64, 64, 2, 2, 16, 4);
-    default: return hipErrorInvalidValue;
-    }
+    constexpr int KB_ = T.kb;
+    IGC_DMODES(T.bm, T.bn, T.wm, T.wn, T.mf, T.stages);
+    return hipErrorInvalidValue;  // not reached: IGC_DMODES returns on every path
 }
 
-// Launch helper for one dtype: the direct-to-LDS tiles of kTiles (stages > 0).
-template <int DT>
-hipError_t launch_conv_dma_dt(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream)
-{
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n * p.splits));
-    constexpr int KB_ = 64;
-    if constexpr (DT == DT_BF16) {
-        switch (tile) {
-        case 6: IGC_DMODES(256, 256, 2, 4, 16, 4);
-        case 7: IGC_DMODES(256, 256, 2, 4, 32, 4);
-        case 8: IGC_DMODES(128, 128, 2, 2, 16, 4);
-        case 9: IGC_DMODES(128, 128, 2, 2, 32, 4);
-        case 10: IGC_DMODES(128, 128, 2, 2, 16, 8);
-        case 11: IGC_DMODES(64, 64, 2, 2, 16, 4);
-        case 14: IGC_DMODES(256, 256, 2, 2, 16, 4);
-        case 15: IGC_DMODES(256, 256, 2, 2, 32, 4);
-        case 18: IGC_DMODES(256, 128, 2, 2, 16, 3);
-        case 19: IGC_DMODES(256, 128, 2, 2, 32, 3);
-        case 20: IGC_DMODES(128, 256, 2, 2, 16, 3);
-        default: break;
-        }
-    } else {
-        switch (tile) {
-        case 7: IGC_DMODES(256, 256, 2, 4, 32, 4);
-        case 9: IGC_DMODES(128, 128, 2, 2, 32, 4);
-        case 12: IGC_DMODES(128, 128, 2, 2, 32, 8);
-        case 13: IGC_DMODES(64, 64, 2, 2, 32, 4);
-        case 15: IGC_DMODES(256, 256, 2, 2, 32, 4);
-        case 19: IGC_DMODES(256, 128, 2, 2, 32, 3);
-        default: break;
-        }
-    }
-    return launch_conv_dma128<DT>(p, tile, mode, big, cblock, stream);
-}
+#define IGC_DMA_INSTANTIATE(DT_, TILE_)                                                                       \
+    template hipError_t launch_conv_dma_tile<DT_, TILE_>(const ConvParams &, Mode, bool, bool, hipStream_t)
+#define IGC_DMA_EXTERN(DT_, TILE_)                                                                            \
+    extern template hipError_t launch_conv_dma_tile<DT_, TILE_>(const ConvParams &, Mode, bool, bool, hipStream_t)
 
 #undef IGC_DMODES
 #undef IGC_DLAUNCH

@@ -38,7 +38,7 @@ struct WinRows {
     unsigned off[N];              // wraps for rows above or left of the input
     unsigned valid[(N + 1) / 2];  // row i: bits 16 * (i & 1) + t * R + r
 
-    __device__ void init(const ConvParams &p, int g0, int first, int stride, int chunk, int64_t xbase)
+    __device__ __attribute__((always_inline)) void init(const ConvParams &p, int g0, int first, int stride, int chunk, int64_t xbase)
     {
         const int glast = p.N * p.Do * p.Ho - 1;
 #pragma unroll

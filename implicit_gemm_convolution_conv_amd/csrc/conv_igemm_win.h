@@ -233,35 +233,35 @@ void conv_win_kernel(ConvParams p)
     }
 
     // ---------------------------------------------------------------- epilogue
-    Epilogue ep(p, DT == DT_FP8);
     uint16_t *yb = static_cast<uint16_t *>(p.y);
     constexpr int QUADS = MF / 16 * (MF / 16);
     const Off ybase = ((Off)nimg * p.K) * (Off)p.P + (Off)od * P2;  // + k * P + q
+    with_epilogue(p, DT == DT_FP8, [&](auto &ep) __attribute__((always_inline)) {
 #pragma unroll
-    for (int a = 0; a < FM; ++a) {
+        for (int a = 0; a < FM; ++a) {
 #pragma unroll
-        for (int qd = 0; qd < QUADS; ++qd) {
-            const int q = q0 + wm * WTM + a * MF + (MF == 16 ? 4 * lgrp : 8 * qd + 4 * lgrp);
-            const bool vec = (P2 & 3) == 0 && q + 3 < qend;
+            for (int qd = 0; qd < QUADS; ++qd) {
+                const int q = q0 + wm * WTM + a * MF + (MF == 16 ? 4 * lgrp : 8 * qd + 4 * lgrp);
+                const bool vec = (P2 & 3) == 0 && q + 3 < qend;
 #pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const int col = n0 + wn * WTN + b * MF + lrow;
-                if (q >= qend || col >= p.K)
-                    continue;
-                const f32x4 v = quad<MF>(acc[a][b], qd);
-                uint16_t *dst = yb + ybase + (Off)col * p.P + q;
-                if (vec) {
-                    *reinterpret_cast<u32x2 *>(dst) = ep.four(v, col);
-                } else {
+                for (int b = 0; b < FN; ++b) {
+                    const int col = n0 + wn * WTN + b * MF + lrow;
+                    if (q >= qend || col >= p.K)
+                        continue;
+                    const f32x4 v = quad<MF>(acc[a][b], qd);
+                    uint16_t *dst = yb + ybase + (Off)col * p.P + q;
+                    if (vec) {
+                        *reinterpret_cast<u32x2 *>(dst) = ep.four(v, col);
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (q + e < qend)
-                            dst[e] = (uint16_t)ep.one(v[e], col);
+                        for (int e = 0; e < 4; ++e)
+                            if (q + e < qend)
+                                dst[e] = (uint16_t)ep.one(v[e], col);
+                    }
                 }
             }
         }
-    }
-    ep.flush();
+    });
 }
 
 template <int DT>

@@ -168,22 +168,22 @@ __global__ __launch_bounds__(256) void conv_pw_ncdhw_kernel(ConvParams p)
     }
 
     // y[n][k][s]: lane holds positions 4*lgrp..+3 of each 16-row block for output channel lrow of each column block
-    Epilogue ep(p, false);
     uint16_t *yb = static_cast<uint16_t *>(p.y);
+    with_epilogue(p, false, [&](auto &ep) __attribute__((always_inline)) {
 #pragma unroll
-    for (int b = 0; b < SB; ++b) {
-        const int s = s0 + (BM / 4) * wave + 16 * b + 4 * lgrp;
-        if (s >= S)
-            continue;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int k = k0 + 16 * kb + lrow;
-            if (k >= K)
+        for (int b = 0; b < SB; ++b) {
+            const int s = s0 + (BM / 4) * wave + 16 * b + 4 * lgrp;
+            if (s >= S)
                 continue;
-            *reinterpret_cast<u32x2 *>(yb + ((int64_t)n * K + k) * S + s) = ep.four(acc[b][kb], k);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int k = k0 + 16 * kb + lrow;
+                if (k >= K)
+                    continue;
+                *reinterpret_cast<u32x2 *>(yb + ((int64_t)n * K + k) * S + s) = ep.four(acc[b][kb], k);
+            }
         }
-    }
-    ep.flush();
+    });
 }
 
 }  // namespace

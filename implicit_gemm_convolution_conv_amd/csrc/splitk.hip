@@ -22,37 +22,37 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ConvParams p)
     const int64_t ynum = (int64_t)p.M * p.Ncol;
     const float *part = p.part;
     const int splits = p.splits;
-    Epilogue ep(p, p.scales != nullptr);
     uint16_t *y = static_cast<uint16_t *>(p.y);
     const int64_t step = (int64_t)gridDim.x * 256 * 4;
     const bool vec = (ynum & 3) == 0;
     const bool same_k = (p.P & 3) == 0;  // 4 consecutive elements (from a multiple of 4) share a channel
-    for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < ynum; i += step) {
-        if (vec) {
-            f32x4 acc = *reinterpret_cast<const f32x4 *>(part + i);
-            for (int j = 1; j < splits; ++j)
-                acc += *reinterpret_cast<const f32x4 *>(part + (int64_t)j * ynum + i);
-            u32x2 pk;
-            if (same_k) {
-                pk = ep.four(acc, (int)((i / p.P) % p.K));
-            } else {
-                uint32_t r[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    r[e] = ep.one(acc[e], (int)(((i + e) / p.P) % p.K));
-                pk = u32x2{r[0] | (r[1] << 16), r[2] | (r[3] << 16)};
-            }
-            *reinterpret_cast<u32x2 *>(y + i) = pk;
-        } else {
-            for (int e = 0; e < 4 && i + e < ynum; ++e) {
-                float a = part[i + e];
+    with_epilogue(p, p.scales != nullptr, [&](auto &ep) __attribute__((always_inline)) {
+        for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < ynum; i += step) {
+            if (vec) {
+                f32x4 acc = *reinterpret_cast<const f32x4 *>(part + i);
                 for (int j = 1; j < splits; ++j)
-                    a += part[(int64_t)j * ynum + i + e];
-                y[i + e] = (uint16_t)ep.one(a, (int)(((i + e) / p.P) % p.K));
+                    acc += *reinterpret_cast<const f32x4 *>(part + (int64_t)j * ynum + i);
+                u32x2 pk;
+                if (same_k) {
+                    pk = ep.four(acc, (int)((i / p.P) % p.K));
+                } else {
+                    uint32_t r[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        r[e] = ep.one(acc[e], (int)(((i + e) / p.P) % p.K));
+                    pk = u32x2{r[0] | (r[1] << 16), r[2] | (r[3] << 16)};
+                }
+                *reinterpret_cast<u32x2 *>(y + i) = pk;
+            } else {
+                for (int e = 0; e < 4 && i + e < ynum; ++e) {
+                    float a = part[i + e];
+                    for (int j = 1; j < splits; ++j)
+                        a += part[(int64_t)j * ynum + i + e];
+                    y[i + e] = (uint16_t)ep.one(a, (int)(((i + e) / p.P) % p.K));
+                }
             }
         }
-    }
-    ep.flush();
+    });
 }
 
 __global__ void amax_clear_kernel(float *out)

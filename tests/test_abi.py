@@ -316,8 +316,9 @@ def test_point_gradient_entry_points():
     assert B.conv_packed_w_t_cols((18, 5, 1, 3, 7)) == 64
     ldn = 9536  # 9500 images rounded up to 64
     base = (588 * ldn * 2 + 255) // 256 * 256 + (1280 * ldn * 2 + 255) // 256 * 256
-    # 64x64 tiles over 588 x 1280: 200 tiles, no split
-    assert B.conv_bwd_weight_workspace_bytes(xs, ws, st, z, one, B.IGC_BF16, B.IGC_NCDHW) == base
+    # a 149-step reduction: 128x128 tiles over 588 x 1280 (50 tiles), 10 splits of 15 steps, fp32 slices
+    assert B.conv_bwd_weight_workspace_bytes(xs, ws, st, z, one, B.IGC_BF16, B.IGC_NCDHW) == \
+        base + 10 * 1280 * 588 * 4
     # 37 images of 5 x 3 x 7 -> 18 channels: one reduction step over 64 (padded) images, too short to split
     small = B.conv_bwd_weight_workspace_bytes((37, 5, 1, 3, 7), (18, 5, 1, 3, 7), (1, 3, 7), z, one, B.IGC_BF16,
                                               B.IGC_NDHWC)
