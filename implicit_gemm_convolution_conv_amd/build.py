@@ -8,6 +8,7 @@ shared library next to this file. Always recompiles.
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -33,14 +34,34 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# Kernels allowed to use private (scratch) memory: the 4-wave 256x256 direct-to-LDS tiles (256 fp32
+# accumulators per lane, kept only as a measured negative result) and the fp8 register-staged 256x256
+# tile with 64-bit offsets. Anywhere else scratch means a register spill or a kernel argument copied
+# to private memory, which slows the kernel several times over: the build fails.
+SCRATCH_OK = ("conv_igemm_dma_kernelILi256ELi256ELi2ELi2E", "conv_igemm_kernelILi256ELi256ELi2ELi4ELi16ELi1ELi0ELb1E")
+
+
+def _scratch_kernels(remarks: str) -> list[str]:
+    bad = []
+    for blk in re.split(r"Function Name: ", remarks)[1:]:
+        name = blk.split()[0]
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", blk)
+        if m and int(m.group(1)) > 0 and not any(k in name for k in SCRATCH_OK):
+            bad.append(f"{name} ({m.group(1)} bytes/lane)")
+    return bad
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the gfx target feature above; that warning is expected
-    err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+    err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l and "remark:" not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{err}")
+    bad = _scratch_kernels(res.stderr)
+    if bad:
+        raise RuntimeError(f"kernels in {src} use scratch memory:\n" + "\n".join(bad))
     return obj
 
 
