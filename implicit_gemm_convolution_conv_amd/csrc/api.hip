@@ -179,6 +179,38 @@ bool is_temporal(const Geometry &g)
     return g.R == 1 && g.S == 1 && g.ph == 0 && g.pw == 0 && g.sh == 1 && g.sw == 1;
 }
 
+// Tile of a point-output GEMM (forward point path and the backward GEMMs): one
+// round of tiles on the GPU is what these grids take, so the tile shape that
+// fills the round best wins, among 256x256, 256x192 (bf16) and 128x128 (two
+// per CU); grids too small for 128x128 tiles take 64x64 as elsewhere.
+// Measured on MI355X with the 9500-image patch embed: forward (1280 x 9500
+// over 588) 256x192 27.7 us, 256x256 33.5 us, 128x128 34 us; backward data
+// (588 x 9500 over 1280) 128x128 27.8 us, 256x192 38 us, 256x256 46.6 us.
+int point_tile(int64_t M, int64_t Ncol, bool bf16)
+{
+    auto nblocks = [&](int t) {
+        return (M + kTiles[t].bm - 1) / kTiles[t].bm * ((Ncol + kTiles[t].bn - 1) / kTiles[t].bn);
+    };
+    if (nblocks(21) >= 512)
+        return 21;
+    if (nblocks(21) < 160 && nblocks(24) < 256)
+        return 26;
+    int best = 21;
+    double best_fill = 0.0;
+    for (int t : {21, 40, 24}) {
+        if (t == 40 && !bf16)
+            continue;
+        const int64_t slots = kTiles[t].bm * kTiles[t].bn > 128 * 128 ? 256 : 512;  // workgroups resident at once
+        const int64_t n = nblocks(t), rounds = (n + slots - 1) / slots;
+        const double fill = (double)n / (double)(rounds * slots);
+        if (fill > best_fill + 1e-9) {
+            best = t;
+            best_fill = fill;
+        }
+    }
+    return best;
+}
+
 int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int32_t *pad, const int32_t *dil,
               int dtype, int x_layout, Plan &pl)
 {
@@ -306,7 +338,8 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         // reaches ~160 workgroups, the point-output GEMM of the patch embed
         // (190 workgroups) included; smaller grids take the 128x128 (two
         // workgroups per CU) or 64x64 (4-stage ring) direct-to-LDS tiles.
-        tile = nblocks(21) >= 160 ? 21 : (nblocks(24) >= 256 ? 24 : 26);
+        tile = path == IGC_PATH_POINT ? point_tile(p.M, p.Ncol, esz == 2)
+                                      : (nblocks(21) >= 160 ? 21 : (nblocks(24) >= 256 ? 24 : 26));
         // Where the whole-channel-block im2col order applies and each tile's
         // reach into x (and the whole packed filter) fits a 2^31-byte buffer
         // range, a buffer-addressed 256x256 tile
@@ -323,7 +356,7 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
             return fail(IGC_ERR_UNSUPPORTED, "tile %d: fp8 with 64-byte steps needs 32x32 MFMA blocks", tile);
         if (esz == 2 && (tile == 12 || tile == 13))
             return fail(IGC_ERR_UNSUPPORTED, "tile %d is an fp8-only tile", tile);
-        if (esz == 1 && (tile == 20 || tile == 30))
+        if (esz == 1 && (tile == 20 || tile == 30 || tile == 40))
             return fail(IGC_ERR_UNSUPPORTED, "tile %d is a bf16-only tile", tile);
         if (is_window(kTiles[tile]) && path != IGC_PATH_GENERIC)
             return fail(IGC_ERR_UNSUPPORTED, "tile %d (input window) runs the generic im2col path only", tile);
@@ -398,6 +431,8 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
     // Workgroups resident on one XCD (32 CUs): one 256x256 or two smaller tiles per CU.
     const int resident = 32 * (ts.bm * ts.bn >= 256 * 256 ? 1 : 2);
     p.group_m = (int)std::max<int64_t>(1, resident / tn);
+    if (path == IGC_PATH_POINT)  // few tile rows: all of them per column, so an image block is fetched once per XCD
+        p.group_m = (int)std::max<int64_t>(p.group_m, std::min<int64_t>(tm, 8));
     if (g_force_group_m.load() > 0)
         p.group_m = g_force_group_m.load();
     p.ksplit = p.nk;
@@ -470,13 +505,10 @@ int plan_point_gemm(int64_t M, int64_t Ncol, int64_t Rk, int64_t ldw, int64_t ld
     p.ldw = (int)ldw;
     p.P = 1;
     p.Do = p.Ho = p.Wo = 1;
-    auto nblocks = [&](int t) {
-        return (M + kTiles[t].bm - 1) / kTiles[t].bm * ((Ncol + kTiles[t].bn - 1) / kTiles[t].bn);
-    };
     int tile = g_force_tile.load();
     if (tile < 0 || tile >= kNumTiles || is_buffer(kTiles[tile]) || is_window(kTiles[tile]) ||
         is_pointwise_tile(tile) || tile == 12 || tile == 13) {
-        tile = nblocks(21) >= 160 ? 21 : (nblocks(24) >= 256 ? 24 : 26);
+        tile = point_tile(M, Ncol, true);
         // A long reduction that will be split (backward weights over the batch): 128x128 tiles, then
         // enough splits to fill the GPU; measured on the 9500-image patch embed (588 x 1280 over 9536):
         // 128x128 with 8 splits 51.5 us, 64x64 with 4-10 splits 61-64 us.
@@ -494,7 +526,7 @@ int plan_point_gemm(int64_t M, int64_t Ncol, int64_t Rk, int64_t ldw, int64_t ld
     p.tiles_m = (int)tm;
     p.tiles_n = (int)tn;
     const int resident = 32 * (ts.bm * ts.bn >= 256 * 256 ? 1 : 2);
-    p.group_m = (int)std::max<int64_t>(1, resident / tn);
+    p.group_m = (int)std::max<int64_t>({(int64_t)1, resident / tn, std::min<int64_t>(tm, 8)});
     if (g_force_group_m.load() > 0)
         p.group_m = g_force_group_m.load();
     pl.path = IGC_PATH_POINT;

@@ -23,6 +23,7 @@ IGC_DMA_EXTERN(DT_BF16, 23);
 IGC_DMA_EXTERN(DT_BF16, 24);
 IGC_DMA_EXTERN(DT_BF16, 25);
 IGC_DMA_EXTERN(DT_BF16, 26);
+IGC_DMA_EXTERN(DT_BF16, 40);
 IGC_DMA_EXTERN(DT_FP8, 7);
 IGC_DMA_EXTERN(DT_FP8, 9);
 IGC_DMA_EXTERN(DT_FP8, 12);
@@ -56,6 +57,7 @@ hipError_t launch_conv_dma_bf16(const ConvParams &p, int tile, Mode mode, bool b
     case 24: return launch_conv_dma_tile<DT_BF16, 24>(p, mode, big, cblock, stream);
     case 25: return launch_conv_dma_tile<DT_BF16, 25>(p, mode, big, cblock, stream);
     case 26: return launch_conv_dma_tile<DT_BF16, 26>(p, mode, big, cblock, stream);
+    case 40: return launch_conv_dma_tile<DT_BF16, 40>(p, mode, big, cblock, stream);
     default: return hipErrorInvalidValue;
     }
 }

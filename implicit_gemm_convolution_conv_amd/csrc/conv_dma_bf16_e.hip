@@ -5,4 +5,5 @@ namespace igc {
 IGC_DMA_INSTANTIATE(DT_BF16, 24);
 IGC_DMA_INSTANTIATE(DT_BF16, 25);
 IGC_DMA_INSTANTIATE(DT_BF16, 26);
+IGC_DMA_INSTANTIATE(DT_BF16, 40);
 }  // namespace igc

@@ -76,7 +76,11 @@ def test_path_selection():
     # a single input plane of 2 GB cannot fit one buffer window: 64-bit global-address loads
     p = _plan((1, 128, 3, 4096, 2049), (128, 128, 3, 3, 3), pd=(1, 1, 1))
     assert (p["big"], p["loads"]) == ("1", "global-lds")
-    assert _plan((9500, 3, 1, 14, 14), (1280, 3, 1, 14, 14), (1, 14, 14), lay=B.IGC_NCDHW)["grid"] == "190"
+    # point output: the tile that fills one round of the GPU best, 256x192 (5 x 50 = 250 tiles) for the patch embed
+    p = _plan((9500, 3, 1, 14, 14), (1280, 3, 1, 14, 14), (1, 14, 14), lay=B.IGC_NCDHW)
+    assert (p["tile"], p["grid"], p["group_m"]) == ("256x192", "250", "5")
+    p = _plan((9500, 3, 1, 14, 14), (1280, 3, 1, 14, 14), (1, 14, 14), lay=B.IGC_NCDHW, dt=B.IGC_FP8_E4M3FN)
+    assert (p["tile"], p["grid"]) == ("256x256", "190")  # 256x192 is a bf16-only tile
     assert _plan((1, 1024, 240, 160, 90), (1024, 1024, 3, 1, 1), pd=(1, 0, 0))["big"] == "1"
     p = _plan((1, 64, 4, 16, 16), (64, 64, 3, 3, 3), pd=(1, 1, 1))
     assert (p["tile"], p["stages"]) == ("64x64", "4")

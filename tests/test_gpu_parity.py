@@ -262,7 +262,7 @@ DMA_CASES = [g for g in GEOMS if g[0] in ("ragged_linear_c24", "c128_cblock_mult
                                            "temporal_3x1x1", "temporal_strided_dilated", "c8_tiny")]
 
 
-@pytest.mark.parametrize("tile", [6, 7, 8, 9, 14, 15, 18, 19, 20, 21, 22, 23, 24, 25, 26])
+@pytest.mark.parametrize("tile", [6, 7, 8, 9, 14, 15, 18, 19, 20, 21, 22, 23, 24, 25, 26, 40])
 @pytest.mark.parametrize("case", DMA_CASES, ids=[g[0] for g in DMA_CASES])
 def test_dma_tiles_bf16(tile, case):
     name, xs, ws, st, pd, dl = case
@@ -270,7 +270,7 @@ def test_dma_tiles_bf16(tile, case):
         _bf16_case(f"dma tile {tile} {name}", xs, ws, st, pd, dl, seed=zlib.crc32(name.encode()) % 1000)
 
 
-@pytest.mark.parametrize("tile", [6, 7, 8, 9, 14, 15, 21, 22])
+@pytest.mark.parametrize("tile", [6, 7, 8, 9, 14, 15, 21, 22, 40])
 def test_dma_tiles_integer_bit_exact(tile):
     _announce(f"dma tile {tile} integer")
     with forced(tile=tile):
@@ -310,7 +310,7 @@ def test_dma_tiles_agree_bitwise():
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
-@pytest.mark.parametrize("tile", [8, 10, 11, 21, 22, 23, 24, 25, 26])
+@pytest.mark.parametrize("tile", [8, 10, 11, 21, 22, 23, 24, 25, 26, 40])
 @pytest.mark.parametrize("layout", ["NCDHW", "NDHWC"])
 def test_point_output_dma_tiles(tile, layout):
     with forced(tile=tile):
@@ -320,7 +320,7 @@ def test_point_output_dma_tiles(tile, layout):
                    (0, 0, 0), (1, 1, 1), seed=9, dist=("normal", 1.0), x_layout=layout)
 
 
-@pytest.mark.parametrize("tile", [8, 10, 11, 21])
+@pytest.mark.parametrize("tile", [8, 10, 11, 21, 40])
 def test_point_output_dma_integer_bit_exact(tile):
     _announce(f"integer point dma tile {tile}")
     with forced(tile=tile):
