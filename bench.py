@@ -311,7 +311,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", default=None, help="comma list of extra workloads (c1,c2,c4,c4t,c5,pw,c3ex,c2grad)")
+    ap.add_argument("--only", default=None, help="comma list of extra workloads (c1,c2,c4,c4t,c5,pw,c3ex,c2grad,c3s,c5s)")
     ap.add_argument("--profile", action="store_true",
                     help="counter-collection run: the headline conv `steps` times, then one 1 GiB device copy "
                          "(the reference for scaling FETCH_SIZE / WRITE_SIZE); prints nothing else")
@@ -354,7 +354,8 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        names = args.only.split(",") if args.only else ["c1", "c2", "c4", "c4t", "c5", "pw", "c3ex", "c2grad"]
+        names = args.only.split(",") if args.only else ["c1", "c2", "c4", "c4t", "c5", "pw", "c3ex", "c2grad",
+                                                         "c3s", "c5s"]
         for name in names:
             log(f"[bench] extra workload {name}")
             if name == "c3ex":

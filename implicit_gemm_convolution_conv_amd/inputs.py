@@ -22,6 +22,11 @@ them; the draws themselves are synthetic):
 * ``c5``  large conv3d bf16 (x and y above 2^31 elements): N=1 C=1024 D=240
   H=160 W=90, K=1024, 3x1x1, pad (1, 0, 0); x ~ U(-1, 1),
   w ~ N(0, 1/sqrt(3C)).
+* ``c3s`` one GPU's share of c3 split 8 ways over output channels: the c3
+  activations with a 256-channel filter slice (no exchange between GPUs).
+* ``c5s`` one GPU's share of c5 split 8 ways over time: 30 output planes,
+  read from 32 input planes (its 30 plus the (T - 1) * dd = 2 halo planes a
+  neighbour would send), no padding (an interior shard).
 * ``pw``  1x1x1 conv3d bf16 on NCDHW activations, C=512 -> K=48 over
   D=240 H=320 W=180 (14 GB of activations): the shape the FlyDSL page's
   1x1x1 measurement implies (its description gives the 14 GB A operand and
@@ -82,6 +87,14 @@ WORKLOADS = {
     "c5": Workload("c5", (1, 1024, 240, 160, 90), (1024, 1024, 3, 1, 1), pad=(1, 0, 0),
                    x_dist=("uniform", 1.0), w_dist=("normal", 1.0 / math.sqrt(_R(1024, 3, 1, 1))), seed=5,
                    note="large conv3d fwd bf16 N=1 C=1024 D=240 H=160 W=90 K=1024 3x1x1 pad (1,0,0)"),
+    "c3s": Workload("c3s", (1, 2048, 60, 80, 45), (256, 2048, 3, 3, 3), pad=(1, 1, 1), x_layout="NDHWC",
+                    x_dist=("normal", 1.0), w_dist=("normal", 1.0 / math.sqrt(_R(2048, 3, 3, 3))), seed=3,
+                    note="c3 share of one of 8 GPUs (output channels 256 of 2048): conv3d fwd bf16 NDHWC "
+                         "N=1 C=2048 D=60 H=80 W=45 K=256 3x3x3 s1 p1"),
+    "c5s": Workload("c5s", (1, 1024, 32, 160, 90), (1024, 1024, 3, 1, 1),
+                    x_dist=("uniform", 1.0), w_dist=("normal", 1.0 / math.sqrt(_R(1024, 3, 1, 1))), seed=5,
+                    note="c5 share of one of 8 GPUs (30 of 240 output planes, 2 halo planes): conv3d fwd bf16 "
+                         "N=1 C=1024 D=32 H=160 W=90 K=1024 3x1x1 pad 0"),
     "pw": Workload("pw", (1, 512, 240, 320, 180), (48, 512, 1, 1, 1),
                    x_dist=("normal", 1.0), w_dist=("normal", 1.0 / math.sqrt(512)), seed=6,
                    note="1x1x1 conv3d fwd bf16 NCDHW (no transpose) N=1 C=512 D=240 H=320 W=180 K=48"),

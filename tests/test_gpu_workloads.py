@@ -186,3 +186,66 @@ def test_pointwise_ncdhw_page_workload():
     for kk in range(k):
         assert torch.equal(y[:, kk].view(torch.int16), x[:, perm[kk]].view(torch.int16)), kk
     _free()
+
+
+@pytest.mark.parametrize("name", ["c3s", "c5s"])
+def test_one_gpu_share_sampled(name):
+    # one GPU's share of an 8-way split, at its real shape: the kernel that GPU would run
+    wl = I.WORKLOADS[name]
+    _announce(f"{name} one-GPU share, sampled vs oracle")
+    x, w = I.make(wl, P.DEV)
+    xs, ws = wl.x_shape, wl.w_shape
+    wp = PL.packed_weight(w, "bf16", "NDHWC")
+    xk = x if wl.x_layout == "NDHWC" else PL.packed_input(x, "bf16")
+    y = PL.output(xs, ws, wl.stride, wl.pad, wl.dil, P.DEV)
+    B.conv_fwd(xk, wp, y, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    pts = P.sample_points(1, ws[0], *y.shape[2:], rng, n_random=400)
+    ref = O.conv3d_points(P.bits(x), P.bits(w), pts, wl.stride, wl.pad, wl.dil, x_layout=wl.x_layout)
+    P.check_close(P.gather(y, pts), ref, wl.reduction, float(x.abs().max()), float(w.abs().max()), name)
+    _free()
+
+
+def test_shards_reassemble_the_full_output():
+    # the two splits the path shards along, on a reduced c3 / c5 geometry: output channels (each GPU a
+    # filter slice, no exchange) and time (each GPU its output planes from its input planes plus the halo
+    # planes its neighbours send, zero planes at the ends); every launch runs the same tile, so the shards'
+    # outputs are the full output's slices bit for bit
+    _announce("shards reassemble the full output")
+    g = I.generator(8, P.DEV)
+    xs, ws = (1, 256, 12, 20, 18), (192, 256, 3, 3, 3)
+    x = I.draw(xs, ("normal", 1.0), g, P.DEV)
+    w = I.draw(ws, ("normal", 0.02), g, P.DEV)
+    one, pad1 = (1, 1, 1), (1, 1, 1)
+    B.conv_debug_force(B.IGC_PATH_AUTO, 24, 0)
+    try:
+        xk = PL.packed_input(x, "bf16")
+        full = PL.output(xs, ws, one, pad1, one, P.DEV)
+        B.conv_fwd(xk, PL.packed_weight(w, "bf16", "NDHWC"), full, xs, ws, one, pad1, one, B.IGC_BF16, B.IGC_NDHWC)
+        for k0 in range(0, 192, 64):  # 3 GPUs, 64 output channels each
+            wsh = (64,) + ws[1:]
+            part = PL.output(xs, wsh, one, pad1, one, P.DEV)
+            B.conv_fwd(xk, PL.packed_weight(w[k0:k0 + 64].contiguous(), "bf16", "NDHWC"), part, xs, wsh, one,
+                       pad1, one, B.IGC_BF16, B.IGC_NDHWC)
+            torch.cuda.synchronize()
+            assert torch.equal(part.view(torch.int16), full[:, k0:k0 + 64].contiguous().view(torch.int16)), k0
+        # time split of a 3x1x1 conv with pad (1, 0, 0): 3 GPUs of 4 output planes; GPU g reads padded
+        # input planes 4g .. 4g + 5 (its own 4 and one halo plane per side), with no padding of its own
+        wt = I.draw((128, 256, 3, 1, 1), ("normal", 0.03), g, P.DEV)
+        wtp = PL.packed_weight(wt, "bf16", "NDHWC")
+        tpad = (1, 0, 0)
+        full = PL.output(xs, wt.shape, one, tpad, one, P.DEV)
+        B.conv_fwd(xk, wtp, full, xs, wt.shape, one, tpad, one, B.IGC_BF16, B.IGC_NDHWC)
+        xpad = torch.nn.functional.pad(xk, (0, 0, 0, 0, 0, 0, 1, 1))  # zero plane before and after (NDHWC)
+        for d0 in range(0, 12, 4):
+            xsh = xpad[:, d0:d0 + 6].contiguous()
+            shp = (1, 256, 6, 20, 18)
+            part = PL.output(shp, wt.shape, one, (0, 0, 0), one, P.DEV)
+            B.conv_fwd(xsh, wtp, part, shp, wt.shape, one, (0, 0, 0), one, B.IGC_BF16, B.IGC_NDHWC)
+            torch.cuda.synchronize()
+            assert part.shape[2] == 4
+            assert torch.equal(part.view(torch.int16), full[:, :, d0:d0 + 4].contiguous().view(torch.int16)), d0
+    finally:
+        B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)
+    _free()
