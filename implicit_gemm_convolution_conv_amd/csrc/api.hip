@@ -345,12 +345,16 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         // range, a buffer-addressed 256x256 tile
         // replaces the large tile: activations issued two steps ahead (3 x 32 KB
         // ring), the filter one step ahead (2 x 32 KB). bf16 takes tile 29
-        // (loads spread over the first half of each step's MFMA rows); fp8 the
-        // ping-pong wave groups of tile 33 (1-2 % faster there, 10 % slower on bf16).
+        // (loads spread over the first half of each step's MFMA rows); fp8 with
+        // long reductions the ping-pong wave groups of tile 33 (1-2 % faster on
+        // c4, 10 % slower on bf16).
         const bool buffer_ok = path != IGC_PATH_POINT && g.C % (128 / esz) == 0 &&
                                buffer_x_span(g, esz) < 0x7ffffff0 && g.K * ldw * esz < (int64_t(1) << 31);
+        // fp8 with a long reduction takes the ping-pong wave groups of tile 33; with a short one (a 3x1x1
+        // filter: 48 steps on c4t) tile 33 measured 4 % slower than tile 29 (2.43 against 2.33 ms).
+        const int64_t fp8_steps = g.T * g.R * g.S * (g.C / 128);
         if (tile == 21 && buffer_ok)
-            tile = (esz == 1 && g.T * g.R * g.S <= 32) ? 33 : 29;
+            tile = (esz == 1 && g.T * g.R * g.S <= 32 && fp8_steps >= 128) ? 33 : 29;
     } else {
         if (kTiles[tile].stages && kTiles[tile].mf == 16 && esz == 1 && kTiles[tile].kb == 64)
             return fail(IGC_ERR_UNSUPPORTED, "tile %d: fp8 with 64-byte steps needs 32x32 MFMA blocks", tile);
