@@ -10,6 +10,7 @@
 namespace igc {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ amax
 // Non-negative floats order like their bit patterns, so the maximum of
@@ -21,23 +22,37 @@ __global__ void amax_zero_kernel(float *out)
         *out = 0.0f;
 }
 
+// Each lane keeps eight independent 16-byte loads in flight per round and
+// folds them with packed 16-bit maxima; the grid covers the CUs 16 times.
 __global__ __launch_bounds__(256) void amax_kernel(const uint16_t *t, int64_t n, unsigned *out)
 {
+    constexpr int U = 8;
     const int64_t nvec = n >> 3;  // 8 bf16 per 16-byte load
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    unsigned m = 0;
     const i32x4 *tv = reinterpret_cast<const i32x4 *>(t);
-    for (int64_t i = gid; i < nvec; i += stride) {
+    us2 mx = {0, 0};
+    int64_t i = gid;
+    for (; i + (U - 1) * stride < nvec; i += U * stride) {
+        i32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = __builtin_nontemporal_load(tv + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, (unsigned)v[u][q] & 0x7fff7fffu));
+    }
+    for (; i < nvec; i += stride) {
         const i32x4 v = tv[i];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const unsigned u = (unsigned)v[q];
-            m = max(m, max(u & 0x7fffu, (u >> 16) & 0x7fffu));
-        }
+        for (int q = 0; q < 4; ++q)
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, (unsigned)v[q] & 0x7fff7fffu));
     }
-    for (int64_t i = nvec * 8 + gid; i < n; i += stride)
-        m = max(m, (unsigned)(t[i] & 0x7fffu));
+    unsigned m = mx[0] > mx[1] ? mx[0] : mx[1];
+    for (int64_t j = nvec * 8 + gid; j < n; j += stride)
+        m = max(m, (unsigned)(t[j] & 0x7fffu));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
         m = max(m, (unsigned)__shfl_xor((int)m, off));
@@ -104,84 +119,119 @@ __device__ inline uint32_t e4m3_rne_sat(float v)
 }
 
 // ------------------------------------------------------------------ activation pack
-// One workgroup transposes a 64 (channels) x 64 (spatial) tile of one image
-// through LDS. Reads are 16-byte pieces of channel rows (8 spatial), writes
-// are 16-byte pieces of spatial rows (8 bf16 or 16 fp8 channels).
+// Register transpose, no LDS and no barrier. A lane reads CPT channel rows x
+// 8 spatial positions (one 16-byte load per row when S % 8 == 0), transposes
+// them in registers and writes 8 spatial rows x CPT channels (one 16-byte
+// store per row: 8 bf16 values or 16 fp8 codes). Eight lanes side by side
+// along channels and eight along space make every load and every store of a
+// wave cover whole 128-byte lines: 8 channel rows x 128 bytes on the read
+// side, 8 spatial rows x 128 bytes on the write side. A workgroup (4 waves)
+// covers 8*CPT channels x 256 spatial positions.
+//
+// Block order, measured on MI355X: bf16 walks the channel blocks of one
+// spatial range together (whole output rows written side by side) with
+// nontemporal stores; fp8 walks the spatial blocks of one channel block.
+//
+// fp8 codes: a lane first takes the largest |bf16| it holds. When that value
+// times |inv| is below 448, no product can saturate or be NaN, and the
+// hardware conversion (round to nearest even into E4M3FN) gives the code;
+// otherwise the lane encodes with e4m3_rne_sat. Both give the same bits
+// wherever both apply.
 template <bool FP8, bool VEC_S>
 __global__ __launch_bounds__(256) void pack_x_kernel(const uint16_t *x, void *out, int64_t C, int64_t S,
                                                      int64_t cblocks, int64_t sblocks, const float *pair)
 {
-    __shared__ uint32_t tile[64][65];
+    constexpr int CPT = FP8 ? 16 : 8;  // channels per lane
+    constexpr int CB = 8 * CPT;        // channels per workgroup
     const int64_t b = blockIdx.x;
-    const int64_t sb = b % sblocks;
-    const int64_t rest = b / sblocks;
-    const int64_t cb = rest % cblocks;
-    const int64_t n = rest / cblocks;
-    const int64_t c0 = cb * 64, s0 = sb * 64;
-    const int tid = threadIdx.x;
-
-    {  // load: thread -> channel row (tid / 8 + 32 p), spatial piece (tid % 8)
-        const int sc = (tid & 7) * 8;
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int cl = (tid >> 3) + 32 * p;
-            const int64_t c = c0 + cl;
-            const int64_t s = s0 + sc;
-            if (c >= C)
-                continue;
-            const uint16_t *src = x + (n * C + c) * S + s;
-            if (VEC_S) {
-                if (s < S) {
-                    const i32x4 v = *reinterpret_cast<const i32x4 *>(src);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        tile[cl][sc + 2 * q] = (uint32_t)v[q] & 0xffffu;
-                        tile[cl][sc + 2 * q + 1] = (uint32_t)v[q] >> 16;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (s + e < S)
-                        tile[cl][sc + e] = src[e];
-            }
-        }
+    int64_t sb, cb, n;
+    if (FP8) {
+        sb = b % sblocks;
+        const int64_t r = b / sblocks;
+        cb = r % cblocks;
+        n = r / cblocks;
+    } else {
+        cb = b % cblocks;
+        const int64_t r = b / cblocks;
+        sb = r % sblocks;
+        n = r / sblocks;
     }
-    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t c = cb * CB + (lane & 7) * CPT;  // C % CPT == 0: all CPT channels in range or none
+    const int64_t s = sb * 256 + wave * 64 + (lane >> 3) * 8;
+    if (c >= C || s >= S)
+        return;
+    const int ns = S - s < 8 ? (int)(S - s) : 8;  // spatial positions in range (8 unless at the ragged end)
 
-    if (!FP8) {  // store: thread -> spatial row (tid / 8 + 32 p), 8 channels (tid % 8)
-        const int cc = (tid & 7) * 8;
-        uint16_t *o = static_cast<uint16_t *>(out);
+    uint32_t r[CPT][4];  // r[i][q]: channel c + i, positions s + 2q (low half) and s + 2q + 1 (high half)
+    const uint16_t *src = x + (n * C + c) * S + s;
+    if (VEC_S) {
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int sl = (tid >> 3) + 32 * p;
-            const int64_t s = s0 + sl, c = c0 + cc;
-            if (s >= S || c >= C)
-                continue;
-            i32x4 v;
+        for (int i = 0; i < CPT; ++i) {
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(src + i * S);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                v[q] = (int)(tile[cc + 2 * q][sl] | (tile[cc + 2 * q + 1][sl] << 16));
-            *reinterpret_cast<i32x4 *>(o + (n * S + s) * C + c) = v;
+                r[i][q] = (uint32_t)v[q];
         }
-    } else {  // store: thread -> spatial row (tid / 4), 16 channels (tid % 4)
-        const float inv = pair[1];
-        const int cc = (tid & 3) * 16;
-        const int sl = tid >> 2;
-        const int64_t s = s0 + sl, c = c0 + cc;
-        if (s < S && c < C) {
-            i32x4 v;
+    } else {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                uint32_t wd = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float f = __uint_as_float(tile[cc + 4 * q + e][sl] << 16) * inv;
-                    wd |= e4m3_rne_sat(f) << (8 * e);
-                }
-                v[q] = (int)wd;
+                const uint32_t lo = 2 * q < ns ? src[i * S + 2 * q] : 0u;
+                const uint32_t hi = 2 * q + 1 < ns ? src[i * S + 2 * q + 1] : 0u;
+                r[i][q] = lo | (hi << 16);
             }
-            *reinterpret_cast<i32x4 *>(static_cast<uint8_t *>(out) + (n * S + s) * C + c) = v;
+    }
+
+    if (!FP8) {
+        uint16_t *o = static_cast<uint16_t *>(out) + (n * S + s) * C + c;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (e >= ns)
+                break;
+            i32x4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {  // channels 2q, 2q+1 at position e
+                const uint32_t lo = r[2 * q][e >> 1], hi = r[2 * q + 1][e >> 1];
+                v[q] = (e & 1) ? (int)((lo >> 16) | (hi & 0xffff0000u)) : (int)((lo & 0xffffu) | (hi << 16));
+            }
+            __builtin_nontemporal_store(v, reinterpret_cast<i32x4 *>(o + e * C));
+        }
+    } else {
+        const float inv = pair[1];
+        us2 mx = {0, 0};
+#pragma unroll
+        for (int i = 0; i < CPT; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, r[i][q] & 0x7fff7fffu));
+        const uint32_t m16 = mx[0] > mx[1] ? mx[0] : mx[1];
+        // false for NaN too (a NaN input or inv makes the comparison false)
+        const bool hw = __uint_as_float(m16 << 16) * __builtin_fabsf(inv) < 448.0f;
+        uint8_t *o = static_cast<uint8_t *>(out) + (n * S + s) * C + c;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (e >= ns)
+                break;
+            i32x4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {  // channels 4q .. 4q+3 at position e
+                float f[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t wd = r[4 * q + j][e >> 1];
+                    f[j] = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16)) * inv;
+                }
+                if (hw) {
+                    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+                    v[q] = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], pk, true);
+                } else {
+                    v[q] = (int)(e4m3_rne_sat(f[0]) | (e4m3_rne_sat(f[1]) << 8) | (e4m3_rne_sat(f[2]) << 16) |
+                                 (e4m3_rne_sat(f[3]) << 24));
+                }
+            }
+            *reinterpret_cast<i32x4 *>(o + e * C) = v;
         }
     }
 }
@@ -189,7 +239,10 @@ __global__ __launch_bounds__(256) void pack_x_kernel(const uint16_t *x, void *ou
 hipError_t launch_pack_x(const uint16_t *x, void *out, int64_t N, int64_t C, int64_t S, Dtype dt,
                          const float *pair, hipStream_t stream)
 {
-    const int64_t cblocks = (C + 63) / 64, sblocks = (S + 63) / 64;
+    const int64_t cb_ch = dt == DT_FP8 ? 128 : 64;
+    const int64_t cblocks = (C + cb_ch - 1) / cb_ch, sblocks = (S + 255) / 256;
+    if (N * cblocks * sblocks > (int64_t(1) << 24))  // a dispatch holds at most 2^32 work-items
+        return hipErrorInvalidValue;
     const dim3 grid((unsigned)(N * cblocks * sblocks));
     const bool vec = (S % 8) == 0;
     if (dt == DT_FP8) {

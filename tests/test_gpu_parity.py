@@ -239,6 +239,32 @@ def test_pack_bf16_is_a_transpose():
         assert np.array_equal(P.bits(out), np.moveaxis(P.bits(x), 1, -1))
 
 
+@pytest.mark.parametrize("order", ["sorted", "shuffled"])
+def test_fp8_pack_every_bf16_pattern(order):
+    # Every bf16 bit pattern (NaNs, infinities, subnormals and both zeros included), packed to fp8 under
+    # several inverse scales and compared code for code with the oracle's encoder. "sorted" puts 128
+    # neighbouring patterns in each lane's 16 channels x 8 positions, so most lanes hold no value that
+    # can saturate; "shuffled" mixes magnitudes in every lane.
+    _announce(f"fp8 pack, all 65536 bf16 patterns, {order}")
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    if order == "shuffled":
+        pats = pats[np.random.default_rng(43).permutation(65536)]
+    xb = np.ascontiguousarray(pats.reshape(4096, 16).T)  # x[0, c, 0, 0, s] = pats[16 s + c]
+    xs = (1, 16, 1, 1, 4096)
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).reshape(xs).to(P.DEV)
+    for inv in (1.0, 448.0 / 3.0, 2.0 ** -7, 1.5, 3.0e38, 1.0e-30):
+        inv32 = np.float32(inv)
+        pair = torch.tensor([1.0, float(inv32)], dtype=torch.float32, device=P.DEV)
+        xq = torch.empty((1, 1, 1, 4096, 16), dtype=torch.uint8, device=P.DEV)
+        B.conv_pack_x(x, xq, xs, B.IGC_FP8_E4M3FN, pair)
+        torch.cuda.synchronize()
+        ref = O.quantize_e4m3(xb, inv32)  # (16, 4096) codes
+        got = xq.cpu().numpy().reshape(4096, 16).T
+        bad = np.nonzero(got != ref)
+        assert bad[0].size == 0, (f"inv={inv32}: {bad[0].size} codes differ, e.g. bf16 {xb[bad][:4]} -> "
+                                  f"{got[bad][:4]} vs oracle {ref[bad][:4]}")
+
+
 def test_amax_handles_tails_and_zero():
     _announce("amax tails / zero tensor")
     g = I.generator(42, P.DEV)
