@@ -28,7 +28,7 @@ IGC_PATH_AUTO, IGC_PATH_GENERIC, IGC_PATH_TEMPORAL, IGC_PATH_POINT, IGC_PATH_POI
 
 EXPORTS = ("conv_out_dims", "conv_packed_w_cols", "conv_amax", "conv_fp8_scales", "conv_pack_x", "conv_pack_w",
            "conv_fwd", "conv_fwd_ws", "conv_fwd_ex", "conv_fwd_workspace_bytes", "conv_plan", "conv_plan_ws", "conv_debug_force",
-           "conv_debug_force_splits", "conv_packed_w_t_cols", "conv_pack_w_t", "conv_bwd_data",
+           "conv_debug_force_splits", "conv_debug_force_grid", "conv_packed_w_t_cols", "conv_pack_w_t", "conv_bwd_data",
            "conv_bwd_weight_workspace_bytes", "conv_bwd_weight", "conv_last_error")
 
 
@@ -72,6 +72,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.conv_bwd_weight.argtypes = [P, P, P, P, P, P, P, P, I32, I32, P, ctypes.c_size_t, P]
         lib.conv_debug_force.argtypes = [I32, I32, I32]
         lib.conv_debug_force_splits.argtypes = [I32]
+        lib.conv_debug_force_grid.argtypes = [I32]
         lib.conv_last_error.restype = ctypes.c_char_p
         for name in EXPORTS:
             if name not in ("conv_packed_w_cols", "conv_fwd_workspace_bytes", "conv_packed_w_t_cols",
@@ -249,6 +250,10 @@ def conv_bwd_weight(x, dy, dw, xshape, wshape, stride, pad, dilation, dtype, x_l
 
 def conv_debug_force_splits(splits):
     _check("conv_debug_force_splits", load().conv_debug_force_splits(int(splits)))
+
+
+def conv_debug_force_grid(workgroups):
+    _check("conv_debug_force_grid", load().conv_debug_force_grid(int(workgroups)))
 
 
 def conv_last_error() -> str:

@@ -25,7 +25,7 @@ struct TileShape {
     int bm, bn, wm, wn, mf, stages, kb;
     int sb = 0;
 };
-constexpr int kNumTiles = 41;
+constexpr int kNumTiles = 42;
 // tiles 35..39: the NCDHW 1x1x1 kernel (conv_pw.hip), chosen by its path only
 constexpr int kPointwiseFirst = 35, kPointwiseLast = 39;
 constexpr bool is_pointwise_tile(int t) { return t >= kPointwiseFirst && t <= kPointwiseLast; }
@@ -71,6 +71,7 @@ constexpr TileShape kTiles[kNumTiles] = {
     {512, 64, 4, 1, 16, 2, 64},       // two workgroups per CU
     {256, 64, 4, 1, 16, 4, 64},       // 256 positions, 32-channel steps, 4 x 20 KB: two workgroups per CU
     {256, 192, 2, 4, 16, 2, 128},     // direct-to-LDS, 2 x 56 KB ring: grids of 192..256 tiles of 256x256
+    {256, 256, 2, 4, 16, 3, 128, 2},  // as 29, persistent: one workgroup per CU walks its tiles as one step stream
 };
 
 // Everything a conv kernel needs, passed by value as kernel arguments.

@@ -273,6 +273,11 @@ IGC_API int conv_debug_force(int path, int tile, int group_m);
  * workspace). A split on a tile that cannot split returns IGC_ERR_UNSUPPORTED. */
 IGC_API int conv_debug_force_splits(int splits);
 
+/* Testing hook: cap the workgroups of the persistent tile (41) at this many
+ * (0 = automatic: one per CU, at most one per output tile), so that small
+ * problems also walk several tiles per workgroup. */
+IGC_API int conv_debug_force_grid(int workgroups);
+
 /* Text of the last error on this thread ("" if none). Valid until the next call. */
 IGC_API const char *conv_last_error(void);
 

@@ -55,6 +55,7 @@ CASES = [
     ("dma_tile21_temporal", (2, 64, 9, 6, 7), (96, 64, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1), "NDHWC", 21, 1),
     ("window_tile16", (1, 64, 4, 18, 20), (72, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 16, 0),
     ("buffer_tile29", (2, 128, 6, 10, 12), (200, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 29, 0),
+    ("persistent_tile41", (2, 128, 6, 10, 12), (200, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 41, 0),
     ("pingpong_tile33", (1, 128, 5, 9, 11), (136, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 33, 0),
     ("taps_tile34", (1, 128, 5, 9, 11), (136, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 34, 0),
     ("pointwise_ncdhw", (2, 48, 3, 7, 8), (80, 48, 1, 1, 1), (1, 1, 1), (0, 0, 0), (1, 1, 1), "NCDHW", -1, 0),
@@ -99,7 +100,7 @@ def test_bias_and_amax_bf16(case):
 
 
 @pytest.mark.parametrize("case", [c for c in CASES if c[0] in ("register_tile0", "dma_tile26", "buffer_tile29",
-                                                               "pingpong_tile33", "pointwise_ncdhw", "point_output",
+                                                               "persistent_tile41", "pingpong_tile33", "pointwise_ncdhw", "point_output",
                                                                "split_c1", "split_odd_tails", "window_tile16",
                                                                "taps_tile34")],
                          ids=lambda c: c[0])

@@ -376,8 +376,8 @@ def test_point_output_fp8(tile):
 
 # ------------------------------------------------------------------ buffer-addressed tiles (27..32)
 
-BUF_TILES_BF16 = [27, 28, 29, 30, 31, 32, 33, 34]
-BUF_TILES_FP8 = [27, 28, 29, 31, 33, 34]
+BUF_TILES_BF16 = [27, 28, 29, 30, 31, 32, 33, 34, 41]
+BUF_TILES_FP8 = [27, 28, 29, 31, 33, 34, 41]
 BUF_CASES = [g for g in GEOMS if g[0] in ("c128_cblock_multi_tile", "asym_pad_stride2", "temporal_3x1x1")] + [
     ("dilated_c64", (1, 64, 6, 11, 13), (80, 64, 3, 3, 3), (1, 1, 1), (2, 1, 2), (2, 1, 2)),
     ("c192_k300_two_col_tiles", (1, 192, 4, 9, 10), (300, 192, 3, 3, 3), (1, 2, 1), (1, 1, 1), (1, 1, 1)),
@@ -391,6 +391,11 @@ BUF_CASES = [g for g in GEOMS if g[0] in ("c128_cblock_multi_tile", "asym_pad_st
     # time padding beyond the filter's reach: a tile's first input plane clamps to its image's last plane
     ("pad_beyond_reach_images", (3, 64, 4, 5, 6), (40, 64, 2, 2, 2), (1, 1, 1), (3, 1, 1), (1, 1, 1)),
 ]
+
+
+def _buffer_steps(ws, esz):
+    """Reduction steps of a buffer tile: every tap times the 128-byte channel blocks."""
+    return ws[2] * ws[3] * ws[4] * (ws[1] * esz // 128)
 
 
 def _window_tile_applies(xs, ws, st, pd, dl):
@@ -408,6 +413,8 @@ def test_buffer_tiles_bf16(tile, case):
     name, xs, ws, st, pd, dl = case
     if tile == 34 and not _window_tile_applies(xs, ws, st, pd, dl):
         pytest.skip("tap-shared window tile: generic path with S >= 2 only")
+    if tile == 41 and _buffer_steps(ws, 2) < 3:
+        pytest.skip("persistent tile: at least 3 reduction steps")
     with forced(tile=tile):
         assert "loads=buffer-lds" in B.conv_plan(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC)
         _bf16_case(f"buffer tile {tile} {name}", xs, ws, st, pd, dl, seed=zlib.crc32(name.encode()) % 1000)
@@ -443,6 +450,63 @@ def test_buffer_tiles_fp8(tile, case):
     mx = float(np.abs(O.e4m3_decode(ops.ref_xq)).max()) * sx
     mw = float(np.abs(O.e4m3_decode(ops.ref_wq)).max()) * sw
     P.check_close(P.y_values(y), ref, int(np.prod(ws[1:])), mx, mw, name)
+
+
+class forced_grid:
+    """Cap the persistent tile's workgroups for the duration of a with-block."""
+
+    def __init__(self, workgroups):
+        self.n = workgroups
+
+    def __enter__(self):
+        B.conv_debug_force_grid(self.n)
+
+    def __exit__(self, *exc):
+        B.conv_debug_force_grid(0)
+
+
+@pytest.mark.parametrize("grid", [1, 3, 8])
+@pytest.mark.parametrize("case", BUF_CASES, ids=[g[0] for g in BUF_CASES])
+def test_persistent_tile_walks_many_tiles(grid, case):
+    # Tile 41 runs tile 29's arithmetic with one workgroup walking several output tiles as one stream of
+    # reduction steps. With the grid capped at 1, 3 or 8 workgroups every workgroup walks many tiles, and
+    # each tile's last steps load the next tile's first: the output must equal
+    # tile 29's bit for bit, every element written (the output starts as NaN).
+    name, xs, ws, st, pd, dl = case
+    if _buffer_steps(ws, 2) < 3:
+        pytest.skip("persistent tile: at least 3 reduction steps")
+    _announce(f"persistent tile, grid {grid}, {name}")
+    g = I.generator(zlib.crc32(name.encode()) % 1000, P.DEV)
+    x = I.draw(xs, ("uniform", 1.0), g, P.DEV)
+    w = I.draw(ws, ("uniform", 1.0), g, P.DEV)
+    yshape = (xs[0], ws[0]) + B.conv_out_dims(xs, ws, st, pd, dl)
+    with forced(tile=29):
+        y29 = P.run_bf16(x, w, st, pd, dl, out=torch.full(yshape, float("nan"), dtype=torch.bfloat16, device=P.DEV))
+    with forced(tile=41), forced_grid(grid):
+        assert "schedule=persistent" in B.conv_plan(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC)
+        y41 = P.run_bf16(x, w, st, pd, dl, out=torch.full(yshape, float("nan"), dtype=torch.bfloat16, device=P.DEV))
+    assert not torch.isnan(y41).any()
+    assert torch.equal(y41.view(torch.int16), y29.view(torch.int16))
+
+
+@pytest.mark.parametrize("grid", [2, 5])
+def test_persistent_tile_fp8_walks_many_tiles(grid):
+    name, xs, ws, st, pd, dl = [f for f in FP8_GEOMS if f[0] == "fp8_temporal"][0]
+    _announce(f"persistent tile fp8, grid {grid}, {name}")
+    g = I.generator(36, P.DEV)
+    x = I.draw(xs, ("normal", 1.0), g, P.DEV)
+    w = I.draw(ws, ("normal", 1.0 / np.sqrt(np.prod(ws[1:]))), g, P.DEV)
+    ops = P.Fp8Operands(x, w)
+    with forced(tile=29):
+        y29 = P.run_fp8(ops, xs, ws, st, pd, dl)
+    with forced(tile=41), forced_grid(grid):
+        y41 = P.run_fp8(ops, xs, ws, st, pd, dl)
+    assert torch.equal(y41.view(torch.int16), y29.view(torch.int16))
+    sx, sw = float(ops.ref_scales[0]), float(ops.ref_scales[2])
+    ref = O.conv3d(ops.ref_xq, ops.ref_wq, st, pd, dl, sx=sx, sw=sw)
+    mx = float(np.abs(O.e4m3_decode(ops.ref_xq)).max()) * sx
+    mw = float(np.abs(O.e4m3_decode(ops.ref_wq)).max()) * sw
+    P.check_close(P.y_values(y41), ref, int(np.prod(ws[1:])), mx, mw, name)
 
 
 def test_buffer_tiles_agree_bitwise_with_global_tiles():
