@@ -56,6 +56,9 @@ CASES = [
     ("window_tile16", (1, 64, 4, 18, 20), (72, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 16, 0),
     ("buffer_tile29", (2, 128, 6, 10, 12), (200, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 29, 0),
     ("persistent_tile41", (2, 128, 6, 10, 12), (200, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 41, 0),
+    # whole 256x256 tiles inside one image with 16-byte aligned rows: the outputs go through LDS
+    ("buffer_tile29_lds_epilogue", (1, 128, 4, 16, 16), (256, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC",
+     29, 0),
     ("pingpong_tile33", (1, 128, 5, 9, 11), (136, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 33, 0),
     ("taps_tile34", (1, 128, 5, 9, 11), (136, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 34, 0),
     ("pointwise_ncdhw", (2, 48, 3, 7, 8), (80, 48, 1, 1, 1), (1, 1, 1), (0, 0, 0), (1, 1, 1), "NCDHW", -1, 0),
@@ -100,7 +103,7 @@ def test_bias_and_amax_bf16(case):
 
 
 @pytest.mark.parametrize("case", [c for c in CASES if c[0] in ("register_tile0", "dma_tile26", "buffer_tile29",
-                                                               "persistent_tile41", "pingpong_tile33", "pointwise_ncdhw", "point_output",
+                                                               "buffer_tile29_lds_epilogue", "persistent_tile41", "pingpong_tile33", "pointwise_ncdhw", "point_output",
                                                                "split_c1", "split_odd_tails", "window_tile16",
                                                                "taps_tile34")],
                          ids=lambda c: c[0])
@@ -120,10 +123,15 @@ def test_bias_integer_bit_exact(case):
     assert float(amax) == float(np.abs(ref).max())
 
 
-@pytest.mark.parametrize("tile,splits", [(-1, 0), (33, 0), (29, 0), (26, 1), (26, 3)])
-def test_bias_and_amax_fp8(tile, splits):
-    _announce(f"epilogue fp8 tile {tile} splits {splits}")
-    xs, ws, st, pd, dl = (1, 128, 5, 9, 11), (136, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)
+@pytest.mark.parametrize("tile,splits,kout", [(-1, 0, 136), (33, 0, 136), (29, 0, 136), (26, 1, 136), (26, 3, 136),
+                                              (29, 0, 256), (41, 0, 256)])
+def test_bias_and_amax_fp8(tile, splits, kout):
+    # kout = 256 on 4 x 16 x 16 outputs: whole tiles inside the image, the LDS-staged epilogue of tile 29
+    _announce(f"epilogue fp8 tile {tile} splits {splits} K {kout}")
+    if kout == 256:
+        xs, ws, st, pd, dl = (1, 128, 4, 16, 16), (256, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)
+    else:
+        xs, ws, st, pd, dl = (1, 128, 5, 9, 11), (136, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)
     g = I.generator(91, P.DEV)
     x = I.draw(xs, ("normal", 1.0), g, P.DEV)
     w = I.draw(ws, ("normal", 1.0 / np.sqrt(np.prod(ws[1:]))), g, P.DEV)

@@ -390,6 +390,10 @@ BUF_CASES = [g for g in GEOMS if g[0] in ("c128_cblock_multi_tile", "asym_pad_st
     ("windows_2d_5x5", (2, 128, 1, 19, 37), (96, 128, 1, 5, 5), (1, 1, 1), (0, 2, 2), (1, 1, 1)),
     # time padding beyond the filter's reach: a tile's first input plane clamps to its image's last plane
     ("pad_beyond_reach_images", (3, 64, 4, 5, 6), (40, 64, 2, 2, 2), (1, 1, 1), (3, 1, 1), (1, 1, 1)),
+    # whole 256x256 tiles inside each image (P = 1024, K = 256): the LDS-staged epilogue; a second image
+    ("lds_epilogue_two_images", (2, 128, 4, 16, 16), (256, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),
+    # P = 1800: 7 whole tiles per image through LDS, the tile across the image boundary stored directly
+    ("lds_epilogue_straddle", (2, 64, 5, 18, 20), (256, 64, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1)),
 ]
 
 
