@@ -59,6 +59,7 @@ void conv_igemm_pp_kernel(ConvParams p)
     constexpr int HA = SLICES ? FM : FM / 2;   // A fragments per half
     static_assert(MODE == MODE_GENERIC || MODE == MODE_TEMPORAL, "im2col modes only");
     static_assert(SA * ASTAGE + SB * BSTAGE <= 160 * 1024, "LDS budget");
+    static_assert(SA * ASTAGE + SB * BSTAGE >= BN * (2 * BM + 16), "room for the LDS-staged epilogue");
 
     __shared__ __attribute__((aligned(1024))) char smem[SA * ASTAGE + SB * BSTAGE];
     char *const as = smem;
@@ -236,6 +237,11 @@ void conv_igemm_pp_kernel(ConvParams p)
         }
     }
 
+    // whole tile inside one image, 16-byte aligned rows: stage the outputs through the idle rings
+    if ((p.P & 7) == 0 && m0 + BM <= p.M && n0 + BN <= p.K && m0 / p.P == (m0 + BM - 1) / p.P) {
+        store_tile_lds<BM, BN, 2, 4, MF, DT>(acc, p, m0, n0, wm, wn, lane, smem);
+        return;
+    }
     store_tile_ncdhw<MF, FM, FN, DT>(acc, p, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
