@@ -291,81 +291,6 @@ __device__ __attribute__((always_inline)) inline void store_tile_ncdhw(const typ
     });
 }
 
-// Epilogue through LDS for a whole tile inside one image: the rings are idle
-// after the last step, so the workgroup writes its bf16 outputs there as
-// [column][row] (column stride 2 * BM + 16 bytes), then every lane stores 16
-// bytes: 8 consecutive rows of one column, so that each column's 2 * BM bytes
-// of y go out as whole 128-byte lines. The direct epilogue writes 32-byte
-// pieces of lines from 4 separate instructions. Same output transform as
-// Epilogue (y = bf16(acc * scale [+ bias])); the amax of y, when asked for,
-// is folded from the bf16 values as they leave LDS. Needs P % 8 == 0 (16-byte
-// aligned rows), the tile's rows in one image and all its columns below K;
-// the caller checks that and falls back to store_tile_ncdhw.
-template <int BM, int BN, int WM, int WN, int MF, int DT>
-__device__ __attribute__((always_inline)) inline void store_tile_lds(
-    const typename AccType<MF>::type (&acc)[BM / WM / MF][BN / WN / MF], const ConvParams &p, int m0, int n0,
-    int wm, int wn, int lane, char *smem)
-{
-    constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / MF, FN = WTN / MF;
-    constexpr int CS = 2 * BM + 16;      // bytes per column in LDS
-    constexpr int NT = WM * WN * 64;     // threads
-    constexpr int PIECES = BM * 2 / 16;  // 16-byte pieces per column
-    static_assert(MF == 16, "16x16 MFMA blocks");
-    static_assert((BN * PIECES) % NT == 0, "whole rounds of pieces");
-    const int lrow = lane & 15, lgrp = lane >> 4;
-    const float sc = DT == DT_FP8 ? p.scales[0] * p.scales[2] : 1.0f;
-    __syncthreads();  // every wave has finished reading the rings
-    auto put = [&](auto with_bias) __attribute__((always_inline)) {
-        constexpr bool BIAS = decltype(with_bias)::value;
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const int col = wn * WTN + b * MF + lrow;
-                const int row = wm * WTM + a * MF + 4 * lgrp;
-                const f32x4 v = quad<MF>(acc[a][b], 0);
-                float bias = 0.0f;
-                if constexpr (BIAS)
-                    bias = p.bias[n0 + col];
-                uint32_t r[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float t = v[e] * sc;
-                    if constexpr (BIAS)
-                        t += bias;
-                    r[e] = f32_to_bf16_rne(t);
-                }
-                *reinterpret_cast<u32x2 *>(smem + col * CS + row * 2) = u32x2{r[0] | (r[1] << 16), r[2] | (r[3] << 16)};
-            }
-    };
-    if (p.bias)
-        put(std::true_type{});
-    else
-        put(std::false_type{});
-    __syncthreads();
-    const int nimg = m0 / p.P;
-    const int sp0 = m0 - nimg * p.P;
-    uint16_t *yb = static_cast<uint16_t *>(p.y);
-    unsigned m = 0;
-#pragma unroll
-    for (int it = 0; it < BN * PIECES / NT; ++it) {
-        const int idx = it * NT + (int)threadIdx.x;
-        const int col = idx / PIECES, piece = idx - col * PIECES;
-        const i32x4 v = *reinterpret_cast<const i32x4 *>(smem + col * CS + piece * 16);
-        *reinterpret_cast<i32x4 *>(yb + ((int64_t)nimg * p.K + n0 + col) * p.P + sp0 + piece * 8) = v;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            m = max(m, max((unsigned)v[q] & 0x7fffu, ((unsigned)v[q] >> 16) & 0x7fffu));
-    }
-    if (p.amax) {
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-            m = max(m, (unsigned)__shfl_xor((int)m, off));
-        if (lane == 0)
-            atomicMax(p.amax, m << 16);
-    }
-}
-
 template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, int SA, int SB, int KB, int SPREAD, int PF = 1,
           bool BPF = false>
 __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN>())))
@@ -584,7 +509,7 @@ void conv_igemm_buf_kernel(ConvParams p)
     constexpr bool LDS_EPI = MF == 16 && SA * ASTAGE + SB * BSTAGE >= BN * (2 * BM + 16);
     if constexpr (LDS_EPI) {
         if ((p.P & 7) == 0 && m0 + BM <= p.M && n0 + BN <= p.K && m0 / p.P == (m0 + BM - 1) / p.P) {
-            store_tile_lds<BM, BN, WM, WN, MF, DT>(acc, p, m0, n0, wm, wn, lane, smem);
+            store_tile_lds<BM, BN, WM, WN, MF, DT, false>(acc, p, m0, n0, wm, wn, lane, smem);
             return;
         }
     }

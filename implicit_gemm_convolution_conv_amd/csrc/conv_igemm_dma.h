@@ -30,6 +30,8 @@
 // order, scales and rounds to bf16.
 #pragma once
 
+#include <type_traits>
+
 #include "conv_igemm.h"
 
 namespace igc {
@@ -51,6 +53,83 @@ __device__ inline void wait_vmcnt()
 // 256x256 tile whose 128x128 wave tiles hold 256 fp32 accumulators per lane.
 template <int BM, int BN, int WM, int WN>
 constexpr int dma_waves_per_eu() { return (WM * WN == 4 && BM * BN >= 256 * 256) ? 1 : 2; }
+
+// Epilogue through LDS for a whole tile: the rings are idle after the last
+// step, so the workgroup writes its bf16 outputs there as [column][row]
+// (column stride 2 * BM + 16 bytes), then every lane stores 16 bytes: 8
+// consecutive rows of one column, so that each column's 2 * BM bytes of y go
+// out as whole 128-byte lines. The direct epilogue writes 32-byte pieces of
+// lines from 4 separate instructions. Same output transform as Epilogue
+// (y = bf16(acc * scale [+ bias])); the amax of y, when asked for, is folded
+// from the bf16 values as they leave LDS.
+// im2col tiles (rows = positions, columns = channels): needs P % 8 == 0
+// (16-byte aligned rows), the tile's rows in one image and all its columns
+// below K. Point tiles (POINT: rows = channels, columns = images, y[n][k]
+// contiguous in k with rows of p.K): needs p.K % 8 == 0 and the whole tile
+// inside the GEMM. The callers check that and otherwise store directly.
+template <int BM, int BN, int WM, int WN, int MF, int DT, bool POINT>
+__device__ __attribute__((always_inline)) inline void store_tile_lds(
+    const typename AccType<MF>::type (&acc)[BM / WM / MF][BN / WN / MF], const ConvParams &p, int m0, int n0,
+    int wm, int wn, int lane, char *smem)
+{
+    constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / MF, FN = WTN / MF;
+    constexpr int CS = 2 * BM + 16;      // bytes per column in LDS
+    constexpr int NT = WM * WN * 64;     // threads
+    constexpr int PIECES = BM * 2 / 16;  // 16-byte pieces per column
+    static_assert(MF == 16, "16x16 MFMA blocks");
+    static_assert((BN * PIECES) % NT == 0, "whole rounds of pieces");
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    const float sc = DT == DT_FP8 ? p.scales[0] * p.scales[2] : 1.0f;
+    __syncthreads();  // every wave has finished reading the rings
+    auto put = [&](auto with_bias) __attribute__((always_inline)) {
+        constexpr bool BIAS = decltype(with_bias)::value;
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                const int col = wn * WTN + b * MF + lrow;
+                const int row = wm * WTM + a * MF + 4 * lgrp;
+                const f32x4 v = quad<MF>(acc[a][b], 0);
+                uint32_t r[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float t = v[e] * sc;
+                    if constexpr (BIAS)
+                        t += p.bias[POINT ? m0 + row + e : n0 + col];  // bias of the output channel
+                    r[e] = f32_to_bf16_rne(t);
+                }
+                *reinterpret_cast<u32x2 *>(smem + col * CS + row * 2) = u32x2{r[0] | (r[1] << 16), r[2] | (r[3] << 16)};
+            }
+    };
+    if (p.bias)
+        put(std::true_type{});
+    else
+        put(std::false_type{});
+    __syncthreads();
+    const int nimg = POINT ? 0 : m0 / p.P;
+    const int sp0 = POINT ? 0 : m0 - nimg * p.P;
+    uint16_t *yb = static_cast<uint16_t *>(p.y);
+    unsigned m = 0;
+#pragma unroll
+    for (int it = 0; it < BN * PIECES / NT; ++it) {
+        const int idx = it * NT + (int)threadIdx.x;
+        const int col = idx / PIECES, piece = idx - col * PIECES;
+        const i32x4 v = *reinterpret_cast<const i32x4 *>(smem + col * CS + piece * 16);
+        const int64_t off = POINT ? (int64_t)(n0 + col) * p.K + m0 + piece * 8
+                                  : ((int64_t)nimg * p.K + n0 + col) * p.P + sp0 + piece * 8;
+        *reinterpret_cast<i32x4 *>(yb + off) = v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            m = max(m, max((unsigned)v[q] & 0x7fffu, ((unsigned)v[q] >> 16) & 0x7fffu));
+    }
+    if (p.amax) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            m = max(m, (unsigned)__shfl_xor((int)m, off));
+        if (lane == 0)
+            atomicMax(p.amax, m << 16);
+    }
+}
 
 template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, bool BIG, bool CBLK, int S, int KB = 64>
 __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN>())))
@@ -460,6 +539,18 @@ void conv_igemm_dma_kernel(ConvParams p)
         emit([&](Off off, const f32x4 &v, int) __attribute__((always_inline)) { *reinterpret_cast<f32x4 *>(pb + off) = v; },
              [&](Off off, float v, int) __attribute__((always_inline)) { pb[off] = v; });
     } else {
+        // whole tiles go out through the idle LDS ring in full 128-byte lines
+        constexpr int NT = WM * WN * 64;
+        constexpr bool LDS_EPI = MF == 16 && S * STAGE >= BN * (2 * BM + 16) && (BN * (BM / 8)) % NT == 0;
+        if constexpr (LDS_EPI) {
+            const bool whole = MODE == MODE_POINT
+                                   ? (p.K & 7) == 0 && m0 + BM <= p.M && n0 + BN <= p.Ncol
+                                   : (p.P & 7) == 0 && m0 + BM <= p.M && n0 + BN <= p.K && m0 / p.P == (m0 + BM - 1) / p.P;
+            if (whole) {
+                store_tile_lds<BM, BN, WM, WN, MF, DT, MODE == MODE_POINT>(acc, p, m0, n0, wm, wn, lane, smem);
+                return;
+            }
+        }
         uint16_t *yb = static_cast<uint16_t *>(p.y);
         with_epilogue(p, DT == DT_FP8, [&](auto &ep) __attribute__((always_inline)) {
             emit(

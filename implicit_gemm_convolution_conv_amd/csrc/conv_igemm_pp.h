@@ -239,7 +239,7 @@ void conv_igemm_pp_kernel(ConvParams p)
 
     // whole tile inside one image, 16-byte aligned rows: stage the outputs through the idle rings
     if ((p.P & 7) == 0 && m0 + BM <= p.M && n0 + BN <= p.K && m0 / p.P == (m0 + BM - 1) / p.P) {
-        store_tile_lds<BM, BN, 2, 4, MF, DT>(acc, p, m0, n0, wm, wn, lane, smem);
+        store_tile_lds<BM, BN, 2, 4, MF, DT, false>(acc, p, m0, n0, wm, wn, lane, smem);
         return;
     }
     store_tile_ncdhw<MF, FM, FN, DT>(acc, p, m0 + wm * WTM, n0 + wn * WTN, lane);

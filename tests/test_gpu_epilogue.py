@@ -63,6 +63,7 @@ CASES = [
     ("taps_tile34", (1, 128, 5, 9, 11), (136, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 34, 0),
     ("pointwise_ncdhw", (2, 48, 3, 7, 8), (80, 48, 1, 1, 1), (1, 1, 1), (0, 0, 0), (1, 1, 1), "NCDHW", -1, 0),
     ("point_output", (40, 3, 1, 14, 14), (68, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1), "NCDHW", -1, 0),
+    ("point_output_lds", (200, 3, 1, 14, 14), (256, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1), "NCDHW", 26, 0),
     ("split_c1", (1, 64, 4, 16, 16), (64, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 26, 5),
     ("split_point", (40, 3, 1, 14, 14), (68, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1), "NCDHW", 26, 4),
     ("split_odd_tails", (1, 16, 3, 5, 7), (25, 16, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 26, 2),
@@ -103,7 +104,7 @@ def test_bias_and_amax_bf16(case):
 
 
 @pytest.mark.parametrize("case", [c for c in CASES if c[0] in ("register_tile0", "dma_tile26", "buffer_tile29",
-                                                               "buffer_tile29_lds_epilogue", "persistent_tile41", "pingpong_tile33", "pointwise_ncdhw", "point_output",
+                                                               "buffer_tile29_lds_epilogue", "persistent_tile41", "pingpong_tile33", "pointwise_ncdhw", "point_output", "point_output_lds",
                                                                "split_c1", "split_odd_tails", "window_tile16",
                                                                "taps_tile34")],
                          ids=lambda c: c[0])

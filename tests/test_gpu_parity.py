@@ -87,6 +87,18 @@ def test_point_output_bf16(layout, k):
                seed=7, dist=("normal", 1.0), x_layout=layout)
 
 
+@pytest.mark.parametrize("tile", [40, 24, 26, 21])
+def test_point_output_whole_tiles(tile):
+    # 512 output channels over 600 images: whole tiles leave through the LDS-staged epilogue (tiles 40, 24, 26),
+    # the image tiles past 600 and every tile of 21 (its ring is too small to stage a tile) store directly
+    with forced(tile=tile):
+        _bf16_case(f"point whole tiles, tile {tile}", (600, 3, 1, 14, 14), (512, 3, 1, 14, 14), (1, 14, 14),
+                   (0, 0, 0), (1, 1, 1), seed=8, dist=("normal", 1.0), x_layout="NCDHW")
+        _announce(f"point whole tiles integer, tile {tile}")
+        _int_case((600, 3, 1, 14, 14), (512, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1), seed=9,
+                  x_layout="NCDHW")
+
+
 def test_2d_and_1d_through_3d():
     _announce("conv2d / conv1d as D=T=1 (and H=R=1)")
     g = I.generator(11, P.DEV)
