@@ -4,7 +4,10 @@
 Step = one forward convolution of the headline workload, conv3d bf16 NDHWC
 N=1 C=2048 D=60 H=80 W=45, K=2048, 3x3x3, stride 1, pad 1 (GEMM
 216000 x 2048 x 55296, 4.892e13 flop), with x already resident in HBM in
-NDHWC and the filter packed once beforehand (it is a layer's constant).
+NDHWC and the filter packed once beforehand (it is a layer's constant). The
+call is conv_fwd_ws with a workspace allocated once beforehand: its last,
+partial round of tiles (96 of 6752) runs split along the reduction, so a step
+is the conv kernel plus the small pass that adds those tiles' partial sums.
 Throughput = 2*M*N*R / time (TFLOPS).
 
 Printed as ONE JSON line on stdout (everything else goes to stderr):
@@ -113,10 +116,22 @@ def bench_workload(name, steps, warmup, torch, B, I, PL):
             wp = PL.packed_weight(w, "bf16", "NDHWC")
             lay = B.IGC_NDHWC
             xk = x if wl.x_layout == "NDHWC" else PL.packed_input(x, "bf16")
-        res["plan"] = B.conv_plan(xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay)
+        # The step is the library's call for this workload: conv_fwd_ws with a preallocated workspace where
+        # the plan uses one (split reduction of an under-filled grid, or the tail split of a partial last
+        # round), conv_fwd otherwise; conv_fwd without the workspace is timed beside it.
+        nws = B.conv_fwd_workspace_bytes(xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay)
+        wsb = torch.empty(nws // 4, dtype=torch.float32, device="cuda") if nws > 0 else None
+        res["plan"] = B.conv_plan_ws(xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay, max(nws, 0))
+        res["workspace_bytes"] = max(nws, 0)
+
+        def plain_step():
+            B.conv_fwd(xk, wp, y, xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay)
 
         def step():
-            B.conv_fwd(xk, wp, y, xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay)
+            if wsb is None:
+                plain_step()
+            else:
+                B.conv_fwd_ws(xk, wp, y, xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay, workspace=wsb)
 
         st = {}
         wall, ev = time_launches(step, steps, warmup, torch, st)
@@ -128,21 +143,12 @@ def bench_workload(name, steps, warmup, torch, B, I, PL):
             time_launches(step, steps, warmup, torch, cst, between=lambda: scratch.fill_(1))
             res.update(cold_kernel_ms_median=cst["median"], cold_kernel_ms_min=cst["min"])
             del scratch
-        nws = B.conv_fwd_workspace_bytes(xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay)
-        if nws > 0:  # under-filled grid: the split reduction through conv_fwd_ws (conv kernel + reduction pass)
-            wsb = torch.empty(nws // 4, dtype=torch.float32, device="cuda")
-            res["split_plan"] = B.conv_plan_ws(xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay, nws)
-
-            def split_step():
-                B.conv_fwd_ws(xk, wp, y, xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay, workspace=wsb)
-
-            sst, cst = {}, {}
-            _, sev = time_launches(split_step, steps, warmup, torch, sst)
-            scratch = torch.empty(1 << 28, dtype=torch.int16, device="cuda")
-            time_launches(split_step, steps, warmup, torch, cst, between=lambda: scratch.fill_(1))
-            res.update(split_kernel_ms=sev, split_kernel_ms_median=sst["median"], split_kernel_ms_min=sst["min"],
-                       split_cold_kernel_ms_median=cst["median"], split_cold_kernel_ms_min=cst["min"])
-            del scratch, wsb
+        if wsb is not None:
+            res["plain_plan"] = B.conv_plan(xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, lay)
+            pst = {}
+            _, pev = time_launches(plain_step, steps, warmup, torch, pst)
+            res.update(plain_kernel_ms=pev, plain_kernel_ms_median=pst["median"], plain_kernel_ms_min=pst["min"])
+            del wsb
         if name == "pw":  # HBM-bound: x and y once, the filter per 64 output channels
             nbytes = 2 * (x.numel() + y.numel() + w.numel())
             res.update(kernel_gbs=nbytes / (ev * 1e-3) / 1e9, hbm_frac=nbytes / (ev * 1e-3) / 1e9 / PEAK_HBM_GBS)
@@ -158,15 +164,25 @@ def bench_workload(name, steps, warmup, torch, B, I, PL):
         n, c, d, h, wd = xshape
         xq = torch.empty((n, d, h, wd, c), dtype=torch.uint8, device="cuda")
         amax = torch.empty(1, dtype=torch.float32, device="cuda")
-        res["plan"] = B.conv_plan(xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_FP8_E4M3FN, B.IGC_NDHWC)
+        fargs = (xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_FP8_E4M3FN, B.IGC_NDHWC)
+        nws = B.conv_fwd_workspace_bytes(*fargs)  # the tail split of a partial last round, when planned
+        wsb = torch.empty(nws // 4, dtype=torch.float32, device="cuda") if nws > 0 else None
+        res["plan"] = B.conv_plan_ws(*fargs, max(nws, 0))
+        res["workspace_bytes"] = max(nws, 0)
 
         def prep():
             B.conv_amax(x, x.numel(), amax)
             B.conv_fp8_scales(amax, scales[0:2])
             B.conv_pack_x(x, xq, xshape, B.IGC_FP8_E4M3FN, scales[0:2])
 
+        def plain_conv():
+            B.conv_fwd(xq, wq, y, *fargs, scales)
+
         def conv():
-            B.conv_fwd(xq, wq, y, xshape, wshape, wl.stride, wl.pad, wl.dil, B.IGC_FP8_E4M3FN, B.IGC_NDHWC, scales)
+            if wsb is None:
+                plain_conv()
+            else:
+                B.conv_fwd_ws(xq, wq, y, *fargs, scales, workspace=wsb)
 
         def e2e():
             prep()
@@ -183,7 +199,11 @@ def bench_workload(name, steps, warmup, torch, B, I, PL):
                    e2e_tflops=flops / (ev_e * 1e-3) / 1e12, pack_ms=ev_p,
                    pack_gbs=3 * x.numel() / (ev_p * 1e-3) / 1e9, amax_ms=ev_a,
                    amax_gbs=2 * x.numel() / (ev_a * 1e-3) / 1e9)
-        del xq, wq, scales
+        if wsb is not None:
+            pst = {}
+            _, pev = time_launches(plain_conv, steps, warmup, torch, pst)
+            res.update(plain_kernel_ms=pev, plain_kernel_ms_median=pst["median"], plain_kernel_ms_min=pst["min"])
+        del xq, wq, scales, wsb
     del x, w, y
     torch.cuda.empty_cache()
     return res
@@ -338,8 +358,11 @@ def main():
         x, w = I.make(wl, "cuda")
         wp = PL.packed_weight(w, "bf16", "NDHWC")
         y = PL.output(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dil, "cuda")
-        for _ in range(args.steps):
-            B.conv_fwd(x, wp, y, wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
+        args5 = (wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
+        nws = B.conv_fwd_workspace_bytes(*args5)
+        wsb = torch.empty(max(nws, 16) // 4, dtype=torch.float32, device="cuda")
+        for _ in range(args.steps):  # the bench's step: conv_fwd_ws with its workspace
+            B.conv_fwd_ws(x, wp, y, *args5, workspace=wsb if nws > 0 else None)
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)  # 1 GiB
         dst = torch.empty_like(src)
         torch.cuda.synchronize()

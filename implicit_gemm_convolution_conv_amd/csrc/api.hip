@@ -56,6 +56,8 @@ std::atomic<int> g_force_splits{0};
 std::atomic<int> g_force_grid{0};
 
 constexpr int64_t kI32Max = 2147483647;
+// Compute units of an MI355X (gfx950): the workgroups of 256x256 tiles that run at once.
+constexpr int64_t kCUs = 256;
 // Element offsets up to this bound use 32-bit arithmetic in the conv kernel;
 // larger tensors switch to 64-bit offsets (invalid im2col taps may compute an
 // offset up to one tensor beyond the valid range before being masked).
@@ -151,6 +153,7 @@ struct Plan {
     int tile;
     bool big, cblock;
     int64_t xspan;  // bound on a tile's reach into x from its buffer base
+    int64_t ws_need = 0;  // workspace bytes the planned split uses (split reduction or tail split)
     ConvParams p;
 };
 
@@ -491,6 +494,31 @@ int plan_splits(Plan &pl, size_t ws_bytes)
     splits = std::max(splits, 1);
     p.ksplit = (p.nk + splits - 1) / splits;
     p.splits = (p.nk + p.ksplit - 1) / p.ksplit;  // every split holds at least one step
+    pl.ws_need = p.splits > 1 ? (int64_t)p.splits * ynum * 4 : 0;
+    // Tail split (buffer-addressed lockstep and ping-pong tiles, one 256x256 workgroup per CU):
+    // when the last round of tiles fills at most half of the CUs, its tiles run
+    // as S workgroups each over 1/S of the reduction, S = CUs / tail tiles (at
+    // most 8, at least 8 steps per split), and a second pass adds the partials;
+    // only for reductions of at least 96 steps.
+    // The last round then takes about 1/S of a tile's time instead of a whole
+    // one. The one-GPU share of c3 (844 tiles: 3 rounds + 76) is the case this
+    // is for. Needs the workspace; conv_debug_force_splits(1) turns it off.
+    p.tail_first = 0;
+    p.tail_splits = 0;
+    if (p.splits == 1 && forced != 1 && is_buffer(kTiles[pl.tile]) && pl.tile != 34 && pl.tile != 41) {
+        const TileShape &t = kTiles[pl.tile];
+        const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
+        const int64_t slots = g_force_grid.load() > 0 ? g_force_grid.load() : kCUs;
+        const int64_t full = ntiles / slots * slots, r = ntiles - full;
+        const int64_t S = std::min<int64_t>(std::min<int64_t>(r > 0 ? slots / r : 0, 8), p.nk / 8);
+        const int64_t need = r * S * t.bm * t.bn * 4;
+        // at least 96 steps per tile: on 48-step tiles (c5s) the second pass cost more than the split saved
+        if (p.nk >= 96 && full > 0 && r > 0 && 2 * r <= slots && S >= 2 && (size_t)need <= ws_bytes) {
+            p.tail_first = (int)full;
+            p.tail_splits = (int)S;
+            pl.ws_need = need;
+        }
+    }
     return p.splits;
 }
 
@@ -754,7 +782,7 @@ int conv_fwd_ex(const void *x, const void *w_packed, void *y, const int64_t xsha
     pl.p.w = w_packed;
     pl.p.y = y;
     pl.p.scales = dtype == IGC_FP8_E4M3FN ? scales_dev : nullptr;
-    pl.p.part = pl.p.splits > 1 ? static_cast<float *>(workspace_dev) : nullptr;
+    pl.p.part = pl.p.splits > 1 || pl.p.tail_splits > 1 ? static_cast<float *>(workspace_dev) : nullptr;
     pl.p.bias = bias_dev;
     pl.p.amax = reinterpret_cast<unsigned *>(y_amax_dev);
     const Mode mode = pl.path == IGC_PATH_POINT ? MODE_POINT : (pl.path == IGC_PATH_TEMPORAL ? MODE_TEMPORAL : MODE_GENERIC);
@@ -766,6 +794,10 @@ int conv_fwd_ex(const void *x, const void *w_packed, void *y, const int64_t xsha
         return fail(IGC_ERR_HIP, "conv_fwd: kernel launch failed");
     if (pl.p.splits > 1 && launch_splitk_reduce(pl.p, st) != hipSuccess)
         return fail(IGC_ERR_HIP, "conv_fwd_ws: split reduction launch failed");
+    if (pl.p.tail_splits > 1 &&
+        launch_tail_reduce(pl.p, kTiles[pl.tile].bm, kTiles[pl.tile].bn,
+                           pl.p.tiles_m * pl.p.tiles_n - pl.p.tail_first, st) != hipSuccess)
+        return fail(IGC_ERR_HIP, "conv_fwd_ws: tail reduction launch failed");
     return ok();
 }
 
@@ -796,7 +828,7 @@ int64_t conv_fwd_workspace_bytes(const int64_t xshape[5], const int64_t wshape[5
     if (rc < 0)
         return rc;
     ok();
-    return rc > 1 ? (int64_t)rc * pl.p.M * pl.p.Ncol * 4 : 0;
+    return pl.ws_need;
 }
 
 int conv_plan_ws(const int64_t xshape[5], const int64_t wshape[5], const int32_t stride[3], const int32_t pad[3],
@@ -813,14 +845,16 @@ int conv_plan_ws(const int64_t xshape[5], const int64_t wshape[5], const int32_t
         const TileShape ts = kTiles[pl.tile];
         snprintf(buf, len,
                  "path=%s tile=%dx%d waves=%d mfma=%dx%d stages=%d bstages=%d kstep=%d order=%s%s big=%d grid=%d "
-                 "group_m=%d nk=%d loads=%s schedule=%s areuse=%s xspan=%lld splits=%d ksplit=%d",
+                 "group_m=%d nk=%d loads=%s schedule=%s areuse=%s xspan=%lld splits=%d ksplit=%d tail=%d/%d",
                  path_name(pl.path), ts.bm, ts.bn, ts.wm * ts.wn, ts.mf, ts.mf, ts.stages ? std::abs(ts.stages) : 2,
                  is_buffer(ts) ? ts.sb : (ts.stages ? std::abs(ts.stages) : 2), step_bytes(ts) / (dtype == IGC_FP8_E4M3FN ? 1 : 2),
                  is_window(ts) ? "window" : (pl.cblock ? "cblock" : "linear"), pl.p.pairs == 2 ? "-paired" : "",
                  pl.big ? 1 : 0, pl.p.tiles_m * pl.p.tiles_n, pl.p.group_m, pl.p.nk,
                  is_buffer(ts) ? "buffer-lds" : (ts.stages > 0 ? "global-lds" : (is_window(ts) ? "window-lds" : "registers")),
                  pl.tile == 33 || pl.tile == 34 ? "pingpong" : (pl.tile == 41 ? "persistent" : "lockstep"), pl.tile == 34 ? "taps" : "none",
-                 pl.path == IGC_PATH_POINT ? 0LL : (long long)pl.xspan, pl.p.splits, pl.p.ksplit);
+                 pl.path == IGC_PATH_POINT ? 0LL : (long long)pl.xspan, pl.p.splits, pl.p.ksplit,
+                 pl.p.tail_splits > 1 ? pl.p.tiles_m * pl.p.tiles_n - pl.p.tail_first : 0,
+                 pl.p.tail_splits > 1 ? pl.p.tail_splits : 1);
     }
     return ok();
 }

@@ -94,6 +94,19 @@ struct KPos {
         tap = tw ? 0 : tap;
         cb += tw ? p.pairs * TKE : 0;
     }
+    // Position of reduction step `step` (advance() applied `step` times from zero).
+    __device__ void seek(const ConvParams &p, int step)
+    {
+        const int q = step / p.pairs;
+        half = step - q * p.pairs;
+        const int taps = p.T * p.R * p.S;
+        const int cbi = q / taps;
+        tap = q - cbi * taps;
+        s = tap % p.S;
+        r = (tap / p.S) % p.R;
+        t = tap / (p.S * p.R);
+        cb = cbi * p.pairs * TKE;
+    }
     // Bytes from an input row's origin to this tap and channel block.
     template <int MODE, int ESZ>
     __device__ unsigned a_shift(const ConvParams &p) const
@@ -329,8 +342,20 @@ void conv_igemm_buf_kernel(ConvParams p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM, wn = wave / WM;
 
+    // Tail split: the workgroups from p.tail_first on share the last, partial
+    // round's tiles, p.tail_splits per tile, each over a contiguous range of
+    // reduction steps; they leave fp32 partial sums for tail_reduce.
+    int bid = (int)blockIdx.x, split = -1, kbeg = 0, nk = p.nk;
+    if (p.tail_splits > 1 && bid >= p.tail_first) {
+        const int t = bid - p.tail_first;
+        const int tile = t / p.tail_splits;
+        split = t - tile * p.tail_splits;
+        bid = p.tail_first + tile;
+        kbeg = (int)((int64_t)split * p.nk / p.tail_splits);
+        nk = (int)((int64_t)(split + 1) * p.nk / p.tail_splits) - kbeg;
+    }
     int tm, tn;
-    tile_coords(p, tm, tn);
+    tile_coords(p, bid, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     // This lane's row within each RPI-row group and the chunk it fetches there:
@@ -419,8 +444,11 @@ void conv_igemm_buf_kernel(ConvParams p)
     // rings differ), plus SMIN-2 whole steps.
     constexpr int AHEAD = (SA == SB ? 0 : LPS - FIRST_IT) + (SMIN - 2) * LPS;
     static_assert(AHEAD < 64, "vmcnt range");
-    const int nk = p.nk;
     KPos<TKE> ka, kb;  // next A and B steps to issue
+    if (kbeg > 0) {
+        ka.seek(p, kbeg);
+        kb.seek(p, kbeg);
+    }
     // j-th DMA instruction of a step in issue order (A rows then B rows, or B then A).
     auto issue_j = [&](int j, int sta, int stb, unsigned ash, unsigned bsh) {
         const bool is_a = A_FIRST ? j < AIT : j >= BIT;
@@ -505,6 +533,21 @@ void conv_igemm_buf_kernel(ConvParams p)
         ib = ib + 1 == SB ? 0 : ib + 1;
     }
 
+    if (split >= 0) {  // tail split: unscaled fp32 sums, [column][row] per tile and split
+        float *dst = p.part + ((int64_t)(bid - p.tail_first) * p.tail_splits + split) * (BM * BN);
+        const int lrow2 = lane & (MF - 1), lgrp2 = lane / MF;
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+#pragma unroll
+                for (int q = 0; q < MF / 16 * (MF / 16); ++q) {
+                    const int col = wn * WTN + b * MF + lrow2;
+                    const int row = wm * WTM + a * MF + (MF == 16 ? 4 * lgrp2 : 8 * q + 4 * lgrp2);
+                    *reinterpret_cast<f32x4 *>(dst + col * BM + row) = quad<MF>(acc[a][b], q);
+                }
+        return;
+    }
     // whole tile inside one image, 16-byte aligned rows: stage the outputs through the idle rings
     constexpr bool LDS_EPI = MF == 16 && SA * ASTAGE + SB * BSTAGE >= BN * (2 * BM + 16);
     if constexpr (LDS_EPI) {
@@ -750,7 +793,8 @@ int persistent_grid(const ConvParams &p);
 template <int DT>
 hipError_t launch_conv_buf_dt(const ConvParams &p, int tile, Mode mode, hipStream_t stream)
 {
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+    const int ntiles = p.tiles_m * p.tiles_n;  // tail split: the tail tiles take tail_splits workgroups each
+    const dim3 grid((unsigned)(p.tail_splits > 1 ? p.tail_first + (ntiles - p.tail_first) * p.tail_splits : ntiles));
 #define IGC_BLAUNCH(BM_, BN_, WM_, WN_, MF_, SA_, SB_, KB_, SP_, ...)                                          \
     do {                                                                                                   \
         if (mode == MODE_TEMPORAL)                                                                         \

@@ -71,8 +71,19 @@ void conv_igemm_pp_kernel(ConvParams p)
     const int g = wave >> 2, wl = wave & 3;
     const int wm = wl & 1, wn = (wl >> 1) + 2 * g;  // 128-row half, 64-column quarter of the tile
 
+    // Tail split (as in conv_igemm_buf_kernel): workgroups from p.tail_first on
+    // run a contiguous step range of a tail tile and leave fp32 partial sums.
+    int bid = (int)blockIdx.x, split = -1, kbeg = 0, nk = p.nk;
+    if (p.tail_splits > 1 && bid >= p.tail_first) {
+        const int t = bid - p.tail_first;
+        const int tile = t / p.tail_splits;
+        split = t - tile * p.tail_splits;
+        bid = p.tail_first + tile;
+        kbeg = (int)((int64_t)split * p.nk / p.tail_splits);
+        nk = (int)((int64_t)(split + 1) * p.nk / p.tail_splits) - kbeg;
+    }
     int tm, tn;
-    tile_coords(p, tm, tn);
+    tile_coords(p, bid, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int lr = lane >> 3;
@@ -89,6 +100,10 @@ void conv_igemm_pp_kernel(ConvParams p)
     const __amdgpu_buffer_rsrc_t xr = tile_x_rsrc(p, xbase);
     const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(p.w, p.wbytes);
     KPos<TKE> ka, kb;  // next activation / filter step to issue
+    if (kbeg > 0) {
+        ka.seek(p, kbeg);
+        kb.seek(p, kbeg);
+    }
 
     // DMA instruction i of an activation / filter step into ring slot st.
     auto issue_a = [&](int st, int i, unsigned sh) {
@@ -159,7 +174,6 @@ void conv_igemm_pp_kernel(ConvParams p)
         };
     };
 
-    const int nk = p.nk;
     // Each group runs its own copy of the loop (the group is fixed per wave);
     // both execute the same barriers: two in the prologue, four per step.
     // DMA instructions issue inside compute phases, between MFMA rows: the
@@ -237,6 +251,16 @@ void conv_igemm_pp_kernel(ConvParams p)
         }
     }
 
+    if (split >= 0) {  // tail split: unscaled fp32 sums, [column][row] per tile and split
+        float *dst = p.part + ((int64_t)(bid - p.tail_first) * p.tail_splits + split) * (BM * BN);
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                *reinterpret_cast<f32x4 *>(dst + (wn * WTN + b * MF + lrow) * BM + wm * WTM + a * MF + 4 * lgrp) =
+                    quad<MF>(acc[a][b], 0);
+        return;
+    }
     // whole tile inside one image, 16-byte aligned rows: stage the outputs through the idle rings
     if ((p.P & 7) == 0 && m0 + BM <= p.M && n0 + BN <= p.K && m0 / p.P == (m0 + BM - 1) / p.P) {
         store_tile_lds<BM, BN, 2, 4, MF, DT, false>(acc, p, m0, n0, wm, wn, lane, smem);
@@ -248,7 +272,8 @@ void conv_igemm_pp_kernel(ConvParams p)
 template <int DT>
 hipError_t launch_conv_pp(const ConvParams &p, Mode mode, hipStream_t stream)
 {
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+    const int ntiles = p.tiles_m * p.tiles_n;  // tail split: the tail tiles take tail_splits workgroups each
+    const dim3 grid((unsigned)(p.tail_splits > 1 ? p.tail_first + (ntiles - p.tail_first) * p.tail_splits : ntiles));
     if (mode == MODE_TEMPORAL)
         hipLaunchKernelGGL((conv_igemm_pp_kernel<DT, MODE_TEMPORAL>), grid, dim3(512), 0, stream, p);
     else

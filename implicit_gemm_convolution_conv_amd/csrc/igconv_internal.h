@@ -109,6 +109,12 @@ struct ConvParams {
     // like y; splits == 1: no split, y written directly
     int splits, ksplit;
     float *part;
+    // tail split (buffer-addressed kernels): with tail_splits > 1, the tiles
+    // from linear index tail_first on (the last, partial round) each run as
+    // tail_splits workgroups over contiguous step ranges; workgroup
+    // tail_first + t * tail_splits + j stores its unscaled fp32 sums of tile
+    // tail_first + t at part + (t * tail_splits + j) * BM * BN, [column][row]
+    int tail_first, tail_splits;
     // fused epilogue extras (null = off): fp32 bias per output channel added
     // before rounding; max |y| merged into *amax as fp32 bits (zeroed before
     // the launch)
@@ -136,6 +142,9 @@ hipError_t launch_conv_pw(const ConvParams &p, int variant, hipStream_t stream);
 // in point-output layout (y[n][k], K per row) channel = i % K, else (i / P) % K
 hipError_t launch_splitk_reduce(const ConvParams &p, hipStream_t stream);
 hipError_t launch_amax_zero(float *amax, hipStream_t stream);
+// Second pass of the tail split: sums each tail tile's partials in split order
+// and applies the epilogue (tiles of bm x bn).
+hipError_t launch_tail_reduce(const ConvParams &p, int bm, int bn, int ntail, hipStream_t stream);
 
 // dst[c][r] = src[r][c] (src rows of `cols` bf16), dst rows of ld >= rows elements, zero past rows
 hipError_t launch_transpose_pad(const uint16_t *src, uint16_t *dst, int64_t rows, int64_t cols, int64_t ld,

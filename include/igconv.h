@@ -173,6 +173,12 @@ IGC_API int conv_fwd(const void *x, const void *w_packed, void *y, const int64_t
  * summation order). The split is chosen only where the grid of output tiles
  * under-fills the GPU, as FlyDSL PR #860's split-K selection does (its rule
  * that the under-fill test alone decides).
+ * Tail split: on the 256x256 buffer-addressed tiles, when the grid's last
+ * round of tiles fills at most half of the GPU's 256 CUs, each of its r tiles
+ * runs as S workgroups over 1/S of the reduction (S = 256 / r, 2..8), using
+ * r * S * 256 * 256 * 4 bytes of workspace, and a second pass adds them in a
+ * fixed order for those tiles only; every other tile is computed and stored
+ * as by conv_fwd. Without that much room the call runs exactly as conv_fwd.
  */
 IGC_API int conv_fwd_ws(const void *x, const void *w_packed, void *y, const int64_t xshape[5],
                 const int64_t wshape[5], const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3],
@@ -200,7 +206,8 @@ IGC_API int conv_fwd_ex(const void *x, const void *w_packed, void *y, const int6
 
 /*
  * Workspace bytes conv_fwd_ws would use for these arguments with unlimited
- * room: splits * 4 * N*K*Do*Ho*Wo when it splits the reduction, else 0.
+ * room: splits * 4 * N*K*Do*Ho*Wo when it splits the reduction, r * S * 256 *
+ * 256 * 4 for a tail split, else 0.
  * Negative status (as conv_fwd) for invalid arguments. Host only.
  */
 IGC_API int64_t conv_fwd_workspace_bytes(const int64_t xshape[5], const int64_t wshape[5], const int32_t stride[3],
@@ -255,7 +262,8 @@ IGC_API int conv_plan(const int64_t xshape[5], const int64_t wshape[5], const in
               const int32_t dilation[3], int dtype, int x_layout, char *buf, size_t len);
 
 /* As conv_plan, for conv_fwd_ws with a workspace of workspace_bytes (the text
- * ends with the split count and reduction steps per split). Host only. */
+ * ends with the split count, reduction steps per split and "tail=r/S": the
+ * tail tiles and their splits, 0/1 without a tail split). Host only. */
 IGC_API int conv_plan_ws(const int64_t xshape[5], const int64_t wshape[5], const int32_t stride[3],
                  const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout, size_t workspace_bytes,
                  char *buf, size_t len);
@@ -275,7 +283,9 @@ IGC_API int conv_debug_force_splits(int splits);
 
 /* Testing hook: cap the workgroups of the persistent tile (41) at this many
  * (0 = automatic: one per CU, at most one per output tile), so that small
- * problems also walk several tiles per workgroup. */
+ * problems also walk several tiles per workgroup. The same count stands in
+ * for the 256 CUs when conv_fwd_ws plans a tail split, so small problems
+ * have a partial last round too. */
 IGC_API int conv_debug_force_grid(int workgroups);
 
 /* Text of the last error on this thread ("" if none). Valid until the next call. */

@@ -266,10 +266,18 @@ def test_split_reduction_plan():
     # a workspace for two slices gives two splits, one byte short of two gives none
     assert _plan_ws(c1x, c1w, 2 * ynum * 4)["splits"] == "2"
     assert _plan_ws(c1x, c1w, 2 * ynum * 4 - 1)["splits"] == "1"
-    # full grids do not split, and need no workspace
+    # full grids do not split the reduction; c3's last round (96 of 6752 tiles) takes the tail split: 2 workgroups
+    # per tile, 2 * 96 fp32 tiles of 256 x 256 of workspace
     big = ((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3))
-    assert B.conv_fwd_workspace_bytes(*big, (1, 1, 1), (1, 1, 1), (1, 1, 1), B.IGC_BF16, B.IGC_NDHWC) == 0
+    assert B.conv_fwd_workspace_bytes(*big, (1, 1, 1), (1, 1, 1), (1, 1, 1), B.IGC_BF16, B.IGC_NDHWC) == 96 * 2 * 256 * 256 * 4
     assert _plan_ws(*big, 1 << 40)["splits"] == "1"
+    assert _plan_ws(*big, 1 << 40)["tail"] == "96/2"
+    assert _plan_ws(*big, 96 * 2 * 256 * 256 * 4 - 1)["tail"] == "0/1"
+    # c3's one-GPU share: 844 tiles = 3 rounds + 76, 3 splits each; a 3x1x1 filter over 54000 tiles (last round
+    # 240 of 256 CUs) does not split, nor does its 48-step share (6752 tiles, a last round of 96)
+    assert _plan_ws((1, 2048, 60, 80, 45), (256, 2048, 3, 3, 3), 1 << 40)["tail"] == "76/3"
+    assert _plan_ws((1, 1024, 240, 160, 90), (1024, 1024, 3, 1, 1), 1 << 40, pd=(1, 0, 0))["tail"] == "0/1"
+    assert _plan_ws((1, 1024, 32, 160, 90), (1024, 1024, 3, 1, 1), 1 << 40, pd=(0, 0, 0))["tail"] == "0/1"
     # few reduction steps: no split (temporal c1-like, 3 steps)
     assert B.conv_fwd_workspace_bytes((1, 64, 4, 16, 16), (64, 64, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1),
                                       B.IGC_BF16, B.IGC_NDHWC) == 0

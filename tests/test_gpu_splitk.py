@@ -195,3 +195,117 @@ def test_split_fp8_integer_bit_exact():
     torch.cuda.synchronize()
     ref = O.conv3d(P.bits(x), P.bits(w), st, pd, dl)
     assert np.array_equal(P.y_values(y), ref)
+
+
+# ------------------------------------------------------------------ tail split of the buffer-addressed tiles
+
+class capped_cus:
+    """Plan the tail split for `n` CUs (and cap persistent grids), for the duration of a with-block."""
+
+    def __init__(self, n):
+        self.n = n
+
+    def __enter__(self):
+        B.conv_debug_force_grid(self.n)
+
+    def __exit__(self, *exc):
+        B.conv_debug_force_grid(0)
+
+
+def _tail(plan):
+    kv = dict(item.split("=") for item in plan.split())
+    r, s = kv["tail"].split("/")
+    return int(r), int(s)
+
+
+# name, x, w, stride, pad, dil, CUs stood in for, expected (tail tiles, splits); every reduction has >= 96 steps
+TAIL_CASES = [
+    # 6 tiles of 256 x 256 on 4 "CUs": 2 tail tiles in 2 splits of 54 steps; tiles stay inside one image
+    ("tail_generic_6_tiles", (1, 256, 4, 16, 24), (256, 256, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), 4, (2, 2)),
+    # 8 M tiles x 2 K tiles on 12: 4 tail tiles in 3 splits of 36 steps; ragged M, K = 300, two images
+    ("tail_ragged_two_images", (2, 256, 3, 11, 29), (300, 256, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), 12,
+     (4, 3)),
+    # temporal 3x1x1 with C = 2048 (96 steps): 5 tiles on 4, one tail tile in 4 splits of 24 steps
+    ("tail_temporal", (1, 2048, 5, 16, 16), (256, 2048, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1), 4, (1, 4)),
+]
+
+
+@pytest.mark.parametrize("tile", [29, 33])
+@pytest.mark.parametrize("case", TAIL_CASES, ids=[c[0] for c in TAIL_CASES])
+def test_tail_split_bf16(case, tile):
+    name, xs, ws, st, pd, dl, cus, want = case
+    _announce(f"tail split bf16 tile {tile} {name}")
+    g = I.generator(95, P.DEV)
+    x = I.draw(xs, ("uniform", 1.0), g, P.DEV)
+    w = I.draw(ws, ("uniform", 1.0), g, P.DEV)
+    with forced(tile=tile), capped_cus(cus):
+        nbytes = B.conv_fwd_workspace_bytes(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC)
+        assert _tail(B.conv_plan_ws(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC, nbytes)) == want
+        assert nbytes == want[0] * want[1] * 256 * 256 * 4
+        wsp = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device=P.DEV)
+        y = P.run_bf16(x, w, st, pd, dl, out=_nan_out(xs, ws, st, pd, dl), workspace=wsp)
+        y_plain = P.run_bf16(x, w, st, pd, dl)
+    assert not torch.isnan(y).any()
+    ref = O.conv3d(P.bits(x), P.bits(w), st, pd, dl)
+    P.check_close(P.y_values(y), ref, int(np.prod(ws[1:])), float(x.abs().max()), float(w.abs().max()), name)
+    # outside the tail tiles the bits are conv_fwd's; inside, another summation order
+    differ = (y.view(torch.int16) != y_plain.view(torch.int16)).float().mean().item()
+    assert differ < 0.5
+
+
+@pytest.mark.parametrize("tile", [29, 33])
+@pytest.mark.parametrize("case", TAIL_CASES, ids=[c[0] for c in TAIL_CASES])
+def test_tail_split_integer_bit_exact(case, tile):
+    name, xs, ws, st, pd, dl, cus, want = case
+    _announce(f"tail split integer tile {tile} {name}")
+    g = I.generator(96, P.DEV)
+    x = I.int_valued(xs, -2, 2, g, P.DEV)
+    w = I.sparse_ternary(ws, 128, g, P.DEV)
+    bias = I.int_valued((ws[0],), -8, 8, g, P.DEV).float()
+    amax = torch.full((1,), float("nan"), dtype=torch.float32, device=P.DEV)
+    with forced(tile=tile), capped_cus(cus):
+        nbytes = B.conv_fwd_workspace_bytes(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC)
+        wsp = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device=P.DEV)
+        y = P.run_bf16(x, w, st, pd, dl, out=_nan_out(xs, ws, st, pd, dl), workspace=wsp, bias=bias, amax=amax)
+    ref = O.conv3d(P.bits(x), P.bits(w), st, pd, dl, bias=bias.cpu().numpy())
+    assert np.array_equal(P.y_values(y), ref)
+    assert float(amax) == float(np.abs(ref).max())
+
+
+@pytest.mark.parametrize("tile", [29, 33])
+def test_tail_split_fp8(tile):
+    # C = 512 in fp8: 108 steps of 128 channels, 4 tail tiles in 3 splits
+    name, xs, ws, st, pd, dl, cus, want = ("tail_fp8_ragged", (2, 512, 3, 11, 29), (300, 512, 3, 3, 3), (1, 1, 1),
+                                           (1, 1, 1), (1, 1, 1), 12, (4, 3))
+    _announce(f"tail split fp8 tile {tile} {name}")
+    g = I.generator(97, P.DEV)
+    x = I.draw(xs, ("normal", 1.0), g, P.DEV)
+    w = I.draw(ws, ("normal", 1.0 / np.sqrt(np.prod(ws[1:]))), g, P.DEV)
+    ops = P.Fp8Operands(x, w)
+    with forced(tile=tile), capped_cus(cus):
+        nbytes = B.conv_fwd_workspace_bytes(xs, ws, st, pd, dl, B.IGC_FP8_E4M3FN, B.IGC_NDHWC)
+        plan = B.conv_plan_ws(xs, ws, st, pd, dl, B.IGC_FP8_E4M3FN, B.IGC_NDHWC, nbytes)
+        assert _tail(plan) == want, plan
+        wsp = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device=P.DEV)
+        y = P.run_fp8(ops, xs, ws, st, pd, dl, out=_nan_out(xs, ws, st, pd, dl), workspace=wsp)
+    sx, sw = float(ops.ref_scales[0]), float(ops.ref_scales[2])
+    ref = O.conv3d(ops.ref_xq, ops.ref_wq, st, pd, dl, sx=sx, sw=sw)
+    mx = float(np.abs(O.e4m3_decode(ops.ref_xq)).max()) * sx
+    mw = float(np.abs(O.e4m3_decode(ops.ref_wq)).max()) * sw
+    P.check_close(P.y_values(y), ref, int(np.prod(ws[1:])), mx, mw, name)
+
+
+def test_tail_split_needs_its_workspace():
+    # 16 bytes short of the tail split's need: the call runs as conv_fwd, bit for bit
+    name, xs, ws, st, pd, dl, cus, want = TAIL_CASES[0]
+    _announce("tail split, workspace 16 bytes short")
+    g = I.generator(98, P.DEV)
+    x = I.draw(xs, ("uniform", 1.0), g, P.DEV)
+    w = I.draw(ws, ("uniform", 1.0), g, P.DEV)
+    with forced(tile=29), capped_cus(cus):
+        nbytes = B.conv_fwd_workspace_bytes(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC)
+        assert _tail(B.conv_plan_ws(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC, nbytes - 16)) == (0, 1)
+        wsp = torch.full(((nbytes - 16) // 4,), float("nan"), dtype=torch.float32, device=P.DEV)
+        y_ws = P.run_bf16(x, w, st, pd, dl, workspace=wsp)
+        y_plain = P.run_bf16(x, w, st, pd, dl)
+    assert torch.equal(y_ws.view(torch.int16), y_plain.view(torch.int16))
