@@ -359,11 +359,9 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         const int64_t fp8_steps = g.T * g.R * g.S * (g.C / 128);
         if (tile == 21 && buffer_ok)
             tile = (esz == 1 && g.T * g.R * g.S <= 32 && fp8_steps >= 128) ? 33 : 29;
-        // Short fp8 reductions take the persistent form of tile 29 (41), whose workgroups load a tile's first
-        // steps while the previous tile's last steps compute: c4t 2.31 against 2.36-2.43 ms. On bf16 it was
-        // 1-2 % slower on c5 (48 steps) and 5 % slower on c3s (864 steps), so bf16 keeps tile 29.
-        if (tile == 29 && esz == 1 && fp8_steps >= 3 && fp8_steps < 128)
-            tile = 41;
+        // The persistent form of tile 29 (41) is an option only: since tile 29 stages its epilogue through
+        // LDS (which tile 41 cannot, its rings holding the next tile's first steps), tile 29 is faster on
+        // c4t too (2.23-2.33 against 2.35-2.36 ms).
     } else {
         if (kTiles[tile].stages && kTiles[tile].mf == 16 && esz == 1 && kTiles[tile].kb == 64)
             return fail(IGC_ERR_UNSUPPORTED, "tile %d: fp8 with 64-byte steps needs 32x32 MFMA blocks", tile);
