@@ -227,10 +227,13 @@ TAIL_CASES = [
      (4, 3)),
     # temporal 3x1x1 with C = 2048 (96 steps): 5 tiles on 4, one tail tile in 4 splits of 24 steps
     ("tail_temporal", (1, 2048, 5, 16, 16), (256, 2048, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1), 4, (1, 4)),
+    # 17 tiles on 16: one tail tile in 8 splits; splits start mid-tap (tile 29: steps 13, 27, 40, ...) and, on
+    # tile 32's paired 64-byte steps, at the second half of a 128-byte line (steps 27, 81, ...)
+    ("tail_one_tile_8_splits", (1, 256, 4, 17, 64), (256, 256, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), 16, (1, 8)),
 ]
 
 
-@pytest.mark.parametrize("tile", [29, 33])
+@pytest.mark.parametrize("tile", [29, 33, 28, 32])  # 32: 64-byte steps, the reduction walked in paired halves
 @pytest.mark.parametrize("case", TAIL_CASES, ids=[c[0] for c in TAIL_CASES])
 def test_tail_split_bf16(case, tile):
     name, xs, ws, st, pd, dl, cus, want = case
@@ -253,7 +256,7 @@ def test_tail_split_bf16(case, tile):
     assert differ < 0.5
 
 
-@pytest.mark.parametrize("tile", [29, 33])
+@pytest.mark.parametrize("tile", [29, 33, 32])
 @pytest.mark.parametrize("case", TAIL_CASES, ids=[c[0] for c in TAIL_CASES])
 def test_tail_split_integer_bit_exact(case, tile):
     name, xs, ws, st, pd, dl, cus, want = case
