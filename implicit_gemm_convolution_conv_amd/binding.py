@@ -28,7 +28,7 @@ IGC_PATH_AUTO, IGC_PATH_GENERIC, IGC_PATH_TEMPORAL, IGC_PATH_POINT, IGC_PATH_POI
 
 EXPORTS = ("conv_out_dims", "conv_packed_w_cols", "conv_amax", "conv_fp8_scales", "conv_pack_x", "conv_pack_w",
            "conv_fwd", "conv_fwd_ws", "conv_fwd_ex", "conv_fwd_workspace_bytes", "conv_plan", "conv_plan_ws", "conv_debug_force",
-           "conv_debug_force_splits", "conv_debug_force_grid", "conv_packed_w_t_cols", "conv_pack_w_t", "conv_bwd_data",
+           "conv_debug_force_splits", "conv_debug_force_grid", "conv_debug_force_tap_raster", "conv_packed_w_t_cols", "conv_pack_w_t", "conv_bwd_data",
            "conv_bwd_weight_workspace_bytes", "conv_bwd_weight", "conv_last_error")
 
 
@@ -73,6 +73,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.conv_debug_force.argtypes = [I32, I32, I32]
         lib.conv_debug_force_splits.argtypes = [I32]
         lib.conv_debug_force_grid.argtypes = [I32]
+        lib.conv_debug_force_tap_raster.argtypes = [I32]
         lib.conv_last_error.restype = ctypes.c_char_p
         for name in EXPORTS:
             if name not in ("conv_packed_w_cols", "conv_fwd_workspace_bytes", "conv_packed_w_t_cols",
@@ -254,6 +255,10 @@ def conv_debug_force_splits(splits):
 
 def conv_debug_force_grid(workgroups):
     _check("conv_debug_force_grid", load().conv_debug_force_grid(int(workgroups)))
+
+
+def conv_debug_force_tap_raster(mode):
+    _check("conv_debug_force_tap_raster", load().conv_debug_force_tap_raster(int(mode)))
 
 
 def conv_last_error() -> str:

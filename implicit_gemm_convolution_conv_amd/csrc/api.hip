@@ -54,6 +54,7 @@ std::atomic<int> g_force_tile{-1};
 std::atomic<int> g_force_group_m{0};
 std::atomic<int> g_force_splits{0};
 std::atomic<int> g_force_grid{0};
+std::atomic<int> g_force_tap_raster{0};
 
 constexpr int64_t kI32Max = 2147483647;
 // Compute units of an MI355X (gfx950): the workgroups of 256x256 tiles that run at once.
@@ -448,6 +449,15 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         p.group_m = (int)std::max<int64_t>(p.group_m, std::min<int64_t>(tm, 8));
     if (g_force_group_m.load() > 0)
         p.group_m = g_force_group_m.load();
+    // Temporal filters on the buffer tiles: a tile's taps read activation windows H*W rows apart, ~56 tiles
+    // on c5, which a raster of consecutive tiles re-fetches from beyond L2 once per tap. Raster groups of
+    // tiles one tap apart share those windows instead (tile_coords).
+    p.tap_stride = 0;
+    if (path == IGC_PATH_TEMPORAL && is_buffer(ts) && g.T > 1) {
+        const int64_t stride = (g.H * g.W * g.dd + ts.bm / 2) / ts.bm;
+        if (stride >= 2 && tm >= (int64_t)p.group_m * stride && g_force_tap_raster.load() >= 0)
+            p.tap_stride = (int)stride;
+    }
     p.ksplit = p.nk;
     return IGC_OK;
 }
@@ -843,7 +853,7 @@ int conv_plan_ws(const int64_t xshape[5], const int64_t wshape[5], const int32_t
         const TileShape ts = kTiles[pl.tile];
         snprintf(buf, len,
                  "path=%s tile=%dx%d waves=%d mfma=%dx%d stages=%d bstages=%d kstep=%d order=%s%s big=%d grid=%d "
-                 "group_m=%d nk=%d loads=%s schedule=%s areuse=%s xspan=%lld splits=%d ksplit=%d tail=%d/%d",
+                 "group_m=%d nk=%d loads=%s schedule=%s areuse=%s xspan=%lld splits=%d ksplit=%d tail=%d/%d tap=%d",
                  path_name(pl.path), ts.bm, ts.bn, ts.wm * ts.wn, ts.mf, ts.mf, ts.stages ? std::abs(ts.stages) : 2,
                  is_buffer(ts) ? ts.sb : (ts.stages ? std::abs(ts.stages) : 2), step_bytes(ts) / (dtype == IGC_FP8_E4M3FN ? 1 : 2),
                  is_window(ts) ? "window" : (pl.cblock ? "cblock" : "linear"), pl.p.pairs == 2 ? "-paired" : "",
@@ -852,7 +862,7 @@ int conv_plan_ws(const int64_t xshape[5], const int64_t wshape[5], const int32_t
                  pl.tile == 33 || pl.tile == 34 ? "pingpong" : (pl.tile == 41 ? "persistent" : "lockstep"), pl.tile == 34 ? "taps" : "none",
                  pl.path == IGC_PATH_POINT ? 0LL : (long long)pl.xspan, pl.p.splits, pl.p.ksplit,
                  pl.p.tail_splits > 1 ? pl.p.tiles_m * pl.p.tiles_n - pl.p.tail_first : 0,
-                 pl.p.tail_splits > 1 ? pl.p.tail_splits : 1);
+                 pl.p.tail_splits > 1 ? pl.p.tail_splits : 1, pl.p.tap_stride);
     }
     return ok();
 }
@@ -1018,6 +1028,14 @@ int conv_debug_force_grid(int workgroups)
     if (workgroups < 0)
         return fail(IGC_ERR_INVALID, "conv_debug_force_grid: workgroups %d < 0", workgroups);
     g_force_grid.store(workgroups);
+    return ok();
+}
+
+int conv_debug_force_tap_raster(int mode)
+{
+    if (mode != -1 && mode != 0)
+        return fail(IGC_ERR_INVALID, "conv_debug_force_tap_raster: mode %d is neither -1 (off) nor 0 (automatic)", mode);
+    g_force_tap_raster.store(mode);
     return ok();
 }
 

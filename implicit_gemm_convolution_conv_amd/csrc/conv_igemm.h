@@ -80,6 +80,14 @@ __device__ inline void tile_coords(const ConvParams &p, int bid, int &tm, int &t
     const int in = lin - g * gsz;
     tm = first + in % rows;
     tn = in / rows;
+    if (p.tap_stride > 0) {  // temporal raster: the group's tiles one tap apart, within whole blocks
+        const int blk = p.group_m * p.tap_stride;
+        if (tm < p.tiles_m / blk * blk) {
+            const int b = tm / blk, r = tm - b * blk;
+            const int gi = r / p.group_m, c = r - gi * p.group_m;  // group gi of the block, member c
+            tm = b * blk + c * p.tap_stride + gi;
+        }
+    }
 }
 
 __device__ inline void tile_coords(const ConvParams &p, int &tm, int &tn) { tile_coords(p, blockIdx.x, tm, tn); }

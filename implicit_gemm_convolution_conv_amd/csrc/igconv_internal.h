@@ -115,6 +115,11 @@ struct ConvParams {
     // tail_first + t * tail_splits + j stores its unscaled fp32 sums of tile
     // tail_first + t at part + (t * tail_splits + j) * BM * BN, [column][row]
     int tail_first, tail_splits;
+    // temporal raster (0 = off): within each block of group_m * tap_stride
+    // M-tiles, the group_m tiles a raster group walks together are tap_stride
+    // tiles apart (about H*W / BM: one temporal tap), so that each tile's next
+    // tap reads the window its neighbour in the group reads at the current one
+    int tap_stride;
     // fused epilogue extras (null = off): fp32 bias per output channel added
     // before rounding; max |y| merged into *amax as fp32 bits (zeroed before
     // the launch)

@@ -288,6 +288,11 @@ IGC_API int conv_debug_force_splits(int splits);
  * have a partial last round too. */
 IGC_API int conv_debug_force_grid(int workgroups);
 
+/* Testing and tuning hook: -1 turns the temporal raster off (raster groups of
+ * consecutive M tiles on temporal filters too), 0 restores the automatic
+ * choice (groups of tiles one temporal tap apart). */
+IGC_API int conv_debug_force_tap_raster(int mode);
+
 /* Text of the last error on this thread ("" if none). Valid until the next call. */
 IGC_API const char *conv_last_error(void);
 

@@ -525,6 +525,45 @@ def test_persistent_tile_fp8_walks_many_tiles(grid):
     P.check_close(P.y_values(y41), ref, int(np.prod(ws[1:])), mx, mw, name)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_temporal_tap_raster(dtype):
+    # 3x1x1 over 8 planes of 32 x 32: taps 1024 rows (4 tiles) apart, 32 M tiles x 4 K tiles, raster groups of
+    # 8: one block of 8 groups whose members are one tap apart. Each tile is still computed once: the output
+    # equals the consecutive raster's bit for bit, and the oracle within tolerance.
+    _announce(f"temporal tap raster {dtype}")
+    xs, ws, st, pd, dl = (1, 128, 8, 32, 32), (1024, 128, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1)
+    g = I.generator(37, P.DEV)
+    x = I.draw(xs, ("normal", 1.0), g, P.DEV)
+    w = I.draw(ws, ("normal", 1.0 / np.sqrt(np.prod(ws[1:]))), g, P.DEV)
+    dt = B.IGC_BF16 if dtype == "bf16" else B.IGC_FP8_E4M3FN
+    if dtype == "bf16":
+        run = lambda: P.run_bf16(x, w, st, pd, dl)
+    else:
+        ops = P.Fp8Operands(x, w)
+        run = lambda: P.run_fp8(ops, xs, ws, st, pd, dl)
+    with forced(tile=29):  # the 128-tile grid would otherwise take the 128x128 direct-to-LDS tile
+        kv = dict(item.split("=") for item in B.conv_plan(xs, ws, st, pd, dl, dt, B.IGC_NDHWC).split())
+        assert (kv["path"], kv["tap"], kv["group_m"], kv["grid"]) == ("temporal", "4", "8", "128"), kv
+        y_tap = run().clone()
+        try:
+            B.conv_debug_force_tap_raster(-1)
+            assert "tap=0" in B.conv_plan(xs, ws, st, pd, dl, dt, B.IGC_NDHWC)
+            y_off = run().clone()
+        finally:
+            B.conv_debug_force_tap_raster(0)
+    assert torch.equal(y_tap.view(torch.int16), y_off.view(torch.int16))
+    if dtype == "bf16":
+        ref = O.conv3d(P.bits(x), P.bits(w), st, pd, dl)
+        P.check_close(P.y_values(y_tap), ref, int(np.prod(ws[1:])), float(x.abs().max()), float(w.abs().max()),
+                      "tap raster")
+    else:
+        sx, sw = float(ops.ref_scales[0]), float(ops.ref_scales[2])
+        ref = O.conv3d(ops.ref_xq, ops.ref_wq, st, pd, dl, sx=sx, sw=sw)
+        mx = float(np.abs(O.e4m3_decode(ops.ref_xq)).max()) * sx
+        mw = float(np.abs(O.e4m3_decode(ops.ref_wq)).max()) * sw
+        P.check_close(P.y_values(y_tap), ref, int(np.prod(ws[1:])), mx, mw, "tap raster fp8")
+
+
 def test_buffer_tiles_agree_bitwise_with_global_tiles():
     # same reduction order (channel block outer, 16x16 blocks, k-slices in order): identical bits
     _announce("buffer tiles vs direct-to-LDS tiles 6 / 21, bitwise")
