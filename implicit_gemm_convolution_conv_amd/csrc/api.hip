@@ -358,8 +358,13 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         // fp8 with a long reduction takes the ping-pong wave groups of tile 33; with a short one (a 3x1x1
         // filter: 48 steps on c4t) tile 33 measured 4 % slower than tile 29 (2.43 against 2.33 ms).
         const int64_t fp8_steps = g.T * g.R * g.S * (g.C / 128);
+        // bf16 on the generic path takes tile 31 (tile 29 with A fragments read two MFMA rows ahead and the
+        // next k-slice's B fragments read early): in alternating runs c3 34.1 against 34.5 ms and c3s 4.27
+        // against 4.41 ms; on the temporal path tile 29 stays ahead (c5 17.2 against 17.7 ms).
         if (tile == 21 && buffer_ok)
-            tile = (esz == 1 && g.T * g.R * g.S <= 32 && fp8_steps >= 128) ? 33 : 29;
+            tile = (esz == 1 && g.T * g.R * g.S <= 32 && fp8_steps >= 128)
+                       ? 33
+                       : (esz == 2 && path == IGC_PATH_GENERIC ? 31 : 29);
         // The persistent form of tile 29 (41) is an option only: since tile 29 stages its epilogue through
         // LDS (which tile 41 cannot, its rings holding the next tile's first steps), tile 29 is faster on
         // c4t too (2.23-2.33 against 2.35-2.36 ms).
