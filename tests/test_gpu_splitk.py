@@ -233,7 +233,7 @@ TAIL_CASES = [
 ]
 
 
-@pytest.mark.parametrize("tile", [29, 33, 28, 32])  # 32: 64-byte steps, the reduction walked in paired halves
+@pytest.mark.parametrize("tile", [29, 31, 33, 28, 32])  # 32: 64-byte steps, the reduction walked in paired halves
 @pytest.mark.parametrize("case", TAIL_CASES, ids=[c[0] for c in TAIL_CASES])
 def test_tail_split_bf16(case, tile):
     name, xs, ws, st, pd, dl, cus, want = case
@@ -256,7 +256,7 @@ def test_tail_split_bf16(case, tile):
     assert differ < 0.5
 
 
-@pytest.mark.parametrize("tile", [29, 33, 32])
+@pytest.mark.parametrize("tile", [29, 31, 33, 32])
 @pytest.mark.parametrize("case", TAIL_CASES, ids=[c[0] for c in TAIL_CASES])
 def test_tail_split_integer_bit_exact(case, tile):
     name, xs, ws, st, pd, dl, cus, want = case
@@ -275,7 +275,7 @@ def test_tail_split_integer_bit_exact(case, tile):
     assert float(amax) == float(np.abs(ref).max())
 
 
-@pytest.mark.parametrize("tile", [29, 33])
+@pytest.mark.parametrize("tile", [29, 31, 33])
 def test_tail_split_fp8(tile):
     # C = 512 in fp8: 108 steps of 128 channels, 4 tail tiles in 3 splits
     name, xs, ws, st, pd, dl, cus, want = ("tail_fp8_ragged", (2, 512, 3, 11, 29), (300, 512, 3, 3, 3), (1, 1, 1),

@@ -1,11 +1,21 @@
-"""GPU parity at the full workload sizes, in the launch configuration bench.py times.
+"""GPU parity at the full workload sizes, through the calls bench.py times.
+
+bench.py times conv_fwd_ws with a workspace of conv_fwd_workspace_bytes: on
+the 256x256 buffer tiles the last, partial round of tiles then runs split along
+the reduction (the tail split), and a second pass adds the partial sums. Every
+full-size check here makes that same call (`_timed_call`) and asserts the plan
+it runs; conv_fwd (no workspace) runs beside it where the plan splits.
 
 Random data: the oracle evaluates sampled output elements one by one (box
-corners, edges, faces and their neighbours, chosen planes and channels, plus
-uniform draws) and the relative-L2 / max-abs tolerance applies over the
-sample. Exact checks at full size: a delta filter (output = shifted copy of
-the input, bit for bit) and all-ones operands (output = C x number of valid
-taps, a closed form), which exercise every address the kernels compute.
+corners, edges, faces and their neighbours, chosen planes and channels,
+uniform draws, and for split plans several elements of every tail tile) and
+the relative-L2 / max-abs tolerance applies over the sample. The tail tiles
+are found from the outputs themselves: outside them conv_fwd_ws and conv_fwd
+run the same instructions and agree bit for bit, inside them the summation
+order differs. Exact checks at full size: a delta filter (output = shifted
+copy of the input, bit for bit) and all-ones operands (output = C x number
+of valid taps, a closed form), which exercise every address the kernels
+compute, for bf16 and for fp8 with unit scales.
 """
 
 import numpy as np
@@ -38,6 +48,113 @@ def _valid_taps(size, ksz, pad, dev):
     return ((pos >= 0) & (pos < size)).sum(1).to(torch.float64)
 
 
+def _plan_kv(plan):
+    return dict(item.split("=") for item in plan.split())
+
+
+def _timed_call(xk, wp, y, wl, dtype, scales=None):
+    """The call bench.py times for workload `wl`: conv_fwd_ws with a NaN-filled workspace of
+    conv_fwd_workspace_bytes (conv_fwd where the plan needs none). Returns the plan string it ran."""
+    args = (wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dil, dtype, B.IGC_NDHWC)
+    nws = B.conv_fwd_workspace_bytes(*args)
+    plan = B.conv_plan_ws(*args, max(nws, 0))
+    if nws > 0:
+        wsb = torch.full((nws // 4,), float("nan"), dtype=torch.float32, device=P.DEV)
+        B.conv_fwd_ws(xk, wp, y, *args, scales, workspace=wsb)
+        torch.cuda.synchronize()
+        del wsb
+    else:
+        B.conv_fwd(xk, wp, y, *args, scales)
+        torch.cuda.synchronize()
+    return plan
+
+
+def _tail_split(plan):
+    r, s = _plan_kv(plan)["tail"].split("/")
+    return int(r), int(s)
+
+
+def _tile_of_workgroup(bid, tiles_m, tiles_n, group_m, tap_stride):
+    """The output tile (m-tile, k-tile) that workgroup `bid` of a launch computes: the kernels' tile schedule
+    restated (workgroups dealt to the 8 XCDs in turn and renumbered so that consecutive tiles share one; tiles
+    walked in groups of group_m tile rows, every column of a group before the next; the temporal raster
+    spreads a group's rows one time tap apart)."""
+    nblk = tiles_m * tiles_n
+    xcd, idx = bid & 7, bid >> 3
+    q, r = nblk >> 3, nblk & 7
+    lin = xcd * q + min(xcd, r) + idx
+    gsz = group_m * tiles_n
+    g = lin // gsz
+    first = g * group_m
+    rows = min(tiles_m - first, group_m)
+    inn = lin - g * gsz
+    tm, tn = first + inn % rows, inn // rows
+    if tap_stride > 0:
+        blk = group_m * tap_stride
+        if tm < tiles_m // blk * blk:
+            b, rr = divmod(tm, blk)
+            gi, c = divmod(rr, group_m)
+            tm = b * blk + c * tap_stride + gi
+    return tm, tn
+
+
+def _tail_tiles(plan, y_shape, tm=256, tn=256):
+    """The (m-tile, k-tile) pairs the tail split computes: the tiles of workgroups tail_first .. ntiles - 1."""
+    kv = _plan_kv(plan)
+    r, _ = _tail_split(plan)
+    _, k, do, ho, wo = y_shape
+    tiles_m, tiles_n = -(-do * ho * wo // tm), -(-k // tn)
+    ntiles = tiles_m * tiles_n
+    assert int(kv["grid"]) == ntiles
+    return {_tile_of_workgroup(b, tiles_m, tiles_n, int(kv["group_m"]), int(kv["tap"]))
+            for b in range(ntiles - r, ntiles)}
+
+
+def _tiles_that_differ(y_ws, y_plain, tm=256, tn=256):
+    """(m-tile, k-tile) pairs of a one-image output where the two results differ in any bit."""
+    n, k = y_ws.shape[:2]
+    assert n == 1
+    diff = (y_ws.view(torch.int16) != y_plain.view(torch.int16)).view(k, -1)
+    idx = diff.nonzero()
+    if idx.numel() == 0:
+        return set()
+    tiles = torch.unique(torch.stack([idx[:, 1] // tm, idx[:, 0] // tn], 1), dim=0)
+    return {(int(a), int(b)) for a, b in tiles.cpu().numpy()}
+
+
+def _points_in_tiles(tiles, y_shape, per_tile, rng, tm=256, tn=256):
+    """`per_tile` random output elements (n, k, od, oh, ow) inside each (m-tile, k-tile) of a one-image output."""
+    _, k, do, ho, wo = y_shape
+    m_total = do * ho * wo
+    pts = []
+    for mt, nt in sorted(tiles):
+        for _ in range(per_tile):
+            m = int(rng.integers(mt * tm, min(m_total, (mt + 1) * tm)))
+            kk = int(rng.integers(nt * tn, min(k, (nt + 1) * tn)))
+            pts.append((0, kk, m // (ho * wo), (m // wo) % ho, m % wo))
+    return np.array(pts, np.int64).reshape(-1, 5)
+
+
+def _check_tail_split(y_ws, y_plain, plan, R, max_x, max_w, rng, what, expect_most_differ=True):
+    """conv_fwd_ws against conv_fwd on the same inputs: they may differ only inside the tail tiles, and there
+    only by summation order (within the tolerance). Returns oracle points, several in every tail tile.
+    bf16 products round in fp32, so another summation order changes some output bits in nearly every tail
+    tile; fp8 products are exact in fp32 and a tile's bits often come out the same either way."""
+    r, s = _tail_split(plan)
+    assert r > 0 and s >= 2, f"{what}: the timed plan has no tail split: {plan}"
+    tail = _tail_tiles(plan, tuple(y_ws.shape))
+    assert len(tail) == r
+    differ = _tiles_that_differ(y_ws, y_plain)
+    assert differ <= tail, f"{what}: tiles outside the tail differ from conv_fwd: {sorted(differ - tail)[:8]}"
+    if expect_most_differ:
+        assert len(differ) >= r // 2, f"{what}: only {len(differ)} of {r} tail tiles differ from conv_fwd"
+    mdiff = float((y_ws.float() - y_plain.float()).abs().max())
+    assert mdiff <= P.ABS_FACTOR * np.sqrt(R) * max_x * max_w, f"{what}: conv_fwd_ws vs conv_fwd {mdiff}"
+    pts = _points_in_tiles(tail, tuple(y_ws.shape), max(1, -(-400 // r)), rng)
+    assert len(pts) >= 400
+    return pts
+
+
 def test_c2_point_output_full():
     wl = I.WORKLOADS["c2"]
     _announce("c2 point-output, all 9500 x 1280 outputs")
@@ -50,28 +167,55 @@ def test_c2_point_output_full():
     _free()
 
 
+def _delta_filter(ws, tap, seed):
+    """One-hot filter: output channel k reads input channel perm[k] at filter tap `tap` (bf16)."""
+    k, c = ws[0], ws[1]
+    perm = torch.randperm(c, generator=torch.Generator().manual_seed(seed))[:k].to(P.DEV)
+    wd = torch.zeros(ws, dtype=torch.bfloat16, device=P.DEV)
+    wd[torch.arange(k, device=P.DEV), perm, tap[0], tap[1], tap[2]] = 1.0
+    return wd, perm
+
+
+def _all_ones_counts(xs, c, dev):
+    """C x the number of valid taps of a 3x3x3 filter with pad 1 at every output position (D, H, W)."""
+    d, h, w = xs[2:]
+    return (_valid_taps(d, 3, 1, dev)[:, None, None] * _valid_taps(h, 3, 1, dev)[None, :, None]
+            * _valid_taps(w, 3, 1, dev)[None, None, :]) * c
+
+
 def test_c3_sampled_and_exact():
     wl = I.WORKLOADS["c3"]
-    _announce("c3 bf16 sampled")
+    _announce("c3 bf16 through conv_fwd_ws (the timed call), sampled and tail tiles vs oracle")
     x, w = I.make(wl, P.DEV)  # x drawn NDHWC
     xs, ws = wl.x_shape, wl.w_shape
     wp = PL.packed_weight(w, "bf16", "NDHWC")
-    y = PL.output(xs, ws, wl.stride, wl.pad, wl.dil, P.DEV)
-    B.conv_fwd(x, wp, y, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
+    y = torch.full((1, ws[0]) + tuple(B.conv_out_dims(xs, ws, wl.stride, wl.pad, wl.dil)), float("nan"),
+                   dtype=torch.bfloat16, device=P.DEV)
+    plan = _timed_call(x, wp, y, wl, B.IGC_BF16)
+    kv = _plan_kv(plan)
+    assert (kv["path"], kv["tile"], kv["loads"], kv["tail"]) == ("generic", "256x256", "buffer-lds", "96/2"), plan
+    assert not torch.isnan(y).any()
+    y_plain = PL.output(xs, ws, wl.stride, wl.pad, wl.dil, P.DEV)
+    B.conv_fwd(x, wp, y_plain, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
     torch.cuda.synchronize()
+    mx, mw = float(x.abs().max()), float(w.abs().max())
     rng = np.random.default_rng(3)
-    pts = P.sample_points(1, ws[0], *y.shape[2:], rng, n_random=600, extra_k=(1023, 1024))
+    tail_pts = _check_tail_split(y, y_plain, plan, wl.reduction, mx, mw, rng, "c3")
+    del y_plain
+    pts = np.concatenate([P.sample_points(1, ws[0], *y.shape[2:], rng, n_random=600, extra_k=(1023, 1024)),
+                          tail_pts])
     ref = O.conv3d_points(P.bits(x), P.bits(w), pts, wl.stride, wl.pad, wl.dil, x_layout="NDHWC")
-    P.check_close(P.gather(y, pts), ref, wl.reduction, float(x.abs().max()), float(w.abs().max()), "c3")
+    P.check_close(P.gather(y, pts), ref, wl.reduction, mx, mw, "c3")
+    n_tail = len(tail_pts)
+    P.check_close(P.gather(y, tail_pts), ref[-n_tail:], wl.reduction, mx, mw, "c3 tail tiles")
 
-    _announce("c3 bf16 delta filter, full size")
+    _announce("c3 bf16 delta filter, full size, conv_fwd_ws")
     k, c = ws[0], ws[1]
-    perm = torch.randperm(c, generator=torch.Generator().manual_seed(0))[:k].to(P.DEV)
-    wd = torch.zeros(ws, dtype=torch.bfloat16, device=P.DEV)
     tap = (2, 0, 1)
-    wd[torch.arange(k, device=P.DEV), perm, tap[0], tap[1], tap[2]] = 1.0
+    wd, perm = _delta_filter(ws, tap, 0)
     wpd = PL.packed_weight(wd, "bf16", "NDHWC")
-    B.conv_fwd(x, wpd, y, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
+    y.fill_(float("nan"))
+    _timed_call(x, wpd, y, wl, B.IGC_BF16)
     xpad = torch.nn.functional.pad(x, (0, 0, 1, 1, 1, 1, 1, 1))  # zero halo on D, H, W of NDHWC
     d, h, wdt = xs[2:]
     shifted = xpad[:, tap[0]:tap[0] + d, tap[1]:tap[1] + h, tap[2]:tap[2] + wdt, :]  # (N, D, H, W, C)
@@ -79,32 +223,79 @@ def test_c3_sampled_and_exact():
     assert torch.equal(y.view(torch.int16), expect.contiguous().view(torch.int16))
     del xpad, shifted, expect, wd, wpd
 
-    _announce("c3 bf16 all-ones, full size")
+    _announce("c3 bf16 all-ones, full size, conv_fwd_ws")
     x.fill_(1.0)
     wones = torch.ones(ws, dtype=torch.bfloat16, device=P.DEV)
     wp = PL.packed_weight(wones, "bf16", "NDHWC")
-    B.conv_fwd(x, wp, y, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
-    cnt = (_valid_taps(d, 3, 1, P.DEV)[:, None, None] * _valid_taps(h, 3, 1, P.DEV)[None, :, None]
-           * _valid_taps(wdt, 3, 1, P.DEV)[None, None, :]) * c
-    assert torch.equal(y.double(), cnt.expand(1, k, d, h, wdt))
+    y.fill_(float("nan"))
+    _timed_call(x, wp, y, wl, B.IGC_BF16)
+    assert torch.equal(y.double(), _all_ones_counts(xs, c, P.DEV).expand(1, k, d, h, wdt))
     _free()
 
 
 @pytest.mark.parametrize("name", ["c4", "c4t"])
 def test_fp8_sampled(name):
     wl = I.WORKLOADS[name]
-    _announce(f"{name} fp8 pack (all codes) and sampled conv")
+    _announce(f"{name} fp8 pack (all codes) and sampled conv through the timed call")
     x, w = I.make(wl, P.DEV)  # x drawn NCDHW bf16
     xs, ws = wl.x_shape, wl.w_shape
     ops = P.Fp8Operands(x, w, check_codes=True)
-    y = P.run_fp8(ops, xs, ws, wl.stride, wl.pad, wl.dil)
-    rng = np.random.default_rng(4)
-    pts = P.sample_points(1, ws[0], *y.shape[2:], rng, n_random=600)
+    y = torch.full((1, ws[0]) + tuple(B.conv_out_dims(xs, ws, wl.stride, wl.pad, wl.dil)), float("nan"),
+                   dtype=torch.bfloat16, device=P.DEV)
+    plan = _timed_call(ops.xq, ops.wq, y, wl, B.IGC_FP8_E4M3FN, ops.scales)
+    kv = _plan_kv(plan)
+    assert not torch.isnan(y).any()
     sx, sw = float(ops.ref_scales[0]), float(ops.ref_scales[2])
-    ref = O.conv3d_points(ops.ref_xq, ops.ref_wq, pts, wl.stride, wl.pad, wl.dil, sx=sx, sw=sw)
     mx = float(np.abs(O.e4m3_decode(ops.ref_xq)).max()) * sx
     mw = float(np.abs(O.e4m3_decode(ops.ref_wq)).max()) * sw
+    rng = np.random.default_rng(4)
+    pts = P.sample_points(1, ws[0], *y.shape[2:], rng, n_random=600)
+    if name == "c4":  # the ping-pong tile with its tail split: 96 tiles in 2 splits
+        assert (kv["schedule"], kv["tail"]) == ("pingpong", "96/2"), plan
+        y_plain = PL.output(xs, ws, wl.stride, wl.pad, wl.dil, P.DEV)
+        B.conv_fwd(ops.xq, ops.wq, y_plain, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_FP8_E4M3FN, B.IGC_NDHWC,
+                   ops.scales)
+        torch.cuda.synchronize()
+        pts = np.concatenate([pts, _check_tail_split(y, y_plain, plan, wl.reduction, mx, mw, rng, name,
+                                                      expect_most_differ=False)])
+        del y_plain
+    else:  # 48 steps: no tail split, the lockstep buffer tile with the temporal raster
+        assert (kv["path"], kv["schedule"], kv["tail"]) == ("temporal", "lockstep", "0/1"), plan
+    ref = O.conv3d_points(ops.ref_xq, ops.ref_wq, pts, wl.stride, wl.pad, wl.dil, sx=sx, sw=sw)
     P.check_close(P.gather(y, pts), ref, wl.reduction, mx, mw, name)
+    _free()
+
+
+def test_c4_fp8_exact_full_size():
+    """fp8 at full size with unit scales: integer activations in [-2, 2] and a one-hot or all-ones filter are
+    exact E4M3FN codes, so the timed call must give a shifted copy of x, and C x the valid taps, bit for bit."""
+    wl = I.WORKLOADS["c4"]
+    xs, ws = wl.x_shape, wl.w_shape
+    k, c = ws[0], ws[1]
+    d, h, wdt = xs[2:]
+    unit = torch.ones(4, dtype=torch.float32, device=P.DEV)
+    _announce("c4 fp8 delta filter, full size, conv_fwd_ws (ping-pong tile, tail split)")
+    xi = I.int_valued(xs, -2, 2, I.generator(40, P.DEV), P.DEV)  # NCDHW bf16
+    xq = PL.packed_input(xi, "fp8", unit[0:2])
+    tap = (0, 2, 1)
+    wd, perm = _delta_filter(ws, tap, 4)
+    wq = PL.packed_weight(wd, "fp8", "NDHWC", unit[2:4])
+    del wd
+    y = torch.full((1, k, d, h, wdt), float("nan"), dtype=torch.bfloat16, device=P.DEV)
+    plan = _timed_call(xq, wq, y, wl, B.IGC_FP8_E4M3FN, unit)
+    assert (_plan_kv(plan)["schedule"], _plan_kv(plan)["tail"]) == ("pingpong", "96/2"), plan
+    xpad = torch.nn.functional.pad(xi, (1, 1, 1, 1, 1, 1))  # zero halo on D, H, W of NCDHW
+    for k0 in range(0, k, 512):
+        expect = xpad[:, perm[k0:k0 + 512], tap[0]:tap[0] + d, tap[1]:tap[1] + h, tap[2]:tap[2] + wdt]
+        assert torch.equal(y[:, k0:k0 + 512].view(torch.int16), expect.contiguous().view(torch.int16)), k0
+    del xpad, expect, xi, wq
+
+    _announce("c4 fp8 all-ones, full size, conv_fwd_ws")
+    xq.fill_(0x38)  # E4M3FN code of 1.0
+    wq = PL.packed_weight(torch.ones(ws, dtype=torch.bfloat16, device=P.DEV), "fp8", "NDHWC", unit[2:4])
+    y.fill_(float("nan"))
+    _timed_call(xq, wq, y, wl, B.IGC_FP8_E4M3FN, unit)
+    assert torch.equal(y.double(), _all_ones_counts(xs, c, P.DEV).expand(1, k, d, h, wdt))
     _free()
 
 
@@ -124,11 +315,12 @@ def test_c5_large_tensor():
         assert torch.equal(xt[:, dd:dd + 16].view(torch.int16),
                            x[:, :, dd:dd + 16].permute(0, 2, 3, 4, 1).contiguous().view(torch.int16))
 
-    _announce("c5 sampled vs oracle (planes across the 2^31 / 2^32 offsets)")
+    _announce("c5 sampled vs oracle (planes across the 2^31 / 2^32 offsets), the timed call")
     wp = PL.packed_weight(w, "bf16", "NDHWC")
-    y = PL.output(xs, ws, wl.stride, wl.pad, wl.dil, P.DEV)
-    B.conv_fwd(xt, wp, y, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
-    torch.cuda.synchronize()
+    y = torch.full((1, k) + tuple(B.conv_out_dims(xs, ws, wl.stride, wl.pad, wl.dil)), float("nan"),
+                   dtype=torch.bfloat16, device=P.DEV)
+    plan = _timed_call(xt, wp, y, wl, B.IGC_BF16)
+    assert (_plan_kv(plan)["loads"], _plan_kv(plan)["tail"]) == ("buffer-lds", "0/1"), plan
     assert y.numel() > 2 ** 31
     rng = np.random.default_rng(5)
     pts = P.sample_points(1, k, *y.shape[2:], rng, n_random=800, extra_d=(145, 146, 147, 238),
@@ -138,18 +330,35 @@ def test_c5_large_tensor():
     del xb
     P.check_close(P.gather(y, pts), ref, wl.reduction, float(x.abs().max()), float(w.abs().max()), "c5")
 
-    _announce("c5 delta filter, full size (bit-exact)")
-    perm = torch.randperm(c, generator=torch.Generator().manual_seed(1))[:k].to(P.DEV)
-    wd = torch.zeros(ws, dtype=torch.bfloat16, device=P.DEV)
-    wd[torch.arange(k, device=P.DEV), perm, 0, 0, 0] = 1.0  # tap t=0: y[:, k, od] = x[:, perm[k], od - 1]
-    wpd = PL.packed_weight(wd, "bf16", "NDHWC")
-    B.conv_fwd(xt, wpd, y, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
-    torch.cuda.synchronize()
+    # delta filters on the first and the last time tap: y[:, k, od] = x[:, perm[k], od - 1 + t]
+    for t, seed in ((0, 1), (2, 11)):
+        _announce(f"c5 delta filter on tap t={t}, full size (bit-exact)")
+        wd, perm = _delta_filter(ws, (t, 0, 0), seed)
+        wpd = PL.packed_weight(wd, "bf16", "NDHWC")
+        del wd
+        y.fill_(float("nan"))
+        _timed_call(xt, wpd, y, wl, B.IGC_BF16)
+        zero_plane = 0 if t == 0 else d - 1
+        assert torch.equal(y[:, :, zero_plane].view(torch.int16),
+                           torch.zeros_like(y[:, :, zero_plane]).view(torch.int16))
+        lo, hi = (1, d) if t == 0 else (0, d - 1)
+        for kk in range(0, k, 128):
+            src = x[:, perm[kk:kk + 128], lo - 1 + t: hi - 1 + t]
+            assert torch.equal(y[:, kk:kk + 128, lo:hi].view(torch.int16), src.view(torch.int16)), (t, kk)
+        del wpd
+
+    _announce("c5 all-ones, full size: 2C on the first and last planes, 3C inside")
+    del x
+    torch.cuda.empty_cache()
+    xt.fill_(1.0)
+    wp = PL.packed_weight(torch.ones(ws, dtype=torch.bfloat16, device=P.DEV), "bf16", "NDHWC")
+    y.fill_(float("nan"))
+    _timed_call(xt, wp, y, wl, B.IGC_BF16)
     del xt
-    assert torch.equal(y[:, :, 0].view(torch.int16), torch.zeros_like(y[:, :, 0]).view(torch.int16))
     for kk in range(0, k, 128):
-        src = x[:, perm[kk:kk + 128], : d - 1]
-        assert torch.equal(y[:, kk:kk + 128, 1:].view(torch.int16), src.view(torch.int16)), kk
+        blk = y[:, kk:kk + 128]
+        assert bool((blk[:, :, 1:d - 1] == 3 * c).all()), kk
+        assert bool((blk[:, :, 0] == 2 * c).all()) and bool((blk[:, :, d - 1] == 2 * c).all()), kk
     _free()
 
 
@@ -190,20 +399,30 @@ def test_pointwise_ncdhw_page_workload():
 
 @pytest.mark.parametrize("name", ["c3s", "c5s"])
 def test_one_gpu_share_sampled(name):
-    # one GPU's share of an 8-way split, at its real shape: the kernel that GPU would run
+    # one GPU's share of an 8-way split, at its real shape: the kernel that GPU would run, through the call
+    # bench.py times (c3s: 844 tiles = 3 rounds of 256 + 76 tail tiles in 3 splits)
     wl = I.WORKLOADS[name]
-    _announce(f"{name} one-GPU share, sampled vs oracle")
+    _announce(f"{name} one-GPU share, sampled vs oracle, the timed call")
     x, w = I.make(wl, P.DEV)
     xs, ws = wl.x_shape, wl.w_shape
     wp = PL.packed_weight(w, "bf16", "NDHWC")
     xk = x if wl.x_layout == "NDHWC" else PL.packed_input(x, "bf16")
-    y = PL.output(xs, ws, wl.stride, wl.pad, wl.dil, P.DEV)
-    B.conv_fwd(xk, wp, y, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
-    torch.cuda.synchronize()
+    y = torch.full((1, ws[0]) + tuple(B.conv_out_dims(xs, ws, wl.stride, wl.pad, wl.dil)), float("nan"),
+                   dtype=torch.bfloat16, device=P.DEV)
+    plan = _timed_call(xk, wp, y, wl, B.IGC_BF16)
+    assert not torch.isnan(y).any()
+    mx, mw = float(x.abs().max()), float(w.abs().max())
     rng = np.random.default_rng(7)
     pts = P.sample_points(1, ws[0], *y.shape[2:], rng, n_random=400)
+    if name == "c3s":
+        assert _plan_kv(plan)["tail"] == "76/3", plan
+        y_plain = PL.output(xs, ws, wl.stride, wl.pad, wl.dil, P.DEV)
+        B.conv_fwd(xk, wp, y_plain, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
+        torch.cuda.synchronize()
+        pts = np.concatenate([pts, _check_tail_split(y, y_plain, plan, wl.reduction, mx, mw, rng, name)])
+        del y_plain
     ref = O.conv3d_points(P.bits(x), P.bits(w), pts, wl.stride, wl.pad, wl.dil, x_layout=wl.x_layout)
-    P.check_close(P.gather(y, pts), ref, wl.reduction, float(x.abs().max()), float(w.abs().max()), name)
+    P.check_close(P.gather(y, pts), ref, wl.reduction, mx, mw, name)
     _free()
 
 
