@@ -25,6 +25,9 @@ IGC_ERR_INVALID, IGC_ERR_UNSUPPORTED, IGC_ERR_ALIGN, IGC_ERR_HIP = -1, -2, -3, -
 IGC_BF16, IGC_FP8_E4M3FN = 0, 1
 IGC_NCDHW, IGC_NDHWC = 0, 1
 IGC_PATH_AUTO, IGC_PATH_GENERIC, IGC_PATH_TEMPORAL, IGC_PATH_POINT, IGC_PATH_POINTWISE = 0, 1, 2, 3, 4
+IGC_TILE_AUTO = -1
+IGC_TILE_DMA_256, IGC_TILE_DMA_128, IGC_TILE_DMA_64, IGC_TILE_DMA_256x192 = 0, 1, 2, 3
+IGC_TILE_BUF, IGC_TILE_BUF_AHEAD, IGC_TILE_BUF_PINGPONG, IGC_TILE_PW = 4, 5, 6, 7
 
 EXPORTS = ("conv_out_dims", "conv_packed_w_cols", "conv_amax", "conv_fp8_scales", "conv_pack_x", "conv_pack_w",
            "conv_fwd", "conv_fwd_ws", "conv_fwd_ex", "conv_fwd_workspace_bytes", "conv_plan", "conv_plan_ws", "conv_debug_force",
@@ -253,8 +256,8 @@ def conv_debug_force_splits(splits):
     _check("conv_debug_force_splits", load().conv_debug_force_splits(int(splits)))
 
 
-def conv_debug_force_grid(workgroups):
-    _check("conv_debug_force_grid", load().conv_debug_force_grid(int(workgroups)))
+def conv_debug_force_grid(cus):
+    _check("conv_debug_force_grid", load().conv_debug_force_grid(int(cus)))
 
 
 def conv_debug_force_tap_raster(mode):

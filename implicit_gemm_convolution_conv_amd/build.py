@@ -34,19 +34,15 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-# Kernels allowed to use private (scratch) memory: the 4-wave 256x256 direct-to-LDS tiles (256 fp32
-# accumulators per lane, kept only as a measured negative result) and the fp8 register-staged 256x256
-# tile with 64-bit offsets. Anywhere else scratch means a register spill or a kernel argument copied
-# to private memory, which slows the kernel several times over: the build fails.
-SCRATCH_OK = ("conv_igemm_dma_kernelILi256ELi256ELi2ELi2E", "conv_igemm_kernelILi256ELi256ELi2ELi4ELi16ELi1ELi0ELb1E")
-
-
+# No kernel may use private (scratch) memory: scratch means a register spill or a
+# kernel argument copied to private memory, which slows a kernel several times
+# over, so the build fails on it.
 def _scratch_kernels(remarks: str) -> list[str]:
     bad = []
     for blk in re.split(r"Function Name: ", remarks)[1:]:
         name = blk.split()[0]
         m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", blk)
-        if m and int(m.group(1)) > 0 and not any(k in name for k in SCRATCH_OK):
+        if m and int(m.group(1)) > 0:
             bad.append(f"{name} ({m.group(1)} bytes/lane)")
     return bad
 
@@ -67,8 +63,11 @@ def _compile(src: str) -> str:
 
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    for f in os.listdir(BUILD):  # objects of sources that no longer exist
+        if f.endswith(".o") and not os.path.exists(os.path.join(CSRC, f[:-2] + ".hip")):
+            os.remove(os.path.join(BUILD, f))
     # the kernel-instantiation units take minutes each, the rest seconds: start those first
-    srcs = sorted(sources(), key=lambda s: not os.path.basename(s).startswith(("conv_dma_", "conv_bf16", "conv_fp8")))
+    srcs = sorted(sources(), key=lambda s: not os.path.basename(s).startswith(("conv_dma_", "conv_buf_")))
     jobs = jobs or min(len(srcs), max(1, os.cpu_count() or 2), 8)
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))

@@ -15,14 +15,8 @@
 #include "igconv_internal.h"
 
 namespace igc {
-hipError_t launch_conv_bf16(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream);
-hipError_t launch_conv_fp8(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream);
-
 hipError_t launch_conv_dma_bf16(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream);
 hipError_t launch_conv_dma_fp8(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream);
-
-hipError_t launch_conv_win_bf16(const ConvParams &p, int tile, bool big, hipStream_t stream);
-hipError_t launch_conv_win_fp8(const ConvParams &p, int tile, bool big, hipStream_t stream);
 
 hipError_t launch_conv_buf_bf16(const ConvParams &p, int tile, Mode mode, hipStream_t stream);
 hipError_t launch_conv_buf_fp8(const ConvParams &p, int tile, Mode mode, hipStream_t stream);
@@ -31,16 +25,11 @@ hipError_t launch_conv(const ConvParams &p, int tile, Mode mode, Dtype dt, bool 
                        hipStream_t stream)
 {
     if (is_pointwise_tile(tile))
-        return launch_conv_pw(p, tile - kPointwiseFirst, stream);
+        return launch_conv_pw(p, stream);
     if (is_buffer(kTiles[tile]))
         return dt == DT_FP8 ? launch_conv_buf_fp8(p, tile, mode, stream) : launch_conv_buf_bf16(p, tile, mode, stream);
-    if (is_window(kTiles[tile]))
-        return dt == DT_FP8 ? launch_conv_win_fp8(p, tile, big, stream) : launch_conv_win_bf16(p, tile, big, stream);
-    if (kTiles[tile].stages)
-        return dt == DT_FP8 ? launch_conv_dma_fp8(p, tile, mode, big, cblock, stream)
-                            : launch_conv_dma_bf16(p, tile, mode, big, cblock, stream);
-    return dt == DT_FP8 ? launch_conv_fp8(p, tile, mode, big, cblock, stream)
-                        : launch_conv_bf16(p, tile, mode, big, cblock, stream);
+    return dt == DT_FP8 ? launch_conv_dma_fp8(p, tile, mode, big, cblock, stream)
+                        : launch_conv_dma_bf16(p, tile, mode, big, cblock, stream);
 }
 }  // namespace igc
 
@@ -49,16 +38,37 @@ namespace {
 using namespace igc;
 
 thread_local std::string g_err;
-std::atomic<int> g_force_path{IGC_PATH_AUTO};
-std::atomic<int> g_force_tile{-1};
-std::atomic<int> g_force_group_m{0};
-std::atomic<int> g_force_splits{0};
-std::atomic<int> g_force_grid{0};
-std::atomic<int> g_force_tap_raster{0};
+// Test hooks (conv_debug_force*): per thread, so that forcing a plan in one
+// thread never changes the plans of calls made by another.
+thread_local int g_force_path = IGC_PATH_AUTO;
+thread_local int g_force_tile = -1;
+thread_local int g_force_group_m = 0;
+thread_local int g_force_splits = 0;
+thread_local int g_force_cus = 0;
+thread_local int g_force_tap_raster = 0;
 
 constexpr int64_t kI32Max = 2147483647;
-// Compute units of an MI355X (gfx950): the workgroups of 256x256 tiles that run at once.
-constexpr int64_t kCUs = 256;
+
+// Compute units of the current device: the workgroups of 256x256 tiles (one
+// per CU, their rings fill its LDS) that run at once. Queried once per device;
+// 256, an MI355X's count, where no device answers (host-only planning calls on
+// a machine without one). conv_debug_force_grid stands in another count.
+int64_t device_cus()
+{
+    if (g_force_cus > 0)
+        return g_force_cus;
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0)
+        return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 // Element offsets up to this bound use 32-bit arithmetic in the conv kernel;
 // larger tensors switch to 64-bit offsets (invalid im2col taps may compute an
 // offset up to one tensor beyond the valid range before being masked).
@@ -129,7 +139,7 @@ int check_geometry(const int64_t *xs, const int64_t *ws, const int32_t *st, cons
 
 // Upper bound on the bytes between a tile's x base (the first input plane its
 // first row can read, see tile_x_base) and the end of the last input plane any
-// of its 256 rows, or of the window rows of the tap-shared kernel, can read.
+// of its 256 rows can read.
 int64_t buffer_x_span(const Geometry &g, int esz)
 {
     const int64_t plane = g.H * g.W * g.C * esz;
@@ -196,16 +206,17 @@ int point_tile(int64_t M, int64_t Ncol, bool bf16)
     auto nblocks = [&](int t) {
         return (M + kTiles[t].bm - 1) / kTiles[t].bm * ((Ncol + kTiles[t].bn - 1) / kTiles[t].bn);
     };
-    if (nblocks(21) >= 512)
-        return 21;
-    if (nblocks(21) < 160 && nblocks(24) < 256)
-        return 26;
-    int best = 21;
+    const int64_t cus = device_cus();
+    if (nblocks(TILE_DMA_256) >= 2 * cus)
+        return TILE_DMA_256;
+    if (nblocks(TILE_DMA_256) < cus * 5 / 8 && nblocks(TILE_DMA_128) < cus)
+        return TILE_DMA_64;
+    int best = TILE_DMA_256;
     double best_fill = 0.0;
-    for (int t : {21, 40, 24}) {
-        if (t == 40 && !bf16)
+    for (int t : {TILE_DMA_256, TILE_DMA_256x192, TILE_DMA_128}) {
+        if (t == TILE_DMA_256x192 && !bf16)
             continue;
-        const int64_t slots = kTiles[t].bm * kTiles[t].bn > 128 * 128 ? 256 : 512;  // workgroups resident at once
+        const int64_t slots = kTiles[t].bm * kTiles[t].bn > 128 * 128 ? cus : 2 * cus;  // resident workgroups
         const int64_t n = nblocks(t), rounds = (n + slots - 1) / slots;
         const double fill = (double)n / (double)(rounds * slots);
         if (fill > best_fill + 1e-9) {
@@ -230,7 +241,7 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
     const int esz = dtype == IGC_FP8_E4M3FN ? 1 : 2;
     const int chunk = 16 / esz;
 
-    const int forced = g_force_path.load();
+    const int forced = g_force_path;
     const bool pointwise_ok = is_pointwise(g) && x_layout == IGC_NCDHW && dtype == IGC_BF16;
     int path;
     if (forced == IGC_PATH_AUTO) {
@@ -275,12 +286,10 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
 
     if (path == IGC_PATH_POINTWISE) {
         const int64_t S = g.D * g.H * g.W;
-        const int ft = g_force_tile.load();
+        const int ft = g_force_tile;
         if (ft >= 0 && !is_pointwise_tile(ft))
-            return fail(IGC_ERR_UNSUPPORTED, "the pointwise path runs tiles %d..%d only (forced %d)", kPointwiseFirst,
-                        kPointwiseLast, ft);
-        // measured on the 14 GB 512->48 shape: 512 positions, 32-channel steps, 4 stages (tile 37) is fastest
-        const int pt = ft >= 0 ? ft : kPointwiseFirst + 2;
+            return fail(IGC_ERR_UNSUPPORTED, "the pointwise path runs tile %d only (forced %d)", (int)TILE_PW, ft);
+        const int pt = TILE_PW;
         const int bm = kTiles[pt].bm;
         if (S % 8 != 0)
             return fail(IGC_ERR_UNSUPPORTED, "pointwise path needs D*H*W %% 8 == 0 (16-byte rows), D*H*W = %lld",
@@ -334,51 +343,41 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
     auto nblocks = [&](int t) {
         return ((int64_t)p.M + kTiles[t].bm - 1) / kTiles[t].bm * (((int64_t)p.Ncol + kTiles[t].bn - 1) / kTiles[t].bn);
     };
-    int tile = g_force_tile.load();
+    int tile = g_force_tile;
     if (is_pointwise_tile(tile))
-        return fail(IGC_ERR_UNSUPPORTED, "tile %d is a pointwise path kernel", tile);
+        return fail(IGC_ERR_UNSUPPORTED, "tile %d is the pointwise path's kernel", tile);
+    const int64_t cus = device_cus();
     if (tile < 0 || tile >= kNumTiles) {
         // Measured on MI355X: the 256x256 direct-to-LDS tile with 128-byte steps
         // (16x16 MFMA blocks, bf16 and fp8) is the fastest whenever its grid
-        // reaches ~160 workgroups, the point-output GEMM of the patch embed
-        // (190 workgroups) included; smaller grids take the 128x128 (two
-        // workgroups per CU) or 64x64 (4-stage ring) direct-to-LDS tiles.
-        tile = path == IGC_PATH_POINT ? point_tile(p.M, p.Ncol, esz == 2)
-                                      : (nblocks(21) >= 160 ? 21 : (nblocks(24) >= 256 ? 24 : 26));
+        // reaches ~160 workgroups (5/8 of the CUs), the point-output GEMM of the
+        // patch embed (190 workgroups) included; smaller grids take the 128x128
+        // (two workgroups per CU) or 64x64 (4-stage ring) direct-to-LDS tiles.
+        tile = path == IGC_PATH_POINT
+                   ? point_tile(p.M, p.Ncol, esz == 2)
+                   : (nblocks(TILE_DMA_256) >= cus * 5 / 8 ? TILE_DMA_256
+                                                           : (nblocks(TILE_DMA_128) >= cus ? TILE_DMA_128 : TILE_DMA_64));
         // Where the whole-channel-block im2col order applies and each tile's
         // reach into x (and the whole packed filter) fits a 2^31-byte buffer
-        // range, a buffer-addressed 256x256 tile
-        // replaces the large tile: activations issued two steps ahead (3 x 32 KB
-        // ring), the filter one step ahead (2 x 32 KB). bf16 takes tile 29
-        // (loads spread over the first half of each step's MFMA rows); fp8 with
-        // long reductions the ping-pong wave groups of tile 33 (1-2 % faster on
-        // c4, 10 % slower on bf16).
+        // range, a buffer-addressed 256x256 tile replaces the large tile:
+        // activations issued two steps ahead (3 x 32 KB ring), the filter one
+        // step ahead (2 x 32 KB).
         const bool buffer_ok = path != IGC_PATH_POINT && g.C % (128 / esz) == 0 &&
                                buffer_x_span(g, esz) < 0x7ffffff0 && g.K * ldw * esz < (int64_t(1) << 31);
-        // fp8 with a long reduction takes the ping-pong wave groups of tile 33; with a short one (a 3x1x1
-        // filter: 48 steps on c4t) tile 33 measured 4 % slower than tile 29 (2.43 against 2.33 ms).
+        // fp8 with a long reduction takes the ping-pong wave groups (1-2 % faster than the lockstep tile on
+        // c4, 10 % slower on bf16 c3); with a short one (a 3x1x1 filter: 48 steps on c4t) they measured 4 %
+        // slower than the lockstep TILE_BUF (2.43 against 2.33 ms).
         const int64_t fp8_steps = g.T * g.R * g.S * (g.C / 128);
-        // bf16 on the generic path takes tile 31 (tile 29 with A fragments read two MFMA rows ahead and the
-        // next k-slice's B fragments read early): in alternating runs c3 34.1 against 34.5 ms and c3s 4.27
-        // against 4.41 ms; on the temporal path tile 29 stays ahead (c5 17.2 against 17.7 ms).
-        if (tile == 21 && buffer_ok)
+        // bf16 on the generic path takes TILE_BUF_AHEAD (A fragments read two MFMA rows ahead, the next
+        // k-slice's B fragments read early): in alternating runs c3 34.1 against 34.5 ms and c3s 4.27 against
+        // 4.41 ms; on the temporal path TILE_BUF stays ahead (c5 17.2 against 17.7 ms).
+        if (tile == TILE_DMA_256 && buffer_ok)
             tile = (esz == 1 && g.T * g.R * g.S <= 32 && fp8_steps >= 128)
-                       ? 33
-                       : (esz == 2 && path == IGC_PATH_GENERIC ? 31 : 29);
-        // The persistent form of tile 29 (41) is an option only: since tile 29 stages its epilogue through
-        // LDS (which tile 41 cannot, its rings holding the next tile's first steps), tile 29 is faster on
-        // c4t too (2.23-2.33 against 2.35-2.36 ms).
+                       ? TILE_BUF_PINGPONG
+                       : (esz == 2 && path == IGC_PATH_GENERIC ? TILE_BUF_AHEAD : TILE_BUF);
     } else {
-        if (kTiles[tile].stages && kTiles[tile].mf == 16 && esz == 1 && kTiles[tile].kb == 64)
-            return fail(IGC_ERR_UNSUPPORTED, "tile %d: fp8 with 64-byte steps needs 32x32 MFMA blocks", tile);
-        if (esz == 2 && (tile == 12 || tile == 13))
-            return fail(IGC_ERR_UNSUPPORTED, "tile %d is an fp8-only tile", tile);
-        if (esz == 1 && (tile == 20 || tile == 30 || tile == 40))
+        if (esz == 1 && tile == TILE_DMA_256x192)
             return fail(IGC_ERR_UNSUPPORTED, "tile %d is a bf16-only tile", tile);
-        if (is_window(kTiles[tile]) && path != IGC_PATH_GENERIC)
-            return fail(IGC_ERR_UNSUPPORTED, "tile %d (input window) runs the generic im2col path only", tile);
-        if (is_window(kTiles[tile]) && esz == 1 && kTiles[tile].mf == 16)
-            return fail(IGC_ERR_UNSUPPORTED, "tile %d: fp8 with 64-byte steps needs 32x32 MFMA blocks", tile);
         if (is_buffer(kTiles[tile])) {
             if (path == IGC_PATH_POINT)
                 return fail(IGC_ERR_UNSUPPORTED, "tile %d (buffer-addressed) runs the im2col paths only", tile);
@@ -387,21 +386,9 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
             if (buffer_x_span(g, esz) >= 0x7ffffff0 || g.K * ldw * esz >= (int64_t(1) << 31))
                 return fail(IGC_ERR_UNSUPPORTED,
                             "tile %d needs each tile's reach into x and the packed filter below 2^31 bytes", tile);
-            if (tile == 41 && g.T * g.R * g.S * (g.C / (128 / esz)) < 3)
-                return fail(IGC_ERR_UNSUPPORTED, "tile %d (persistent) needs at least 3 reduction steps", tile);
-            if (tile == 33 && g.T * g.R * g.S > 32)
+            if (tile == TILE_BUF_PINGPONG && g.T * g.R * g.S > 32)
                 return fail(IGC_ERR_UNSUPPORTED, "tile %d keeps a 32-bit tap mask per row: at most 32 filter taps",
                             tile);
-            if (tile == 34) {
-                const int64_t cols = (g.Wo - 1) * g.sw + (g.S - 1) * g.dw + 1;
-                const int64_t rows = (255 / g.Wo + 2) * cols;
-                if (path != IGC_PATH_GENERIC || g.S < 2 || g.T * g.R > 16 || rows > 352)
-                    return fail(IGC_ERR_UNSUPPORTED,
-                                "tile %d needs the generic path, S >= 2, T*R <= 16 and a window of at most 352 "
-                                "pixels (here %lld)", tile, (long long)rows);
-                p.win_cols = (int)cols;
-                p.win_rows = (int)rows;
-            }
         }
     }
     pl.tile = tile;
@@ -414,53 +401,26 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         pl.cblock = (g.C % tke) == 0;
         p.nk = pl.cblock ? (int)(g.T * g.R * g.S * (g.C / tke)) : (int)(ldw / tke);
     }
-    p.pairs = (ts.stages > 0 && ts.kb == 64 && pl.cblock && (g.C % (2 * tke)) == 0) ? 2 : 1;
-    int64_t tm = ((int64_t)p.M + ts.bm - 1) / ts.bm;
+    const int64_t tm = ((int64_t)p.M + ts.bm - 1) / ts.bm;
     const int64_t tn = ((int64_t)p.Ncol + ts.bn - 1) / ts.bn;
-    if (is_window(ts)) {
-        // Tiles stay inside one output plane; the input box of a tile spans
-        // the input rows of its output rows plus the filter's reach.
-        if (g.C % tke != 0)
-            return fail(IGC_ERR_UNSUPPORTED, "input-window tile needs C %% %d == 0", tke);
-        const int64_t P2 = g.Ho * g.Wo;
-        const int64_t tpp = (P2 + ts.bm - 1) / ts.bm;
-        int64_t span = 1;
-        for (int64_t j = 0; j < tpp; ++j) {
-            const int64_t qa = j * ts.bm, qb = std::min(qa + ts.bm, P2) - 1;
-            span = std::max(span, qb / g.Wo - qa / g.Wo + 1);
-        }
-        const int64_t wh = (span - 1) * g.sh + (g.R - 1) * g.dh + 1;
-        const int64_t ww = (g.Wo - 1) * g.sw + (g.S - 1) * g.dw + 1;
-        const int64_t bytes = g.T * wh * ww * 64;
-        const int64_t nwi = (bytes + 8 * 1024 - 1) / (8 * 1024);  // 8 waves x 1 KB per instruction
-        if (nwi * 8 * 1024 > 96 * 1024)
-            return fail(IGC_ERR_UNSUPPORTED, "input box of %lld bytes exceeds the 96 KB window", (long long)bytes);
-        p.tpp = (int)tpp;
-        p.win_h = (int)wh;
-        p.win_w = (int)ww;
-        p.win_nwi = (int)nwi;
-        tm = g.N * g.Do * tpp;
-        pl.cblock = true;
-        p.nk = (int)(g.T * g.R * g.S * (g.C / tke));
-    }
     if (tm * tn > kI32Max)
         return fail(IGC_ERR_UNSUPPORTED, "grid of %lld tiles too large", (long long)(tm * tn));
     p.tiles_m = (int)tm;
     p.tiles_n = (int)tn;
-    // Workgroups resident on one XCD (32 CUs): one 256x256 or two smaller tiles per CU.
-    const int resident = 32 * (ts.bm * ts.bn >= 256 * 256 ? 1 : 2);
+    // Workgroups resident on one XCD (an eighth of the CUs): one 256x256 or two smaller tiles per CU.
+    const int resident = (int)(cus / 8) * (ts.bm * ts.bn >= 256 * 256 ? 1 : 2);
     p.group_m = (int)std::max<int64_t>(1, resident / tn);
     if (path == IGC_PATH_POINT)  // few tile rows: all of them per column, so an image block is fetched once per XCD
         p.group_m = (int)std::max<int64_t>(p.group_m, std::min<int64_t>(tm, 8));
-    if (g_force_group_m.load() > 0)
-        p.group_m = g_force_group_m.load();
+    if (g_force_group_m > 0)
+        p.group_m = g_force_group_m;
     // Temporal filters on the buffer tiles: a tile's taps read activation windows H*W rows apart, ~56 tiles
     // on c5, which a raster of consecutive tiles re-fetches from beyond L2 once per tap. Raster groups of
     // tiles one tap apart share those windows instead (tile_coords).
     p.tap_stride = 0;
     if (path == IGC_PATH_TEMPORAL && is_buffer(ts) && g.T > 1) {
         const int64_t stride = (g.H * g.W * g.dd + ts.bm / 2) / ts.bm;
-        if (stride >= 2 && tm >= (int64_t)p.group_m * stride && g_force_tap_raster.load() >= 0)
+        if (stride >= 2 && tm >= (int64_t)p.group_m * stride && g_force_tap_raster >= 0)
             p.tap_stride = (int)stride;
     }
     p.ksplit = p.nk;
@@ -470,27 +430,23 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
 // Split reduction (split-K). FlyDSL PR #860 splits the reduction only when the
 // grid of output tiles under-fills the GPU (its split-K selection rule: the
 // under-fill test decides, a long reduction alone does not). Here: the
-// direct-to-LDS kernels, grids below 128 tiles (half the CUs), and at least 5
-// reduction steps per split (about the ring depth: shorter splits are mostly
-// pipeline fill); enough splits to fill the GPU once (256 workgroups of 256x256,
-// 512 of the smaller tiles, which pair on a CU), at most 32, and no more than
-// the workspace holds (splits * elements of y fp32 values).
+// global-address direct-to-LDS kernels, grids below half the CUs, and at least
+// 5 reduction steps per split (about the ring depth: shorter splits are mostly
+// pipeline fill); enough splits to fill the GPU once (one workgroup of 256x256
+// per CU, two of the smaller tiles, which pair on a CU), at most 32, and no
+// more than the workspace holds (splits * elements of y fp32 values).
 // Measured on MI355X (bf16, 64x64 tiles): the 1024x64x1728 GEMM of a
 // 64-channel 3x3x3 conv on 4x16x16 goes from 19.0 to 11.7 us, a 512-channel
 // 3x3 conv on 7x7 from 42 to 15 us. Returns the split count (1 = none) with
 // p.ksplit set, or a negative status for a forced split the tile cannot run.
-bool splits_tile(int tile)
-{
-    const TileShape &t = kTiles[tile];
-    return t.stages > 0 && !is_buffer(t) && !is_pointwise_tile(tile);
-}
+bool splits_tile(int tile) { return !is_buffer(kTiles[tile]) && !is_pointwise_tile(tile); }
 
 int plan_splits(Plan &pl, size_t ws_bytes)
 {
     ConvParams &p = pl.p;
     const int64_t ynum = (int64_t)p.M * p.Ncol;
     const int64_t cap = std::min<int64_t>(ws_bytes / 4 / ynum, 64);
-    const int forced = g_force_splits.load();
+    const int forced = g_force_splits;
     int splits = 1;
     if (forced > 0) {
         if (forced > 1 && !splits_tile(pl.tile))
@@ -500,8 +456,9 @@ int plan_splits(Plan &pl, size_t ws_bytes)
     } else if (splits_tile(pl.tile)) {
         const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
         const TileShape &t = kTiles[pl.tile];
-        const int64_t slots = t.bm * t.bn >= 256 * 256 ? 256 : 512;  // workgroups the GPU holds at once
-        if (grid < 128)
+        const int64_t cus = device_cus();
+        const int64_t slots = t.bm * t.bn >= 256 * 256 ? cus : 2 * cus;  // workgroups the GPU holds at once
+        if (2 * grid < cus)
             splits = (int)std::min<int64_t>(std::min<int64_t>(std::min<int64_t>(slots / grid, p.nk / 5), 32), cap);
     }
     splits = std::max(splits, 1);
@@ -518,10 +475,10 @@ int plan_splits(Plan &pl, size_t ws_bytes)
     // is for. Needs the workspace; conv_debug_force_splits(1) turns it off.
     p.tail_first = 0;
     p.tail_splits = 0;
-    if (p.splits == 1 && forced != 1 && is_buffer(kTiles[pl.tile]) && pl.tile != 34 && pl.tile != 41) {
+    if (p.splits == 1 && forced != 1 && is_buffer(kTiles[pl.tile])) {
         const TileShape &t = kTiles[pl.tile];
         const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
-        const int64_t slots = g_force_grid.load() > 0 ? g_force_grid.load() : kCUs;
+        const int64_t slots = device_cus();
         const int64_t full = ntiles / slots * slots, r = ntiles - full;
         const int64_t S = std::min<int64_t>(std::min<int64_t>(r > 0 ? slots / r : 0, 8), p.nk / 8);
         const int64_t need = r * S * t.bm * t.bn * 4;
@@ -558,30 +515,28 @@ int plan_point_gemm(int64_t M, int64_t Ncol, int64_t Rk, int64_t ldw, int64_t ld
     p.ldw = (int)ldw;
     p.P = 1;
     p.Do = p.Ho = p.Wo = 1;
-    int tile = g_force_tile.load();
-    if (tile < 0 || tile >= kNumTiles || is_buffer(kTiles[tile]) || is_window(kTiles[tile]) ||
-        is_pointwise_tile(tile) || tile == 12 || tile == 13) {
+    int tile = g_force_tile;
+    if (tile < 0 || tile >= kNumTiles || is_buffer(kTiles[tile]) || is_pointwise_tile(tile)) {
         tile = point_tile(M, Ncol, true);
         // A long reduction that will be split (backward weights over the batch): 128x128 tiles, then
         // enough splits to fill the GPU; measured on the 9500-image patch embed (588 x 1280 over 9536):
         // 128x128 with 8 splits 51.5 us, 64x64 with 4-10 splits 61-64 us.
-        if (long_split && tile == 26 && Rk >= 32 * 64)
-            tile = 24;
+        if (long_split && tile == TILE_DMA_64 && Rk >= 32 * 64)
+            tile = TILE_DMA_128;
     }
     const TileShape ts = kTiles[tile];
     const int tke = step_bytes(ts) / 2;
     p.nk = (int)((Rk + tke - 1) / tke);
     p.ksplit = p.nk;
-    p.pairs = 1;
     const int64_t tm = (M + ts.bm - 1) / ts.bm, tn = (Ncol + ts.bn - 1) / ts.bn;
     if (tm * tn > kI32Max)
         return fail(IGC_ERR_UNSUPPORTED, "grid of %lld tiles too large", (long long)(tm * tn));
     p.tiles_m = (int)tm;
     p.tiles_n = (int)tn;
-    const int resident = 32 * (ts.bm * ts.bn >= 256 * 256 ? 1 : 2);
+    const int64_t resident = device_cus() / 8 * (ts.bm * ts.bn >= 256 * 256 ? 1 : 2);
     p.group_m = (int)std::max<int64_t>({(int64_t)1, resident / tn, std::min<int64_t>(tm, 8)});
-    if (g_force_group_m.load() > 0)
-        p.group_m = g_force_group_m.load();
+    if (g_force_group_m > 0)
+        p.group_m = g_force_group_m;
     pl.path = IGC_PATH_POINT;
     pl.tile = tile;
     pl.big = Ncol * ldo > kSmallTensor;  // 64-bit output offsets
@@ -642,23 +597,6 @@ const char *path_name(int path)
 
 }  // namespace
 
-namespace igc {
-int persistent_grid(const ConvParams &p)
-{
-    static const int ncu = [] {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-            n = 256;
-        return n;
-    }();
-    int64_t g = std::min<int64_t>(ncu, (int64_t)p.tiles_m * p.tiles_n);
-    const int forced = g_force_grid.load();
-    if (forced > 0)
-        g = std::min<int64_t>(g, forced);
-    return (int)std::max<int64_t>(g, 1);
-}
-}  // namespace igc
 
 extern "C" {
 
@@ -857,14 +795,12 @@ int conv_plan_ws(const int64_t xshape[5], const int64_t wshape[5], const int32_t
     if (buf && len) {
         const TileShape ts = kTiles[pl.tile];
         snprintf(buf, len,
-                 "path=%s tile=%dx%d waves=%d mfma=%dx%d stages=%d bstages=%d kstep=%d order=%s%s big=%d grid=%d "
-                 "group_m=%d nk=%d loads=%s schedule=%s areuse=%s xspan=%lld splits=%d ksplit=%d tail=%d/%d tap=%d",
-                 path_name(pl.path), ts.bm, ts.bn, ts.wm * ts.wn, ts.mf, ts.mf, ts.stages ? std::abs(ts.stages) : 2,
-                 is_buffer(ts) ? ts.sb : (ts.stages ? std::abs(ts.stages) : 2), step_bytes(ts) / (dtype == IGC_FP8_E4M3FN ? 1 : 2),
-                 is_window(ts) ? "window" : (pl.cblock ? "cblock" : "linear"), pl.p.pairs == 2 ? "-paired" : "",
-                 pl.big ? 1 : 0, pl.p.tiles_m * pl.p.tiles_n, pl.p.group_m, pl.p.nk,
-                 is_buffer(ts) ? "buffer-lds" : (ts.stages > 0 ? "global-lds" : (is_window(ts) ? "window-lds" : "registers")),
-                 pl.tile == 33 || pl.tile == 34 ? "pingpong" : (pl.tile == 41 ? "persistent" : "lockstep"), pl.tile == 34 ? "taps" : "none",
+                 "path=%s tile_id=%d tile=%dx%d waves=%d mfma=%dx%d stages=%d bstages=%d kstep=%d order=%s big=%d "
+                 "grid=%d group_m=%d nk=%d loads=%s schedule=%s xspan=%lld splits=%d ksplit=%d tail=%d/%d tap=%d",
+                 path_name(pl.path), pl.tile, ts.bm, ts.bn, ts.wm * ts.wn, ts.mf, ts.mf, ts.stages,
+                 is_buffer(ts) ? ts.sb : ts.stages, step_bytes(ts) / (dtype == IGC_FP8_E4M3FN ? 1 : 2),
+                 pl.cblock ? "cblock" : "linear", pl.big ? 1 : 0, pl.p.tiles_m * pl.p.tiles_n, pl.p.group_m, pl.p.nk,
+                 is_buffer(ts) ? "buffer-lds" : "global-lds", pl.tile == TILE_BUF_PINGPONG ? "pingpong" : "lockstep",
                  pl.path == IGC_PATH_POINT ? 0LL : (long long)pl.xspan, pl.p.splits, pl.p.ksplit,
                  pl.p.tail_splits > 1 ? pl.p.tiles_m * pl.p.tiles_n - pl.p.tail_first : 0,
                  pl.p.tail_splits > 1 ? pl.p.tail_splits : 1, pl.p.tap_stride);
@@ -886,9 +822,9 @@ int conv_debug_force(int path, int tile, int group_m)
         return fail(IGC_ERR_INVALID, "conv_debug_force: tile %d not in [-1, %d)", tile, kNumTiles);
     if (group_m < 0)
         return fail(IGC_ERR_INVALID, "conv_debug_force: group_m %d < 0", group_m);
-    g_force_path.store(path);
-    g_force_tile.store(tile);
-    g_force_group_m.store(group_m);
+    g_force_path = path;
+    g_force_tile = tile;
+    g_force_group_m = group_m;
     return ok();
 }
 
@@ -1028,11 +964,11 @@ int conv_bwd_weight(const void *x, const void *dy, void *dw, const int64_t xshap
     return ok();
 }
 
-int conv_debug_force_grid(int workgroups)
+int conv_debug_force_grid(int cus)
 {
-    if (workgroups < 0)
-        return fail(IGC_ERR_INVALID, "conv_debug_force_grid: workgroups %d < 0", workgroups);
-    g_force_grid.store(workgroups);
+    if (cus < 0)
+        return fail(IGC_ERR_INVALID, "conv_debug_force_grid: compute units %d < 0", cus);
+    g_force_cus = cus;
     return ok();
 }
 
@@ -1040,7 +976,7 @@ int conv_debug_force_tap_raster(int mode)
 {
     if (mode != -1 && mode != 0)
         return fail(IGC_ERR_INVALID, "conv_debug_force_tap_raster: mode %d is neither -1 (off) nor 0 (automatic)", mode);
-    g_force_tap_raster.store(mode);
+    g_force_tap_raster = mode;
     return ok();
 }
 
@@ -1048,7 +984,7 @@ int conv_debug_force_splits(int splits)
 {
     if (splits < 0)
         return fail(IGC_ERR_INVALID, "conv_debug_force_splits: splits %d < 0", splits);
-    g_force_splits.store(splits);
+    g_force_splits = splits;
     return ok();
 }
 

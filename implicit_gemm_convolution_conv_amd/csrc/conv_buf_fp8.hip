@@ -1,13 +1,11 @@
 // fp8-e4m3 instantiations of the buffer-addressed direct-to-LDS implicit-GEMM conv kernels.
-#include "conv_igemm_ppw.h"
+#include "conv_igemm_pp.h"
 
 namespace igc {
 hipError_t launch_conv_buf_fp8(const ConvParams &p, int tile, Mode mode, hipStream_t stream)
 {
-    if (tile == 33)
+    if (tile == TILE_BUF_PINGPONG)
         return launch_conv_pp<DT_FP8>(p, mode, stream);
-    if (tile == 34)
-        return launch_conv_ppw<DT_FP8>(p, stream);
     return launch_conv_buf_dt<DT_FP8>(p, tile, mode, stream);
 }
 }  // namespace igc

@@ -69,20 +69,18 @@ __device__ inline void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, char *lds, unsi
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
 }
 
-// Reduction position in channel-block order: channel block cb (pairs * TKE
-// channels) outer, then tap (t, r, s), then the `pairs` TKE-wide halves of
-// the block. Every field is uniform across the workgroup.
+// Reduction position in channel-block order: channel block cb (TKE channels,
+// one 128-byte line per row) outer, then tap (t, r, s). Every field is
+// uniform across the workgroup.
 template <int TKE>
 struct KPos {
-    int half = 0, s = 0, r = 0, t = 0, cb = 0;
+    int s = 0, r = 0, t = 0, cb = 0;
     int tap = 0;  // (t * R + r) * S + s
 
     __device__ void advance(const ConvParams &p)
     {
-        const bool hw = ++half == p.pairs;
-        half = hw ? 0 : half;
-        tap += hw;
-        s += hw;
+        ++tap;
+        ++s;
         const bool sw = s == p.S;
         s = sw ? 0 : s;
         r += sw;
@@ -92,26 +90,24 @@ struct KPos {
         const bool tw = t == p.T;
         t = tw ? 0 : t;
         tap = tw ? 0 : tap;
-        cb += tw ? p.pairs * TKE : 0;
+        cb += tw ? TKE : 0;
     }
     // Position of reduction step `step` (advance() applied `step` times from zero).
     __device__ void seek(const ConvParams &p, int step)
     {
-        const int q = step / p.pairs;
-        half = step - q * p.pairs;
         const int taps = p.T * p.R * p.S;
-        const int cbi = q / taps;
-        tap = q - cbi * taps;
+        const int cbi = step / taps;
+        tap = step - cbi * taps;
         s = tap % p.S;
         r = (tap / p.S) % p.R;
         t = tap / (p.S * p.R);
-        cb = cbi * p.pairs * TKE;
+        cb = cbi * TKE;
     }
     // Bytes from an input row's origin to this tap and channel block.
     template <int MODE, int ESZ>
     __device__ unsigned a_shift(const ConvParams &p) const
     {
-        const int c = cb + half * TKE;
+        const int c = cb;
         if constexpr (MODE == MODE_TEMPORAL)
             return (unsigned)((t * p.dd) * (p.H * p.W) * p.C + c) * ESZ;
         else
@@ -121,7 +117,7 @@ struct KPos {
     template <int ESZ>
     __device__ unsigned b_shift(const ConvParams &p) const
     {
-        return (unsigned)((((t * p.R + r) * p.S + s) * p.C + cb + half * TKE) * ESZ);
+        return (unsigned)((((t * p.R + r) * p.S + s) * p.C + cb) * ESZ);
     }
 };
 
@@ -306,7 +302,7 @@ __device__ __attribute__((always_inline)) inline void store_tile_ncdhw(const typ
 
 template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, int SA, int SB, int KB, int SPREAD, int PF = 1,
           bool BPF = false>
-__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN>())))
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void conv_igemm_buf_kernel(ConvParams p)
 {
     constexpr int NW = WM * WN;                // waves
@@ -325,7 +321,7 @@ void conv_igemm_buf_kernel(ConvParams p)
     constexpr int SUB = CPR / (GROUPS * CPL);  // MFMA k-slices per step
     constexpr int ROWS = SUB * FM;             // MFMA rows (FN instructions each) per step
     static_assert(MODE == MODE_GENERIC || MODE == MODE_TEMPORAL, "im2col modes only");
-    static_assert(KB == 64 || KB == 128, "64- or 128-byte steps");
+    static_assert(KB == 128, "128-byte steps");
     static_assert(AIT >= 1 && BIT >= 1 && BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "loader split");
     static_assert(SUB >= 1, "step too short for this MFMA");
     static_assert(SA >= 2 && SB >= 2, "ring depths");
@@ -559,236 +555,6 @@ void conv_igemm_buf_kernel(ConvParams p)
     store_tile_ncdhw<MF, FM, FN, DT>(acc, p, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
-// Persistent form of conv_igemm_buf_kernel: workgroup b runs the tiles b,
-// b + G, b + 2G, ... (G = gridDim.x, about one workgroup per CU). Within a
-// tile the steps run exactly as in conv_igemm_buf_kernel. In a tile's last
-// SMAX-1 steps, where that kernel issues nothing more, this one issues the
-// next tile's first steps into the slots that free up, so the next tile's
-// loads are in flight while this tile's last steps compute and while its
-// epilogue stores go out; a non-persistent grid instead starts each tile
-// with an empty pipeline after the previous workgroup's stores. After an
-// epilogue the workgroup waits for every outstanding memory operation,
-// stores included, before its next step. Tile order, decode, padding and
-// arithmetic are those of conv_igemm_buf_kernel: the two give identical bits.
-// Needs nk >= SMAX (the plan checks it), so a transition only reaches into
-// the next tile.
-template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, int SA, int SB, int KB, int SPREAD>
-__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN>())))
-void conv_igemm_bufp_kernel(ConvParams p)
-{
-    constexpr int NW = WM * WN;
-    constexpr int ESZ = DT == DT_FP8 ? 1 : 2;
-    constexpr int TKE = KB / ESZ;
-    constexpr int RPI = 1024 / KB;
-    constexpr int CPR = KB / 16;
-    constexpr int AIT = BM / (RPI * NW);
-    constexpr int BIT = BN / (RPI * NW);
-    constexpr int LPS = AIT + BIT;
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int FM = WTM / MF, FN = WTN / MF;
-    constexpr int ASTAGE = BM * KB, BSTAGE = BN * KB;
-    constexpr int GROUPS = 64 / MF;
-    constexpr int CPL = DT == DT_BF16 ? 1 : 2;
-    constexpr int SUB = CPR / (GROUPS * CPL);
-    constexpr int ROWS = SUB * FM;
-    static_assert(MODE == MODE_GENERIC || MODE == MODE_TEMPORAL, "im2col modes only");
-    static_assert(KB == 128, "128-byte steps");
-    static_assert(AIT >= 1 && BIT >= 1 && BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "loader split");
-    static_assert(SUB >= 1, "step too short for this MFMA");
-    static_assert(SA >= 2 && SB >= 2, "ring depths");
-    static_assert(SA * ASTAGE + SB * BSTAGE <= 160 * 1024, "LDS budget");
-    static_assert(SPREAD >= 1 && SPREAD <= ROWS, "loads spread within one step");
-
-    __shared__ __attribute__((aligned(1024))) char smem[SA * ASTAGE + SB * BSTAGE];
-    char *const as = smem;
-    char *const bs = smem + SA * ASTAGE;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave % WM, wn = wave / WM;
-    const int lr = lane / CPR;
-    const int jc = (lane & 7) ^ (lane >> 3);
-
-    const int ntiles = p.tiles_m * p.tiles_n;
-    const int G = (int)gridDim.x;  // the launch keeps G <= ntiles
-    const int nk = p.nk;
-
-    const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(p.w, p.wbytes);
-    ImRows<AIT, MODE, ESZ> arows;
-    FilterRows<BIT, ESZ> brows;
-    __amdgpu_buffer_rsrc_t xr;
-    KPos<TKE> ka, kb;  // next A and B steps to issue
-    auto a_tile = [&](int bid) __attribute__((always_inline)) {
-        int tm, tn;
-        tile_coords(p, bid, tm, tn);
-        const int64_t xbase = tile_x_base<ESZ>(p, tm * BM);
-        xr = tile_x_rsrc(p, xbase);
-        arows.init(p, tm * BM + RPI * wave + lr, RPI * NW, jc, xbase);
-        ka = KPos<TKE>{};
-    };
-    auto b_tile = [&](int bid) __attribute__((always_inline)) {
-        int tm, tn;
-        tile_coords(p, bid, tm, tn);
-        brows.init(p, tn * BN + RPI * wave + lr, RPI * NW, jc);
-        kb = KPos<TKE>{};
-    };
-    auto issue = [&](int j, int st, const KPos<TKE> &k, unsigned ash, unsigned bsh) __attribute__((always_inline)) {
-        if (j < AIT)
-            buffer_to_lds16(xr, as + st * ASTAGE + RPI * (wave + j * NW) * KB, arows.at(p, j, k, ash));
-        else
-            buffer_to_lds16(wr, bs + st * BSTAGE + RPI * (wave + (j - AIT) * NW) * KB, brows.off[j - AIT] + bsh);
-    };
-
-    using AccT = typename AccType<MF>::type;
-    using Frag = FragT<DT>;
-    AccT acc[FM][FN];
-    const int lrow = lane & (MF - 1), lgrp = lane / MF, lsw = lane & 7;
-    auto frag = [&](const char *rowp, int h) -> Frag { return lds_frag<DT, MF>(rowp, h, lgrp, lsw); };
-    auto compute = [&](int sa, int sb, auto &&hook) __attribute__((always_inline)) {
-        const char *aw = as + sa * ASTAGE + (wm * WTM + lrow) * KB;
-        const char *bw = bs + sb * BSTAGE + (wn * WTN + lrow) * KB;
-        Frag bf[FN];
-#pragma unroll
-        for (int b = 0; b < FN; ++b)
-            bf[b] = frag(bw + b * MF * KB, 0);
-#pragma unroll
-        for (int h = 0; h < SUB; ++h) {
-            if (h > 0) {
-#pragma unroll
-                for (int b = 0; b < FN; ++b)
-                    bf[b] = frag(bw + b * MF * KB, h);
-            }
-            Frag af[2];
-            af[0] = frag(aw, h);
-#pragma unroll
-            for (int a = 0; a < FM; ++a) {
-                if (a + 1 < FM)
-                    af[(a + 1) & 1] = frag(aw + (a + 1) * MF * KB, h);
-#pragma unroll
-                for (int b = 0; b < FN; ++b)
-                    mfma_acc<DT, MF>(af[a & 1], bf[b], acc[a][b]);
-                hook(h * FM + a);
-            }
-        }
-    };
-
-    constexpr bool A_FIRST = SA <= SB;
-    constexpr int SMIN = SA < SB ? SA : SB, SMAX = SA < SB ? SB : SA;
-    constexpr int FIRST_IT = A_FIRST ? AIT : BIT;
-    constexpr int AHEAD = (SA == SB ? 0 : LPS - FIRST_IT) + (SMIN - 2) * LPS;
-    static_assert(AHEAD < 64, "vmcnt range");
-    auto issue_j = [&](int j, int sta, int stb, unsigned ash, unsigned bsh) __attribute__((always_inline)) {
-        const bool is_a = A_FIRST ? j < AIT : j >= BIT;
-        const int row = A_FIRST ? (is_a ? j : j - AIT) : (is_a ? j - BIT : j);
-        if (is_a)
-            issue(row, sta, ka, ash, 0);
-        else
-            issue(AIT + row, stb, kb, 0, bsh);
-    };
-    auto issue_a_step = [&](int st) __attribute__((always_inline)) {
-        const unsigned sh = ka.template a_shift<MODE, ESZ>(p);
-#pragma unroll
-        for (int j = 0; j < AIT; ++j)
-            issue(j, st, ka, sh, 0);
-        ka.advance(p);
-    };
-    auto issue_b_step = [&](int st) __attribute__((always_inline)) {
-        const unsigned sh = kb.template b_shift<ESZ>(p);
-#pragma unroll
-        for (int j = AIT; j < LPS; ++j)
-            issue(j, st, kb, 0, sh);
-        kb.advance(p);
-    };
-    // Issue A step ja and B step jb of the current tile (counted from its
-    // first step); steps past its end belong to the next tile, if there is one.
-    auto issue_parts = [&](int ja, int jb, int sta, int stb, bool next) __attribute__((always_inline)) {
-        auto a_part = [&]() __attribute__((always_inline)) {
-            if (ja >= 0 && (ja < nk || next))
-                issue_a_step(sta);
-        };
-        auto b_part = [&]() __attribute__((always_inline)) {
-            if (jb >= 0 && (jb < nk || next))
-                issue_b_step(stb);
-        };
-        if (A_FIRST) {
-            a_part();
-            b_part();
-        } else {
-            b_part();
-            a_part();
-        }
-    };
-
-    int bid = (int)blockIdx.x;
-    a_tile(bid);
-    b_tile(bid);
-#pragma unroll
-    for (int j = -(SMAX - 1); j < 0; ++j) {
-        const int ja = j + SA - 1, jb = j + SB - 1;
-        issue_parts(ja, jb, ja >= 0 ? ja % SA : 0, jb >= 0 ? jb % SB : 0, false);
-    }
-    int sa = 0, sb = 0;            // slots of the step to compute
-    int ia = SA - 1, ib = SB - 1;  // slots the step's issues go to
-    for (;;) {
-        const bool next = bid + G < ntiles;
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b)
-                acc[a][b] = AccT{};
-        int ks = 0;
-        // Steady state: every step issues both parts of this tile.
-        for (; ks < nk - SMAX + 1; ++ks) {
-            wait_vmcnt<AHEAD>();
-            asm volatile("s_barrier" ::: "memory");
-            const unsigned ash = ka.template a_shift<MODE, ESZ>(p), bsh = kb.template b_shift<ESZ>(p);
-            const int sta = ia, stb = ib;
-            compute(sa, sb, [&](int row) __attribute__((always_inline)) {
-#pragma unroll
-                for (int j = 0; j < LPS; ++j)
-                    if (j * SPREAD / LPS == row)
-                        issue_j(j, sta, stb, ash, bsh);
-            });
-            ka.advance(p);
-            kb.advance(p);
-            sa = sa + 1 == SA ? 0 : sa + 1;
-            sb = sb + 1 == SB ? 0 : sb + 1;
-            ia = ia + 1 == SA ? 0 : ia + 1;
-            ib = ib + 1 == SB ? 0 : ib + 1;
-        }
-        // Transition: this tile's last SMAX-1 steps; each stream moves to the
-        // next tile when it has issued this tile's last step.
-        for (; ks < nk; ++ks) {
-            wait_vmcnt<0>();
-            asm volatile("s_barrier" ::: "memory");
-            if (next && ks + SA - 1 == nk)
-                a_tile(bid + G);
-            if (next && ks + SB - 1 == nk)
-                b_tile(bid + G);
-            issue_parts(ks + SA - 1, ks + SB - 1, ia, ib, next);
-            compute(sa, sb, [](int) {});
-            sa = sa + 1 == SA ? 0 : sa + 1;
-            sb = sb + 1 == SB ? 0 : sb + 1;
-            ia = ia + 1 == SA ? 0 : ia + 1;
-            ib = ib + 1 == SB ? 0 : ib + 1;
-        }
-        {
-            int tm, tn;
-            tile_coords(p, bid, tm, tn);
-            store_tile_ncdhw<MF, FM, FN, DT>(acc, p, tm * BM + wm * WTM, tn * BN + wn * WTN, lane);
-        }
-        if (!next)
-            break;
-        bid += G;
-        wait_vmcnt<0>();
-    }
-}
-
-// Workgroups of a persistent launch: one per CU (a 256x256 buffer tile fills
-// a CU's LDS), at most one per tile, or the test hook's cap.
-int persistent_grid(const ConvParams &p);
-
 // Launch helper for one dtype: the buffer-addressed tiles of kTiles (sb > 0).
 template <int DT>
 hipError_t launch_conv_buf_dt(const ConvParams &p, int tile, Mode mode, hipStream_t stream)
@@ -808,28 +574,9 @@ hipError_t launch_conv_buf_dt(const ConvParams &p, int tile, Mode mode, hipStrea
         return hipGetLastError();                                                                          \
     } while (0)
     switch (tile) {
-    case 27: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 2, 128, 8);
-    case 28: IGC_BLAUNCH(256, 256, 2, 4, 16, 2, 3, 128, 8);
-    case 29: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 8);
-    case 31: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 8, 2, true);
-    case 41: {
-        const dim3 pgrid((unsigned)persistent_grid(p));
-        if (mode == MODE_TEMPORAL)
-            hipLaunchKernelGGL((conv_igemm_bufp_kernel<256, 256, 2, 4, 16, DT, MODE_TEMPORAL, 3, 2, 128, 8>), pgrid,
-                               dim3(512), 0, stream, p);
-        else
-            hipLaunchKernelGGL((conv_igemm_bufp_kernel<256, 256, 2, 4, 16, DT, MODE_GENERIC, 3, 2, 128, 8>), pgrid,
-                               dim3(512), 0, stream, p);
-        return hipGetLastError();
-    }
+    case TILE_BUF: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 8);
+    case TILE_BUF_AHEAD: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 8, 2, true);
     default: break;
-    }
-    if constexpr (DT == DT_BF16) {  // 16 MFMA rows per step: bf16 only; fp8 16x16 blocks need 128-byte steps
-        switch (tile) {
-        case 30: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 16);
-        case 32: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 5, 64, 4);
-        default: break;
-        }
     }
     return hipErrorInvalidValue;
 #undef IGC_BLAUNCH

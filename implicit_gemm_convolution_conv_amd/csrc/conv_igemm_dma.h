@@ -1,18 +1,18 @@
 // Implicit-GEMM forward convolution, im2col paths, with a multi-stage
 // direct-to-LDS pipeline (gfx950 global_load_lds_dwordx4).
 //
-// Same GEMM as conv_igemm_kernel (rows = output positions, columns = output
-// channels, reduction over (t, r, s, c)), but the operand tiles go from global
-// memory straight into LDS without passing through registers, as the async
+// Rows = output positions, columns = output channels, reduction over
+// (t, r, s, c) with c fastest. The operand tiles go from global memory
+// straight into LDS without passing through registers, as the async
 // global->LDS pipeline of FlyDSL PR #860 does (async DMA commit). Freed of
-// staging registers, the ring holds S stages of 64 bytes of k per row, so a
+// staging registers, the ring holds S stages of 128 bytes of k per row, so a
 // load is issued S-1 reduction steps before its data are consumed, which
 // hides L2-miss latency that a one-step register prefetch exposes.
 //
 // An LDS-DMA instruction writes lane i's 16 bytes at base + 16 * i: one wave
-// instruction fills 16 consecutive 64-byte rows. The LDS layout (chunk q of
-// row r at slot q ^ ((r >> 1) & 3)) is therefore produced by choosing which
-// chunk each lane fetches. Zero padding: a lane whose tap falls outside the
+// instruction fills 8 consecutive 128-byte rows. The LDS layout (chunk q of
+// row r at slot q ^ (r & 7)) is therefore produced by choosing which chunk
+// each lane fetches. Zero padding: a lane whose tap falls outside the
 // input box (or whose row is past M, or whose reduction index is past
 // C*T*R*S) fetches a 16-byte zero line instead.
 //
@@ -48,11 +48,6 @@ __device__ inline void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Waves per SIMD the register budget is sized for: two for 8-wave tiles and
-// for tiles small enough that two workgroups share a CU, one for the 4-wave
-// 256x256 tile whose 128x128 wave tiles hold 256 fp32 accumulators per lane.
-template <int BM, int BN, int WM, int WN>
-constexpr int dma_waves_per_eu() { return (WM * WN == 4 && BM * BN >= 256 * 256) ? 1 : 2; }
 
 // Epilogue through LDS for a whole tile: the rings are idle after the last
 // step, so the workgroup writes its bf16 outputs there as [column][row]
@@ -131,8 +126,8 @@ __device__ __attribute__((always_inline)) inline void store_tile_lds(
     }
 }
 
-template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, bool BIG, bool CBLK, int S, int KB = 64>
-__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(dma_waves_per_eu<BM, BN, WM, WN>())))
+template <int BM, int BN, int WM, int WN, int MF, int DT, int MODE, bool BIG, bool CBLK, int S, int KB = 128>
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void conv_igemm_dma_kernel(ConvParams p)
 {
     using Off = typename OffType<BIG>::type;
@@ -149,9 +144,8 @@ void conv_igemm_dma_kernel(ConvParams p)
     constexpr int FM = WTM / MF, FN = WTN / MF;
     constexpr int STAGE = (BM + BN) * KB;
     static_assert(MODE != MODE_POINT || !CBLK, "point mode reduces in natural order");
-    static_assert(KB == 64 || KB == 128, "64- or 128-byte steps");
+    static_assert(KB == 128, "128-byte steps");
     static_assert(AIT >= 1 && BIT >= 1 && BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "loader split");
-    static_assert(MF == 32 || DT == DT_BF16 || KB == 128, "fp8 16x16 MFMA needs 128-byte steps");
     static_assert(WTM % MF == 0 && WTN % MF == 0, "MFMA blocks");
     static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS budget");
     static_assert(LPS * (S - 2) < 64, "vmcnt range");
@@ -172,9 +166,9 @@ void conv_igemm_dma_kernel(ConvParams p)
     const int m0 = tm * BM, n0 = tn * BN;
 
     // This lane's row within each RPI-row group and the chunk it fetches there:
-    // 128-byte rows keep chunk q at slot q ^ (row & 7), 64-byte rows at q ^ ((row >> 1) & 3).
+    // chunk q of a row sits at slot q ^ (row & 7).
     const int lr = lane / CPR;
-    const int jc = KB == 128 ? ((lane & 7) ^ (lane >> 3)) : ((lane & 3) ^ ((lane >> 3) & 3));
+    const int jc = (lane & 7) ^ (lane >> 3);
 
     const char *xb = static_cast<const char *>(p.x);
     const char *wb = static_cast<const char *>(p.w);
@@ -231,13 +225,11 @@ void conv_igemm_dma_kernel(ConvParams p)
     unsigned tail_mask = 0;
 
     // ---------------------------------------------------------------- k position of the next issue
-    // Channel-block order: channel block (pairs * TKE) outer, tap, then the
-    // `pairs` consecutive TKE-wide halves of each 128-byte line, so the two
-    // halves of a cache line are fetched by consecutive steps. The position
-    // starts at step kbeg.
+    // Channel-block order: channel block (TKE channels, one 128-byte line per
+    // tap) outer, then the tap. The position starts at step kbeg.
     int kc, c = 0, t = 0, r = 0, s = 0;
     bool kval = true;
-    int cbase = 0, half = 0;
+    int cbase = 0;
     if constexpr (MODE == MODE_POINT) {
         kc = kbeg * TKE + jc * CH;
     } else if constexpr (!CBLK) {
@@ -250,14 +242,12 @@ void conv_igemm_dma_kernel(ConvParams p)
         kval = kc < p.Rk;
     } else {
         const int taps = p.T * p.R * p.S;
-        const int q = kbeg / p.pairs;  // step = (channel block * taps + tap) * pairs + half
-        const int tap = q % taps;
-        half = kbeg - q * p.pairs;
-        cbase = q / taps * p.pairs * TKE;
+        const int tap = kbeg % taps;  // step = channel block * taps + tap
+        cbase = kbeg / taps * TKE;
         s = tap % p.S;
         r = (tap / p.S) % p.R;
         t = tap / (p.S * p.R);
-        c = cbase + half * TKE + jc * CH;
+        c = cbase + jc * CH;
         kc = ((t * p.R + r) * p.S + s) * p.C + c;
     }
     Off tapoff = 0;
@@ -275,20 +265,17 @@ void conv_igemm_dma_kernel(ConvParams p)
             kc += TKE;
             return;
         } else if constexpr (CBLK) {
-            if (++half == p.pairs) {
-                half = 0;
-                if (++s == p.S) {
-                    s = 0;
-                    if (++r == p.R) {
-                        r = 0;
-                        if (++t == p.T) {
-                            t = 0;
-                            cbase += p.pairs * TKE;
-                        }
+            if (++s == p.S) {
+                s = 0;
+                if (++r == p.R) {
+                    r = 0;
+                    if (++t == p.T) {
+                        t = 0;
+                        cbase += TKE;
                     }
                 }
             }
-            c = cbase + half * TKE + jc * CH;
+            c = cbase + jc * CH;
             kc = ((t * p.R + r) * p.S + s) * p.C + c;
         } else {
             kc += TKE;
@@ -367,7 +354,7 @@ void conv_igemm_dma_kernel(ConvParams p)
         for (int b = 0; b < FN; ++b)
             acc[a][b] = AccT{};
 
-    const int lrow = lane & (MF - 1), lgrp = lane / MF, lsw = KB == 128 ? (lane & 7) : ((lane >> 1) & 3);
+    const int lrow = lane & (MF - 1), lgrp = lane / MF, lsw = lane & 7;
     auto compute = [&](const char *st) {
         const char *aw = st + (wm * WTM + lrow) * KB;
         const char *bw = st + BM * KB + (wn * WTN + lrow) * KB;

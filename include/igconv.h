@@ -36,7 +36,8 @@
  *    GPU work: on error nothing is enqueued and conv_last_error() describes the
  *    reason. IGC_ERR_HIP reports a failed kernel launch. No C++ exception
  *    crosses this interface. All entry points are thread-safe; the error text
- *    is per thread.
+ *    is per thread, and so are the settings of the conv_debug_force* test
+ *    hooks (a forced plan applies to the calls of the thread that set it).
  */
 #ifndef IGCONV_H
 #define IGCONV_H
@@ -68,6 +69,17 @@ extern "C" {
 /* activation memory layout (x_layout) */
 #define IGC_NCDHW 0
 #define IGC_NDHWC 1
+
+/* tile ids reported by conv_plan ("tile_id=") / forced by conv_debug_force */
+#define IGC_TILE_AUTO (-1)
+#define IGC_TILE_DMA_256 0       /* global-address direct-to-LDS 256x256: grids the buffer tiles cannot take */
+#define IGC_TILE_DMA_128 1       /* global-address direct-to-LDS 128x128, two workgroups per CU */
+#define IGC_TILE_DMA_64 2        /* global-address direct-to-LDS 64x64, 4-stage ring: small grids */
+#define IGC_TILE_DMA_256x192 3   /* global-address direct-to-LDS 256x192 (bf16): point-output grids */
+#define IGC_TILE_BUF 4           /* buffer-addressed 256x256, lockstep waves: temporal filters */
+#define IGC_TILE_BUF_AHEAD 5     /* as IGC_TILE_BUF, fragments read further ahead: bf16 generic filters */
+#define IGC_TILE_BUF_PINGPONG 6  /* as IGC_TILE_BUF, two wave groups in compute / LDS phases: long fp8 reductions */
+#define IGC_TILE_PW 7            /* 1x1x1 filter on NCDHW bf16 activations */
 
 /* execution path reported by conv_plan / forced by conv_debug_force */
 #define IGC_PATH_AUTO 0
@@ -254,7 +266,7 @@ IGC_API int conv_bwd_weight(const void *x, const void *dy, void *dw, const int64
 /*
  * Describe, without running anything, the path and tile conv_fwd would use
  * for these arguments: writes a one-line text such as
- * "path=generic tile=256x256 waves=8 kstep=64 order=cblock big=0 grid=6752"
+ * "path=generic tile_id=5 tile=256x256 waves=8 ... order=cblock big=0 grid=6752 ..."
  * into buf (NUL-terminated, truncated to len). Same validation and return
  * codes as conv_fwd. Host only.
  */
@@ -269,26 +281,29 @@ IGC_API int conv_plan_ws(const int64_t xshape[5], const int64_t wshape[5], const
                  char *buf, size_t len);
 
 /*
- * Testing and tuning hook: force the path (IGC_PATH_*), the tile index (-1 =
- * automatic) and the grouped-raster height in tiles (0 = automatic) for later
- * conv_fwd / conv_plan calls of this process. A forced path or tile that does
- * not apply to a shape makes conv_fwd return IGC_ERR_UNSUPPORTED.
+ * Test hooks. Each setting is per thread (it applies to the later conv_fwd*,
+ * conv_plan* and workspace-size calls of the calling thread only) and stays
+ * until that thread changes it. They exist for tests and tuning runs, not for
+ * production callers.
+ *
+ * conv_debug_force: force the path (IGC_PATH_*), the tile (IGC_TILE_*, -1 =
+ * automatic) and the grouped-raster height in tiles (0 = automatic). A forced
+ * path or tile that does not apply to a shape makes conv_fwd return
+ * IGC_ERR_UNSUPPORTED.
  */
 IGC_API int conv_debug_force(int path, int tile, int group_m);
 
-/* Testing hook: force the split count of conv_fwd_ws / conv_plan_ws (0 =
+/* Test hook: force the split count of conv_fwd_ws / conv_plan_ws (0 =
  * automatic, 1 = never split; more is capped by the reduction steps and the
  * workspace). A split on a tile that cannot split returns IGC_ERR_UNSUPPORTED. */
 IGC_API int conv_debug_force_splits(int splits);
 
-/* Testing hook: cap the workgroups of the persistent tile (41) at this many
- * (0 = automatic: one per CU, at most one per output tile), so that small
- * problems also walk several tiles per workgroup. The same count stands in
- * for the 256 CUs when conv_fwd_ws plans a tail split, so small problems
- * have a partial last round too. */
-IGC_API int conv_debug_force_grid(int workgroups);
+/* Test hook: plan as if the device had `cus` compute units (0 = the device's
+ * own count), so that small problems have a partial last round of 256x256
+ * tiles for conv_fwd_ws to split. */
+IGC_API int conv_debug_force_grid(int cus);
 
-/* Testing and tuning hook: -1 turns the temporal raster off (raster groups of
+/* Test and tuning hook: -1 turns the temporal raster off (raster groups of
  * consecutive M tiles on temporal filters too), 0 restores the automatic
  * choice (groups of tiles one temporal tap apart). */
 IGC_API int conv_debug_force_tap_raster(int mode);

@@ -65,13 +65,13 @@ def test_path_selection():
     assert _plan((2, 16, 1, 15, 15), (32, 16, 1, 14, 14), (1, 14, 14))["path"] == "generic"
     p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 1, 1), pd=(1, 0, 0), dt=B.IGC_FP8_E4M3FN)
     assert p["path"] == "temporal" and p["order"] == "cblock" and p["kstep"] == "128"
-    assert p["schedule"] == "lockstep"  # fp8 with a short reduction (48 steps): tile 29
+    assert (p["schedule"], p["tile_id"]) == ("lockstep", str(B.IGC_TILE_BUF))  # fp8, a short reduction (48 steps)
     p4 = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1), dt=B.IGC_FP8_E4M3FN)
     assert p4["schedule"] == "pingpong" and p4["nk"] == "432"  # fp8, long reduction: ping-pong wave groups
     assert _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))["schedule"] == "lockstep"
     p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))
     assert (p["path"], p["tile"], p["grid"], p["nk"], p["stages"], p["bstages"]) == ("generic", "256x256", "6752", "864", "3", "2")
-    assert p["loads"] == "buffer-lds"
+    assert (p["loads"], p["tile_id"]) == ("buffer-lds", str(B.IGC_TILE_BUF_AHEAD))
     # beyond 2^31 bytes: each tile rebases its buffer at the first input plane it reads (4 planes = 118 MB here)
     p = _plan((1, 1024, 240, 160, 90), (1024, 1024, 3, 1, 1), pd=(1, 0, 0))
     assert (p["big"], p["loads"]) == ("1", "buffer-lds")
@@ -101,47 +101,64 @@ def test_path_selection():
 
 def test_forced_path_and_tile():
     try:
-        B.conv_debug_force(B.IGC_PATH_GENERIC, 1, 0)
+        B.conv_debug_force(B.IGC_PATH_GENERIC, B.IGC_TILE_DMA_128, 0)
         p = _plan((1, 64, 8, 8, 8), (64, 64, 3, 1, 1), pd=(1, 0, 0))
-        assert (p["path"], p["tile"]) == ("generic", "128x128")
+        assert (p["path"], p["tile"], p["tile_id"]) == ("generic", "128x128", str(B.IGC_TILE_DMA_128))
         B.conv_debug_force(B.IGC_PATH_POINT, -1, 0)
         with pytest.raises(B.IgcError) as e:
             _plan((1, 64, 8, 8, 8), (64, 64, 3, 1, 1), pd=(1, 0, 0))
         assert e.value.status == B.IGC_ERR_UNSUPPORTED
-        B.conv_debug_force(B.IGC_PATH_AUTO, 6, 0)  # direct-to-LDS 16x16 tile cannot run fp8
+        B.conv_debug_force(B.IGC_PATH_AUTO, B.IGC_TILE_DMA_256x192, 0)  # a bf16-only tile
         with pytest.raises(B.IgcError) as e:
             _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1), dt=B.IGC_FP8_E4M3FN)
         assert e.value.status == B.IGC_ERR_UNSUPPORTED
-        B.conv_debug_force(B.IGC_PATH_AUTO, 27, 0)  # buffer-addressed tiles: im2col paths, whole channel blocks
+        B.conv_debug_force(B.IGC_PATH_AUTO, B.IGC_TILE_BUF, 0)  # buffer-addressed tiles: im2col paths, whole channel blocks
         p = _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1))
-        assert (p["loads"], p["stages"], p["bstages"]) == ("buffer-lds", "2", "2")
+        assert (p["loads"], p["stages"], p["bstages"]) == ("buffer-lds", "3", "2")
         for xs, ws in (((2, 16, 1, 14, 14), (32, 16, 1, 14, 14)), ((1, 96, 4, 4, 4), (8, 96, 3, 3, 3))):
             with pytest.raises(B.IgcError) as e:
                 _plan(xs, ws, (1, 14, 14) if xs[0] == 2 else (1, 1, 1), pd=(0, 0, 0) if xs[0] == 2 else (1, 1, 1))
             assert e.value.status == B.IGC_ERR_UNSUPPORTED
-        B.conv_debug_force(B.IGC_PATH_AUTO, 33, 0)  # ping-pong tile: tap masks of 32 bits
-        assert _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1))["loads"] == "buffer-lds"
+        B.conv_debug_force(B.IGC_PATH_AUTO, B.IGC_TILE_BUF_PINGPONG, 0)  # ping-pong tile: tap masks of 32 bits
+        assert _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1))["schedule"] == "pingpong"
         with pytest.raises(B.IgcError) as e:
             _plan((1, 64, 8, 8, 8), (64, 64, 4, 3, 3), pd=(1, 1, 1))
         assert e.value.status == B.IGC_ERR_UNSUPPORTED
-        B.conv_debug_force(B.IGC_PATH_AUTO, 34, 0)  # tap-shared activation windows
-        p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))
-        assert (p["areuse"], p["schedule"], p["nk"]) == ("taps", "pingpong", "864")
-        for xs, ws, pad in (((1, 64, 8, 8, 8), (64, 64, 3, 1, 1), (1, 0, 0)),        # temporal path
-                            ((1, 64, 8, 8, 8), (64, 64, 3, 3, 1), (1, 1, 0)),        # S = 1: nothing to share
-                            ((1, 64, 4, 4, 400), (64, 64, 3, 3, 3), (1, 1, 1))):     # window above 352 pixels
-            with pytest.raises(B.IgcError) as e:
-                _plan(xs, ws, pd=pad)
-            assert e.value.status == B.IGC_ERR_UNSUPPORTED
-        with pytest.raises(B.IgcError) as e:  # 64-byte fp8 steps need 32x32 blocks
-            B.conv_debug_force(B.IGC_PATH_AUTO, 32, 0)
-            _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1), dt=B.IGC_FP8_E4M3FN)
+        B.conv_debug_force(B.IGC_PATH_AUTO, B.IGC_TILE_PW, 0)  # the pointwise kernel serves the pointwise path only
+        with pytest.raises(B.IgcError) as e:
+            _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1))
         assert e.value.status == B.IGC_ERR_UNSUPPORTED
-        B.conv_debug_force(B.IGC_PATH_AUTO, 7, 5)
+        B.conv_debug_force(B.IGC_PATH_AUTO, B.IGC_TILE_DMA_64, 5)
         p = _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1), dt=B.IGC_FP8_E4M3FN)
-        assert (p["stages"], p["kstep"], p["group_m"]) == ("4", "64", "5")
+        assert (p["stages"], p["kstep"], p["group_m"]) == ("4", "128", "5")
+        with pytest.raises(B.IgcError) as e:  # tile ids past the table
+            B.conv_debug_force(B.IGC_PATH_AUTO, 8, 0)
+        assert e.value.status == B.IGC_ERR_INVALID
     finally:
         B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)
+
+
+def test_debug_hooks_are_per_thread():
+    # a tile forced in one thread leaves the plans of another thread alone
+    import threading
+    geom = ((1, 64, 8, 8, 8), (64, 64, 3, 3, 3))
+    auto = _plan(*geom, pd=(1, 1, 1))
+    seen = {}
+
+    def other():
+        seen["plan"] = _plan(*geom, pd=(1, 1, 1))
+
+    try:
+        B.conv_debug_force(B.IGC_PATH_AUTO, B.IGC_TILE_DMA_128, 0)
+        B.conv_debug_force_splits(1)
+        assert _plan(*geom, pd=(1, 1, 1))["tile_id"] == str(B.IGC_TILE_DMA_128)
+        t = threading.Thread(target=other)
+        t.start()
+        t.join()
+    finally:
+        B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)
+        B.conv_debug_force_splits(0)
+    assert seen["plan"] == auto
 
 
 @pytest.mark.parametrize("args,status", [
@@ -181,28 +198,10 @@ def test_null_pointers_rejected_before_any_launch():
     assert rc == B.IGC_ERR_ALIGN
 
 
-def test_window_tile_limits():
-    try:
-        B.conv_debug_force(B.IGC_PATH_AUTO, 16, 0)
-        p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))
-        assert (p["order"], p["grid"], p["nk"]) == ("window", str(60 * 15 * 8), str(27 * 64))
-        with pytest.raises(B.IgcError) as e:  # box of 3 planes x 9 rows x 1002 columns exceeds LDS
-            _plan((1, 64, 4, 16, 1000), (64, 64, 3, 3, 3), pd=(1, 1, 1))
-        assert e.value.status == B.IGC_ERR_UNSUPPORTED
-        with pytest.raises(B.IgcError) as e:  # temporal filters take the temporal path
-            _plan((1, 64, 8, 8, 8), (64, 64, 3, 1, 1), pd=(1, 0, 0))
-        assert e.value.status == B.IGC_ERR_UNSUPPORTED
-        with pytest.raises(B.IgcError) as e:  # 64-byte channel blocks
-            _plan((1, 48, 8, 8, 8), (64, 48, 3, 3, 3), pd=(1, 1, 1))
-        assert e.value.status == B.IGC_ERR_UNSUPPORTED
-    finally:
-        B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)
-
-
 def _tile_reach(xs, ws, st, pd, dl, esz, bm=256):
-    """Brute force over every 256-row tile: the byte range its valid im2col reads (and the window rows of the
-    tap-shared kernel: every input pixel of every output row the tile touches, plus one more output row) cover,
-    relative to the tile's buffer base, the first input plane its first row can read."""
+    """Brute force over every 256-row tile: the byte range its valid im2col reads cover (every input pixel of
+    every output row the tile touches, plus one more output row, a superset of its rows' reads), relative to the
+    tile's buffer base, the first input plane its first row can read."""
     n_, c, d, h, w = xs
     _, _, t_, r_, s_ = ws
     do = (d + 2 * pd[0] - dl[0] * (t_ - 1) - 1) // st[0] + 1
@@ -301,7 +300,7 @@ def test_forced_splits():
         B.conv_debug_force_splits(1)
         assert B.conv_fwd_workspace_bytes(c1x, c1w, (1, 1, 1), (1, 1, 1), (1, 1, 1), B.IGC_BF16, B.IGC_NDHWC) == 0
         B.conv_debug_force_splits(3)
-        B.conv_debug_force(B.IGC_PATH_AUTO, 29, 0)  # buffer-addressed tile: no split
+        B.conv_debug_force(B.IGC_PATH_AUTO, B.IGC_TILE_BUF, 0)  # buffer-addressed tile: no split
         with pytest.raises(B.IgcError) as e:
             _plan_ws(c1x, c1w, 1 << 30)
         assert e.value.status == B.IGC_ERR_UNSUPPORTED
@@ -359,3 +358,4 @@ def test_point_gradient_entry_points():
     rc = lib.conv_bwd_weight(16, 32, 48, a, b, B._i32(st), B._i32(z), B._i32(one), B.IGC_BF16, B.IGC_NCDHW, 64,
                              base - 1, None)
     assert rc == B.IGC_ERR_INVALID  # workspace below the two transposes
+

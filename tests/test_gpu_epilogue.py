@@ -49,24 +49,33 @@ def _out(xs, ws, st, pd, dl):
 
 # name, x, w, stride, pad, dil, layout, tile, splits
 CASES = [
-    ("register_tile0", (1, 64, 5, 9, 11), (96, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 0, 0),
-    ("register_tile5_mf32", (2, 24, 5, 7, 9), (40, 24, 3, 3, 3), (1, 2, 1), (1, 1, 2), (1, 1, 2), "NDHWC", 5, 0),
-    ("dma_tile26", (1, 64, 4, 16, 16), (64, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 26, 1),
-    ("dma_tile21_temporal", (2, 64, 9, 6, 7), (96, 64, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1), "NDHWC", 21, 1),
-    ("window_tile16", (1, 64, 4, 18, 20), (72, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 16, 0),
-    ("buffer_tile29", (2, 128, 6, 10, 12), (200, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 29, 0),
-    ("persistent_tile41", (2, 128, 6, 10, 12), (200, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 41, 0),
+    ("dma_256", (1, 64, 5, 9, 11), (96, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", B.IGC_TILE_DMA_256, 0),
+    ("dma_128_linear_strided", (2, 24, 5, 7, 9), (40, 24, 3, 3, 3), (1, 2, 1), (1, 1, 2), (1, 1, 2), "NDHWC",
+     B.IGC_TILE_DMA_128, 0),
+    ("dma_64", (1, 64, 4, 16, 16), (64, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", B.IGC_TILE_DMA_64, 1),
+    ("dma_256_temporal", (2, 64, 9, 6, 7), (96, 64, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1), "NDHWC",
+     B.IGC_TILE_DMA_256, 1),
+    ("buffer", (2, 128, 6, 10, 12), (200, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", B.IGC_TILE_BUF, 0),
+    ("buffer_ahead", (1, 64, 4, 18, 20), (72, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC",
+     B.IGC_TILE_BUF_AHEAD, 0),
     # whole 256x256 tiles inside one image with 16-byte aligned rows: the outputs go through LDS
-    ("buffer_tile29_lds_epilogue", (1, 128, 4, 16, 16), (256, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC",
-     29, 0),
-    ("pingpong_tile33", (1, 128, 5, 9, 11), (136, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 33, 0),
-    ("taps_tile34", (1, 128, 5, 9, 11), (136, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 34, 0),
+    ("buffer_lds_epilogue", (1, 128, 4, 16, 16), (256, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC",
+     B.IGC_TILE_BUF, 0),
+    ("buffer_ahead_lds_epilogue", (1, 128, 4, 16, 16), (256, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC",
+     B.IGC_TILE_BUF_AHEAD, 0),
+    ("pingpong", (1, 128, 5, 9, 11), (136, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC",
+     B.IGC_TILE_BUF_PINGPONG, 0),
+    ("pingpong_lds_epilogue", (1, 128, 4, 16, 16), (256, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC",
+     B.IGC_TILE_BUF_PINGPONG, 0),
     ("pointwise_ncdhw", (2, 48, 3, 7, 8), (80, 48, 1, 1, 1), (1, 1, 1), (0, 0, 0), (1, 1, 1), "NCDHW", -1, 0),
     ("point_output", (40, 3, 1, 14, 14), (68, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1), "NCDHW", -1, 0),
-    ("point_output_lds", (200, 3, 1, 14, 14), (256, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1), "NCDHW", 26, 0),
-    ("split_c1", (1, 64, 4, 16, 16), (64, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 26, 5),
-    ("split_point", (40, 3, 1, 14, 14), (68, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1), "NCDHW", 26, 4),
-    ("split_odd_tails", (1, 16, 3, 5, 7), (25, 16, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 26, 2),
+    ("point_output_lds", (200, 3, 1, 14, 14), (256, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1), "NCDHW",
+     B.IGC_TILE_DMA_64, 0),
+    ("split_c1", (1, 64, 4, 16, 16), (64, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", B.IGC_TILE_DMA_64, 5),
+    ("split_point", (40, 3, 1, 14, 14), (68, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1), "NCDHW",
+     B.IGC_TILE_DMA_64, 4),
+    ("split_odd_tails", (1, 16, 3, 5, 7), (25, 16, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC",
+     B.IGC_TILE_DMA_64, 2),
 ]
 
 
@@ -103,10 +112,11 @@ def test_bias_and_amax_bf16(case):
         assert torch.equal(y0.view(torch.int16), y_noextra.view(torch.int16))
 
 
-@pytest.mark.parametrize("case", [c for c in CASES if c[0] in ("register_tile0", "dma_tile26", "buffer_tile29",
-                                                               "buffer_tile29_lds_epilogue", "persistent_tile41", "pingpong_tile33", "pointwise_ncdhw", "point_output", "point_output_lds",
-                                                               "split_c1", "split_odd_tails", "window_tile16",
-                                                               "taps_tile34")],
+@pytest.mark.parametrize("case", [c for c in CASES if c[0] in ("dma_256", "dma_64", "buffer", "buffer_ahead",
+                                                               "buffer_lds_epilogue", "buffer_ahead_lds_epilogue",
+                                                               "pingpong", "pingpong_lds_epilogue", "pointwise_ncdhw",
+                                                               "point_output", "point_output_lds", "split_c1",
+                                                               "split_odd_tails")],
                          ids=lambda c: c[0])
 def test_bias_integer_bit_exact(case):
     name, xs, ws, st, pd, dl, layout, tile, splits = case
@@ -124,10 +134,12 @@ def test_bias_integer_bit_exact(case):
     assert float(amax) == float(np.abs(ref).max())
 
 
-@pytest.mark.parametrize("tile,splits,kout", [(-1, 0, 136), (33, 0, 136), (29, 0, 136), (26, 1, 136), (26, 3, 136),
-                                              (29, 0, 256), (41, 0, 256)])
+@pytest.mark.parametrize("tile,splits,kout", [(-1, 0, 136), (B.IGC_TILE_BUF_PINGPONG, 0, 136), (B.IGC_TILE_BUF, 0, 136),
+                                              (B.IGC_TILE_DMA_64, 1, 136), (B.IGC_TILE_DMA_64, 3, 136),
+                                              (B.IGC_TILE_BUF, 0, 256), (B.IGC_TILE_BUF_AHEAD, 0, 256),
+                                              (B.IGC_TILE_BUF_PINGPONG, 0, 256)])
 def test_bias_and_amax_fp8(tile, splits, kout):
-    # kout = 256 on 4 x 16 x 16 outputs: whole tiles inside the image, the LDS-staged epilogue of tile 29
+    # kout = 256 on 4 x 16 x 16 outputs: whole tiles inside the image, the LDS-staged epilogue of the buffer tiles
     _announce(f"epilogue fp8 tile {tile} splits {splits} K {kout}")
     if kout == 256:
         xs, ws, st, pd, dl = (1, 128, 4, 16, 16), (256, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)

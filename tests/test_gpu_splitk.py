@@ -57,23 +57,29 @@ def _plan_splits(xs, ws, st, pd, dl, lay, nbytes, dtype=B.IGC_BF16):
 # name, x (N,C,D,H,W), w (K,C,T,R,S), stride, pad, dil, layout, tile, splits
 SPLIT_CASES = [
     # linear reduction order (C % 64 != 0): a split starts mid-tap
-    ("linear_c24", (2, 24, 5, 7, 9), (40, 24, 3, 3, 3), (1, 2, 1), (1, 1, 2), (1, 1, 2), "NDHWC", 26, 3),
+    ("linear_c24", (2, 24, 5, 7, 9), (40, 24, 3, 3, 3), (1, 2, 1), (1, 1, 2), (1, 1, 2), "NDHWC", B.IGC_TILE_DMA_64, 3),
     # channel-block order over two channel blocks, 128x128 tiles
-    ("cblock_c128", (2, 128, 6, 10, 12), (200, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 24, 5),
-    # 64-byte steps paired over a 128-byte line; 11 steps per split starts the second split on the odd half
-    ("paired_halves", (1, 64, 5, 9, 11), (96, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 11, 5),
+    ("cblock_c128", (2, 128, 6, 10, 12), (200, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC",
+     B.IGC_TILE_DMA_128, 5),
+    # channel-block order, 11 steps per split: the second split starts mid-way through the taps of a block
+    ("cblock_mid_taps", (1, 128, 5, 9, 11), (96, 128, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC",
+     B.IGC_TILE_DMA_64, 5),
     # temporal decode, one step per split
-    ("temporal", (2, 64, 9, 6, 7), (96, 64, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1), "NDHWC", 26, 3),
+    ("temporal", (2, 64, 9, 6, 7), (96, 64, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1), "NDHWC", B.IGC_TILE_DMA_64, 3),
     # point output: image rows of 588 elements, the chunk straddling a row end belongs to the last split
-    ("point_tail", (40, 3, 1, 14, 14), (68, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1), "NCDHW", 26, 4),
+    ("point_tail", (40, 3, 1, 14, 14), (68, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1), "NCDHW",
+     B.IGC_TILE_DMA_64, 4),
     # Do*Ho*Wo = 105 (scalar partial stores) and an odd element count (scalar reduction)
-    ("odd_tails", (1, 16, 3, 5, 7), (25, 16, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 26, 2),
+    ("odd_tails", (1, 16, 3, 5, 7), (25, 16, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", B.IGC_TILE_DMA_64, 2),
     # the 256x256 tile, many splits of a short grid
-    ("tile21_c1", (1, 64, 4, 16, 16), (64, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 21, 9),
-    # 8-stage ring, fewer steps per split than stages
-    ("ring8_short", (1, 32, 4, 8, 8), (48, 32, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 10, 6),
+    ("tile256_c1", (1, 64, 4, 16, 16), (64, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC",
+     B.IGC_TILE_DMA_256, 9),
+    # 4-stage ring, fewer steps per split than stages
+    ("ring4_short", (1, 32, 4, 8, 8), (48, 32, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC",
+     B.IGC_TILE_DMA_64, 12),
     # more splits than steps: capped at one step each
-    ("splits_beyond_steps", (1, 64, 3, 6, 6), (32, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", 26, 1000),
+    ("splits_beyond_steps", (1, 64, 3, 6, 6), (32, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC",
+     B.IGC_TILE_DMA_64, 1000),
 ]
 
 
@@ -99,7 +105,7 @@ def test_split_bf16(case):
     P.check_close(P.y_values(y), ref, R, float(x.abs().max()), float(w.abs().max()), name)
 
 
-@pytest.mark.parametrize("case", [c for c in SPLIT_CASES if c[0] in ("linear_c24", "paired_halves", "point_tail",
+@pytest.mark.parametrize("case", [c for c in SPLIT_CASES if c[0] in ("linear_c24", "cblock_mid_taps", "point_tail",
                                                                        "odd_tails", "cblock_c128")],
                          ids=lambda c: c[0])
 def test_split_integer_bit_exact(case):
@@ -154,7 +160,7 @@ def test_split_workspace_too_small_lowers_splits():
     P.check_close(P.y_values(y), ref, wl.reduction, float(x.abs().max()), float(w.abs().max()), "c1 two slices")
 
 
-@pytest.mark.parametrize("tile,splits", [(-1, 0), (26, 3), (21, 9)])
+@pytest.mark.parametrize("tile,splits", [(-1, 0), (B.IGC_TILE_DMA_64, 3), (B.IGC_TILE_DMA_256, 9)])
 def test_split_fp8(tile, splits):
     _announce(f"split fp8 tile {tile} splits {splits}")
     xs, ws, st, pd, dl = (1, 64, 4, 16, 16), (64, 64, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)
@@ -189,7 +195,7 @@ def test_split_fp8_integer_bit_exact():
     wq = torch.empty((ws[0], B.conv_packed_w_cols(ws, B.IGC_FP8_E4M3FN)), dtype=torch.uint8, device=P.DEV)
     B.conv_pack_w(w, wq, ws, B.IGC_FP8_E4M3FN, B.IGC_NDHWC, ones[2:4])
     y = _nan_out(xs, ws, st, pd, dl)
-    with forced(26, 4):
+    with forced(B.IGC_TILE_DMA_64, 4):
         B.conv_fwd_ws(xq, wq, y, xs, ws, st, pd, dl, B.IGC_FP8_E4M3FN, B.IGC_NDHWC, ones,
                       workspace=_workspace(xs, ws, st, pd, dl, 4))
     torch.cuda.synchronize()
@@ -227,13 +233,12 @@ TAIL_CASES = [
      (4, 3)),
     # temporal 3x1x1 with C = 2048 (96 steps): 5 tiles on 4, one tail tile in 4 splits of 24 steps
     ("tail_temporal", (1, 2048, 5, 16, 16), (256, 2048, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1), 4, (1, 4)),
-    # 17 tiles on 16: one tail tile in 8 splits; splits start mid-tap (tile 29: steps 13, 27, 40, ...) and, on
-    # tile 32's paired 64-byte steps, at the second half of a 128-byte line (steps 27, 81, ...)
+    # 17 tiles on 16: one tail tile in 8 splits of its 108 steps, which start mid-way through a channel block's taps
     ("tail_one_tile_8_splits", (1, 256, 4, 17, 64), (256, 256, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), 16, (1, 8)),
 ]
 
 
-@pytest.mark.parametrize("tile", [29, 31, 33, 28, 32])  # 32: 64-byte steps, the reduction walked in paired halves
+@pytest.mark.parametrize("tile", [B.IGC_TILE_BUF, B.IGC_TILE_BUF_AHEAD, B.IGC_TILE_BUF_PINGPONG])
 @pytest.mark.parametrize("case", TAIL_CASES, ids=[c[0] for c in TAIL_CASES])
 def test_tail_split_bf16(case, tile):
     name, xs, ws, st, pd, dl, cus, want = case
@@ -256,7 +261,7 @@ def test_tail_split_bf16(case, tile):
     assert differ < 0.5
 
 
-@pytest.mark.parametrize("tile", [29, 31, 33, 32])
+@pytest.mark.parametrize("tile", [B.IGC_TILE_BUF, B.IGC_TILE_BUF_AHEAD, B.IGC_TILE_BUF_PINGPONG])
 @pytest.mark.parametrize("case", TAIL_CASES, ids=[c[0] for c in TAIL_CASES])
 def test_tail_split_integer_bit_exact(case, tile):
     name, xs, ws, st, pd, dl, cus, want = case
@@ -275,7 +280,7 @@ def test_tail_split_integer_bit_exact(case, tile):
     assert float(amax) == float(np.abs(ref).max())
 
 
-@pytest.mark.parametrize("tile", [29, 31, 33])
+@pytest.mark.parametrize("tile", [B.IGC_TILE_BUF, B.IGC_TILE_BUF_AHEAD, B.IGC_TILE_BUF_PINGPONG])
 def test_tail_split_fp8(tile):
     # C = 512 in fp8: 108 steps of 128 channels, 4 tail tiles in 3 splits
     name, xs, ws, st, pd, dl, cus, want = ("tail_fp8_ragged", (2, 512, 3, 11, 29), (300, 512, 3, 3, 3), (1, 1, 1),
@@ -305,7 +310,7 @@ def test_tail_split_needs_its_workspace():
     g = I.generator(98, P.DEV)
     x = I.draw(xs, ("uniform", 1.0), g, P.DEV)
     w = I.draw(ws, ("uniform", 1.0), g, P.DEV)
-    with forced(tile=29), capped_cus(cus):
+    with forced(tile=B.IGC_TILE_BUF), capped_cus(cus):
         nbytes = B.conv_fwd_workspace_bytes(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC)
         assert _tail(B.conv_plan_ws(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC, nbytes - 16)) == (0, 1)
         wsp = torch.full(((nbytes - 16) // 4,), float("nan"), dtype=torch.float32, device=P.DEV)

@@ -437,7 +437,7 @@ def test_shards_reassemble_the_full_output():
     x = I.draw(xs, ("normal", 1.0), g, P.DEV)
     w = I.draw(ws, ("normal", 0.02), g, P.DEV)
     one, pad1 = (1, 1, 1), (1, 1, 1)
-    B.conv_debug_force(B.IGC_PATH_AUTO, 24, 0)
+    B.conv_debug_force(B.IGC_PATH_AUTO, B.IGC_TILE_DMA_128, 0)
     try:
         xk = PL.packed_input(x, "bf16")
         full = PL.output(xs, ws, one, pad1, one, P.DEV)
