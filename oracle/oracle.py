@@ -29,7 +29,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "conv_oracle.c")
-_SO = os.path.join(_HERE, "liboracle.so")
+# ORACLE_SANITIZED=1 loads a build with AddressSanitizer and UndefinedBehaviorSanitizer (the process must preload
+# the ASan runtime, see tests/test_oracle_sanitized.py)
+_SANITIZED = os.environ.get("ORACLE_SANITIZED") == "1"
+_SO = os.path.join(_HERE, "liboracle_san.so" if _SANITIZED else "liboracle.so")
 
 F64, BF16, E4M3 = 0, 1, 2
 _LAYOUTS = {"NCDHW": 0, "NDHWC": 1}
@@ -37,15 +40,19 @@ _LAYOUTS = {"NCDHW": 0, "NDHWC": 1}
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile conv_oracle.c into liboracle.so next to it (gcc, OpenMP, no FMA contraction)."""
-    if force or not os.path.exists(_SO):
-        tmp = _SO + ".tmp"
+def build(force: bool = True, sanitized: bool | None = None) -> str:
+    """Compile conv_oracle.c into liboracle.so next to it (gcc, OpenMP, no FMA contraction); with sanitized, into
+    liboracle_san.so with AddressSanitizer and UndefinedBehaviorSanitizer (host code, every error fatal)."""
+    sanitized = _SANITIZED if sanitized is None else sanitized
+    so = os.path.join(_HERE, "liboracle_san.so" if sanitized else "liboracle.so")
+    if force or not os.path.exists(so):
+        tmp = so + ".tmp"
+        san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
         cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
-               "-fno-fast-math", "-Wall", "-o", tmp, _SRC, "-lm"]
+               "-fno-fast-math", "-Wall", *(san if sanitized else []), "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _SO)
-    return _SO
+        os.replace(tmp, so)
+    return so
 
 
 def _load():
