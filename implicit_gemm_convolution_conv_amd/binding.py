@@ -30,7 +30,7 @@ IGC_TILE_DMA_256, IGC_TILE_DMA_128, IGC_TILE_DMA_64, IGC_TILE_DMA_256x192 = 0, 1
 IGC_TILE_BUF, IGC_TILE_BUF_AHEAD, IGC_TILE_BUF_PINGPONG, IGC_TILE_PW = 4, 5, 6, 7
 
 EXPORTS = ("conv_out_dims", "conv_packed_w_cols", "conv_amax", "conv_fp8_scales", "conv_pack_x", "conv_pack_w",
-           "conv_fwd", "conv_fwd_ws", "conv_fwd_ex", "conv_fwd_workspace_bytes", "conv_plan", "conv_plan_ws", "conv_debug_force",
+           "conv_fwd", "conv_fwd_ws", "conv_fwd_ex", "conv_fwd_noalloc", "conv_fwd_workspace_bytes", "conv_plan", "conv_plan_ws", "conv_debug_force",
            "conv_debug_force_splits", "conv_debug_force_grid", "conv_debug_force_tap_raster", "conv_packed_w_t_cols", "conv_pack_w_t", "conv_bwd_data",
            "conv_bwd_weight_workspace_bytes", "conv_bwd_weight", "conv_last_error")
 
@@ -63,6 +63,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.conv_plan.argtypes = [P, P, P, P, P, I32, I32, ctypes.c_char_p, ctypes.c_size_t]
         lib.conv_fwd_ws.argtypes = [P, P, P, P, P, P, P, P, I32, I32, P, P, ctypes.c_size_t, P]
         lib.conv_fwd_ex.argtypes = [P, P, P, P, P, P, P, P, I32, I32, P, P, P, P, ctypes.c_size_t, P]
+        lib.conv_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, I32, I32, P, P, P, P]
         lib.conv_fwd_workspace_bytes.argtypes = [P, P, P, P, P, I32, I32]
         lib.conv_fwd_workspace_bytes.restype = I64
         lib.conv_plan_ws.argtypes = [P, P, P, P, P, I32, I32, ctypes.c_size_t, ctypes.c_char_p, ctypes.c_size_t]
@@ -185,6 +186,15 @@ def conv_fwd_ex(x, w_packed, y, xshape, wshape, stride, pad, dilation, dtype, x_
                                              _i32(stride), _i32(pad), _i32(dilation), int(dtype), int(x_layout),
                                              _dev(scales_dev), _dev(bias), _dev(y_amax), _dev(workspace), nbytes,
                                              _stream(stream, y)))
+
+
+def conv_fwd_noalloc(x, w_packed, y, xshape, wshape, stride, pad, dilation, dtype, x_layout, scales_dev=None,
+                     bias=None, y_amax=None, stream=None):
+    """conv_fwd_ex with its workspace in the library's static device scratch (allocates nothing)."""
+    _check("conv_fwd_noalloc", load().conv_fwd_noalloc(_dev(x), _dev(w_packed), _dev(y), _i64(xshape, 5),
+                                                       _i64(wshape, 5), _i32(stride), _i32(pad), _i32(dilation),
+                                                       int(dtype), int(x_layout), _dev(scales_dev), _dev(bias),
+                                                       _dev(y_amax), _stream(stream, y)))
 
 
 def conv_fwd_workspace_bytes(xshape, wshape, stride, pad, dilation, dtype, x_layout) -> int:

@@ -5,6 +5,7 @@
 // error return leaves the stream untouched.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <cstdlib>
 #include <cstdarg>
 #include <cstdint>
@@ -73,6 +74,34 @@ int64_t device_cus()
 // larger tensors switch to 64-bit offsets (invalid im2col taps may compute an
 // offset up to one tensor beyond the valid range before being masked).
 constexpr int64_t kSmallTensor = int64_t(1) << 30;
+
+// Device scratch of conv_fwd_noalloc, one copy per GPU, held until the process
+// ends. 64 MiB is the largest workspace an automatic plan asks for on a
+// 256-CU device: a split-K grid fills at most one round of 256x256 fp32 tiles
+// (256 x 256 KB), and a tail split at most r * S <= 256 of them.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+// Device address of this device's copy of `scratch`, looked up once per device
+// (the current one) and kept: host code passes this pointer, never the
+// array's name, which on the host is only a stand-in for the symbol. Null if
+// the lookup fails.
+void *scratch_ptr()
+{
+    static std::mutex mu;
+    static void *ptrs[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return nullptr;
+        ptrs[dev] = p;
+    }
+    return ptrs[dev];
+}
 
 int fail(int code, const char *fmt, ...)
 {
@@ -758,6 +787,34 @@ int conv_fwd_ws(const void *x, const void *w_packed, void *y, const int64_t xsha
 {
     return conv_fwd_ex(x, w_packed, y, xshape, wshape, stride, pad, dilation, dtype, x_layout, scales_dev, nullptr,
                        nullptr, workspace_dev, workspace_bytes, stream);
+}
+
+int conv_fwd_noalloc(const void *x, const void *w_packed, void *y, const int64_t xshape[5],
+                     const int64_t wshape[5], const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3],
+                     int dtype, int x_layout, const float *scales_dev, const float *bias_dev, float *y_amax_dev,
+                     void *stream)
+{
+    Plan pl;
+    int rc = make_plan(xshape, wshape, stride, pad, dilation, dtype, x_layout, pl);
+    if (rc)
+        return rc;
+    rc = plan_splits(pl, SIZE_MAX);
+    if (rc < 0)
+        return rc;
+    const int64_t need = pl.ws_need;
+    if (need > (int64_t)kScratchBytes)
+        return fail(IGC_ERR_UNSUPPORTED, "conv_fwd_noalloc: the plan needs %lld bytes of workspace, the static "
+                    "scratch holds %zu", (long long)need, kScratchBytes);
+    void *ws = nullptr;
+    if (need > 0) {
+        ws = scratch_ptr();
+        if (!ws)
+            return fail(IGC_ERR_HIP, "conv_fwd_noalloc: device address of the static scratch not available");
+    }
+    // the same plan as conv_fwd_ws with conv_fwd_workspace_bytes of workspace: every fp32 partial the
+    // split writes is written before it is read, so nothing in the scratch needs clearing
+    return conv_fwd_ex(x, w_packed, y, xshape, wshape, stride, pad, dilation, dtype, x_layout, scales_dev, bias_dev,
+                       y_amax_dev, ws, (size_t)need, stream);
 }
 
 int conv_fwd(const void *x, const void *w_packed, void *y, const int64_t xshape[5], const int64_t wshape[5],

@@ -217,6 +217,29 @@ IGC_API int conv_fwd_ex(const void *x, const void *w_packed, void *y, const int6
                 void *workspace_dev, size_t workspace_bytes, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): conv_fwd_ex
+ * with its workspace taken from a static device array of the library instead
+ * of the caller. Same arguments, layouts, plan, result and errors as
+ * conv_fwd_ex with a workspace of conv_fwd_workspace_bytes bytes (bit for bit
+ * the same output), without the workspace arguments. Allocates nothing: the
+ * scratch is a 64 MiB `__device__` array, one per GPU the library runs on,
+ * held until the process ends; its device address is looked up once per
+ * device (the current one) on the first call that needs it.
+ * Limit: a plan whose workspace exceeds 64 MiB returns IGC_ERR_UNSUPPORTED
+ * before any work is enqueued (automatic plans need at most 64 MiB on a
+ * 256-CU device; a forced split can need more). The scratch keeps the last
+ * call's partial sums and needs no clearing (every value is written before
+ * it is read). Every call on one GPU shares that GPU's scratch: calls that
+ * overlap in time on one GPU (other streams, other threads) race and must be
+ * ordered by the caller.
+ */
+IGC_API int conv_fwd_noalloc(const void *x, const void *w_packed, void *y, const int64_t xshape[5],
+                const int64_t wshape[5], const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3],
+                int dtype, int x_layout, const float *scales_dev, const float *bias_dev, float *y_amax_dev,
+                void *stream);
+
+/*
  * Workspace bytes conv_fwd_ws would use for these arguments with unlimited
  * room: splits * 4 * N*K*Do*Ho*Wo when it splits the reduction, r * S * 256 *
  * 256 * 4 for a tail split, else 0.

@@ -359,3 +359,22 @@ def test_point_gradient_entry_points():
                              base - 1, None)
     assert rc == B.IGC_ERR_INVALID  # workspace below the two transposes
 
+
+def test_noalloc_rejects_a_workspace_beyond_its_scratch_before_any_launch():
+    # a forced 64-way split of a 1024 x 1280 output (64 x 5 MiB of fp32 partials) needs more than the 64 MiB
+    # static scratch: rejected with a message, nothing enqueued (null tensors are never touched)
+    xs, ws = (1, 64, 4, 16, 16), (1280, 64, 3, 3, 3)
+    lib = B.load()
+    one = B._i32((1, 1, 1))
+    try:
+        B.conv_debug_force(B.IGC_PATH_AUTO, B.IGC_TILE_DMA_64, 0)
+        B.conv_debug_force_splits(64)
+        need = B.conv_fwd_workspace_bytes(xs, ws, (1, 1, 1), (1, 1, 1), (1, 1, 1), B.IGC_BF16, B.IGC_NDHWC)
+        assert need > 64 << 20
+        rc = lib.conv_fwd_noalloc(16, 32, 48, B._i64(xs, 5), B._i64(ws, 5), one, one, one, B.IGC_BF16,
+                                  B.IGC_NDHWC, None, None, None, None)
+        assert rc == B.IGC_ERR_UNSUPPORTED
+        assert "static scratch" in B.conv_last_error()
+    finally:
+        B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)
+        B.conv_debug_force_splits(0)
