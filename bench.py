@@ -41,9 +41,8 @@ KERNEL_SOURCES = ["implicit_gemm_convolution_conv_amd/csrc/conv_igemm.h",
                   "implicit_gemm_convolution_conv_amd/csrc/conv_igemm_dma.h",
                   "implicit_gemm_convolution_conv_amd/csrc/conv_igemm_buf.h",
                   "implicit_gemm_convolution_conv_amd/csrc/conv_igemm_pp.h",
-                  "implicit_gemm_convolution_conv_amd/csrc/conv_igemm_ppw.h",
-                  "implicit_gemm_convolution_conv_amd/csrc/conv_pw.hip",
                   "implicit_gemm_convolution_conv_amd/csrc/conv_buf_bf16.hip",
+                  "implicit_gemm_convolution_conv_amd/csrc/splitk.hip",
                   "implicit_gemm_convolution_conv_amd/csrc/igconv_internal.h",
                   "implicit_gemm_convolution_conv_amd/csrc/api.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv_igemm_c3_bf16_traffic.json")
@@ -273,19 +272,50 @@ def bench_grad(steps, warmup, torch, B, I, PL):
     return res
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_threads():
+    """Threads the oracle runs on: every core of the process's affinity mask, within the OMP_NUM_THREADS budget
+    of the host when it sets one (the GPU hosts give one GPU's process a share of their cores that way)."""
+    affinity = len(os.sched_getaffinity(0))
+    budget = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    return min(affinity, budget) if budget > 0 else affinity, affinity
+
+
 def cpu_baseline(seconds: float, I):
-    """The fp64 oracle on a bounded random sample of the headline workload's outputs."""
+    """The fp64 oracle on a bounded random sample of the headline workload's outputs, and on the whole of the two
+    small workloads (c1, c2)."""
     import numpy as np
     import torch
     from oracle import oracle as O
+
+    threads, affinity = oracle_threads()
+    O.set_threads(threads)
+    full = {}
+    for name in ("c1", "c2"):  # evaluated in full: every output element
+        wl = I.WORKLOADS[name]
+        x, w = I.make(wl, "cpu")
+        xb, wb = I.bf16_bits(x), I.bf16_bits(w)
+        flop = conv_flops(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dil)
+        t0 = time.perf_counter()
+        O.conv3d(xb, wb, wl.stride, wl.pad, wl.dil)
+        t = time.perf_counter() - t0
+        full[name] = {"seconds": round(t, 3), "tflops": round(flop / t / 1e12, 6), "workload": wl.note}
 
     wl = I.WORKLOADS["c3"]
     x, w = I.make(wl, "cuda")  # same seeded draw as the GPU run
     xb, wb = I.bf16_bits(x), I.bf16_bits(w)
     del x, w
     torch.cuda.empty_cache()
-    cores = min(len(os.sched_getaffinity(0)), 16)
-    O.set_threads(cores)
     n, c, d, h, wd = wl.x_shape
     k = wl.w_shape[0]
     do, ho, wo = O.out_dims(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dil)
@@ -298,7 +328,7 @@ def cpu_baseline(seconds: float, I):
         O.conv3d_points(xb, wb, pts, wl.stride, wl.pad, wl.dil, x_layout="NDHWC")
         return time.perf_counter() - t0
 
-    npts = 8 * cores
+    npts = 8 * threads
     t = run(npts)
     while t < 0.5:
         npts *= 4
@@ -308,7 +338,23 @@ def cpu_baseline(seconds: float, I):
     return {"value": round(2.0 * R * npts / t / 1e12, 6), "unit": "TFLOPS", "cores": O.get_threads(),
             "kind": "oracle",
             "sample": f"{npts} random output elements of {wl.note} (each a {R}-term fp64 dot product), "
-                      f"{t:.1f} s"}
+                      f"{t:.1f} s; extrapolated linearly to the whole output",
+            "affinity_cores": affinity, "cpu_model": cpu_model(), "full": full}
+
+
+def copy_rates(steps, torch):
+    """Device-to-device copy rate of 1 GiB on this GPU (GB/s, bytes read + written): the ceiling a kernel that
+    reads and writes every byte once reaches here, next to the 8 TB/s HBM peak."""
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    nbytes = src.numel() * 2
+    st = {}
+    time_launches(lambda: dst.copy_(src), steps, 3, torch, st)
+    copy = 2 * nbytes / (st["median"] * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"d2d_copy_gbs": round(copy, 1), "bytes": nbytes,
+            "note": "1 GiB tensor copied with torch copy_ (hipMemcpy device to device); median of the event times"}
 
 
 def traffic_bytes():
@@ -331,7 +377,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", default=None, help="comma list of extra workloads (c1,c2,c4,c4t,c5,pw,c3ex,c2grad,c3s,c5s)")
+    ap.add_argument("--only", default=None,
+                    help="comma list of extra workloads (copy,c1,c2,c4,c4t,c5,pw,c3ex,c2grad,c3s,c5s)")
     ap.add_argument("--profile", action="store_true",
                     help="counter-collection run: the headline conv `steps` times, then one 1 GiB device copy "
                          "(the reference for scaling FETCH_SIZE / WRITE_SIZE); prints nothing else")
@@ -377,17 +424,25 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        names = args.only.split(",") if args.only else ["c1", "c2", "c4", "c4t", "c5", "pw", "c3ex", "c2grad",
+        names = args.only.split(",") if args.only else ["copy", "c1", "c2", "c4", "c4t", "c5", "pw", "c3ex", "c2grad",
                                                          "c3s", "c5s"]
         for name in names:
             log(f"[bench] extra workload {name}")
-            if name == "c3ex":
-                extra[name] = bench_epilogue(max(5, args.steps // 2), args.warmup, torch, B, I, PL)
+            if name == "copy":
+                extra[name] = copy_rates(max(20, args.steps), torch)
+            elif name == "c3ex":
+                extra[name] = bench_epilogue(max(20, args.steps), args.warmup, torch, B, I, PL)
             elif name == "c2grad":
                 extra[name] = bench_grad(max(20, args.steps), args.warmup, torch, B, I, PL)
             else:
-                extra[name] = bench_workload(name, max(5, args.steps // 2), args.warmup, torch, B, I, PL)
+                extra[name] = bench_workload(name, max(20, args.steps), args.warmup, torch, B, I, PL)
             log(f"[bench] {name}: {json.dumps(extra[name])}")
+        ceiling = extra.get("copy", {}).get("d2d_copy_gbs")
+        if ceiling:  # data-movement kernels against the measured copy rate as well as the 8 TB/s peak
+            for rec in extra.values():
+                for key in ("pack_gbs", "transpose_gbs", "amax_gbs", "kernel_gbs", "amax_pass_gbs"):
+                    if key in rec:
+                        rec[key.replace("_gbs", "_vs_copy")] = round(rec[key] / ceiling, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
