@@ -82,14 +82,19 @@ __device__ inline void tile_coords(const ConvParams &p, int bid, int &tm, int &t
 
 __device__ inline void tile_coords(const ConvParams &p, int &tm, int &tn) { tile_coords(p, blockIdx.x, tm, tn); }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
-__device__ inline uint32_t f32_to_bf16_rne(float f)
+// Two fp32 values -> their bf16 bits (a in the low half), rounded to nearest
+// even by gfx950's packed conversion (one v_cvt_pk_bf16_f32). Over all 2^32
+// fp32 bit patterns it gives the bits of the software rounding it replaces,
+// (u + 0x7fff + lsb) >> 16 with NaN -> (u >> 16) | 0x40, NaNs included.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __attribute__((always_inline)) inline uint32_t bf16_pack2(float a, float b)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __attribute__((always_inline)) inline uint32_t f32_to_bf16_rne(float f) { return bf16_pack2(f, 0.0f) & 0xffffu; }
 
 // Output transform of every epilogue: y = bf16(acc * scale + bias[k]), the
 // scale s_x * s_w for fp8 and 1 for bf16, the bias (fp32, one per output
@@ -130,21 +135,21 @@ struct Epilogue {
         float b = 0.0f;
         if constexpr (EXTRAS)
             b = bias ? bias[k] : 0.0f;
-        uint32_t r[4];
+        float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float v = acc[e] * sc;
+            v[e] = acc[e] * sc;
             if constexpr (EXTRAS) {
                 if (bias)
-                    v += b;
-            }
-            r[e] = f32_to_bf16_rne(v);
-            if constexpr (EXTRAS) {
-                if (amax)
-                    m = max(m, r[e] & 0x7fffu);
+                    v[e] += b;
             }
         }
-        return u32x2{r[0] | (r[1] << 16), r[2] | (r[3] << 16)};
+        const u32x2 r = {bf16_pack2(v[0], v[1]), bf16_pack2(v[2], v[3])};
+        if constexpr (EXTRAS) {
+            if (amax)
+                m = max(m, max(max(r[0] & 0x7fffu, (r[0] >> 16) & 0x7fffu), max(r[1] & 0x7fffu, (r[1] >> 16) & 0x7fffu)));
+        }
+        return r;
     }
     // four outputs of channels k .. k + 3 (point output: channels are the rows)
     __device__ __attribute__((always_inline)) u32x2 four_channels(const f32x4 &acc, int k)

@@ -85,15 +85,14 @@ __device__ __attribute__((always_inline)) inline void store_tile_lds(
                 const int col = wn * WTN + b * MF + lrow;
                 const int row = wm * WTM + a * MF + 4 * lgrp;
                 const f32x4 v = quad<MF>(acc[a][b], 0);
-                uint32_t r[4];
+                float t[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float t = v[e] * sc;
+                    t[e] = v[e] * sc;
                     if constexpr (BIAS)
-                        t += p.bias[POINT ? m0 + row + e : n0 + col];  // bias of the output channel
-                    r[e] = f32_to_bf16_rne(t);
+                        t[e] += p.bias[POINT ? m0 + row + e : n0 + col];  // bias of the output channel
                 }
-                *reinterpret_cast<u32x2 *>(smem + col * CS + row * 2) = u32x2{r[0] | (r[1] << 16), r[2] | (r[3] << 16)};
+                *reinterpret_cast<u32x2 *>(smem + col * CS + row * 2) = u32x2{bf16_pack2(t[0], t[1]), bf16_pack2(t[2], t[3])};
             }
     };
     if (p.bias)

@@ -266,41 +266,54 @@ hipError_t launch_pack_x(const uint16_t *x, void *out, int64_t N, int64_t C, int
 // ------------------------------------------------------------------ filter pack
 // out[k][col], col < ldw: the element of w[k] at reduction index col in
 // (t, r, s, c) order (channel_last) or (c, t, r, s) order; zero past C*T*R*S.
+// Each thread writes one 16-byte run of a packed row (16 fp8 codes or 8 bf16
+// values; ldw is a multiple of 64, so a run never crosses a row): whole
+// 16-byte stores, as Primus-Turbo PR #399 found fp8 operand preparation to
+// need (its fp8 scatter-store coalescing commit), rather than single bytes.
 template <bool FP8>
 __global__ __launch_bounds__(256) void pack_w_kernel(const uint16_t *w, void *out, int64_t K, int64_t C, int64_t T,
                                                      int64_t R, int64_t S, int64_t ldw, bool channel_last,
                                                      const float *pair)
 {
-    const int64_t total = K * ldw;
+    constexpr int E = FP8 ? 16 : 8;  // elements per 16-byte run
+    const int64_t runs = ldw / E;     // runs per packed row
+    const int64_t total = K * runs;
     const int64_t rk = C * T * R * S;
     const int64_t taps = T * R * S;
     const float inv = FP8 ? pair[1] : 1.0f;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t k = i / ldw, col = i - k * ldw;
-        uint32_t bits = 0;
-        if (col < rk) {
-            int64_t c, tap;
-            if (channel_last) {
-                tap = col / C;
-                c = col - tap * C;
-            } else {
-                c = col / taps;
-                tap = col - c * taps;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t k = q / runs, col0 = (q - k * runs) * E;
+        uint32_t word[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int64_t col = col0 + e;
+            uint32_t bits = 0;
+            if (col < rk) {
+                int64_t c, tap;
+                if (channel_last) {
+                    tap = col / C;
+                    c = col - tap * C;
+                } else {
+                    c = col / taps;
+                    tap = col - c * taps;
+                }
+                bits = w[(k * C + c) * taps + tap];  // w[k][c][t][r][s], taps flattened (t, r, s)
             }
-            bits = w[(k * C + c) * taps + tap];  // w[k][c][t][r][s], taps flattened (t, r, s)
+            if (FP8)
+                word[e / 4] |= e4m3_rne_sat(__uint_as_float(bits << 16) * inv) << (8 * (e % 4));
+            else
+                word[e / 2] |= bits << (16 * (e % 2));
         }
-        if (FP8)
-            static_cast<uint8_t *>(out)[i] = (uint8_t)e4m3_rne_sat(__uint_as_float(bits << 16) * inv);
-        else
-            static_cast<uint16_t *>(out)[i] = (uint16_t)bits;
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<u32x4 *>(static_cast<char *>(out) + q * 16) = u32x4{word[0], word[1], word[2], word[3]};
     }
 }
 
 hipError_t launch_pack_w(const uint16_t *w, void *out, int64_t K, int64_t C, int64_t T, int64_t R, int64_t S,
                          int64_t ldw, bool channel_last, Dtype dt, const float *pair, hipStream_t stream)
 {
-    const int64_t total = K * ldw;
+    const int64_t total = K * ldw / (dt == DT_FP8 ? 16 : 8);
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536)
         blocks = 65536;

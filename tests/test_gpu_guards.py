@@ -153,10 +153,11 @@ def test_guards_fp8_integer(case):
     assert np.array_equal(P.y_values(y), ref)
 
 
+@pytest.mark.parametrize("tile", [-1, B.IGC_TILE_DMA_64])
 @pytest.mark.parametrize("layout", ["NCDHW", "NDHWC"])
-def test_guards_point_output(layout):
+def test_guards_point_output(layout, tile):
     # 130 images of 588 elements (rows only 8-byte aligned), 68 channels: the last image row ends at the margin
-    _announce(f"guards point output {layout}")
+    _announce(f"guards point output {layout} tile {tile}")
     xs, ws, st, pd, dl = (130, 3, 1, 14, 14), (68, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1)
     g = I.generator(302, P.DEV)
     x = I.int_valued(xs, -2, 2, g, P.DEV)
@@ -170,7 +171,8 @@ def test_guards_point_output(layout):
     B.conv_pack_w(w, wg.view, ws, B.IGC_BF16, lay)
     yg = Guarded((xs[0], ws[0], 1, 1, 1), torch.bfloat16, CANARY)
     yg.view.fill_(float("nan"))
-    B.conv_fwd(xg.view, wg.view, yg.view, xs, ws, st, pd, dl, B.IGC_BF16, lay)
+    with forced(tile):
+        B.conv_fwd(xg.view, wg.view, yg.view, xs, ws, st, pd, dl, B.IGC_BF16, lay)
     torch.cuda.synchronize()
     assert yg.margins_intact() and xg.margins_intact() and wg.margins_intact()
     ref = O.conv3d(P.bits(x), P.bits(w), st, pd, dl)

@@ -91,9 +91,10 @@ DMA_TILES = [B.IGC_TILE_DMA_256, B.IGC_TILE_DMA_128, B.IGC_TILE_DMA_64, B.IGC_TI
 DMA_TILES_FP8 = [B.IGC_TILE_DMA_256, B.IGC_TILE_DMA_128, B.IGC_TILE_DMA_64]
 BUF_TILES_BF16 = [B.IGC_TILE_BUF, B.IGC_TILE_BUF_AHEAD, B.IGC_TILE_BUF_PINGPONG]
 BUF_TILES_FP8 = BUF_TILES_BF16
+POINT_TILES = DMA_TILES  # bf16 point-output GEMMs
 
 
-@pytest.mark.parametrize("tile", DMA_TILES)
+@pytest.mark.parametrize("tile", POINT_TILES)
 def test_point_output_whole_tiles(tile):
     # 512 output channels over 600 images: whole tiles leave through the LDS-staged epilogue (256x192, 128x128,
     # 64x64), the image tiles past 600 and every 256x256 tile (its ring is too small to stage a tile) store directly
@@ -339,7 +340,7 @@ def test_dma_tiles_fp8(tile, case):
     P.check_close(P.y_values(y), ref, int(np.prod(ws[1:])), mx, mw, name)
 
 
-@pytest.mark.parametrize("tile", DMA_TILES)
+@pytest.mark.parametrize("tile", POINT_TILES)
 @pytest.mark.parametrize("layout", ["NCDHW", "NDHWC"])
 def test_point_output_dma_tiles(tile, layout):
     with forced(tile=tile):
@@ -349,7 +350,7 @@ def test_point_output_dma_tiles(tile, layout):
                    (0, 0, 0), (1, 1, 1), seed=9, dist=("normal", 1.0), x_layout=layout)
 
 
-@pytest.mark.parametrize("tile", DMA_TILES)
+@pytest.mark.parametrize("tile", POINT_TILES)
 def test_point_output_dma_integer_bit_exact(tile):
     _announce(f"integer point dma tile {tile}")
     with forced(tile=tile):

@@ -69,6 +69,9 @@ SPLIT_CASES = [
     # point output: image rows of 588 elements, the chunk straddling a row end belongs to the last split
     ("point_tail", (40, 3, 1, 14, 14), (68, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1), "NCDHW",
      B.IGC_TILE_DMA_64, 4),
+    # the 256x192 point tile split 3 ways (4, 4 and 2 steps; the straddling chunks in the last split)
+    ("point_256x192_split", (300, 3, 1, 14, 14), (200, 3, 1, 14, 14), (1, 14, 14), (0, 0, 0), (1, 1, 1), "NCDHW",
+     B.IGC_TILE_DMA_256x192, 3),
     # Do*Ho*Wo = 105 (scalar partial stores) and an odd element count (scalar reduction)
     ("odd_tails", (1, 16, 3, 5, 7), (25, 16, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "NDHWC", B.IGC_TILE_DMA_64, 2),
     # the 256x256 tile, many splits of a short grid
@@ -106,6 +109,7 @@ def test_split_bf16(case):
 
 
 @pytest.mark.parametrize("case", [c for c in SPLIT_CASES if c[0] in ("linear_c24", "cblock_mid_taps", "point_tail",
+                                                                       "point_256x192_split",
                                                                        "odd_tails", "cblock_c128")],
                          ids=lambda c: c[0])
 def test_split_integer_bit_exact(case):
