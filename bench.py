@@ -382,6 +382,8 @@ def main():
     ap.add_argument("--profile", action="store_true",
                     help="counter-collection run: the headline conv `steps` times, then one 1 GiB device copy "
                          "(the reference for scaling FETCH_SIZE / WRITE_SIZE); prints nothing else")
+    ap.add_argument("--profile-group-m", type=int, default=0,
+                    help="with --profile: grouped-raster height in tiles (0 = the planner's choice)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path (one process, one device).",
@@ -408,6 +410,9 @@ def main():
         args5 = (wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dil, B.IGC_BF16, B.IGC_NDHWC)
         nws = B.conv_fwd_workspace_bytes(*args5)
         wsb = torch.empty(max(nws, 16) // 4, dtype=torch.float32, device="cuda")
+        if args.profile_group_m > 0:  # a raster-height sweep: same tiles and arithmetic, another tile order
+            B.conv_debug_force(B.IGC_PATH_AUTO, -1, args.profile_group_m)
+        log(f"[bench] profile plan: {B.conv_plan_ws(*args5, max(nws, 0))}")
         for _ in range(args.steps):  # the bench's step: conv_fwd_ws with its workspace
             B.conv_fwd_ws(x, wp, y, *args5, workspace=wsb if nws > 0 else None)
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)  # 1 GiB

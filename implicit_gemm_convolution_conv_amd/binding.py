@@ -92,18 +92,29 @@ def _check(func: str, status: int) -> None:
         raise IgcError(func, status, conv_last_error())
 
 
+_ARRAY_TYPES = {(ctypes.c_int64, 5): ctypes.c_int64 * 5, (ctypes.c_int32, 3): ctypes.c_int32 * 3}
+_ARRAYS: dict = {}  # marshalled shape / stride / pad arrays by value: the C side only reads them
+
+
+def _array(ctype, v, n):
+    key = (ctype, tuple(v))
+    arr = _ARRAYS.get(key)
+    if arr is None:
+        vals = tuple(int(a) for a in v)
+        if len(vals) != n:
+            raise ValueError(f"expected {n} values, got {vals}")
+        if len(_ARRAYS) > 4096:
+            _ARRAYS.clear()
+        arr = _ARRAYS[key] = _ARRAY_TYPES[(ctype, n)](*vals)
+    return arr
+
+
 def _i64(v, n):
-    v = tuple(int(a) for a in v)
-    if len(v) != n:
-        raise ValueError(f"expected {n} values, got {v}")
-    return (ctypes.c_int64 * n)(*v)
+    return _array(ctypes.c_int64, v, n)
 
 
 def _i32(v):
-    v = tuple(int(a) for a in v)
-    if len(v) != 3:
-        raise ValueError(f"expected 3 values, got {v}")
-    return (ctypes.c_int32 * 3)(*v)
+    return _array(ctypes.c_int32, v, 3)
 
 
 def _dev(t) -> int:
