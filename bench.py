@@ -70,18 +70,46 @@ def kernel_hash():
     return h.hexdigest()[:16]
 
 
-def time_launches(fn, steps, warmup, torch, stats=None, between=None):
+_SPIN = {}
+
+
+def spin_cycles(torch, ms):
+    """Argument of torch.cuda._sleep (a bounded spin kernel) that keeps the stream busy for about `ms`."""
+    if "per_ms" not in _SPIN:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        b.synchronize()
+        _SPIN["per_ms"] = 1e6 / max(a.elapsed_time(b), 1e-3)
+    return int(_SPIN["per_ms"] * ms)
+
+
+def time_launches(fn, steps, warmup, torch, stats=None, between=None, queued=False):
     """Run fn warmup times, then `steps` times with an event pair around each call
     on the current stream (the one the library launches on). Returns (wall ms per
     step, mean event ms per call); `stats`, if a dict, also receives the median
     and minimum event ms. `between`, if given, runs before every timed call
-    outside its events (the cold-cache figure evicts the caches with it)."""
+    outside its events (the cold-cache figure evicts the caches with it).
+
+    With `queued`, a spin kernel holds the stream while the host enqueues every
+    timed call, so that no call waits for the host's launch of the next one:
+    the events then time the GPU's work alone, which is what a kernel of a few
+    microseconds needs (without it a call's events also span the host time of
+    its launch whenever the GPU had drained the queue). The wall time is then
+    not a throughput and is returned as None; stats["gap"] is the time per call
+    between the calls' event pairs (near zero when the queue never drained)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    if queued:
+        spin = spin_cycles(torch, 2.0 + 0.25 * steps)
     t0 = time.perf_counter()
+    if queued:
+        torch.cuda._sleep(spin)
     for a, b in evs:
         if between is not None:
             between()
@@ -96,7 +124,19 @@ def time_launches(fn, steps, warmup, torch, stats=None, between=None):
         stats["median"] = times[len(times) // 2] if len(times) % 2 else 0.5 * (times[len(times) // 2 - 1] +
                                                                                 times[len(times) // 2])
         stats["min"] = times[0]
-    return wall, ev
+        if queued:
+            stats["gap"] = (evs[0][0].elapsed_time(evs[-1][1]) - sum(times)) / steps
+            # and the calls back to back with one event pair around them all: the per-call time of a
+            # stream of calls, with no timestamp work between the kernels
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(spin)
+            a.record(stream)
+            for _ in range(steps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            stats["b2b"] = a.elapsed_time(b) / steps
+    return (None if queued else wall), ev
 
 
 def bench_workload(name, steps, warmup, torch, B, I, PL):
@@ -136,6 +176,12 @@ def bench_workload(name, steps, warmup, torch, B, I, PL):
         wall, ev = time_launches(step, steps, warmup, torch, st)
         res.update(ms=wall, kernel_ms=ev, kernel_ms_median=st["median"], kernel_ms_min=st["min"],
                    tflops=flops / (wall * 1e-3) / 1e12, kernel_tflops=flops / (ev * 1e-3) / 1e12)
+        if name in ("c1", "c2"):  # a few microseconds: the GPU's own time per call, with the calls queued
+            qst = {}
+            _, qev = time_launches(step, steps, warmup, torch, qst, queued=True)
+            res.update(queued_kernel_ms=qev, queued_kernel_ms_median=qst["median"], queued_kernel_ms_min=qst["min"],
+                       queued_gap_ms=qst["gap"], queued_kernel_tflops=flops / (qst["median"] * 1e-3) / 1e12,
+                       back_to_back_ms=qst["b2b"], back_to_back_tflops=flops / (qst["b2b"] * 1e-3) / 1e12)
         if name in ("c1", "c2"):  # working set fits the MALL: also with the caches evicted before every call
             scratch = torch.empty(1 << 28, dtype=torch.int16, device="cuda")  # 512 MB
             cst = {}
@@ -260,8 +306,11 @@ def bench_grad(steps, warmup, torch, B, I, PL):
     for key, fn in (("dgrad", lambda: B.conv_bwd_data(dy, wt, dx, xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NCDHW)),
                     ("wgrad", lambda: B.conv_bwd_weight(x, dy, dw, xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NCDHW,
                                                        wsb))):
-        stt, cst = {}, {}
+        stt, cst, qst = {}, {}, {}
         _, ev = time_launches(fn, steps, warmup, torch, stt)
+        time_launches(fn, steps, warmup, torch, qst, queued=True)
+        res.update({f"{key}_queued_ms_median": qst["median"], f"{key}_queued_gap_ms": qst["gap"],
+                    f"{key}_back_to_back_ms": qst["b2b"]})
         scratch = torch.empty(1 << 28, dtype=torch.int16, device="cuda")
         time_launches(fn, steps, warmup, torch, cst, between=lambda: scratch.fill_(1))
         del scratch

@@ -127,8 +127,15 @@ def _dev(t) -> int:
     return t.data_ptr()
 
 
+# torch's current stream of a device as a raw pointer; the public torch.cuda.current_stream builds a Stream
+# object on every call, which costs more host time than a small launch takes on the GPU
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream, t) -> int:
     if stream is None:
+        if _raw_stream is not None:
+            return _raw_stream(t.device.index if t.device.index is not None else torch.cuda.current_device())
         return torch.cuda.current_stream(t.device).cuda_stream
     return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
 
