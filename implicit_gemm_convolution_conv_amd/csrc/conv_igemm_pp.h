@@ -86,8 +86,9 @@ void conv_igemm_pp_kernel(ConvParams p)
     tile_coords(p, bid, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
+    // rows 8 * (wl + 4 i) + lr: r & 7 = lr, (r >> 3) & 1 = wl & 1 (lds_swizzle)
     const int lr = lane >> 3;
-    const int jc = (lane & 7) ^ (lane >> 3);
+    const int jc = (lane & 7) ^ lds_swizzle<DT>(lr | ((wl & 1) << 3));
 
     // group 1 loads activation rows, group 0 filter rows: RPI * (wl + 4 i) + lr
     ImRowsMasked<IT, MODE, ESZ> arows;  // the plan keeps T * R * S <= 32 on this kernel
@@ -137,7 +138,7 @@ void conv_igemm_pp_kernel(ConvParams p)
             acc[a][b] = AccT{};
     Frag af[HA], bf[FN];
 
-    const int lrow = lane & (MF - 1), lgrp = lane / MF, lsw = lane & 7;
+    const int lrow = lane & (MF - 1), lgrp = lane / MF, lsw = lds_swizzle<DT>(lrow);
     // Memory phase: fragments of half q of the step in slots (sa, sb).
     auto read_half = [&](int sa, int sb, int q) {
         const char *aw = as + sa * ASTAGE + (wm * WTM + lrow) * KB;
