@@ -44,7 +44,8 @@ KERNEL_SOURCES = ["implicit_gemm_convolution_conv_amd/csrc/conv_igemm.h",
                   "implicit_gemm_convolution_conv_amd/csrc/conv_buf_bf16.hip",
                   "implicit_gemm_convolution_conv_amd/csrc/splitk.hip",
                   "implicit_gemm_convolution_conv_amd/csrc/igconv_internal.h",
-                  "implicit_gemm_convolution_conv_amd/csrc/api.hip"]
+                  "implicit_gemm_convolution_conv_amd/csrc/api.hip",
+                  "implicit_gemm_convolution_conv_amd/csrc/tile_table.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv_igemm_c3_bf16_traffic.json")
 
 

@@ -4,6 +4,7 @@
 // the caller's stream. Validation finishes before the first launch, so an
 // error return leaves the stream untouched.
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <mutex>
 #include <cstdlib>
@@ -14,6 +15,7 @@
 
 #include "igconv.h"
 #include "igconv_internal.h"
+#include "tile_table.h"
 
 namespace igc {
 hipError_t launch_conv_dma_bf16(const ConvParams &p, int tile, Mode mode, bool big, bool cblock, hipStream_t stream);
@@ -256,6 +258,34 @@ int point_tile(int64_t M, int64_t Ncol, bool bf16)
     return best;
 }
 
+// Nearest swept shape (tile_table.h) of the same element size and path: distance |log2| of the ratio of
+// 256x256 tiles per CU plus |log2| of the ratio of 128-byte reduction steps, at most kSweptReach. Returns
+// its fastest tile if runs(tile), else its runner-up if runs(it), else -1.
+template <typename Runs>
+int swept_tile(int esz, int path, double tiles_per_cu, int64_t steps, Runs &&runs)
+{
+    const SweptShape *best = nullptr;
+    double bd = 0.0;
+    for (int i = 0; i < kNumSwept; ++i) {
+        const SweptShape &e = kSwept[i];
+        if (e.esz != esz || e.path != path)
+            continue;
+        const double d = std::fabs(std::log2(std::max(tiles_per_cu, 1e-6) / e.tiles_per_cu)) +
+                         std::fabs(std::log2((double)std::max<int64_t>(steps, 1) / e.steps));
+        if (!best || d < bd) {
+            best = &e;
+            bd = d;
+        }
+    }
+    if (!best || bd > kSweptReach)
+        return -1;
+    if (runs(best->tile))
+        return best->tile;
+    if (best->second >= 0 && runs(best->second))
+        return best->second;
+    return -1;
+}
+
 int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int32_t *pad, const int32_t *dil,
               int dtype, int x_layout, Plan &pl)
 {
@@ -404,6 +434,23 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
             tile = (esz == 1 && g.T * g.R * g.S <= 32 && fp8_steps >= 128)
                        ? TILE_BUF_PINGPONG
                        : (esz == 2 && path == IGC_PATH_GENERIC ? TILE_BUF_AHEAD : TILE_BUF);
+        // The measured choice replaces that rule where a swept shape is near: the winner (or, if it
+        // cannot run this shape, the runner-up) of the nearest shape of the same dtype and path in
+        // tile_table.h, which sweep.py writes from timing every tile on one GPU.
+        if (path == IGC_PATH_GENERIC || path == IGC_PATH_TEMPORAL) {
+            const int taps = (int)(g.T * g.R * g.S);
+            auto runs = [&](int t) {
+                if (t == TILE_BUF || t == TILE_BUF_AHEAD || t == TILE_BUF_PINGPONG)
+                    return buffer_ok && (t != TILE_BUF_PINGPONG || taps <= 32);
+                if (t == TILE_DMA_256x192)
+                    return esz == 2;
+                return t == TILE_DMA_256 || t == TILE_DMA_128 || t == TILE_DMA_64;
+            };
+            const int t = swept_tile(esz, path, (double)nblocks(TILE_DMA_256) / (double)cus,
+                                     (rk * esz + 127) / 128, runs);
+            if (t >= 0)
+                tile = t;
+        }
     } else {
         if (esz == 1 && tile == TILE_DMA_256x192)
             return fail(IGC_ERR_UNSUPPORTED, "tile %d is a bf16-only tile", tile);

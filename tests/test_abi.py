@@ -67,11 +67,12 @@ def test_path_selection():
     assert p["path"] == "temporal" and p["order"] == "cblock" and p["kstep"] == "128"
     assert (p["schedule"], p["tile_id"]) == ("lockstep", str(B.IGC_TILE_BUF))  # fp8, a short reduction (48 steps)
     p4 = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1), dt=B.IGC_FP8_E4M3FN)
-    assert p4["schedule"] == "pingpong" and p4["nk"] == "432"  # fp8, long reduction: ping-pong wave groups
+    # fp8, long reduction: the size rule would take the ping-pong wave groups; the swept table's winner is tile 4
+    assert (p4["schedule"], p4["tile_id"], p4["nk"]) == ("lockstep", str(B.IGC_TILE_BUF), "432")
     assert _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))["schedule"] == "lockstep"
     p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))
     assert (p["path"], p["tile"], p["grid"], p["nk"], p["stages"], p["bstages"]) == ("generic", "256x256", "6752", "864", "3", "2")
-    assert (p["loads"], p["tile_id"]) == ("buffer-lds", str(B.IGC_TILE_BUF_AHEAD))
+    assert (p["loads"], p["tile_id"]) == ("buffer-lds", str(B.IGC_TILE_BUF))  # the swept table's winner
     # beyond 2^31 bytes: each tile rebases its buffer at the first input plane it reads (4 planes = 118 MB here)
     p = _plan((1, 1024, 240, 160, 90), (1024, 1024, 3, 1, 1), pd=(1, 0, 0))
     assert (p["big"], p["loads"]) == ("1", "buffer-lds")
@@ -97,6 +98,31 @@ def test_path_selection():
     with pytest.raises(B.IgcError) as e:  # fp8 operands come from the NDHWC pack
         _plan((1, 64, 4, 6, 10), (48, 64, 1, 1, 1), dt=B.IGC_FP8_E4M3FN, lay=B.IGC_NCDHW)
     assert e.value.status == B.IGC_ERR_UNSUPPORTED
+
+
+def _swept_entries():
+    """(esz, path, tile) of every entry of the generated tile table, in the sweep's shape order."""
+    path = os.path.join(os.path.dirname(B.__file__), "csrc", "tile_table.h")
+    rows = re.findall(r"^    \{(\d+), (\d+), [0-9.]+, \d+, \d+, (\d+), ", open(path).read(), re.M)
+    return [tuple(int(v) for v in r) for r in rows]
+
+
+def test_swept_table_drives_the_plan():
+    from implicit_gemm_convolution_conv_amd import sweep as S
+    entries = _swept_entries()
+    assert len(entries) == len(S.SHAPES) and entries
+    for (esz, path, tile), (name, dtype, xs, ws, pad) in zip(entries, S.SHAPES):
+        assert esz == (1 if dtype == S.FP8 else 2), name
+        dt = B.IGC_FP8_E4M3FN if dtype == S.FP8 else B.IGC_BF16
+        p = _plan(xs, ws, pd=pad, dt=dt)
+        assert p["path"] == ("temporal" if path == S.PATH_TEMPORAL else "generic"), name
+        assert p["tile_id"] == str(tile), (name, p["tile_id"], tile)  # each swept shape plans onto its winner
+    # the c1 shape's winner (64x64 with a split reduction) and a grid of 8 large tiles' winner (128x128)
+    assert _plan((1, 64, 4, 16, 16), (64, 64, 3, 3, 3), pd=(1, 1, 1))["tile_id"] == str(B.IGC_TILE_DMA_64)
+    assert _plan((1, 256, 8, 16, 16), (256, 256, 3, 3, 3), pd=(1, 1, 1))["tile_id"] == str(B.IGC_TILE_DMA_128)
+    # beyond the table's reach the size rule decides: 3x3x3 over 16384 channels (6912 steps) on 8 tiles
+    p = _plan((1, 16384, 4, 16, 32), (256, 16384, 3, 3, 3), pd=(1, 1, 1))
+    assert p["tile_id"] == str(B.IGC_TILE_DMA_64), p
 
 
 def test_forced_path_and_tile():

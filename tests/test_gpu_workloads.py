@@ -250,8 +250,8 @@ def test_fp8_sampled(name):
     mw = float(np.abs(O.e4m3_decode(ops.ref_wq)).max()) * sw
     rng = np.random.default_rng(4)
     pts = P.sample_points(1, ws[0], *y.shape[2:], rng, n_random=600)
-    if name == "c4":  # the ping-pong tile with its tail split: 96 tiles in 2 splits
-        assert (kv["schedule"], kv["tail"]) == ("pingpong", "96/2"), plan
+    if name == "c4":  # the swept table's winner, the lockstep buffer tile, with its tail split: 96 tiles in 2 splits
+        assert (kv["schedule"], kv["tile_id"], kv["tail"]) == ("lockstep", str(B.IGC_TILE_BUF), "96/2"), plan
         y_plain = PL.output(xs, ws, wl.stride, wl.pad, wl.dil, P.DEV)
         B.conv_fwd(ops.xq, ops.wq, y_plain, xs, ws, wl.stride, wl.pad, wl.dil, B.IGC_FP8_E4M3FN, B.IGC_NDHWC,
                    ops.scales)
@@ -274,7 +274,7 @@ def test_c4_fp8_exact_full_size():
     k, c = ws[0], ws[1]
     d, h, wdt = xs[2:]
     unit = torch.ones(4, dtype=torch.float32, device=P.DEV)
-    _announce("c4 fp8 delta filter, full size, conv_fwd_ws (ping-pong tile, tail split)")
+    _announce("c4 fp8 delta filter, full size, conv_fwd_ws (tile 4, tail split)")
     xi = I.int_valued(xs, -2, 2, I.generator(40, P.DEV), P.DEV)  # NCDHW bf16
     xq = PL.packed_input(xi, "fp8", unit[0:2])
     tap = (0, 2, 1)
@@ -283,7 +283,7 @@ def test_c4_fp8_exact_full_size():
     del wd
     y = torch.full((1, k, d, h, wdt), float("nan"), dtype=torch.bfloat16, device=P.DEV)
     plan = _timed_call(xq, wq, y, wl, B.IGC_FP8_E4M3FN, unit)
-    assert (_plan_kv(plan)["schedule"], _plan_kv(plan)["tail"]) == ("pingpong", "96/2"), plan
+    assert (_plan_kv(plan)["tile_id"], _plan_kv(plan)["tail"]) == (str(B.IGC_TILE_BUF), "96/2"), plan
     xpad = torch.nn.functional.pad(xi, (1, 1, 1, 1, 1, 1))  # zero halo on D, H, W of NCDHW
     for k0 in range(0, k, 512):
         expect = xpad[:, perm[k0:k0 + 512], tap[0]:tap[0] + d, tap[1]:tap[1] + h, tap[2]:tap[2] + wdt]
