@@ -24,9 +24,10 @@ hipError_t launch_conv_dma_fp8(const ConvParams &p, int tile, Mode mode, bool bi
 hipError_t launch_conv_buf_bf16(const ConvParams &p, int tile, Mode mode, hipStream_t stream);
 hipError_t launch_conv_buf_fp8(const ConvParams &p, int tile, Mode mode, hipStream_t stream);
 
-hipError_t launch_conv(const ConvParams &p, int tile, Mode mode, Dtype dt, bool big, bool cblock,
+hipError_t launch_conv(const ConvParams &plan, int tile, Mode mode, Dtype dt, bool big, bool cblock,
                        hipStream_t stream)
 {
+    const ConvParams p = with_divisors(plan);
     if (is_pointwise_tile(tile))
         return launch_conv_pw(p, stream);
     if (is_buffer(kTiles[tile]))

@@ -64,17 +64,21 @@ __device__ inline void tile_coords(const ConvParams &p, int bid, int &tm, int &t
     const int q = nblk >> 3, r = nblk & 7;
     const int lin = xcd * q + min(xcd, r) + idx;
     const int gsz = p.group_m * p.tiles_n;
-    const int g = lin / gsz;
+    const int g = p.div_gsz.div(lin);
     const int first = g * p.group_m;
     const int rows = min(p.tiles_m - first, p.group_m);
     const int in = lin - g * gsz;
-    tm = first + in % rows;
-    tn = in / rows;
+    if (rows == p.group_m) {
+        tn = p.div_gm.div(in);
+    } else {  // the last, shorter group
+        tn = in / rows;
+    }
+    tm = first + in - tn * rows;
     if (p.tap_stride > 0) {  // temporal raster: the group's tiles one tap apart, within whole blocks
         const int blk = p.group_m * p.tap_stride;
-        if (tm < p.tiles_m / blk * blk) {
-            const int b = tm / blk, r = tm - b * blk;
-            const int gi = r / p.group_m, c = r - gi * p.group_m;  // group gi of the block, member c
+        if (tm < p.div_blk.div(p.tiles_m) * blk) {
+            const int b = p.div_blk.div(tm), r = tm - b * blk;
+            const int gi = p.div_gm.div(r), c = r - gi * p.group_m;  // group gi of the block, member c
             tm = b * blk + c * p.tap_stride + gi;
         }
     }

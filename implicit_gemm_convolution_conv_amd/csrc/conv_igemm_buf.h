@@ -49,8 +49,8 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int bytes
 template <int ESZ>
 __device__ inline int64_t tile_x_base(const ConvParams &p, int m0)
 {
-    const int nimg = m0 / p.P;
-    const int od = (m0 - nimg * p.P) / (p.Ho * p.Wo);
+    const int nimg = p.div_P.div(m0);
+    const int od = p.div_HW.div(m0 - nimg * p.P);
     const int id = min(max(0, od * p.sd - p.pd), p.D - 1);
     return ((int64_t)nimg * p.D + id) * ((int64_t)p.H * p.W) * p.C * ESZ;
 }
@@ -135,11 +135,11 @@ struct ImRows {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int m = min(first + i * stride, p.M - 1);
-            const int nimg = m / p.P;
+            const int nimg = p.div_P.div(m);
             const int sp = m - nimg * p.P;
-            const int od = sp / hw;
+            const int od = p.div_HW.div(sp);
             const int rem = sp - od * hw;
-            const int oh = rem / p.Wo;
+            const int oh = p.div_Wo.div(rem);
             const int ow = rem - oh * p.Wo;
             d[i] = od * p.sd - p.pd;
             h[i] = oh * p.sh - p.ph;

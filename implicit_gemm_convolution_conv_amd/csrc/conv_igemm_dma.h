@@ -100,7 +100,7 @@ __device__ __attribute__((always_inline)) inline void store_tile_lds(
     else
         put(std::false_type{});
     __syncthreads();
-    const int nimg = POINT ? 0 : m0 / p.P;
+    const int nimg = POINT ? 0 : p.div_P.div(m0);
     const int sp0 = POINT ? 0 : m0 - nimg * p.P;
     uint16_t *yb = static_cast<uint16_t *>(p.y);
     unsigned m = 0;
@@ -192,11 +192,11 @@ void conv_igemm_dma_kernel(ConvParams p)
         for (int i = 0; i < AIT; ++i) {
             const int m = m0 + RPI * (wave + i * NW) + lr;
             if (m < p.M) {
-                const int nimg = m / p.P;
+                const int nimg = p.div_P.div(m);
                 const int sp = m - nimg * p.P;
-                const int od = sp / hw;
+                const int od = p.div_HW.div(sp);
                 const int rem = sp - od * hw;
-                const int oh = rem / p.Wo;
+                const int oh = p.div_Wo.div(rem);
                 const int ow = rem - oh * p.Wo;
                 a_id0[i] = od * p.sd - p.pd;
                 a_ih0[i] = oh * p.sh - p.ph;

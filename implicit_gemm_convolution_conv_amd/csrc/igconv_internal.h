@@ -47,6 +47,31 @@ constexpr TileShape kTiles[kNumTiles] = {
     {512, 64, 4, 1, 16, 4, 64},       // 512 positions x 64 output channels, 32-channel steps, 4 x 36 KB
 };
 
+// Quotient by a divisor fixed for a launch, with one multiply-high instead of
+// an integer division sequence: the round-up method of Granlund and Montgomery
+// ("Division by invariant integers using multiplication", PLDI 1994). With
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1, the 33-bit factor
+// f = 2^32 + m satisfies 2^(32+l) < f * d <= 2^(32+l) + d, so for
+// 0 <= n < 2^31, n / d = floor(n * f / 2^(32+l)) = (mulhi(n, m) + n) >> l,
+// and the sum stays below 2^32.
+struct FastDiv {
+    unsigned m = 1, l = 0;  // d = 1
+
+    __host__ void set(long long d)
+    {
+        d = d < 1 ? 1 : d;
+        l = 0;
+        while ((1ll << l) < d)
+            ++l;
+        m = (unsigned)((((1ull << l) - (unsigned long long)d) << 32) / (unsigned long long)d + 1);
+    }
+    __host__ __device__ __attribute__((always_inline)) int div(int n) const
+    {
+        const unsigned hi = (unsigned)(((unsigned long long)(unsigned)n * m) >> 32);
+        return (int)((hi + (unsigned)n) >> l);
+    }
+};
+
 // Everything a conv kernel needs, passed by value as kernel arguments.
 struct ConvParams {
     const void *x;          // activations (NDHWC for im2col modes; rows of the B operand for point mode)
@@ -91,7 +116,25 @@ struct ConvParams {
     // the launch)
     const float *bias;
     unsigned *amax;
+    // divisors of the tile walk and the row decode (with_divisors fills them)
+    FastDiv div_P, div_HW, div_Wo;  // P, Ho * Wo, Wo
+    FastDiv div_gsz, div_gm;        // group_m * tiles_n, group_m
+    FastDiv div_blk;                // group_m * tap_stride (temporal raster block)
 };
+
+// p with its divisor fields set from its sizes; every launch of a kernel that
+// takes ConvParams passes the result.
+inline ConvParams with_divisors(const ConvParams &p)
+{
+    ConvParams q = p;
+    q.div_P.set(p.P);
+    q.div_HW.set((long long)p.Ho * p.Wo);
+    q.div_Wo.set(p.Wo);
+    q.div_gsz.set((long long)p.group_m * p.tiles_n);
+    q.div_gm.set(p.group_m);
+    q.div_blk.set(p.tap_stride > 0 ? (long long)p.group_m * p.tap_stride : 1);
+    return q;
+}
 
 // One launch of the implicit-GEMM kernel selected by (tile, mode, dtype,
 // 64-bit addressing, channel-block-outer reduction order).

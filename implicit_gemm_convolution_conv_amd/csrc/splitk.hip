@@ -115,7 +115,7 @@ hipError_t launch_tail_reduce(const ConvParams &p, int bm, int bn, int ntail, hi
 {
     const int quads = bm / 4 * bn;
     hipLaunchKernelGGL(tail_reduce_kernel, dim3((unsigned)((quads + 255) / 256), (unsigned)ntail), dim3(256), 0, stream,
-                       p, bm, bn);
+                       with_divisors(p), bm, bn);
     return hipGetLastError();
 }
 

@@ -404,3 +404,21 @@ def test_noalloc_rejects_a_workspace_beyond_its_scratch_before_any_launch():
     finally:
         B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)
         B.conv_debug_force_splits(0)
+
+
+def test_fast_division_matches_integer_division(tmp_path):
+    """The multiply-high division the kernels use for the tile walk and the row decode (FastDiv, the
+    round-up method of Granlund and Montgomery) against plain integer division, compiled for the host."""
+    import shutil
+    import subprocess
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    if not os.path.exists(hipcc) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc is not installed")
+    exe = tmp_path / "fastdiv_check"
+    src = os.path.join(ROOT, "tests", "fastdiv_check.cpp")
+    inc = os.path.join(ROOT, "implicit_gemm_convolution_conv_amd", "csrc")
+    subprocess.run([hipcc, "-O2", "-std=c++17", "-x", "hip", "--cuda-host-only", "-I", inc, src, "-o", str(exe)],
+                   check=True, capture_output=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert " 0 mismatches" in r.stdout
