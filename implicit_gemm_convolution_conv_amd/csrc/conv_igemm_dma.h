@@ -153,6 +153,7 @@ void conv_igemm_dma_kernel(ConvParams p)
 
     __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
+    preload_setup_params(p);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;

@@ -65,6 +65,7 @@ void conv_igemm_pp_kernel(ConvParams p)
     char *const as = smem;
     char *const bs = smem + SA * ASTAGE;
 
+    preload_setup_params(p);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

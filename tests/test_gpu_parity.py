@@ -69,6 +69,8 @@ GEOMS = [
     ("temporal_3x1x1", (2, 64, 9, 6, 7), (96, 64, 3, 1, 1), (1, 1, 1), (1, 0, 0), (1, 1, 1)),
     ("temporal_strided_dilated", (1, 32, 11, 5, 9), (48, 32, 3, 1, 1), (2, 1, 1), (2, 0, 0), (2, 1, 1)),
     ("pointwise_1x1x1", (2, 48, 3, 7, 5), (80, 48, 1, 1, 1), (1, 1, 1), (0, 0, 0), (1, 1, 1)),
+    # NDHWC 1x1x1, stride 1: the flat [N*D*H*W, C] x [C, K] GEMM, 9 row tiles and 2 column tiles, both ragged
+    ("pointwise_1x1x1_flat_multi_tile", (2, 96, 5, 17, 13), (300, 96, 1, 1, 1), (1, 1, 1), (0, 0, 0), (1, 1, 1)),
     ("odd_spatial_vec_off", (1, 16, 3, 5, 7), (24, 16, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1)),
 ]
 
