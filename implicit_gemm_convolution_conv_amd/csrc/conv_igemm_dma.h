@@ -461,19 +461,16 @@ void conv_igemm_dma_kernel(ConvParams p)
             }
         }
         if constexpr (MODE == MODE_POINT) {
-            // Point output: the next step's loads go out one by one between this step's MFMA rows
-            // (one A fragment feeds only FN MFMAs here, so their issue in front of the first row
-            // delayed it): the patch embed 22.2 -> 21.2 us back to back. The im2col tiles that use
-            // this kernel (small grids) issue first, which measured 1 % faster for them.
+            // Point output: the next step's loads go out after this step's first MFMA row rather than in
+            // front of it (one A fragment feeds few MFMAs here, and the issue delayed the first of them).
+            // Measured on the patch embed (back to back, C = 3 / 6 / 12: -1.5 / -5 / -7 %) and its
+            // backward GEMMs (equal); spreading the issue over all rows of the step instead left the last
+            // loads too little time with a two-stage ring (backward data +24 %).
             const bool more = ks + S - 1 < nk;
             const int st = (ks + S - 1) % S;
-            constexpr int LPSJ = AIT + BIT;
-            constexpr int ROWSJ = CPR / ((64 / MF) * (DT == DT_BF16 ? 1 : 2)) * FM;  // MFMA rows of a step
             compute(smem + (ks % S) * STAGE, [&](int row) __attribute__((always_inline)) {
-#pragma unroll
-                for (int j = 0; j < LPSJ; ++j)
-                    if (more && j * ROWSJ / LPSJ == row)
-                        issue_j(st, j);
+                if (more && row == 0)
+                    issue(st);
             });
             if (more && ks + S < nk)
                 advance();

@@ -40,7 +40,7 @@ constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 16, 2, 128},     // 8 waves of 128x64, 2 x 64 KB ring
     {128, 128, 2, 2, 16, 2, 128},     // 4 waves of 64x64, 2 x 32 KB ring
     {64, 64, 2, 2, 16, 4, 128},       // 4 waves of 32x32, 4 x 16 KB ring
-    {256, 192, 2, 4, 16, 2, 128},     // 8 waves of 128x48, 2 x 56 KB ring
+    {256, 192, 4, 2, 16, 2, 128},     // 8 waves of 64x96, 2 x 56 KB ring
     {256, 256, 2, 4, 16, 3, 128, 2},  // rings of 3 (activations) and 2 (filter) x 32 KB, loads over 8 of 16 MFMA rows
     {256, 256, 2, 4, 16, 3, 128, 2},
     {256, 256, 2, 4, 16, 3, 128, 2},
