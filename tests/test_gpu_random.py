@@ -1,0 +1,202 @@
+"""Seeded random geometries with integer-valued operands: whatever plan the library
+picks for a shape (path, tile, raster, split reduction, tail split), conv_fwd and
+conv_fwd_ws (with the workspace conv_fwd_workspace_bytes asks for) must reproduce
+the fp64 oracle bit for bit.
+
+x holds integers in [-2, 2] and the filter at most 128 entries of +-1 per output
+channel, so every partial sum is exact in fp32 and every output exact in bf16 (and
+the fp8 codes are exact with unit scales): an addressing, padding, tile-walk,
+division or split mistake anywhere shows up as a wrong value, not as rounding.
+
+Every case prints its geometry and the plan before it touches the GPU.
+"""
+
+import random
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from implicit_gemm_convolution_conv_amd import binding as B
+from implicit_gemm_convolution_conv_amd import inputs as I
+from oracle import oracle as O
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+MAX_MACS = 300_000_000  # keeps each oracle call well under a second on 16 threads
+
+
+def _out_dim(x, k, s, p, d):
+    return (x + 2 * p - d * (k - 1) - 1) // s + 1
+
+
+def _im2col_geometries(n, seed, channels, temporal=False):
+    """temporal: T x 1 x 1 filters with unit h/w stride and no h/w padding (the temporal path's shapes)."""
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        C = rng.choice(channels)
+        K = rng.randint(1, 300)
+        T, R, S = rng.choice([1, 2, 3]), rng.choice([1, 2, 3, 5]), rng.choice([1, 2, 3])
+        st = tuple(rng.choice([1, 1, 2]) for _ in range(3))
+        dl = tuple(rng.choice([1, 1, 1, 2]) for _ in range(3))
+        pd = tuple(rng.randint(0, k - 1) if k > 1 else 0 for k in (T, R, S))
+        if temporal:
+            T, R, S = rng.choice([2, 3, 5]), 1, 1
+            st, dl = (st[0], 1, 1), (dl[0], 1, 1)
+            pd = (rng.randint(0, T - 1), 0, 0)
+        N = rng.choice([1, 1, 2, 3])
+        big = rng.random() < 0.5  # half the cases grids of tens to hundreds of tiles
+        xs = (N, C, rng.randint(1, 9), rng.randint(1, 40 if big else 14), rng.randint(1, 40 if big else 14))
+        ws = (K, C, T, R, S)
+        od = [_out_dim(xs[2 + i], ws[2 + i], st[i], pd[i], dl[i]) for i in range(3)]
+        if min(od) < 1:
+            continue
+        if N * od[0] * od[1] * od[2] * K * C * T * R * S > MAX_MACS:
+            continue
+        out.append((xs, ws, st, pd, dl))
+    return out
+
+
+def _point_geometries(n, seed):
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        C = rng.randint(1, 6)
+        T, R, S = 1, rng.randint(2, 16), rng.randint(2, 16)
+        if (C * T * R * S) % 2:  # image rows of a multiple of 4 bytes
+            continue
+        N, K = rng.randint(1, 700), rng.randint(1, 400)
+        if N * K * C * T * R * S > MAX_MACS:
+            continue
+        layout = rng.choice(["NCDHW", "NDHWC"])
+        out.append(((N, C, T, R, S), (K, C, T, R, S), (T, R, S), (0, 0, 0), (1, 1, 1), layout))
+    return out
+
+
+# channel counts: multiples of 8 (bf16) or 16 (fp8), many of them whole 128-byte channel blocks (64 bf16, 128
+# fp8), which the buffer-addressed tiles need
+BF16 = (_im2col_geometries(80, 2026, [8, 24, 40, 64, 64, 72, 128, 128, 192, 256])
+        + _im2col_geometries(16, 2029, [8, 64, 128, 192], temporal=True))
+FP8 = _im2col_geometries(24, 2027, [16, 48, 128, 128, 256]) + _im2col_geometries(8, 2030, [16, 128, 256], temporal=True)
+POINT = _point_geometries(20, 2028)
+
+
+def _workspace(xs, ws, st, pd, dl, dt, lay):
+    nws = B.conv_fwd_workspace_bytes(xs, ws, st, pd, dl, dt, lay)
+    if nws <= 0:
+        return None
+    return torch.full((max(nws, 16) // 4,), float("nan"), dtype=torch.float32, device=P.DEV)
+
+
+class _forced_tile:
+    """For a with-block, force the first tile of `tiles`, from position `start` on (cyclically), that can run
+    the shape (IGC_PATH_AUTO keeps the path); .ok is False when none can, and nothing is forced then."""
+
+    def __init__(self, tiles, start, args):
+        self.order = [tiles[(start + i) % len(tiles)] for i in range(len(tiles))]
+        self.args, self.ok, self.tile = args, False, None
+
+    def __enter__(self):
+        for t in self.order:
+            B.conv_debug_force(B.IGC_PATH_AUTO, t, 0)
+            try:
+                self.plan = B.conv_plan(*self.args)
+                self.ok, self.tile = True, t
+                break
+            except B.IgcError:
+                B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)
+        return self
+
+    def __exit__(self, *exc):
+        B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)
+
+
+BF16_TILES = [B.IGC_TILE_DMA_256, B.IGC_TILE_DMA_128, B.IGC_TILE_DMA_64, B.IGC_TILE_DMA_256x192, B.IGC_TILE_BUF,
+              B.IGC_TILE_BUF_AHEAD, B.IGC_TILE_BUF_PINGPONG]
+FP8_TILES = [B.IGC_TILE_DMA_256, B.IGC_TILE_DMA_128, B.IGC_TILE_DMA_64, B.IGC_TILE_BUF, B.IGC_TILE_BUF_AHEAD,
+             B.IGC_TILE_BUF_PINGPONG]
+
+
+def _operands(xs, ws, seed):
+    g = I.generator(seed, P.DEV)
+    return I.int_valued(xs, -2, 2, g, P.DEV), I.sparse_ternary(ws, 128, g, P.DEV)
+
+
+@pytest.mark.parametrize("case", BF16, ids=[f"bf16_{i}" for i in range(len(BF16))])
+def test_random_bf16_bit_exact(case):
+    xs, ws, st, pd, dl = case
+    plan = B.conv_plan(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC)
+    print(f"[case] bf16 x {xs} w {ws} stride {st} pad {pd} dil {dl}: {plan}", flush=True)
+    x, w = _operands(xs, ws, seed=zlib.crc32(repr(case).encode()) % 1000)
+    ref = O.conv3d(P.bits(x), P.bits(w), st, pd, dl)
+    y = P.run_bf16(x, w, st, pd, dl)
+    assert np.array_equal(P.y_values(y), ref), "conv_fwd"
+    wsb = _workspace(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC)
+    if wsb is not None:
+        print(f"[case] ... conv_fwd_ws: {B.conv_plan_ws(xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC, wsb.numel() * 4)}",
+              flush=True)
+        y = P.run_bf16(x, w, st, pd, dl, workspace=wsb)
+        assert np.array_equal(P.y_values(y), ref), "conv_fwd_ws"
+    with _forced_tile(BF16_TILES, BF16.index(case), (xs, ws, st, pd, dl, B.IGC_BF16, B.IGC_NDHWC)) as f:
+        if f.ok:
+            print(f"[case] ... forced tile {f.tile}: {f.plan}", flush=True)
+            y = P.run_bf16(x, w, st, pd, dl)
+            assert np.array_equal(P.y_values(y), ref), f"forced tile {f.tile}"
+
+
+@pytest.mark.parametrize("case", FP8, ids=[f"fp8_{i}" for i in range(len(FP8))])
+def test_random_fp8_bit_exact(case):
+    xs, ws, st, pd, dl = case
+    plan = B.conv_plan(xs, ws, st, pd, dl, B.IGC_FP8_E4M3FN, B.IGC_NDHWC)
+    print(f"[case] fp8 x {xs} w {ws} stride {st} pad {pd} dil {dl}: {plan}", flush=True)
+    x, w = _operands(xs, ws, seed=zlib.crc32(repr(case).encode()) % 1000)
+    ones = torch.ones(4, dtype=torch.float32, device=P.DEV)  # integers |v| <= 2 are exact E4M3FN codes
+    n, c, d, h, wd = xs
+    xq = torch.empty((n, d, h, wd, c), dtype=torch.uint8, device=P.DEV)
+    B.conv_pack_x(x, xq, xs, B.IGC_FP8_E4M3FN, ones[0:2])
+    wq = torch.empty((ws[0], B.conv_packed_w_cols(ws, B.IGC_FP8_E4M3FN)), dtype=torch.uint8, device=P.DEV)
+    B.conv_pack_w(w, wq, ws, B.IGC_FP8_E4M3FN, B.IGC_NDHWC, ones[2:4])
+    ref = O.conv3d(P.bits(x), P.bits(w), st, pd, dl)
+    y = torch.empty((n, ws[0]) + B.conv_out_dims(xs, ws, st, pd, dl), dtype=torch.bfloat16, device=P.DEV)
+    B.conv_fwd(xq, wq, y, xs, ws, st, pd, dl, B.IGC_FP8_E4M3FN, B.IGC_NDHWC, ones)
+    torch.cuda.synchronize()
+    assert np.array_equal(P.y_values(y), ref), "conv_fwd"
+    wsb = _workspace(xs, ws, st, pd, dl, B.IGC_FP8_E4M3FN, B.IGC_NDHWC)
+    if wsb is not None:
+        y.fill_(float("nan"))
+        B.conv_fwd_ws(xq, wq, y, xs, ws, st, pd, dl, B.IGC_FP8_E4M3FN, B.IGC_NDHWC, ones, workspace=wsb)
+        torch.cuda.synchronize()
+        assert np.array_equal(P.y_values(y), ref), "conv_fwd_ws"
+    with _forced_tile(FP8_TILES, FP8.index(case), (xs, ws, st, pd, dl, B.IGC_FP8_E4M3FN, B.IGC_NDHWC)) as f:
+        if f.ok:
+            print(f"[case] ... forced tile {f.tile}: {f.plan}", flush=True)
+            y.fill_(float("nan"))
+            B.conv_fwd(xq, wq, y, xs, ws, st, pd, dl, B.IGC_FP8_E4M3FN, B.IGC_NDHWC, ones)
+            torch.cuda.synchronize()
+            assert np.array_equal(P.y_values(y), ref), f"forced tile {f.tile}"
+
+
+@pytest.mark.parametrize("case", POINT, ids=[f"point_{i}" for i in range(len(POINT))])
+def test_random_point_output_bit_exact(case):
+    xs, ws, st, pd, dl, layout = case
+    lay = B.IGC_NDHWC if layout == "NDHWC" else B.IGC_NCDHW
+    plan = B.conv_plan(xs, ws, st, pd, dl, B.IGC_BF16, lay)
+    print(f"[case] point x {xs} w {ws} {layout}: {plan}", flush=True)
+    x, w = _operands(xs, ws, seed=zlib.crc32(repr(case).encode()) % 1000)
+    ref = O.conv3d(P.bits(x), P.bits(w), st, pd, dl)
+    y = P.run_bf16(x, w, st, pd, dl, x_layout=layout)
+    assert np.array_equal(P.y_values(y), ref), "conv_fwd"
+    wsb = _workspace(xs, ws, st, pd, dl, B.IGC_BF16, lay)
+    if wsb is not None:
+        y = P.run_bf16(x, w, st, pd, dl, x_layout=layout, workspace=wsb)
+        assert np.array_equal(P.y_values(y), ref), "conv_fwd_ws"
+    # the global-address tiles run point output
+    with _forced_tile(BF16_TILES[:4], POINT.index(case), (xs, ws, st, pd, dl, B.IGC_BF16, lay)) as f:
+        if f.ok:
+            print(f"[case] ... forced tile {f.tile}: {f.plan}", flush=True)
+            y = P.run_bf16(x, w, st, pd, dl, x_layout=layout)
+            assert np.array_equal(P.y_values(y), ref), f"forced tile {f.tile}"
