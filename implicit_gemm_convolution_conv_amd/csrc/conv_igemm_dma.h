@@ -297,16 +297,16 @@ void conv_igemm_dma_kernel(ConvParams p)
         update_tapoff();
     };
 
-    // Instruction j of a reduction step into LDS stage st: A rows (j < AIT) then B rows.
-    auto issue_j = [&](int st, int j) __attribute__((always_inline)) {
+    // Issue one reduction step into LDS stage st: A then B, one instruction per 16-row group.
+    auto issue = [&](int st) __attribute__((always_inline)) {
         char *stage = smem + st * STAGE;
-        if (j < AIT) {
-            const int i = j;
+#pragma unroll
+        for (int i = 0; i < AIT; ++i) {
             if constexpr (MODE == MODE_POINT) {
                 const char *src = a_row[i] ? a_row[i] + (int64_t)kc * ESZ : zero;
                 __builtin_amdgcn_global_load_lds(
                     src, (__attribute__((address_space(3))) void *)(stage + RPI * (wave + i * NW) * KB), 16, 0, 0);
-                return;
+                continue;
             }
             bool ok;
             if constexpr (MODE == MODE_TEMPORAL) {
@@ -319,11 +319,10 @@ void conv_igemm_dma_kernel(ConvParams p)
             const char *src = ok ? xb + (a_base[i] + tapoff) * ESZ : zero;
             __builtin_amdgcn_global_load_lds(
                 src, (__attribute__((address_space(3))) void *)(stage + RPI * (wave + i * NW) * KB), 16, 0, 0);
-            return;
         }
         char *bst = stage + BM * KB;
-        {
-            const int i = j - AIT;
+#pragma unroll
+        for (int i = 0; i < BIT; ++i) {
             const char *src = zero;
             if constexpr (MODE == MODE_POINT) {
                 if (b_row[i] && kc + CH <= p.Rk) {
@@ -346,11 +345,6 @@ void conv_igemm_dma_kernel(ConvParams p)
             __builtin_amdgcn_global_load_lds(
                 src, (__attribute__((address_space(3))) void *)(bst + RPI * (wave + i * NW) * KB), 16, 0, 0);
         }
-    };
-    auto issue = [&](int st) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < AIT + BIT; ++j)
-            issue_j(st, j);
     };
 
     // ---------------------------------------------------------------- MFMA
