@@ -87,6 +87,45 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     return LIB
 
 
+# Host code of the planner (api.hip: validation, plans, workspace sizes, error paths) built with
+# AddressSanitizer and UndefinedBehaviorSanitizer, linked with the kernel objects of the last
+# build() (their device code is untouched: every sanitizer flag goes to the host pass only). The
+# result needs clang's ASan runtime preloaded, since the Python interpreter is not instrumented.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str | None:
+    res = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip().splitlines()[-1] if res.stdout.strip() else ""
+    if not os.path.isabs(path) or not os.path.exists(path):
+        import glob
+        found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+        path = found[-1] if found else ""
+    return path or None
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in sources() if not s.endswith("api.hip")]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError("run build() first; missing objects: " + ", ".join(missing))
+    os.makedirs(out_dir, exist_ok=True)
+    api = os.path.join(out_dir, "api_san.o")
+    flags = [f if f != "-O3" else "-O1" for f in CFLAGS] + ["-g"]
+    res = subprocess.run([HIPCC, *flags, *HOST_SANITIZE, "-c", os.path.join(CSRC, "api.hip"), "-o", api],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"sanitized compile of api.hip failed:\n{res.stderr}")
+    lib = os.path.join(out_dir, "libigconv_san.so")
+    res = subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Xarch_host", "-fsanitize=address",
+                          "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", lib, api, *objs],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{res.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)
