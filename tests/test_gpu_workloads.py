@@ -362,6 +362,58 @@ def test_c5_large_tensor():
     _free()
 
 
+def test_two_images_above_2_31_elements():
+    """N = 2 with x above 2^31 elements: the pages' large-input fix admits one image only, here each tile's buffer
+    window is rebased at the first input plane it can read, in whichever image. A 3x3x3 bf16 conv over
+    2 x 1024 x 80 x 161 x 89 activations (2.35 G elements, P % 256 = 208, so tiles straddle the two images)
+    through the conv_fwd_ws call: random operands on sampled elements on both sides of the image boundary and
+    across the 2^31-element offset, then a delta filter bit for bit over the whole output."""
+    wl = I.Workload("two images", (2, 1024, 80, 161, 89), (256, 1024, 3, 3, 3), pad=(1, 1, 1), x_layout="NDHWC",
+                    x_dist=("normal", 1.0), w_dist=("normal", 1.0 / np.sqrt(1024 * 27)), seed=9)
+    xs, ws = wl.x_shape, wl.w_shape
+    n, c, d, h, wdt = xs
+    k = ws[0]
+    _announce("two images > 2^31 elements, 3x3x3 bf16: sampled vs oracle")
+    x, w = I.make(wl, P.DEV)  # x drawn NDHWC
+    assert x.numel() > 2 ** 31
+    wp = PL.packed_weight(w, "bf16", "NDHWC")
+    y = torch.full((n, k) + tuple(B.conv_out_dims(xs, ws, wl.stride, wl.pad, wl.dil)), float("nan"),
+                   dtype=torch.bfloat16, device=P.DEV)
+    plan = _timed_call(x, wp, y, wl, B.IGC_BF16)
+    kv = _plan_kv(plan)
+    assert (kv["path"], kv["loads"], kv["big"]) == ("generic", "buffer-lds", "1"), plan
+    assert not torch.isnan(y).any()
+    rng = np.random.default_rng(9)
+    pts = P.sample_points(n, k, *y.shape[2:], rng, n_random=600, extra_d=(0, 1, d - 2, d - 1))
+    # both sides of the image boundary, in the tile that straddles it, and around element offset 2^31 of x
+    edge = [(0, int(rng.integers(0, k)), d - 1, h - 1, wdt - 1 - i) for i in range(40)]
+    edge += [(1, int(rng.integers(0, k)), 0, 0, i) for i in range(40)]
+    m31 = (2 ** 31) // c  # the input row holding element 2^31 of NDHWC x
+    for dm in range(-20, 20):
+        m = m31 + dm
+        img, sp = divmod(m, d * h * wdt)
+        edge.append((img, int(rng.integers(0, k)), sp // (h * wdt), (sp // wdt) % h, sp % wdt))
+    pts = np.concatenate([pts, np.array(edge, np.int64)])
+    xb = P.bits(x)
+    ref = O.conv3d_points(xb, P.bits(w), pts, wl.stride, wl.pad, wl.dil, x_layout="NDHWC")
+    del xb
+    P.check_close(P.gather(y, pts), ref, wl.reduction, float(x.abs().max()), float(w.abs().max()), "two images")
+
+    _announce("two images > 2^31 elements: delta filter, full size, bit-exact")
+    tap = (0, 2, 1)
+    wd, perm = _delta_filter(ws, tap, 4)
+    wpd = PL.packed_weight(wd, "bf16", "NDHWC")
+    y.fill_(float("nan"))
+    _timed_call(x, wpd, y, wl, B.IGC_BF16)
+    for img in range(n):
+        xpad = torch.nn.functional.pad(x[img:img + 1], (0, 0, 1, 1, 1, 1, 1, 1))  # zero halo on D, H, W
+        shifted = xpad[:, tap[0]:tap[0] + d, tap[1]:tap[1] + h, tap[2]:tap[2] + wdt, :]
+        expect = shifted[..., perm].permute(0, 4, 1, 2, 3).contiguous()
+        assert torch.equal(y[img:img + 1].view(torch.int16), expect.view(torch.int16)), img
+        del xpad, shifted, expect
+    _free()
+
+
 def test_pointwise_ncdhw_page_workload():
     """1x1x1 conv on 14 GB of NCDHW activations, read without a transpose: sampled positions against the oracle
     (a 1x1x1 conv of the gathered columns), then a one-hot filter that must copy channels bit for bit."""
