@@ -1055,8 +1055,8 @@ int conv_bwd_weight(const void *x, const void *dy, void *dw, const int64_t xshap
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t rk = g.C * g.T * g.R * g.S;
     // x is [N][rk] in either layout (a point-output image is rk contiguous elements), dy is [N][K]
-    if (launch_transpose_pad(static_cast<const uint16_t *>(x), xt, g.N, rk, L.ldn, st) != hipSuccess ||
-        launch_transpose_pad(static_cast<const uint16_t *>(dy), dyt, g.N, g.K, L.ldn, st) != hipSuccess)
+    if (launch_transpose_pad2(static_cast<const uint16_t *>(x), xt, rk, static_cast<const uint16_t *>(dy), dyt, g.K,
+                              g.N, L.ldn, st) != hipSuccess)
         return fail(IGC_ERR_HIP, "conv_bwd_weight: transpose launch failed");
     pl.p.x = dyt;
     pl.p.w = xt;

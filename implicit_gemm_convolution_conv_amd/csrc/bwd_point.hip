@@ -22,53 +22,88 @@ namespace igc {
 
 namespace {
 
-typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+// One operand of the transpose pass: dst[c][r] = src[r][c] for r < rows, c < cols, and dst[c][r] = 0 for
+// rows <= r < ld (ld % 64 == 0, dst 16-byte aligned); v = 8 when cols % 8 == 0 and src is 16-byte aligned,
+// 4 when cols % 4 == 0 and src is 8-byte aligned, else 1: the elements one row load takes.
+struct TransposeOp {
+    const uint16_t *src;
+    uint16_t *dst;
+    int64_t rows, cols, ld;
+    int v;
+    int blocks_x;  // workgroups along the columns: ceil(cols / 256)
+};
 
-// dst[c][r] = src[r][c] for r < rows, c < cols; dst[c][r] = 0 for rows <= r < ld.
-// One workgroup per 64 x 64 block (64 rows r of src x 64 columns c), 256 threads.
-// Loads: consecutive lanes read consecutive 4-byte pairs of one src row (EVEN:
-// cols even and src 4-byte aligned), else consecutive 2-byte elements, so each
-// wave instruction reads whole 128-byte row segments. Stores: 8 lanes per dst
-// row, 16 bytes (8 consecutive r) each; dst rows of ld elements, ld % 8 == 0,
-// dst 16-byte aligned.
-template <bool EVEN>
-__global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t *src, uint16_t *dst, int64_t rows,
-                                                            int64_t cols, int64_t ld)
+// Both operands of the backward-weights GEMM in one launch (workgroups [0, a.blocks_x * ld / 64) transpose
+// a, the rest b). Register transpose, no LDS and no barrier, as the activation pack does it: a lane reads 8 src
+// rows x 8 columns, transposes them in registers and writes 8 dst rows x 8 elements, one 16-byte store each.
+// In a wave, lanes side by side cover 8 x 8 = 64 src rows and lanes 8 apart 64 columns, so each load
+// instruction reads whole 128-byte pieces of 8 src rows (with 16-byte loads) and each store writes whole
+// 128-byte pieces of 8 dst rows; a workgroup (4 waves) covers 64 rows x 256 columns.
+__global__ __launch_bounds__(256) void transpose_pad_kernel(TransposeOp a, TransposeOp b)
 {
-    __shared__ uint16_t tile[64][66];  // [r][c]; the 66-element pitch spreads the column reads over banks
-    const int tid = threadIdx.x;
-    const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
-    if (EVEN) {
+    const int64_t na = (int64_t)a.blocks_x * (a.ld / 64);
+    const bool first = (int64_t)blockIdx.x < na;
+    const TransposeOp op = first ? a : b;
+    const int64_t blk = first ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - na;
+    const int64_t bx = blk % op.blocks_x, by = blk / op.blocks_x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t r = by * 64 + (lane & 7) * 8;                                  // this lane's 8 src rows
+    const int64_t c = (bx * 4 + wave) * 64 + (int64_t)(lane >> 3) * 8;            // and 8 columns
+    if (c >= op.cols || r >= op.ld)
+        return;
+    const int64_t rows = op.rows, cols = op.cols;
+    const int nc = cols - c < 8 ? (int)(cols - c) : 8;  // columns in range (a multiple of v when v > 1)
+    uint32_t v[8][4];  // v[i][q]: src row r + i, columns c + 2q (low half) and c + 2q + 1 (high half)
 #pragma unroll
-        for (int pass = 0; pass < 8; ++pass) {  // 8 rows per pass, 32 lanes x 2 elements per row
-            const int lr = pass * 8 + (tid >> 5), lc = (tid & 31) * 2;
-            const int64_t r = r0 + lr, c = c0 + lc;
-            uint32_t u = 0;
-            if (r < rows && c < cols)  // c even, cols even: the pair is whole
-                u = *reinterpret_cast<const uint32_t *>(src + r * cols + c);
-            *reinterpret_cast<uint32_t *>(&tile[lr][lc]) = u;
-        }
-    } else {
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
-        for (int pass = 0; pass < 16; ++pass) {  // 4 rows per pass, 64 lanes x 1 element per row
-            const int lr = pass * 4 + (tid >> 6), lc = tid & 63;
-            const int64_t r = r0 + lr, c = c0 + lc;
-            tile[lr][lc] = (r < rows && c < cols) ? src[r * cols + c] : (uint16_t)0;
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {  // 32 dst rows per pass, 8 lanes x 16 bytes per row
-        const int lc = pass * 32 + (tid >> 3), q = tid & 7;
-        const int64_t c = c0 + lc, r = r0 + 8 * q;
-        if (c >= cols || r >= ld)
+        for (int q = 0; q < 4; ++q)
+            v[i][q] = 0u;
+        if (r + i >= rows)
             continue;
-        u16x8 v;
+        const uint16_t *row = op.src + (r + i) * cols + c;
+        if (op.v == 8) {
+            const i32x4 t = *reinterpret_cast<const i32x4 *>(row);  // nc == 8: cols % 8 == 0
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            v[e] = tile[8 * q + e][lc];  // rows past `rows` were loaded as 0
-        *reinterpret_cast<u16x8 *>(dst + c * ld + r) = v;
+            for (int q = 0; q < 4; ++q)
+                v[i][q] = (uint32_t)t[q];
+        } else if (op.v == 4) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (4 * h < nc) {
+                    const uint2 t = *reinterpret_cast<const uint2 *>(row + 4 * h);
+                    v[i][2 * h] = t.x;
+                    v[i][2 * h + 1] = t.y;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t lo = 2 * q < nc ? row[2 * q] : 0u;
+                const uint32_t hi = 2 * q + 1 < nc ? row[2 * q + 1] : 0u;
+                v[i][q] = lo | (hi << 16);
+            }
+        }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (e >= nc)
+            break;
+        i32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // src rows r + 2q and r + 2q + 1 at column c + e
+            const uint32_t lo = v[2 * q][e >> 1], hi = v[2 * q + 1][e >> 1];
+            o[q] = (e & 1) ? (int)((lo >> 16) | (hi & 0xffff0000u)) : (int)((lo & 0xffffu) | (hi << 16));
+        }
+        *reinterpret_cast<i32x4 *>(op.dst + (c + e) * op.ld + r) = o;  // ld % 8 == 0, r % 8 == 0: aligned
+    }
+}
+
+TransposeOp transpose_op(const uint16_t *src, uint16_t *dst, int64_t rows, int64_t cols, int64_t ld)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src);
+    const int v = (cols % 8 == 0 && a % 16 == 0) ? 8 : (cols % 4 == 0 && a % 8 == 0) ? 4 : 1;
+    return TransposeOp{src, dst, rows, cols, ld, v, (int)((cols + 255) / 256)};
 }
 
 // w_t[j][k] = w[k][c][t][r][s] with j = ((c * T + t) * R + r) * S + s (channel-first
@@ -99,15 +134,12 @@ __global__ __launch_bounds__(256) void pack_w_t_kernel(const uint16_t *w, uint16
 
 }  // namespace
 
-hipError_t launch_transpose_pad(const uint16_t *src, uint16_t *dst, int64_t rows, int64_t cols, int64_t ld,
-                                hipStream_t stream)
+hipError_t launch_transpose_pad2(const uint16_t *src_a, uint16_t *dst_a, int64_t cols_a, const uint16_t *src_b,
+                                 uint16_t *dst_b, int64_t cols_b, int64_t rows, int64_t ld, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((ld + 63) / 64));
-    const bool even = (cols & 1) == 0 && (reinterpret_cast<uintptr_t>(src) & 3) == 0;
-    if (even)
-        hipLaunchKernelGGL(transpose_pad_kernel<true>, grid, dim3(256), 0, stream, src, dst, rows, cols, ld);
-    else
-        hipLaunchKernelGGL(transpose_pad_kernel<false>, grid, dim3(256), 0, stream, src, dst, rows, cols, ld);
+    const TransposeOp a = transpose_op(src_a, dst_a, rows, cols_a, ld), b = transpose_op(src_b, dst_b, rows, cols_b, ld);
+    const int64_t blocks = ((int64_t)a.blocks_x + b.blocks_x) * (ld / 64);
+    hipLaunchKernelGGL(transpose_pad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, b);
     return hipGetLastError();
 }
 

@@ -159,9 +159,11 @@ hipError_t launch_amax_zero(float *amax, hipStream_t stream);
 // and applies the epilogue (tiles of bm x bn).
 hipError_t launch_tail_reduce(const ConvParams &p, int bm, int bn, int ntail, hipStream_t stream);
 
-// dst[c][r] = src[r][c] (src rows of `cols` bf16), dst rows of ld >= rows elements, zero past rows
-hipError_t launch_transpose_pad(const uint16_t *src, uint16_t *dst, int64_t rows, int64_t cols, int64_t ld,
-                                hipStream_t stream);
+// dst_a[c][r] = src_a[r][c] and dst_b[c][r] = src_b[r][c] (src rows of cols_a / cols_b bf16, `rows` rows
+// each), dst rows of ld >= rows elements (ld a multiple of 64), zero past rows; one launch for both
+hipError_t launch_transpose_pad2(const uint16_t *src_a, uint16_t *dst_a, int64_t cols_a, const uint16_t *src_b,
+                                 uint16_t *dst_b, int64_t cols_b, int64_t rows, int64_t ld, hipStream_t stream);
+
 // w_t[j][k]: the filter transposed, j in the activation layout's (c, t, r, s) or (t, r, s, c) order
 hipError_t launch_pack_w_t(const uint16_t *w, uint16_t *wt, int64_t K, int64_t C, int64_t T, int64_t R, int64_t S,
                            int64_t ldk, bool channel_last, hipStream_t stream);
