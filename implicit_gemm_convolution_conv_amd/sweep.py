@@ -6,8 +6,8 @@ timed through ``conv_fwd_ws`` (with the workspace that tile's plan asks for) and
 ``csrc/tile_table.h``. ``make_plan`` then takes, for a shape it has not seen, the winner of the nearest swept
 shape of the same dtype and path, and falls back to its size rule when that tile cannot run the shape.
 
-    python -m implicit_gemm_convolution_conv_amd.sweep --json gpurun_out/tile_sweep.json   (on a GPU)
-    python -m implicit_gemm_convolution_conv_amd.sweep --from-json gpurun_out/tile_sweep.json --header \\
+    python -m implicit_gemm_convolution_conv_amd.sweep --json tile_sweep.json   (on a GPU)
+    python -m implicit_gemm_convolution_conv_amd.sweep --from-json tile_sweep.json --header \\
         implicit_gemm_convolution_conv_amd/csrc/tile_table.h                               (anywhere)
 """
 
