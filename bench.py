@@ -128,15 +128,20 @@ def time_launches(fn, steps, warmup, torch, stats=None, between=None, queued=Fal
         if queued:
             stats["gap"] = (evs[0][0].elapsed_time(evs[-1][1]) - sum(times)) / steps
             # and the calls back to back with one event pair around them all: the per-call time of a
-            # stream of calls, with no timestamp work between the kernels
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda._sleep(spin)
-            a.record(stream)
-            for _ in range(steps):
-                fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            stats["b2b"] = a.elapsed_time(b) / steps
+            # stream of calls, with no timestamp work between the kernels; nine such batches, their
+            # per-call times' mean and median
+            per_call = []
+            for _ in range(9):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(spin)
+                a.record(stream)
+                for _ in range(steps):
+                    fn()
+                b.record(stream)
+                torch.cuda.synchronize()
+                per_call.append(a.elapsed_time(b) / steps)
+            stats["b2b"] = sum(per_call) / len(per_call)
+            stats["b2b_median"] = sorted(per_call)[len(per_call) // 2]
     return (None if queued else wall), ev
 
 
@@ -182,7 +187,12 @@ def bench_workload(name, steps, warmup, torch, B, I, PL):
             _, qev = time_launches(step, steps, warmup, torch, qst, queued=True)
             res.update(queued_kernel_ms=qev, queued_kernel_ms_median=qst["median"], queued_kernel_ms_min=qst["min"],
                        queued_gap_ms=qst["gap"], queued_kernel_tflops=flops / (qst["median"] * 1e-3) / 1e12,
-                       back_to_back_ms=qst["b2b"], back_to_back_tflops=flops / (qst["b2b"] * 1e-3) / 1e12)
+                       back_to_back_ms=qst["b2b"], back_to_back_tflops=flops / (qst["b2b"] * 1e-3) / 1e12,
+                       back_to_back_ms_median=qst["b2b_median"],
+                       kernel_time_note="an event pair around a lone call adds 2-3 us of GPU-side timestamp work; "
+                                        "back_to_back_ms_median (median over 9 batches of calls issued back to "
+                                        "back, one event pair per batch) is the per-call kernel time and agrees "
+                                        "with rocprofv3's kernel durations")
         if name in ("c1", "c2"):  # working set fits the MALL: also with the caches evicted before every call
             scratch = torch.empty(1 << 28, dtype=torch.int16, device="cuda")  # 512 MB
             cst = {}
@@ -311,7 +321,7 @@ def bench_grad(steps, warmup, torch, B, I, PL):
         _, ev = time_launches(fn, steps, warmup, torch, stt)
         time_launches(fn, steps, warmup, torch, qst, queued=True)
         res.update({f"{key}_queued_ms_median": qst["median"], f"{key}_queued_gap_ms": qst["gap"],
-                    f"{key}_back_to_back_ms": qst["b2b"]})
+                    f"{key}_back_to_back_ms": qst["b2b"], f"{key}_back_to_back_ms_median": qst["b2b_median"]})
         scratch = torch.empty(1 << 28, dtype=torch.int16, device="cuda")
         time_launches(fn, steps, warmup, torch, cst, between=lambda: scratch.fill_(1))
         del scratch
