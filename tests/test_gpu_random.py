@@ -8,9 +8,11 @@ channel, so every partial sum is exact in fp32 and every output exact in bf16 (a
 the fp8 codes are exact with unit scales): an addressing, padding, tile-walk,
 division or split mistake anywhere shows up as a wrong value, not as rounding.
 
-Every case prints its geometry and the plan before it touches the GPU.
+Every case prints its geometry and the plan before it touches the GPU. IGC_RANDOM_SCALE=n in the
+environment multiplies the number of cases of every kind by n (the first cases stay the same).
 """
 
+import os
 import random
 import zlib
 
@@ -79,10 +81,12 @@ def _point_geometries(n, seed):
 
 # channel counts: multiples of 8 (bf16) or 16 (fp8), many of them whole 128-byte channel blocks (64 bf16, 128
 # fp8), which the buffer-addressed tiles need
-BF16 = (_im2col_geometries(80, 2026, [8, 24, 40, 64, 64, 72, 128, 128, 192, 256])
-        + _im2col_geometries(16, 2029, [8, 64, 128, 192], temporal=True))
-FP8 = _im2col_geometries(24, 2027, [16, 48, 128, 128, 256]) + _im2col_geometries(8, 2030, [16, 128, 256], temporal=True)
-POINT = _point_geometries(20, 2028)
+SCALE = max(1, int(os.environ.get("IGC_RANDOM_SCALE", "1")))
+BF16 = (_im2col_geometries(200 * SCALE, 2026, [8, 24, 40, 64, 64, 72, 128, 128, 192, 256])
+        + _im2col_geometries(40 * SCALE, 2029, [8, 64, 128, 192], temporal=True))
+FP8 = (_im2col_geometries(60 * SCALE, 2027, [16, 48, 128, 128, 256])
+       + _im2col_geometries(20 * SCALE, 2030, [16, 128, 256], temporal=True))
+POINT = _point_geometries(40 * SCALE, 2028)
 
 
 def _workspace(xs, ws, st, pd, dl, dt, lay):
