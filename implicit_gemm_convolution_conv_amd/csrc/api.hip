@@ -408,11 +408,12 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         return fail(IGC_ERR_UNSUPPORTED, "tile %d is the pointwise path's kernel", tile);
     const int64_t cus = device_cus();
     if (tile < 0 || tile >= kNumTiles) {
-        // Measured on MI355X: the 256x256 direct-to-LDS tile with 128-byte steps
-        // (16x16 MFMA blocks, bf16 and fp8) is the fastest whenever its grid
-        // reaches ~160 workgroups (5/8 of the CUs), the point-output GEMM of the
-        // patch embed (190 workgroups) included; smaller grids take the 128x128
-        // (two workgroups per CU) or 64x64 (4-stage ring) direct-to-LDS tiles.
+        // Size rule (the fallback where no swept shape is near). Measured on
+        // MI355X: the 256x256 direct-to-LDS tile with 128-byte steps (16x16 MFMA
+        // blocks, bf16 and fp8) is the fastest whenever its grid reaches ~160
+        // workgroups (5/8 of the CUs); smaller grids take the 128x128 (two
+        // workgroups per CU) or 64x64 (4-stage ring) direct-to-LDS tiles. The
+        // point-output path picks the tile that fills one round best.
         tile = path == IGC_PATH_POINT
                    ? point_tile(p.M, p.Ncol, esz == 2)
                    : (nblocks(TILE_DMA_256) >= cus * 5 / 8 ? TILE_DMA_256
@@ -424,13 +425,12 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         // step ahead (2 x 32 KB).
         const bool buffer_ok = path != IGC_PATH_POINT && g.C % (128 / esz) == 0 &&
                                buffer_x_span(g, esz) < 0x7ffffff0 && g.K * ldw * esz < (int64_t(1) << 31);
-        // fp8 with a long reduction takes the ping-pong wave groups (1-2 % faster than the lockstep tile on
-        // c4, 10 % slower on bf16 c3); with a short one (a 3x1x1 filter: 48 steps on c4t) they measured 4 %
-        // slower than the lockstep TILE_BUF (2.43 against 2.33 ms).
+        // In this rule fp8 with a long reduction takes the ping-pong wave groups (measured 1-2 % faster than
+        // the lockstep tile on the 3x3x3 c2048 shape before the fp8 swizzle, 10 % slower on bf16; with a
+        // 48-step 3x1x1 reduction 4 % slower: 2.43 against 2.33 ms), and bf16 on the generic path takes
+        // TILE_BUF_AHEAD. The sweep's table overrides both where it reaches: on the c2048 shapes it
+        // measured TILE_BUF ahead for both dtypes.
         const int64_t fp8_steps = g.T * g.R * g.S * (g.C / 128);
-        // bf16 on the generic path takes TILE_BUF_AHEAD (A fragments read two MFMA rows ahead, the next
-        // k-slice's B fragments read early): in alternating runs c3 34.1 against 34.5 ms and c3s 4.27 against
-        // 4.41 ms; on the temporal path TILE_BUF stays ahead (c5 17.2 against 17.7 ms).
         if (tile == TILE_DMA_256 && buffer_ok)
             tile = (esz == 1 && g.T * g.R * g.S <= 32 && fp8_steps >= 128)
                        ? TILE_BUF_PINGPONG
