@@ -158,9 +158,11 @@ IGC_API int conv_pack_w(const void *w_kctrs_bf16, void *w_packed, const int64_t 
  *  y        bf16 output, NCDHW {N, K, Do, Ho, Wo}; every element is written.
  *  scales_dev  fp8 only: device float[4] = {s_x, inv_x, s_w, inv_w} (the two
  *           conv_fp8_scales pairs); y = bf16(acc * (s_x * s_w)). NULL for bf16.
- * Output rows M = N*Do*Ho*Wo must be < 2^31; x, y above 2^31 elements are
- * addressed with 64-bit offsets. Returns IGC_ERR_UNSUPPORTED for a shape no
- * path accepts (the message says which requirement failed).
+ * y must not overlap x or w_packed. Output rows M = N*Do*Ho*Wo must be
+ * < 2^31; x and y above 2^31 elements are supported (32-bit buffer windows
+ * rebased per output tile while a tile's reach stays below 2^31 bytes,
+ * 64-bit offsets beyond). Returns IGC_ERR_UNSUPPORTED for a shape no path
+ * accepts (the message says which requirement failed).
  */
 IGC_API int conv_fwd(const void *x, const void *w_packed, void *y, const int64_t xshape[5], const int64_t wshape[5],
              const int32_t stride[3], const int32_t pad[3], const int32_t dilation[3], int dtype, int x_layout,
