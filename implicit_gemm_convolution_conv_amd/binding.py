@@ -28,6 +28,7 @@ IGC_PATH_AUTO, IGC_PATH_GENERIC, IGC_PATH_TEMPORAL, IGC_PATH_POINT, IGC_PATH_POI
 IGC_TILE_AUTO = -1
 IGC_TILE_DMA_256, IGC_TILE_DMA_128, IGC_TILE_DMA_64, IGC_TILE_DMA_256x192 = 0, 1, 2, 3
 IGC_TILE_BUF, IGC_TILE_BUF_AHEAD, IGC_TILE_BUF_PINGPONG, IGC_TILE_PW = 4, 5, 6, 7
+IGC_TILE_BUF_128 = 8
 
 EXPORTS = ("conv_out_dims", "conv_packed_w_cols", "conv_amax", "conv_fp8_scales", "conv_pack_x", "conv_pack_w",
            "conv_fwd", "conv_fwd_ws", "conv_fwd_ex", "conv_fwd_noalloc", "conv_fwd_workspace_bytes", "conv_plan", "conv_plan_ws", "conv_debug_force",

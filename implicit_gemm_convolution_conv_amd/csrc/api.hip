@@ -441,7 +441,7 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         if (path == IGC_PATH_GENERIC || path == IGC_PATH_TEMPORAL) {
             const int taps = (int)(g.T * g.R * g.S);
             auto runs = [&](int t) {
-                if (t == TILE_BUF || t == TILE_BUF_AHEAD || t == TILE_BUF_PINGPONG)
+                if (is_buffer(kTiles[t]))
                     return buffer_ok && (t != TILE_BUF_PINGPONG || taps <= 32);
                 if (t == TILE_DMA_256x192)
                     return esz == 2;
@@ -542,11 +542,11 @@ int plan_splits(Plan &pl, size_t ws_bytes)
     p.ksplit = (p.nk + splits - 1) / splits;
     p.splits = (p.nk + p.ksplit - 1) / p.ksplit;  // every split holds at least one step
     pl.ws_need = p.splits > 1 ? (int64_t)p.splits * ynum * 4 : 0;
-    // Tail split (buffer-addressed lockstep and ping-pong tiles, one 256x256 workgroup per CU):
-    // when the last round of tiles fills at most half of the CUs, its tiles run
-    // as S workgroups each over 1/S of the reduction, S = CUs / tail tiles (at
-    // most 8, at least 8 steps per split), and a second pass adds the partials;
-    // only for reductions of at least 96 steps.
+    // Tail split (buffer-addressed tiles; a round is one 256x256 workgroup per CU,
+    // or two 128x128 ones): when the last round of tiles fills at most half of
+    // the slots, its tiles run as S workgroups each over 1/S of the reduction,
+    // S = slots / tail tiles (at most 8, at least 8 steps per split), and a
+    // second pass adds the partials; only for reductions of at least 96 steps.
     // The last round then takes about 1/S of a tile's time instead of a whole
     // one. The one-GPU share of c3 (844 tiles: 3 rounds + 76) is the case this
     // is for. Needs the workspace; conv_debug_force_splits(1) turns it off.
@@ -555,7 +555,7 @@ int plan_splits(Plan &pl, size_t ws_bytes)
     if (p.splits == 1 && forced != 1 && is_buffer(kTiles[pl.tile])) {
         const TileShape &t = kTiles[pl.tile];
         const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
-        const int64_t slots = device_cus();
+        const int64_t slots = t.bm * t.bn >= 256 * 256 ? device_cus() : 2 * device_cus();
         const int64_t full = ntiles / slots * slots, r = ntiles - full;
         const int64_t S = std::min<int64_t>(std::min<int64_t>(r > 0 ? slots / r : 0, 8), p.nk / 8);
         const int64_t need = r * S * t.bm * t.bn * 4;

@@ -591,6 +591,11 @@ hipError_t launch_conv_buf_dt(const ConvParams &p, int tile, Mode mode, hipStrea
     switch (tile) {
     case TILE_BUF: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 8);
     case TILE_BUF_AHEAD: IGC_BLAUNCH(256, 256, 2, 4, 16, 3, 2, 128, 8, 2, true);
+    case TILE_BUF_128:  // loads over the step's 8 (bf16) or 4 (fp8) MFMA rows
+        if constexpr (DT == DT_FP8)
+            IGC_BLAUNCH(128, 128, 2, 2, 16, 3, 2, 128, 4);
+        else
+            IGC_BLAUNCH(128, 128, 2, 2, 16, 3, 2, 128, 8);
     default: break;
     }
     return hipErrorInvalidValue;

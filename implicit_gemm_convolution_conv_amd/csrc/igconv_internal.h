@@ -33,8 +33,9 @@ enum TileId {
     TILE_BUF_AHEAD = 5,     // as TILE_BUF, A fragments read two MFMA rows ahead: bf16 generic path
     TILE_BUF_PINGPONG = 6,  // as TILE_BUF, two wave groups alternating compute and LDS phases: long fp8 reductions
     TILE_PW = 7,            // 1x1x1 filters on NCDHW bf16 activations (conv_pw.hip)
+    TILE_BUF_128 = 8,       // buffer-addressed 128x128, two workgroups per CU: grids of about half a round
 };
-constexpr int kNumTiles = 8;
+constexpr int kNumTiles = 9;
 constexpr bool is_pointwise_tile(int t) { return t == TILE_PW; }
 constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 16, 2, 128},     // 8 waves of 128x64, 2 x 64 KB ring
@@ -45,6 +46,7 @@ constexpr TileShape kTiles[kNumTiles] = {
     {256, 256, 2, 4, 16, 3, 128, 2},
     {256, 256, 2, 4, 16, 3, 128, 2},
     {512, 64, 4, 1, 16, 4, 64},       // 512 positions x 64 output channels, 32-channel steps, 4 x 36 KB
+    {128, 128, 2, 2, 16, 3, 128, 2},  // 4 waves of 64x64, rings of 3 + 2 x 16 KB (80 KB: two per CU)
 };
 
 // Quotient by a divisor fixed for a launch, with one multiply-high instead of

@@ -55,14 +55,14 @@ SHAPES = [
 ]
 
 def candidates(dtype, tiles_per_cu, big):
-    """Tile ids (include/igconv.h) timed on a shape: the 256-wide tiles everywhere, the 128x128 and 64x64 tiles
-    on grids of under two 256x256 tiles per CU (where they can fill the GPU), the bf16-only 256x192 tile
-    where offsets stay 32-bit."""
+    """Tile ids (include/igconv.h) timed on a shape: the 256-wide tiles everywhere, the 128x128 (global-address
+    and buffer-addressed) and 64x64 tiles on grids of under two 256x256 tiles per CU (where they can fill the
+    GPU), the bf16-only 256x192 tile where offsets stay 32-bit."""
     c = [0, 4, 5, 6]
     if dtype == BF16 and not big:
         c.append(3)
     if tiles_per_cu < 2:
-        c += [1, 2]
+        c += [1, 2, 8]
     return sorted(c)
 
 

@@ -80,6 +80,7 @@ extern "C" {
 #define IGC_TILE_BUF_AHEAD 5     /* as IGC_TILE_BUF, fragments read further ahead: bf16 generic filters */
 #define IGC_TILE_BUF_PINGPONG 6  /* as IGC_TILE_BUF, two wave groups in compute / LDS phases: long fp8 reductions */
 #define IGC_TILE_PW 7            /* 1x1x1 filter on NCDHW bf16 activations */
+#define IGC_TILE_BUF_128 8       /* buffer-addressed 128x128, two workgroups per CU: grids of about half a round */
 
 /* execution path reported by conv_plan / forced by conv_debug_force */
 #define IGC_PATH_AUTO 0

@@ -158,7 +158,7 @@ def test_forced_path_and_tile():
         p = _plan((1, 64, 8, 8, 8), (64, 64, 3, 3, 3), pd=(1, 1, 1), dt=B.IGC_FP8_E4M3FN)
         assert (p["stages"], p["kstep"], p["group_m"]) == ("4", "128", "5")
         with pytest.raises(B.IgcError) as e:  # tile ids past the table
-            B.conv_debug_force(B.IGC_PATH_AUTO, B.IGC_TILE_PW + 1, 0)
+            B.conv_debug_force(B.IGC_PATH_AUTO, B.IGC_TILE_BUF_128 + 1, 0)
         assert e.value.status == B.IGC_ERR_INVALID
     finally:
         B.conv_debug_force(B.IGC_PATH_AUTO, -1, 0)

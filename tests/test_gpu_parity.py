@@ -91,7 +91,7 @@ def test_point_output_bf16(layout, k):
 
 DMA_TILES = [B.IGC_TILE_DMA_256, B.IGC_TILE_DMA_128, B.IGC_TILE_DMA_64, B.IGC_TILE_DMA_256x192]
 DMA_TILES_FP8 = [B.IGC_TILE_DMA_256, B.IGC_TILE_DMA_128, B.IGC_TILE_DMA_64]
-BUF_TILES_BF16 = [B.IGC_TILE_BUF, B.IGC_TILE_BUF_AHEAD, B.IGC_TILE_BUF_PINGPONG]
+BUF_TILES_BF16 = [B.IGC_TILE_BUF, B.IGC_TILE_BUF_AHEAD, B.IGC_TILE_BUF_PINGPONG, B.IGC_TILE_BUF_128]
 BUF_TILES_FP8 = BUF_TILES_BF16
 POINT_TILES = DMA_TILES  # bf16 point-output GEMMs
 

@@ -120,9 +120,9 @@ class _forced_tile:
 
 
 BF16_TILES = [B.IGC_TILE_DMA_256, B.IGC_TILE_DMA_128, B.IGC_TILE_DMA_64, B.IGC_TILE_DMA_256x192, B.IGC_TILE_BUF,
-              B.IGC_TILE_BUF_AHEAD, B.IGC_TILE_BUF_PINGPONG]
+              B.IGC_TILE_BUF_AHEAD, B.IGC_TILE_BUF_PINGPONG, B.IGC_TILE_BUF_128]
 FP8_TILES = [B.IGC_TILE_DMA_256, B.IGC_TILE_DMA_128, B.IGC_TILE_DMA_64, B.IGC_TILE_BUF, B.IGC_TILE_BUF_AHEAD,
-             B.IGC_TILE_BUF_PINGPONG]
+             B.IGC_TILE_BUF_PINGPONG, B.IGC_TILE_BUF_128]
 
 
 def _operands(xs, ws, seed):

@@ -321,3 +321,42 @@ def test_tail_split_needs_its_workspace():
         y_ws = P.run_bf16(x, w, st, pd, dl, workspace=wsp)
         y_plain = P.run_bf16(x, w, st, pd, dl)
     assert torch.equal(y_ws.view(torch.int16), y_plain.view(torch.int16))
+
+
+# The 128x128 buffer tile runs two workgroups per CU, so a round holds twice the CUs' tiles. 34 x 2 tiles of
+# 128 x 128 on 16 CUs (32 slots): 64 in two full rounds, 4 tail tiles in 8 splits of the 108 steps (which start
+# mid-way through a channel block's taps), for bf16 (C = 256) and fp8 (C = 512).
+TAIL_128_CASES = [
+    ("bf16", B.IGC_BF16, (1, 256, 4, 17, 64), (256, 256, 3, 3, 3), (4, 8)),
+    ("fp8", B.IGC_FP8_E4M3FN, (1, 512, 4, 17, 64), (256, 512, 3, 3, 3), (4, 8)),
+]
+
+
+@pytest.mark.parametrize("case", TAIL_128_CASES, ids=[c[0] for c in TAIL_128_CASES])
+def test_tail_split_128_tile_integer_bit_exact(case):
+    name, dt, xs, ws, want = case
+    st, pd, dl, cus = (1, 1, 1), (1, 1, 1), (1, 1, 1), 16
+    _announce(f"tail split, 128x128 buffer tile, {name}")
+    g = I.generator(99, P.DEV)
+    x = I.int_valued(xs, -2, 2, g, P.DEV)
+    w = I.sparse_ternary(ws, 128, g, P.DEV)
+    with forced(tile=B.IGC_TILE_BUF_128), capped_cus(cus):
+        nbytes = B.conv_fwd_workspace_bytes(xs, ws, st, pd, dl, dt, B.IGC_NDHWC)
+        plan = B.conv_plan_ws(xs, ws, st, pd, dl, dt, B.IGC_NDHWC, nbytes)
+        assert _tail(plan) == want, plan
+        assert nbytes == want[0] * want[1] * 128 * 128 * 4
+        wsp = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device=P.DEV)
+        if dt == B.IGC_BF16:
+            y = P.run_bf16(x, w, st, pd, dl, out=_nan_out(xs, ws, st, pd, dl), workspace=wsp)
+        else:
+            ones = torch.ones(4, dtype=torch.float32, device=P.DEV)  # integers |v| <= 2 are exact E4M3FN codes
+            n, c, d, h, wd = xs
+            xq = torch.empty((n, d, h, wd, c), dtype=torch.uint8, device=P.DEV)
+            B.conv_pack_x(x, xq, xs, dt, ones[0:2])
+            wq = torch.empty((ws[0], B.conv_packed_w_cols(ws, dt)), dtype=torch.uint8, device=P.DEV)
+            B.conv_pack_w(w, wq, ws, dt, B.IGC_NDHWC, ones[2:4])
+            y = _nan_out(xs, ws, st, pd, dl)
+            B.conv_fwd_ws(xq, wq, y, xs, ws, st, pd, dl, dt, B.IGC_NDHWC, ones, workspace=wsp)
+            torch.cuda.synchronize()
+    ref = O.conv3d(P.bits(x), P.bits(w), st, pd, dl)
+    assert np.array_equal(P.y_values(y), ref)
