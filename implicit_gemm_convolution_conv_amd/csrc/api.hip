@@ -414,10 +414,16 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         // workgroups (5/8 of the CUs); smaller grids take the 128x128 (two
         // workgroups per CU) or 64x64 (4-stage ring) direct-to-LDS tiles. The
         // point-output path picks the tile that fills one round best.
+        // A long reduction on a grid that 64x64 tiles would fill too far to split (the split needs a grid
+        // below half the CUs) but 128x128 tiles would not: 128x128 with its split. Measured (fp8 3x3x3,
+        // C1024 on 4x16x16 / C2048 on 4x8x8): 32 / 45 us against 88 / 173 us for 64x64 unsplit.
+        const int64_t steps = (rk * esz + 127) / 128;
+        const bool split128 = steps >= 64 && 2 * nblocks(TILE_DMA_64) >= cus && 2 * nblocks(TILE_DMA_128) < cus;
         tile = path == IGC_PATH_POINT
                    ? point_tile(p.M, p.Ncol, esz == 2)
-                   : (nblocks(TILE_DMA_256) >= cus * 5 / 8 ? TILE_DMA_256
-                                                           : (nblocks(TILE_DMA_128) >= cus ? TILE_DMA_128 : TILE_DMA_64));
+                   : (nblocks(TILE_DMA_256) >= cus * 5 / 8
+                          ? TILE_DMA_256
+                          : (nblocks(TILE_DMA_128) >= cus || split128 ? TILE_DMA_128 : TILE_DMA_64));
         // Where the whole-channel-block im2col order applies and each tile's
         // reach into x (and the whole packed filter) fits a 2^31-byte buffer
         // range, a buffer-addressed 256x256 tile replaces the large tile:

@@ -37,6 +37,7 @@ SHAPES = [
     ("3x3x3 C64 16x64x64 K256", BF16, (1, 64, 16, 64, 64), (256, 64, 3, 3, 3), (1, 1, 1)),
     ("3x3x3 C64 8x32x32 K128", BF16, (1, 64, 8, 32, 32), (128, 64, 3, 3, 3), (1, 1, 1)),
     ("c1 3x3x3 C64 4x16x16 K64", BF16, (1, 64, 4, 16, 16), (64, 64, 3, 3, 3), (1, 1, 1)),
+    ("3x3x3 C512 4x16x16 K512", BF16, (1, 512, 4, 16, 16), (512, 512, 3, 3, 3), (1, 1, 1)),
     ("c5 3x1x1 C1024 240x160x90 K1024", BF16, (1, 1024, 240, 160, 90), (1024, 1024, 3, 1, 1), (1, 0, 0)),
     ("c5 share 32 planes", BF16, (1, 1024, 32, 160, 90), (1024, 1024, 3, 1, 1), (0, 0, 0)),
     ("3x1x1 C2048 30x40x48 K1024", BF16, (1, 2048, 30, 40, 48), (1024, 2048, 3, 1, 1), (1, 0, 0)),
@@ -48,6 +49,7 @@ SHAPES = [
     ("3x3x3 C512 16x32x32 K512", FP8, (1, 512, 16, 32, 32), (512, 512, 3, 3, 3), (1, 1, 1)),
     ("3x3x3 C256 16x64x64 K512", FP8, (1, 256, 16, 64, 64), (512, 256, 3, 3, 3), (1, 1, 1)),
     ("3x3x3 C128 4x16x16 K128", FP8, (1, 128, 4, 16, 16), (128, 128, 3, 3, 3), (1, 1, 1)),
+    ("3x3x3 C1024 4x16x16 K512", FP8, (1, 1024, 4, 16, 16), (512, 1024, 3, 3, 3), (1, 1, 1)),
     ("c4t 3x1x1 C2048 60x80x45 K2048", FP8, (1, 2048, 60, 80, 45), (2048, 2048, 3, 1, 1), (1, 0, 0)),
     ("3x1x1 C1024 30x40x48 K1024", FP8, (1, 1024, 30, 40, 48), (1024, 1024, 3, 1, 1), (1, 0, 0)),
     ("3x1x1 C2048 8x32x64 K2048", FP8, (1, 2048, 8, 32, 64), (2048, 2048, 3, 1, 1), (1, 0, 0)),

@@ -120,8 +120,12 @@ def test_swept_table_drives_the_plan():
     # the c1 shape's winner (64x64 with a split reduction) and a grid of 8 large tiles' winner (128x128)
     assert _plan((1, 64, 4, 16, 16), (64, 64, 3, 3, 3), pd=(1, 1, 1))["tile_id"] == str(B.IGC_TILE_DMA_64)
     assert _plan((1, 256, 8, 16, 16), (256, 256, 3, 3, 3), pd=(1, 1, 1))["tile_id"] == str(B.IGC_TILE_DMA_128)
-    # beyond the table's reach the size rule decides: 3x3x3 over 16384 channels (6912 steps) on 8 tiles
+    # beyond the table's reach the size rule decides: 3x3x3 over 16384 channels (6912 steps) on 8 tiles of
+    # 256x256: 128 tiles of 64x64 would fill half the CUs, too many to split, so 128x128 with its split
     p = _plan((1, 16384, 4, 16, 32), (256, 16384, 3, 3, 3), pd=(1, 1, 1))
+    assert p["tile_id"] == str(B.IGC_TILE_DMA_128), p
+    # and a short reduction keeps 64x64: 3x3x3 over 64 channels on the same grid (27 steps)
+    p = _plan((1, 64, 4, 16, 32), (256, 64, 3, 3, 3), pd=(1, 1, 1))
     assert p["tile_id"] == str(B.IGC_TILE_DMA_64), p
 
 
