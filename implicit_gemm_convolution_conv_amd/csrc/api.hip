@@ -431,16 +431,11 @@ int make_plan(const int64_t *xs, const int64_t *ws, const int32_t *st, const int
         // step ahead (2 x 32 KB).
         const bool buffer_ok = path != IGC_PATH_POINT && g.C % (128 / esz) == 0 &&
                                buffer_x_span(g, esz) < 0x7ffffff0 && g.K * ldw * esz < (int64_t(1) << 31);
-        // In this rule fp8 with a long reduction takes the ping-pong wave groups (measured 1-2 % faster than
-        // the lockstep tile on the 3x3x3 c2048 shape before the fp8 swizzle, 10 % slower on bf16; with a
-        // 48-step 3x1x1 reduction 4 % slower: 2.43 against 2.33 ms), and bf16 on the generic path takes
-        // TILE_BUF_AHEAD. The sweep's table overrides both where it reaches: on the c2048 shapes it
-        // measured TILE_BUF ahead for both dtypes.
-        const int64_t fp8_steps = g.T * g.R * g.S * (g.C / 128);
+        // In this rule every buffer-addressable grid takes TILE_BUF: on every swept shape where the buffer
+        // tiles run, the lockstep tile was the fastest of them or within 0.3 % (the ping-pong wave groups
+        // 2-10 % slower on fp8, 10 % on bf16; TILE_BUF_AHEAD level or up to 3 % slower).
         if (tile == TILE_DMA_256 && buffer_ok)
-            tile = (esz == 1 && g.T * g.R * g.S <= 32 && fp8_steps >= 128)
-                       ? TILE_BUF_PINGPONG
-                       : (esz == 2 && path == IGC_PATH_GENERIC ? TILE_BUF_AHEAD : TILE_BUF);
+            tile = TILE_BUF;
         // The measured choice replaces that rule where a swept shape is near: the winner (or, if it
         // cannot run this shape, the runner-up) of the nearest shape of the same dtype and path in
         // tile_table.h, which sweep.py writes from timing every tile on one GPU.

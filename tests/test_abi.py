@@ -67,7 +67,7 @@ def test_path_selection():
     assert p["path"] == "temporal" and p["order"] == "cblock" and p["kstep"] == "128"
     assert (p["schedule"], p["tile_id"]) == ("lockstep", str(B.IGC_TILE_BUF))  # fp8, a short reduction (48 steps)
     p4 = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1), dt=B.IGC_FP8_E4M3FN)
-    # fp8, long reduction: the size rule would take the ping-pong wave groups; the swept table's winner is tile 4
+    # fp8, long reduction: the lockstep buffer tile (the swept table's winner and the size rule's choice)
     assert (p4["schedule"], p4["tile_id"], p4["nk"]) == ("lockstep", str(B.IGC_TILE_BUF), "432")
     assert _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))["schedule"] == "lockstep"
     p = _plan((1, 2048, 60, 80, 45), (2048, 2048, 3, 3, 3), pd=(1, 1, 1))
